@@ -1,0 +1,117 @@
+/*
+ * qkgemv.h -- C ABI of libqkgemv.so, the MI355X (gfx950) mixed k-quant GEMV.
+ *
+ * Operation.  y = dequant(W[N, K]) @ x[K, ncols] for weights stored in GGML
+ * k-quant superblocks, the format chosen per tensor by a type flag.  This is
+ * the "Mixed-Quant GEMV" of the T4 dossier's kernel prompt ("HARDWARE GROUND
+ * TRUTH: 2x NVIDIA Tesla T4 (Kaggle)", section SPEC: y[N] = dequant(W[N,K]) @
+ * x[K] with fp16 x and a tensor-type flag), widened to a few columns for the
+ * batched verification of drafted tokens that the same dossier asks for
+ * (design-doc prompt, deliverable 3, "MTP Verify Plan") and that the B70 plan
+ * ("Qwen3.6 27B Single-B70 Maximum-Speed Requirements And Execution Plan",
+ * Phase 3 item 7 "multi-row equivalents for verifier widths", Phase 4 "True
+ * Xe2 Batched Verification") builds.
+ *
+ * Dequantisation (design-doc prompt, section QUANTIZATION MIX; the other
+ * layouts per the GGML logic the kernel prompt names as the reference):
+ *   Q4_K (144 B / 256 w):  w = d * (sc * q) - dmin * m,  q 4-bit, sc/m 6-bit
+ *   Q5_K (176 B / 256 w):  the same with 5-bit q
+ *   Q6_K (210 B / 256 w):  w = d * sc * (q - 32),  q 6-bit, sc int8 per 16 w
+ * Accumulation is fp32 throughout (design-doc prompt, "PHYSICS & CONTRACT").
+ *
+ * Memory layout (all little-endian, all buffers on the device):
+ *   W  row-major superblocks: superblock s of row n starts at byte
+ *      (n * K/256 + s) * qk_block_bytes(type).  GGUF prints a projection as
+ *      [K_in, N_out]; that tensor is W[N, K] here.
+ *   x  fp16, row-major [K][ncols]  (ncols == 1: a plain vector of K halves)
+ *   y  fp32, row-major [N][ncols]
+ *
+ * Ownership.  Every pointer is owned by the caller; the library keeps no
+ * state, allocates nothing and never synchronises.  `stream` is a hipStream_t
+ * (NULL = the null stream); every call only enqueues work on it and returns.
+ * Calls are thread-safe.  Results are deterministic: the same inputs give the
+ * same bits on every call (no atomics, fixed summation order).
+ *
+ * Errors.  Arguments are checked before anything is enqueued; a bad argument
+ * returns a negative code and launches nothing.  A launch failure returns
+ * QK_ELAUNCH.  Faults inside a kernel surface at the caller's next
+ * synchronisation on the stream.  qk_strerror() names every code.
+ */
+#ifndef QKGEMV_H
+#define QKGEMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Tensor-type flag: the GGUF / GGML type ids of the three formats. */
+enum {
+    QK_Q4_K = 12,
+    QK_Q5_K = 13,
+    QK_Q6_K = 14
+};
+
+/* Return codes. */
+enum {
+    QK_OK = 0,
+    QK_EINVAL_TYPE = -1,  /* type is not one of QK_Q4_K / QK_Q5_K / QK_Q6_K        */
+    QK_EINVAL_SHAPE = -2, /* N < 1, K < 256, K % 256 != 0, ncols not in 1..8,
+                             or a size whose byte count overflows int64          */
+    QK_EINVAL_PTR = -3,   /* a NULL pointer, W or x not 16-byte aligned, or y /
+                             out not 4-byte aligned                               */
+    QK_ELAUNCH = -4       /* the HIP launch failed (message via qk_strerror)      */
+};
+
+#define QK_MAX_NCOLS 8
+
+/*
+ * qk_gemv -- y[n][c] = sum_k dequant(W)[n][k] * x[k][c], fp32 accumulation.
+ *
+ *   type   QK_Q4_K, QK_Q5_K or QK_Q6_K (one flag for the whole tensor)
+ *   W      device pointer to N rows of K/256 superblocks, 16-byte aligned
+ *   x      device pointer to K*ncols fp16 values, 16-byte aligned
+ *   y      device pointer to N*ncols fp32 values, 4-byte aligned (written)
+ *   N      rows (output features), >= 1
+ *   K      columns of W (input features), a multiple of 256
+ *   ncols  columns of x and y, 1..8: 1 is the decode GEMV, 2..8 the
+ *          few-column verify form; W is read once per call in both
+ *   stream hipStream_t to enqueue on
+ *
+ * Accuracy: |y - y_exact| <= 1e-4 * sum_k |w * x| for every (n, c), where
+ * y_exact is the f64 dot of the dequantised weights; x is never quantised.
+ */
+int qk_gemv(int type, const void *W, const void *x, void *y,
+            int64_t N, int64_t K, int ncols, void *stream);
+
+/*
+ * qk_dequant -- out[n][k] = dequant(W)[n][k] as fp32, bit-exact: for Q4_K and
+ * Q5_K the two products are exact and the subtraction is rounded once to
+ * nearest-even; Q6_K values are exact.  The check path for the unpacking the
+ * GEMV kernels use; not on the timed path.
+ *
+ *   out    device pointer to N*K fp32 values, 4-byte aligned (written)
+ *   other arguments as for qk_gemv
+ */
+int qk_dequant(int type, const void *W, void *out, int64_t N, int64_t K, void *stream);
+
+/* Bytes per 256-weight superblock: 144 / 176 / 210, or -1 for a bad type. */
+int qk_block_bytes(int type);
+
+/* Bytes per row of K weights, (K/256) * qk_block_bytes(type), or -1 for a bad
+ * type or a K that is not a positive multiple of 256. */
+int64_t qk_row_bytes(int type, int64_t K);
+
+/* Static description of a return code; for QK_ELAUNCH the HIP error text of
+ * the calling thread's last failed launch.  Never NULL. */
+const char *qk_strerror(int code);
+
+/* Library version string, e.g. "qkgemv 0.1.0 gfx950". */
+const char *qk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QKGEMV_H */

@@ -1,0 +1,120 @@
+"""ctypes binding of libqkgemv.so (declared in include/qkgemv.h).
+
+Argument marshalling only: every step of the GEMV runs in the library's HIP
+kernels.  The raw entry points keep the C names and take integer device
+addresses; ``gemv`` / ``dequant`` accept torch tensors and pass their data
+pointers and the current HIP stream.  If the library is not built, every call
+raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqkgemv.so")
+
+Q4_K, Q5_K, Q6_K = 12, 13, 14
+QK_OK, QK_EINVAL_TYPE, QK_EINVAL_SHAPE, QK_EINVAL_PTR, QK_ELAUNCH = 0, -1, -2, -3, -4
+MAX_NCOLS = 8
+
+EXPORTS = ("qk_gemv", "qk_dequant", "qk_block_bytes", "qk_row_bytes", "qk_strerror", "qk_version")
+
+
+class QKError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {qk_strerror(code)} (code {code})")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libqkgemv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run quant_dequant_gemv_amd/build.py "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(path)
+    P, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.qk_gemv.argtypes = [c_int, P, P, P, i64, i64, c_int, P]
+    lib.qk_gemv.restype = c_int
+    lib.qk_dequant.argtypes = [c_int, P, P, i64, i64, P]
+    lib.qk_dequant.restype = c_int
+    lib.qk_block_bytes.argtypes = [c_int]
+    lib.qk_block_bytes.restype = c_int
+    lib.qk_row_bytes.argtypes = [c_int, i64]
+    lib.qk_row_bytes.restype = i64
+    lib.qk_strerror.argtypes = [c_int]
+    lib.qk_strerror.restype = ctypes.c_char_p
+    lib.qk_version.argtypes = []
+    lib.qk_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------- raw C names
+
+def qk_gemv(qtype: int, W: int, x: int, y: int, N: int, K: int, ncols: int, stream: int = 0) -> int:
+    return load_library().qk_gemv(qtype, W, x, y, N, K, ncols, stream)
+
+
+def qk_dequant(qtype: int, W: int, out: int, N: int, K: int, stream: int = 0) -> int:
+    return load_library().qk_dequant(qtype, W, out, N, K, stream)
+
+
+def qk_block_bytes(qtype: int) -> int:
+    return load_library().qk_block_bytes(qtype)
+
+
+def qk_row_bytes(qtype: int, K: int) -> int:
+    return load_library().qk_row_bytes(qtype, K)
+
+
+def qk_strerror(code: int) -> str:
+    return load_library().qk_strerror(code).decode()
+
+
+def qk_version() -> str:
+    return load_library().qk_version().decode()
+
+
+# ---------------------------------------------------------------- torch helpers
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def gemv(qtype: int, W, x, N: int, K: int, out=None, stream=None):
+    """y = dequant(W) @ x on the GPU.  W: uint8 device tensor of N rows of
+    superblocks; x: float16 device tensor [K] or [K, ncols]; returns float32
+    [N, ncols] (or writes ``out``)."""
+    import torch
+    ncols = 1 if x.dim() == 1 else int(x.shape[1])
+    if out is None:
+        out = torch.empty((N, ncols), dtype=torch.float32, device=x.device)
+    if x.dtype != torch.float16 or out.dtype != torch.float32 or W.dtype != torch.uint8:
+        raise TypeError("W must be uint8, x float16, out float32")
+    if not (W.is_contiguous() and x.is_contiguous() and out.is_contiguous()):
+        raise ValueError("tensors must be contiguous")
+    rc = qk_gemv(qtype, W.data_ptr(), x.data_ptr(), out.data_ptr(), N, K, ncols, _stream_handle(stream))
+    if rc != QK_OK:
+        raise QKError(rc, "qk_gemv")
+    return out
+
+
+def dequant(qtype: int, W, N: int, K: int, out=None, stream=None):
+    """fp32 [N, K] dequantised weights on the GPU."""
+    import torch
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.float32, device=W.device)
+    rc = qk_dequant(qtype, W.data_ptr(), out.data_ptr(), N, K, _stream_handle(stream))
+    if rc != QK_OK:
+        raise QKError(rc, "qk_dequant")
+    return out

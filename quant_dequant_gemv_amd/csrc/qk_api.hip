@@ -1,0 +1,88 @@
+// qk_api.hip -- the C ABI declared in include/qkgemv.h: argument checks,
+// type x ncols dispatch, launch on the caller's stream.
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/qkgemv.h"
+#include "qk_launch.h"
+
+#ifndef QKGEMV_VERSION
+#define QKGEMV_VERSION "0.1.0"
+#endif
+
+namespace {
+
+thread_local char g_launch_msg[256] = "launch failed";
+
+int block_bytes(int type) {
+    switch (type) {
+    case QK_Q4_K: return 144;
+    case QK_Q5_K: return 176;
+    case QK_Q6_K: return 210;
+    default: return -1;
+    }
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Shared shape check.  Rows and columns must keep every byte offset inside
+// int64 and every per-launch index inside the kernels' 32-bit ranges.
+int check_shape(int type, int64_t N, int64_t K, int ncols) {
+    if (block_bytes(type) < 0) return QK_EINVAL_TYPE;
+    if (N < 1 || K < 256 || (K % 256) != 0) return QK_EINVAL_SHAPE;
+    if (ncols < 1 || ncols > QK_MAX_NCOLS) return QK_EINVAL_SHAPE;
+    if (K > (int64_t)1 << 30 || N > ((int64_t)1 << 31) - 1) return QK_EINVAL_SHAPE;
+    const int64_t row_bytes = (K / 256) * block_bytes(type);
+    if (N > INT64_MAX / row_bytes) return QK_EINVAL_SHAPE;
+    if (N > INT64_MAX / ((int64_t)K * 4)) return QK_EINVAL_SHAPE;
+    return QK_OK;
+}
+
+int launched(hipError_t e) {
+    if (e == hipSuccess) return QK_OK;
+    snprintf(g_launch_msg, sizeof g_launch_msg, "launch failed: %s", hipGetErrorString(e));
+    return QK_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qk_block_bytes(int type) { return block_bytes(type); }
+
+int64_t qk_row_bytes(int type, int64_t K) {
+    const int bb = block_bytes(type);
+    if (bb < 0 || K < 256 || (K % 256) != 0) return -1;
+    return (K / 256) * bb;
+}
+
+int qk_gemv(int type, const void *W, const void *x, void *y, int64_t N, int64_t K, int ncols, void *stream) {
+    const int rc = check_shape(type, N, K, ncols);
+    if (rc) return rc;
+    if (!W || !x || !y || !aligned(W, 16) || !aligned(x, 16) || !aligned(y, 4)) return QK_EINVAL_PTR;
+    hipStream_t st = (hipStream_t)stream;
+    if (ncols == 1) return launched(qk::launch_gemv1(type, W, x, y, N, K, st));
+    return launched(qk::launch_gemv_multi(type, W, x, y, N, K, ncols, st));
+}
+
+int qk_dequant(int type, const void *W, void *out, int64_t N, int64_t K, void *stream) {
+    const int rc = check_shape(type, N, K, 1);
+    if (rc) return rc;
+    if (!W || !out || !aligned(W, 16) || !aligned(out, 4)) return QK_EINVAL_PTR;
+    return launched(qk::launch_dequant(type, W, out, N, K, (hipStream_t)stream));
+}
+
+const char *qk_strerror(int code) {
+    switch (code) {
+    case QK_OK: return "ok";
+    case QK_EINVAL_TYPE: return "invalid type: expected QK_Q4_K (12), QK_Q5_K (13) or QK_Q6_K (14)";
+    case QK_EINVAL_SHAPE: return "invalid shape: need N >= 1, K a positive multiple of 256, 1 <= ncols <= 8";
+    case QK_EINVAL_PTR: return "invalid pointer: NULL, or W/x not 16-byte aligned, or y/out not 4-byte aligned";
+    case QK_ELAUNCH: return g_launch_msg;
+    default: return "unknown error code";
+    }
+}
+
+const char *qk_version(void) { return "qkgemv " QKGEMV_VERSION " gfx950"; }
+
+}  // extern "C"

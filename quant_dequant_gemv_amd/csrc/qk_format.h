@@ -1,0 +1,222 @@
+// qk_format.h -- gfx950 device-side decoding of GGML k-quant superblocks.
+//
+// Formats (GGML k-quant layout, the reference named by the T4 dossier's
+// "Mixed-Quant GEMV" prompt, section SPEC; the Q4_K struct and formula are in
+// its design-doc prompt, section QUANTIZATION MIX):
+//   Q4_K 144 B: d f16 @0, dmin f16 @2, scales[12] @4, qs[128] @16
+//   Q5_K 176 B: d @0, dmin @2, scales[12] @4, qh[32] @16, qs[128] @48
+//   Q6_K 210 B: ql[128] @0, qh[64] @128, scales[16] int8 @192, d f16 @208
+//
+// Work unit.  A superblock is split into 4 "units" of 64 weights, one per
+// lane; the unit index q = 0..3 is a per-lane constant in every kernel.
+//   Q4_K/Q5_K unit q : sub-blocks 2q (low nibbles of qs[32q..32q+31]) and
+//                      2q+1 (high nibbles), i.e. weights 64q .. 64q+63.
+//   Q6_K unit q=2n+b : half n, rows l = 16b..16b+15 of all four quarters t,
+//                      i.e. weights 128n + 32t + 16b + (0..15), t = 0..3.
+//
+// Quant "patterns".  Quants are turned into packed fp16 pairs without any
+// conversion instruction: a 16-bit pattern p < 2048 read as an fp16 is
+// exactly p * 2^-24 (subnormal for p < 1024, smallest exponent above).  Masks
+// pick the quant bits in place, so a pattern holds s*q for a power of two s
+// (s = 1 for bits 0..3, s = 16 for bits 4..7 of a byte); 1/s and 2^24 are
+// folded into the per-sub-block scale.  From one 32-bit word w of quant
+// bytes (l, l+1, l+2, l+3):
+//   pair A = weights (l, l+2)   from bytes 0 and 2 of w
+//   pair B = weights (l+1, l+3) from bytes 1 and 3 (w >> 8)
+// so x is kept with each group of four halves reordered to (0, 2, 1, 3).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qk {
+
+enum : int { Q4_K = 12, Q5_K = 13, Q6_K = 14 };
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+template <int T> struct Fmt;
+template <> struct Fmt<Q4_K> { static constexpr int bytes = 144; static constexpr int group = 32; };
+template <> struct Fmt<Q5_K> { static constexpr int bytes = 176; static constexpr int group = 32; };
+template <> struct Fmt<Q6_K> { static constexpr int bytes = 210; static constexpr int group = 16; };
+
+// fp32 += a.lo*b.lo + a.hi*b.hi with fp16 operands (v_dot2_f32_f16).
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t v) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t v) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
+
+// Weight loads.  NT selects the nontemporal (streaming) form: every weight
+// byte is read once per call, so there is nothing to keep in the caches.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const uint8_t *p) {
+    if constexpr (NT) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+        return *reinterpret_cast<const uint4 *>(p);
+    }
+}
+template <bool NT>
+__device__ __forceinline__ uint2 ld8(const uint8_t *p) {
+    if constexpr (NT) {
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+        return make_uint2(v.x, v.y);
+    } else {
+        return *reinterpret_cast<const uint2 *>(p);
+    }
+}
+template <bool NT>
+__device__ __forceinline__ uint32_t ld2(const uint8_t *p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
+    else return *reinterpret_cast<const uint16_t *>(p);
+}
+
+__device__ __forceinline__ uint32_t word(const uint4 &v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// ---------------------------------------------------------------------------
+// Q4_K / Q5_K 6-bit scales and mins of the unit's two sub-blocks (2q, 2q+1).
+// scales[12] as three words S0 = bytes 0..3, S1 = 4..7, S2 = 8..11:
+//   j < 4 : sc_j = byte j of S0 & 63,  m_j = byte j of S1 & 63
+//   j >= 4: sc_j = nibble lo of byte j-4 of S2 | (bits 6..7 of byte j-4 of S0) << 4
+//           m_j  = nibble hi of byte j-4 of S2 | (bits 6..7 of byte j-4 of S1) << 4
+// Both sub-blocks of a unit sit in adjacent bytes, so one per-lane shift and
+// a per-lane set of masks covers all four units without branching.
+// ---------------------------------------------------------------------------
+struct KScaleSel {
+    // per-lane bit offsets / widths: for q < 2 the fields are 6-bit bytes of
+    // S0 (sc) and S1 (m); for q >= 2 a nibble of S2 plus 2 bits of S0 / S1.
+    uint32_t o, wn, o2, w2, sl;
+    __device__ explicit KScaleSel(int q) {
+        const bool hi = q >= 2;
+        o = 16u * (uint32_t)(q & 1);  // bit offset of byte j (j = 2q or 2q-4) in its word
+        wn = hi ? 4u : 0u;            // nibble width taken from S2 (0: none)
+        o2 = o + (hi ? 6u : 0u);      // offset of the bits taken from S0 / S1
+        w2 = hi ? 2u : 6u;
+        sl = hi ? 4u : 0u;            // where those bits land
+    }
+};
+
+struct KScales { uint32_t sc_lo, sc_hi, m_lo, m_hi; };
+
+__device__ __forceinline__ uint32_t bfe(uint32_t v, uint32_t off, uint32_t w) {
+    return __builtin_amdgcn_ubfe(v, off, w);
+}
+
+__device__ __forceinline__ KScales k_scales(const uint4 &hdr, const KScaleSel &s) {
+    const uint32_t S0 = hdr.y, S1 = hdr.z, S2 = hdr.w;
+    KScales r;
+    r.sc_lo = bfe(S2, s.o, s.wn) | (bfe(S0, s.o2, s.w2) << s.sl);
+    r.sc_hi = bfe(S2, s.o + 8, s.wn) | (bfe(S0, s.o2 + 8, s.w2) << s.sl);
+    r.m_lo = bfe(S2, s.o + 4, s.wn) | (bfe(S1, s.o2, s.w2) << s.sl);
+    r.m_hi = bfe(S2, s.o + 12, s.wn) | (bfe(S1, s.o2 + 8, s.w2) << s.sl);
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Raw registers of one unit and its pattern decoder.
+// ---------------------------------------------------------------------------
+template <int T> struct Unit;
+
+// Q4_K: the 16-byte header and the unit's 32 bytes of qs.  The four lanes of
+// a superblock load the same header (one cache line, served once).
+// Patterns of qs word i (l = 4i):
+//   p[0] = low-sub-block pair A  (s = 1)    p[1] = low pair B  (s = 1)
+//   p[2] = high-sub-block pair A (s = 16)   p[3] = high pair B (s = 16)
+template <> struct Unit<Q4_K> {
+    uint4 h, a, b;
+    template <bool NT>
+    __device__ __forceinline__ void load(const uint8_t *sb, int q) {
+        h = ld16<NT>(sb);
+        a = ld16<NT>(sb + 16 + 32 * q);
+        b = ld16<NT>(sb + 32 + 32 * q);
+    }
+    __device__ __forceinline__ uint4 header() const { return h; }
+    __device__ __forceinline__ uint32_t qword(int i) const { return i < 4 ? word(a, i) : word(b, i - 4); }
+    __device__ __forceinline__ void patterns(int i, int /*q*/, uint32_t p[4]) const {
+        const uint32_t w = qword(i), t = w >> 8;
+        p[0] = w & 0x000f000fu;
+        p[1] = t & 0x000f000fu;
+        p[2] = w & 0x00f000f0u;
+        p[3] = t & 0x00f000f0u;
+    }
+};
+
+// Q5_K: as Q4_K plus the high-bit plane qh[32]; bit j of qh[l] is bit 4 of the
+// quant of weight 32j + l.  For unit q the two bits of interest of each qh
+// byte are bits 2q (low sub-block) and 2q+1 (high sub-block).
+template <> struct Unit<Q5_K> {
+    uint4 h, qh0, qh1, a, b;
+    template <bool NT>
+    __device__ __forceinline__ void load(const uint8_t *sb, int q) {
+        h = ld16<NT>(sb);
+        qh0 = ld16<NT>(sb + 16);
+        qh1 = ld16<NT>(sb + 32);
+        a = ld16<NT>(sb + 48 + 32 * q);
+        b = ld16<NT>(sb + 64 + 32 * q);
+    }
+    __device__ __forceinline__ uint4 header() const { return h; }
+    __device__ __forceinline__ uint32_t qword(int i) const { return i < 4 ? word(a, i) : word(b, i - 4); }
+    __device__ __forceinline__ uint32_t hword(int i) const { return i < 4 ? word(qh0, i) : word(qh1, i - 4); }
+    __device__ __forceinline__ void patterns(int i, int q, uint32_t p[4]) const {
+        const uint32_t w = qword(i), t = w >> 8;
+        const uint32_t H = hword(i) >> (2 * q);  // bit 0 / bit 1 of each byte: low / high sub-block
+        p[0] = (w & 0x000f000fu) | ((H << 4) & 0x00100010u);
+        p[1] = (t & 0x000f000fu) | ((H >> 4) & 0x00100010u);
+        p[2] = (w & 0x00f000f0u) | ((H << 7) & 0x01000100u);
+        p[3] = (t & 0x00f000f0u) | ((H >> 1) & 0x01000100u);
+    }
+};
+
+// Q6_K unit q = 2n + b.  A = ql[64n + 16b ..] (quarters 0 low / 2 high nibble),
+// B = ql[64n + 32 + 16b ..] (quarters 1 / 3), C = qh[32n + 16b ..] (2 bits per
+// quarter: bits 2t..2t+1).  Superblocks are 2-byte aligned only; these are
+// unaligned 16-byte loads, which the HSA unaligned access mode allows.
+// Patterns of word i (rows l = 16b + 4i ..):
+//   p[2t] = quarter t pair A, p[2t+1] = quarter t pair B;  s = 1 for t < 2, 16 for t >= 2.
+template <> struct Unit<Q6_K> {
+    uint4 a, b, c;
+    uint2 sc;      // scales[8n .. 8n+7]
+    uint32_t d;    // fp16 d in the low half
+    template <bool NT>
+    __device__ __forceinline__ void load(const uint8_t *sb, int q) {
+        const int n = q >> 1, bb = q & 1;
+        a = ld16<NT>(sb + 64 * n + 16 * bb);
+        b = ld16<NT>(sb + 64 * n + 32 + 16 * bb);
+        c = ld16<NT>(sb + 128 + 32 * n + 16 * bb);
+        sc = ld8<NT>(sb + 192 + 8 * n);
+        d = ld2<NT>(sb + 208);
+    }
+    __device__ __forceinline__ void patterns(int i, int /*q*/, uint32_t p[8]) const {
+        const uint32_t A = word(a, i), B = word(b, i), C = word(c, i);
+        const uint32_t c4 = C << 4, c2 = C << 2;
+        const uint32_t A8 = A >> 8, B8 = B >> 8, c4b = C >> 4, c2b = C >> 6;
+        p[0] = (A & 0x000f000fu) | (c4 & 0x00300030u);
+        p[1] = (A8 & 0x000f000fu) | (c4b & 0x00300030u);
+        p[2] = (B & 0x000f000fu) | (c2 & 0x00300030u);
+        p[3] = (B8 & 0x000f000fu) | (c2b & 0x00300030u);
+        p[4] = (A & 0x00f000f0u) | (c4 & 0x03000300u);
+        p[5] = (A8 & 0x00f000f0u) | (c4b & 0x03000300u);
+        p[6] = (B & 0x00f000f0u) | (c2 & 0x03000300u);
+        p[7] = (B8 & 0x00f000f0u) | (c2b & 0x03000300u);
+    }
+    // signed scale of quarter t for this unit (b = q & 1): scales[8n + 2t + b]
+    __device__ __forceinline__ int scale(int t, int q) const {
+        const int idx = 2 * t + (q & 1);
+        const uint32_t wv = idx < 4 ? sc.x : sc.y;
+        return (int)(int8_t)(uint8_t)(wv >> (8 * (idx & 3)));
+    }
+};
+
+}  // namespace qk

@@ -1,0 +1,357 @@
+// qk_kernels.hip -- gfx950 kernels of the k-quant GEMV and their launchers.
+//
+// gemv1_kernel : y = dequant(W) @ x for one column, the decode GEMV of the T4
+//                dossier's "Mixed-Quant GEMV" prompt (section SPEC).  Every
+//                weight byte is read from HBM once, with 16-byte loads
+//                (HARD CONSTRAINTS: 128-bit loads); quants are unpacked in
+//                registers and dotted with x by v_dot2_f32_f16 into fp32
+//                accumulators (design-doc prompt, PHYSICS & CONTRACT: fp32
+//                accumulation; fp16x2 is fine for the GEMV).  x is not
+//                quantised.
+// dequant_kernel: the same unit loads and unpacking, writing fp32 weights --
+//                the bit-exact check path.
+//
+// Factored form.  For a Q4_K/Q5_K sub-block j of 32 weights,
+//     sum_i w_i x_i = d*sc_j * sum_i q_i x_i  -  dmin*m_j * sum_i x_i ,
+// and for a Q6_K group g of 16 weights,
+//     sum_i w_i x_i = d*sc_g * (sum_i q_i x_i - 32 * sum_i x_i).
+// The group sums of x are formed once per lane (x stays in registers), so
+// the per-weight work is the quant unpack and one half of a dot2.
+#include "qk_format.h"
+#include "qk_launch.h"
+
+namespace qk {
+
+constexpr int WG = 256;  // threads per workgroup
+
+// ---------------------------------------------------------------------------
+// x held in registers.  A lane works on one fixed 64-weight unit column u of
+// K for every row it visits, so it loads the 64 x values of that unit once,
+// as 32 dwords of fp16 pairs in the order the quant patterns produce:
+//   Q4_K/Q5_K: xr[2i], xr[2i+1]      = pairs A, B of qs word i, low sub-block
+//              xr[16+2i], xr[17+2i]  = the same for the high sub-block
+//              (pair A = weights (4i, 4i+2), pair B = (4i+1, 4i+3))
+//   Q6_K:      xr[8t+2i], xr[8t+2i+1] = pairs A, B of word i of quarter t
+// plus the fp32 sums of x per scale group (fixed summation order):
+//   Q4_K/Q5_K: xsum[0..1] per sub-block;  Q6_K: xsum[0..3] per quarter.
+// ---------------------------------------------------------------------------
+template <int T>
+struct XReg {
+    uint32_t xr[32];
+    float xsum[4];
+};
+
+// Sixteen consecutive halves (two 16-byte vectors) -> 8 pair dwords + fp32 sum.
+__device__ __forceinline__ float x_pairs16(const uint4 &v0, const uint4 &v1, uint32_t *o) {
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // group j = halves 4j .. 4j+3 = words w[2j], w[2j+1]
+        o[2 * j] = (w[2 * j] & 0xffffu) | (w[2 * j + 1] << 16);            // (0, 2)
+        o[2 * j + 1] = (w[2 * j] >> 16) | (w[2 * j + 1] & 0xffff0000u);    // (1, 3)
+        s += (f16_lo(w[2 * j]) + f16_hi(w[2 * j])) + (f16_lo(w[2 * j + 1]) + f16_hi(w[2 * j + 1]));
+    }
+    return s;
+}
+
+// Load the x of unit u (superblock s = u/4, q = u%4) of a row.
+template <int T>
+__device__ __forceinline__ void load_x(XReg<T> &X, const uint16_t *__restrict__ x, int u) {
+    const uint4 *xv = reinterpret_cast<const uint4 *>(x);  // 8 halves per vector
+    if constexpr (T == Q6_K) {
+        const int s = u >> 2, n = (u >> 1) & 1, b = u & 1;
+        uint4 v[8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int k = 256 * s + 128 * n + 32 * t + 16 * b;  // first weight of quarter t
+            v[2 * t] = xv[k >> 3];
+            v[2 * t + 1] = xv[(k >> 3) + 1];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) X.xsum[t] = x_pairs16(v[2 * t], v[2 * t + 1], X.xr + 8 * t);
+    } else {
+        uint4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = xv[8 * u + j];  // weights 64u .. 64u+63
+        const float s0 = x_pairs16(v[0], v[1], X.xr + 0);
+        const float s1 = x_pairs16(v[2], v[3], X.xr + 8);
+        const float s2 = x_pairs16(v[4], v[5], X.xr + 16);
+        const float s3 = x_pairs16(v[6], v[7], X.xr + 24);
+        X.xsum[0] = s0 + s1;
+        X.xsum[1] = s2 + s3;
+    }
+}
+
+// Dot of one unit with the register-held x of the same unit column.
+template <int T>
+__device__ __forceinline__ float unit_dot(const Unit<T> &U, int q, const KScaleSel &sel, const XReg<T> &X) {
+    float aL = 0.f, aH = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t p[4];
+        U.patterns(i, q, p);
+        aL = dot2(p[0], X.xr[2 * i], aL);
+        aL = dot2(p[1], X.xr[2 * i + 1], aL);
+        aH = dot2(p[2], X.xr[16 + 2 * i], aH);
+        aH = dot2(p[3], X.xr[17 + 2 * i], aH);
+    }
+    const uint4 h = U.header();
+    const KScales s = k_scales(h, sel);
+    const float d = f16_lo(h.x), dmin = f16_hi(h.x);
+    // patterns hold q * 2^-24 (low sub-block) and 16q * 2^-24 (high)
+    const float fl = d * (float)s.sc_lo * 0x1p24f;
+    const float fh = d * (float)s.sc_hi * 0x1p20f;
+    return fl * aL + fh * aH - dmin * ((float)s.m_lo * X.xsum[0] + (float)s.m_hi * X.xsum[1]);
+}
+
+template <>
+__device__ __forceinline__ float unit_dot<Q6_K>(const Unit<Q6_K> &U, int q, const KScaleSel &, const XReg<Q6_K> &X) {
+    float R[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t p[8];
+        U.patterns(i, q, p);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            R[t] = dot2(p[2 * t], X.xr[8 * t + 2 * i], R[t]);
+            R[t] = dot2(p[2 * t + 1], X.xr[8 * t + 2 * i + 1], R[t]);
+        }
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const float k = t < 2 ? 0x1p24f : 0x1p20f;  // patterns hold s*q*2^-24, s = 1 or 16
+        acc += (float)U.scale(t, q) * (R[t] * k - 32.f * X.xsum[t]);
+    }
+    return f16_lo(U.d) * acc;
+}
+
+// ---------------------------------------------------------------------------
+// One column, x-stationary and row-balanced.
+//
+// Workgroup b owns the contiguous rows [b*N/G, (b+1)*N/G) (G = gridDim.x), so
+// every workgroup streams the same number of bytes to within one row.  K is
+// walked in segments of at most `useg` units.  Inside a segment lane
+// t < P*useg owns unit column uc = t % useg and row phase ph = t / useg: it
+// holds x of that unit in registers and visits rows r0+ph, r0+ph+P, ... ; a
+// wave therefore reads up to 16 consecutive superblocks of one row per load.
+// The lane's rows are streamed through a ring of D unit buffers (the math on
+// one row overlaps the loads of the next D).  Loads are unconditional, with
+// addresses clamped into the tensor past the end, so that the compiler keeps
+// exact counts of the loads in flight.  Each unit's partial sum goes to LDS;
+// at the end every row's partials are added in a fixed order.
+// ---------------------------------------------------------------------------
+template <int T, int D, bool NT>
+__global__ void __launch_bounds__(512, 4) gemv1_kernel(const uint8_t *__restrict__ W,
+                                                   const uint16_t *__restrict__ x,
+                                                   float *__restrict__ y, int N, int K, int useg, int P) {
+    extern __shared__ __attribute__((aligned(16))) float part[];  // [rows of this wg][useg]
+    constexpr int BB = Fmt<T>::bytes;
+    const int tid = (int)threadIdx.x;
+    const int r0 = (int)((int64_t)blockIdx.x * N / gridDim.x);
+    const int r1 = (int)((int64_t)(blockIdx.x + 1) * N / gridDim.x);
+    const int R = r1 - r0;
+    const int U = K >> 6;
+    const size_t row_bytes = (size_t)(K >> 8) * BB;
+    const int ph = tid / useg, uc = tid - ph * useg;
+    const bool lane_ok = ph < P;
+    const int rows_lane = (R + P - 1) / P;  // same schedule for every lane
+
+    for (int s0 = 0; s0 < U; s0 += useg) {
+        const int ns = min(useg, U - s0);
+        const bool col_ok = lane_ok && uc < ns;
+        const int u = s0 + min(uc, ns - 4 + (uc & 3));  // clamped, same q
+        const int q = u & 3;
+        const KScaleSel sel(q);
+        XReg<T> X;
+        load_x<T>(X, x, u);
+        const uint8_t *wcol = W + (size_t)(u >> 2) * BB;
+        const int ph_c = lane_ok ? ph : 0;
+
+        auto row_of = [&](int i) { return r0 + ph_c + P * i; };
+        Unit<T> buf[D];
+#pragma unroll
+        for (int p = 0; p < D; ++p) buf[p].template load<NT>(wcol + (size_t)min(row_of(p), r1 - 1) * row_bytes, q);
+
+        for (int i0 = 0; i0 < rows_lane; i0 += D) {
+#pragma unroll
+            for (int p = 0; p < D; ++p) {
+                const int i = i0 + p;
+                const int row = row_of(i);
+                float v = 0.f;
+                if (col_ok && i < rows_lane && row < r1) v = unit_dot<T>(buf[p], q, sel, X);
+                buf[p].template load<NT>(wcol + (size_t)min(row_of(i + D), r1 - 1) * row_bytes, q);
+                if (col_ok && i < rows_lane && row < r1) {
+                    float *dst = part + (size_t)(row - r0) * useg + uc;
+                    *dst = s0 == 0 ? v : *dst + v;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // y[row] = sum of its partials, 4 lanes per row, fixed order
+    const int cols = min(useg, U);
+    for (int rr = tid >> 2; rr < R; rr += (int)blockDim.x >> 2) {
+        const float *pr = part + (size_t)rr * useg;
+        float a = 0.f;
+        for (int c = (tid & 3); c < cols; c += 4) a += pr[c];
+        a += __shfl_xor(a, 1);
+        a += __shfl_xor(a, 2);
+        if ((tid & 3) == 0) y[r0 + rr] = a;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantisation, one 64-weight unit per thread, through the same unit loads
+// and pattern decoders as the GEMV.  Q4_K/Q5_K: w = (d*sc)*q - dmin*m (both
+// products exact in fp32, one rounding); Q6_K: w = d * (sc*(q-32)) (exact).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t pat_lo(uint32_t p, int shift) { return (p & 0xffffu) >> shift; }
+__device__ __forceinline__ uint32_t pat_hi(uint32_t p, int shift) { return (p >> 16) >> shift; }
+
+template <int T>
+__global__ void __launch_bounds__(WG) dequant_kernel(const uint8_t *__restrict__ W, float *__restrict__ out,
+                                                     int64_t N, int K) {
+    constexpr int BB = Fmt<T>::bytes;
+    const int64_t unit = (int64_t)blockIdx.x * WG + threadIdx.x;
+    const int upr = K >> 6;
+    if (unit >= N * upr) return;
+    const int64_t row = unit / upr;
+    const int u = (int)(unit - row * upr);
+    const int s = u >> 2, q = u & 3;
+    const uint8_t *sb = W + ((size_t)row * (size_t)(K >> 8) + (size_t)s) * BB;
+    float *o = out + (size_t)row * (size_t)K + 256 * s;
+    Unit<T> U;
+    U.template load<false>(sb, q);
+    if constexpr (T == Q6_K) {
+        const float d = f16_lo(U.d);
+        const int kb = 128 * (q >> 1) + 16 * (q & 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t p[8];
+            U.patterns(i, q, p);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int sh = t < 2 ? 0 : 4;
+                const int sc = U.scale(t, q);
+                const uint32_t pa = p[2 * t], pb = p[2 * t + 1];
+                float4 w;
+                w.x = d * (float)(sc * ((int)pat_lo(pa, sh) - 32));
+                w.y = d * (float)(sc * ((int)pat_lo(pb, sh) - 32));
+                w.z = d * (float)(sc * ((int)pat_hi(pa, sh) - 32));
+                w.w = d * (float)(sc * ((int)pat_hi(pb, sh) - 32));
+                *reinterpret_cast<float4 *>(o + kb + 32 * t + 4 * i) = w;
+            }
+        }
+    } else {
+        const uint4 h = U.header();
+        const KScales s4 = k_scales(h, KScaleSel(q));
+        const float d = f16_lo(h.x), dmin = f16_hi(h.x);
+        const float dl = d * (float)s4.sc_lo, dh = d * (float)s4.sc_hi;
+        const float ml = dmin * (float)s4.m_lo, mh = dmin * (float)s4.m_hi;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t p[4];
+            U.patterns(i, q, p);
+            float4 lo, hi;
+            lo.x = dl * (float)pat_lo(p[0], 0) - ml;
+            lo.y = dl * (float)pat_lo(p[1], 0) - ml;
+            lo.z = dl * (float)pat_hi(p[0], 0) - ml;
+            lo.w = dl * (float)pat_hi(p[1], 0) - ml;
+            hi.x = dh * (float)pat_lo(p[2], 4) - mh;
+            hi.y = dh * (float)pat_lo(p[3], 4) - mh;
+            hi.z = dh * (float)pat_hi(p[2], 4) - mh;
+            hi.w = dh * (float)pat_hi(p[3], 4) - mh;
+            *reinterpret_cast<float4 *>(o + 64 * q + 4 * i) = lo;
+            *reinterpret_cast<float4 *>(o + 64 * q + 32 + 4 * i) = hi;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.
+// ---------------------------------------------------------------------------
+constexpr int LDS_PART = 96 * 1024;  // LDS for the per-unit partial sums
+
+// Launch geometry of the ncols = 1 kernel.
+struct Geo { int G, threads, useg, P; };
+
+static int cu_count() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            cus = v;
+        else
+            cus = 256;
+    }
+    return cus;
+}
+
+// Rows are split evenly over G workgroups (one per CU unless the partial
+// sums would not fit in LDS); within a workgroup P row phases of useg lanes
+// each, P chosen so that every lane gets the fewest rows with the fewest
+// waves.
+static Geo geometry(int64_t N, int64_t K, int cus) {
+    Geo g;
+    const int64_t U = K / 64;
+    g.useg = (int)(U < 512 ? U : 512);
+    int64_t G = N < cus ? N : cus;
+    while ((N + G - 1) / G * g.useg * 4 > LDS_PART) G *= 2;
+    if (G > N) G = N;
+    g.G = (int)G;
+    const int64_t R = (N + G - 1) / G;
+    const int pmax = 512 / g.useg;
+    int best_p = 1;
+    int64_t best_t = INT64_MAX;
+    for (int p = 1; p <= pmax; ++p) {
+        const int64_t t = (R + p - 1) / p;
+        if (t < best_t) { best_t = t; best_p = p; }
+    }
+    g.P = best_p;
+    const int lanes = g.P * g.useg;
+    g.threads = (lanes + 63) / 64 * 64;
+    return g;
+}
+
+template <int T, int D, bool NT>
+static hipError_t launch1(const void *W, const void *x, void *y, int64_t N, int64_t K, Geo geo, hipStream_t st) {
+    const size_t lds = (size_t)((N + geo.G - 1) / geo.G) * geo.useg * 4;
+    hipLaunchKernelGGL((gemv1_kernel<T, D, NT>), dim3(geo.G), dim3(geo.threads), lds, st,
+                       (const uint8_t *)W, (const uint16_t *)x, (float *)y, (int)N, (int)K, geo.useg, geo.P);
+    return hipGetLastError();
+}
+
+template <int T>
+static hipError_t gemv1_dispatch(const void *W, const void *x, void *y, int64_t N, int64_t K, hipStream_t st) {
+    return launch1<T, 2, false>(W, x, y, N, K, geometry(N, K, cu_count()), st);
+}
+
+hipError_t launch_gemv1(int type, const void *W, const void *x, void *y, int64_t N, int64_t K, hipStream_t st) {
+    switch (type) {
+    case Q4_K: return gemv1_dispatch<Q4_K>(W, x, y, N, K, st);
+    case Q5_K: return gemv1_dispatch<Q5_K>(W, x, y, N, K, st);
+    case Q6_K: return gemv1_dispatch<Q6_K>(W, x, y, N, K, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int T>
+static hipError_t launch_deq(const void *W, void *out, int64_t N, int64_t K, hipStream_t st) {
+    const int64_t units = N * (K / 64);
+    const unsigned grid = (unsigned)((units + WG - 1) / WG);
+    hipLaunchKernelGGL((dequant_kernel<T>), dim3(grid), dim3(WG), 0, st, (const uint8_t *)W, (float *)out, N, (int)K);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant(int type, const void *W, void *out, int64_t N, int64_t K, hipStream_t st) {
+    switch (type) {
+    case Q4_K: return launch_deq<Q4_K>(W, out, N, K, st);
+    case Q5_K: return launch_deq<Q5_K>(W, out, N, K, st);
+    case Q6_K: return launch_deq<Q6_K>(W, out, N, K, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qk

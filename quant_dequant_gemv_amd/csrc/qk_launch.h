@@ -1,0 +1,21 @@
+// qk_launch.h -- internal launch entry points (C++ linkage) behind the C ABI.
+// Arguments are validated by the callers in qk_api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qk {
+
+// ncols == 1: the streaming GEMV.
+hipError_t launch_gemv1(int type, const void *W, const void *x, void *y, int64_t N, int64_t K,
+                        hipStream_t stream);
+
+// ncols in 2..8: the few-column verify form (matrix cores).
+hipError_t launch_gemv_multi(int type, const void *W, const void *x, void *y, int64_t N, int64_t K,
+                             int ncols, hipStream_t stream);
+
+// fp32 dequantisation of the whole tensor.
+hipError_t launch_dequant(int type, const void *W, void *out, int64_t N, int64_t K, hipStream_t stream);
+
+}  // namespace qk

@@ -18,3 +18,11 @@ def pytest_configure(config):
 def orc():
     import oracle
     return oracle.load()
+
+
+def pytest_runtest_logstart(nodeid, location):
+    # Name the case on the real stderr before it runs, so that a run which
+    # ends abruptly still shows which test (and so which shape) was on the GPU.
+    if "gpu" in nodeid or "smoke" in nodeid:
+        sys.__stderr__.write(f"[start] {nodeid}\n")
+        sys.__stderr__.flush()

@@ -1,0 +1,85 @@
+"""CPU-only: the C-ABI library loads and exports every function include/qkgemv.h
+declares; host-side argument validation returns the documented codes without
+launching anything (no GPU is touched by any call here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quant_dequant_gemv_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qkgemv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH),
+                                reason="libqkgemv.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qk_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in binding.EXPORTS:
+        assert n in names
+    assert "qk_gemv" in names and "qk_dequant" in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in qkgemv.h but not exported"
+
+
+def test_sizes_and_strings():
+    assert binding.qk_block_bytes(binding.Q4_K) == 144
+    assert binding.qk_block_bytes(binding.Q5_K) == 176
+    assert binding.qk_block_bytes(binding.Q6_K) == 210
+    assert binding.qk_block_bytes(7) == -1
+    assert binding.qk_row_bytes(binding.Q4_K, 5120) == 20 * 144
+    assert binding.qk_row_bytes(binding.Q6_K, 17408) == 68 * 210
+    assert binding.qk_row_bytes(binding.Q4_K, 300) == -1
+    assert binding.qk_row_bytes(99, 256) == -1
+    assert "gfx950" in binding.qk_version()
+    for code in (0, -1, -2, -3, -4, -99):
+        assert isinstance(binding.qk_strerror(code), str) and binding.qk_strerror(code)
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address: never dereferenced, the checks fail first
+
+
+@pytest.mark.parametrize("args,code", [
+    ((99, FAKE, FAKE, FAKE, 4, 256, 1), binding.QK_EINVAL_TYPE),
+    ((binding.Q4_K, FAKE, FAKE, FAKE, 0, 256, 1), binding.QK_EINVAL_SHAPE),
+    ((binding.Q4_K, FAKE, FAKE, FAKE, 4, 255, 1), binding.QK_EINVAL_SHAPE),
+    ((binding.Q4_K, FAKE, FAKE, FAKE, 4, 0, 1), binding.QK_EINVAL_SHAPE),
+    ((binding.Q5_K, FAKE, FAKE, FAKE, 4, 512 + 128, 1), binding.QK_EINVAL_SHAPE),
+    ((binding.Q6_K, FAKE, FAKE, FAKE, 4, 256, 0), binding.QK_EINVAL_SHAPE),
+    ((binding.Q6_K, FAKE, FAKE, FAKE, 4, 256, 9), binding.QK_EINVAL_SHAPE),
+    ((binding.Q4_K, 0, FAKE, FAKE, 4, 256, 1), binding.QK_EINVAL_PTR),
+    ((binding.Q4_K, FAKE, 0, FAKE, 4, 256, 1), binding.QK_EINVAL_PTR),
+    ((binding.Q4_K, FAKE, FAKE, 0, 4, 256, 1), binding.QK_EINVAL_PTR),
+    ((binding.Q4_K, FAKE + 8, FAKE, FAKE, 4, 256, 1), binding.QK_EINVAL_PTR),
+    ((binding.Q4_K, FAKE, FAKE + 2, FAKE, 4, 256, 1), binding.QK_EINVAL_PTR),
+    ((binding.Q4_K, FAKE, FAKE, FAKE + 2, 4, 256, 1), binding.QK_EINVAL_PTR),
+])
+def test_gemv_validation_codes(args, code):
+    assert binding.qk_gemv(*args, 0) == code
+
+
+def test_dequant_validation_codes():
+    assert binding.qk_dequant(1, FAKE, FAKE, 4, 256, 0) == binding.QK_EINVAL_TYPE
+    assert binding.qk_dequant(binding.Q4_K, FAKE, FAKE, 4, 100, 0) == binding.QK_EINVAL_SHAPE
+    assert binding.qk_dequant(binding.Q4_K, 0, FAKE, 4, 256, 0) == binding.QK_EINVAL_PTR
+    assert binding.qk_dequant(binding.Q4_K, FAKE, FAKE + 1, 4, 256, 0) == binding.QK_EINVAL_PTR
+
+
+def test_python_wrappers_raise_not_fallback():
+    with pytest.raises(binding.QKError) as e:
+        err = binding.qk_gemv(99, FAKE, FAKE, FAKE, 4, 256, 1, 0)
+        raise binding.QKError(err, "qk_gemv")
+    assert e.value.code == binding.QK_EINVAL_TYPE

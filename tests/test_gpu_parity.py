@@ -1,0 +1,131 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+* qk_dequant is bit-exact (-0 == +0) on every format and shape;
+* qk_gemv (ncols = 1) is within |y - y_ref| <= 1e-4 * sum|w*x| per row, at
+  sizes the oracle does whole (several tiles, ragged row counts) and at the
+  full projection shapes on sampled rows, in the launch configuration the
+  benchmark uses;
+* exactness pins: one-hot x returns a dequantised column bit-exactly, scaling
+  x by a power of two scales y exactly, and repeated calls are bitwise equal.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_row_bound, gpu_dequant, gpu_gemv, needs_gpu, same_f32
+from kquant_pack import load_golden
+from quant_dequant_gemv_amd import synth
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+Q4, Q5, Q6 = synth.Q4_K, synth.Q5_K, synth.Q6_K
+TYPES = [Q4, Q5, Q6]
+NAMES = {Q4: "Q4_K", Q5: "Q5_K", Q6: "Q6_K"}
+
+# (N, K): tiny, ragged row counts, several superblocks, the real K values, and
+# a K beyond one staged x tile (28928 weights) so the tile loop runs twice.
+SMALL_SHAPES = [(1, 256), (47, 512), (48, 5120), (1023, 768), (129, 6144), (96, 17408), (40, 29184)]
+
+
+def _case(qt, N, K, seed):
+    return synth.superblocks(qt, N, K, seed), synth.activations(K, 1, seed)
+
+
+@pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
+@pytest.mark.parametrize("N,K", SMALL_SHAPES)
+def test_dequant_bit_exact(qt, N, K):
+    W, _ = _case(qt, N, K, 100 + N)
+    assert same_f32(gpu_dequant(qt, W, N, K), oracle.dequant(qt, W, K))
+
+
+def test_dequant_worked_examples():
+    import glob, os
+    for path in sorted(glob.glob(os.path.join(os.path.dirname(__file__), "golden", "q*_e*.txt"))):
+        qt, form, block, values = load_golden(path)
+        w = gpu_dequant(qt, block[None, :], 1, 256)[0]
+        assert same_f32(w, oracle.dequant(qt, block[None, :], 256)[0]), path
+        for i, v in values.items():
+            assert w[i] == np.float32(v), (path, i)
+
+
+def test_dequant_full_small_config():
+    c = synth.SMALL
+    W = synth.superblocks(c["qtype"], c["N"], c["K"], c["seed"])
+    assert same_f32(gpu_dequant(c["qtype"], W, c["N"], c["K"]), oracle.dequant(c["qtype"], W, c["K"]))
+
+
+@pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
+@pytest.mark.parametrize("N,K", SMALL_SHAPES)
+def test_gemv_row_bound(qt, N, K):
+    W, x = _case(qt, N, K, 200 + N)
+    y = gpu_gemv(qt, W, x, N, K)
+    y_ref, S = oracle.gemv(qt, W, x, K)
+    assert_row_bound(y, y_ref, S, f"{NAMES[qt]} N={N} K={K}")
+
+
+def test_gemv_small_config_all_rows():
+    c = synth.SMALL
+    W = synth.superblocks(c["qtype"], c["N"], c["K"], c["seed"])
+    x = synth.activations(c["K"], 1, c["seed"])
+    y = gpu_gemv(c["qtype"], W, x, c["N"], c["K"])
+    y_ref, S = oracle.gemv(c["qtype"], W, x, c["K"])
+    worst = assert_row_bound(y, y_ref, S, "Q4_K 1024x5120")
+    assert worst < 1e-5  # the factored fp32 form is far inside the bound
+
+
+@pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
+def test_gemv_one_hot_is_a_column(qt):
+    N, K = 77, 1024
+    W = synth.superblocks(qt, N, K, 7)
+    w = oracle.dequant(qt, W, K)
+    for k in (0, 1, 2, 3, 5, 31, 32, 63, 64, 100, 255, 256, 511, 700, K - 1):
+        x = np.zeros((K, 1), dtype=np.float16)
+        x[k, 0] = 1.0
+        y = gpu_gemv(qt, W, x, N, K)[:, 0]
+        assert same_f32(y, w[:, k]), f"{NAMES[qt]} column {k}"
+
+
+@pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
+def test_gemv_power_of_two_and_determinism(qt):
+    N, K = 300, 5120
+    W, x = _case(qt, N, K, 9)
+    y1 = gpu_gemv(qt, W, x, N, K)
+    y2 = gpu_gemv(qt, W, x, N, K)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), "not deterministic"
+    y4 = gpu_gemv(qt, W, (x.astype(np.float32) * 4).astype(np.float16), N, K)
+    assert np.array_equal(y4, y1 * 4), "power-of-two scaling not exact"
+
+
+@pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
+def test_gemv_subnormal_x(qt):
+    N, K = 64, 2048
+    W = synth.superblocks(qt, N, K, 11)
+    x = (synth.activations(K, 1, 11).astype(np.float32) * 2.0 ** -18).astype(np.float16)
+    assert (np.abs(x) < 2.0 ** -14).mean() > 0.5  # mostly fp16 subnormals
+    y = gpu_gemv(qt, W, x, N, K)
+    y_ref, S = oracle.gemv(qt, W, x, K)
+    assert_row_bound(y, y_ref, S, f"{NAMES[qt]} subnormal x")
+
+
+def _sampled_full_shape(qt, N, K, seed, nsample=192):
+    W = synth.superblocks(qt, N, K, seed)
+    x = synth.activations(K, 1, seed)
+    y = gpu_gemv(qt, W, x, N, K)
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, nsample)]))
+    y_ref, S = oracle.gemv(qt, W[rows], x, K)
+    assert_row_bound(y[rows], y_ref, S, f"{NAMES[qt]} {N}x{K} sampled")
+    assert np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("case", synth.Q4K_PROJECTIONS + synth.MIXED, ids=lambda c: c["name"])
+def test_gemv_full_shapes_sampled(case):
+    _sampled_full_shape(case["qtype"], case["N"], case["K"], case["seed"])
+
+
+@pytest.mark.parametrize("name,qt,N,K", [("ssm_alpha", Q6, 48, 5120), ("attn_k", Q4, 1024, 5120)])
+def test_gemv_stream_small_shapes(name, qt, N, K):
+    W, x = _case(qt, N, K, 1000 + N)
+    y = gpu_gemv(qt, W, x, N, K)
+    y_ref, S = oracle.gemv(qt, W, x, K)
+    assert_row_bound(y, y_ref, S, name)
