@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X k-quant GEMV: weight GB/s, fraction of HBM peak, and
+the implied tokens/s of a 64-layer decode weight stream.
+
+One step is one pass over the Q4_K projection workload of a 27B hybrid
+DeltaNet/GQA decoder at hidden size 5120: three GEMVs, N = 10240 (fused
+DeltaNet QKV), 12288 (attention Q) and 17408 (FFN gate/up), K = 5120, one
+column, fp16 x.  Weights are seeded synthetic superblocks (the real GGUF
+weights are not available); enough distinct copies are rotated that every step
+reads them from HBM, not from the 256 MB Infinity Cache.
+
+Printed: one JSON line (rank 0).  `value` is weight bytes / wall time of the
+timed steps; `roofline.achieved` is the algorithmic bytes of one launch of the
+dominant kernel over its average duration, measured with HIP events on the
+launch stream; `cpu_baseline` times the CPU oracle on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+MIN_ROTATION_BYTES = 1.2e9  # > 4x the 256 MB Infinity Cache
+METRIC = "weight GB/s and % of HBM peak per GEMV; implied tok/s for 64-layer stream"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["quant_dequant_gemv_amd/csrc/qk_kernels.hip", "quant_dequant_gemv_amd/csrc/qk_format.h"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(qt, N, K, ncols=1):
+    from quant_dequant_gemv_amd import synth
+    return N * synth.row_bytes(qt, K) + 2 * K * ncols + 4 * N * ncols
+
+
+class Launcher:
+    """Direct ctypes calls of qk_gemv with pre-computed device addresses."""
+
+    def __init__(self):
+        from quant_dequant_gemv_amd import binding
+        self.lib = binding.load_library()
+
+    def gemv(self, qt, W, x, y, N, K, ncols, stream):
+        rc = self.lib.qk_gemv(qt, W, x, y, N, K, ncols, stream)
+        if rc != 0:
+            from quant_dequant_gemv_amd import binding
+            raise binding.QKError(rc, "qk_gemv")
+
+
+def make_tensors(torch, entries, seed_offset=0):
+    """Device weights (with rotation copies), x and y for each entry."""
+    from quant_dequant_gemv_amd import synth
+    out = []
+    for e in entries:
+        W = synth.superblocks(e["qtype"], e["N"], e["K"], e["seed"] + seed_offset)
+        Wd = torch.from_numpy(W.reshape(-1)).cuda()
+        x = torch.from_numpy(synth.activations(e["K"], e.get("ncols", 1), e["seed"])).cuda()
+        y = torch.empty((e["N"], e.get("ncols", 1)), dtype=torch.float32, device="cuda")
+        out.append(dict(e, W=[Wd], x=x, y=y, bytes=Wd.numel()))
+    return out
+
+
+def add_rotation(tensors):
+    total = sum(t["bytes"] for t in tensors)
+    copies = max(2, int(-(-MIN_ROTATION_BYTES // total)))
+    for t in tensors:
+        t["W"] += [t["W"][0].clone() for _ in range(copies - 1)]
+    return copies
+
+
+def capture(torch, launcher, calls):
+    """One HIP graph replaying `calls` = [(tensor, copy index), ...] in order."""
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for t, c in calls:
+            launcher.gemv(t["qtype"], t["W"][c].data_ptr(), t["x"].data_ptr(), t["y"].data_ptr(),
+                          t["N"], t["K"], t["x"].shape[1], s.cuda_stream)
+    return g
+
+
+def graph_span(torch, g, reps=3):
+    """Median HIP-event span (s) of one replay on the current stream."""
+    stream = torch.cuda.current_stream()
+    g.replay()
+    torch.cuda.synchronize()
+    spans = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        spans.append(a.elapsed_time(b) * 1e-3)
+    return sorted(spans)[len(spans) // 2]
+
+
+def per_shape(torch, launcher, tensors, copies):
+    """Average kernel duration per tensor: one graph of back-to-back launches
+    of that tensor alone (rotating its copies), event span / launches."""
+    from quant_dequant_gemv_amd import synth
+    out = []
+    for t in tensors:
+        n = 4 * copies
+        g = capture(torch, launcher, [(t, i % copies) for i in range(n)])
+        us = graph_span(torch, g) / n * 1e6
+        del g
+        out.append({"name": t["name"], "type": synth.TYPE_NAMES[t["qtype"]], "N": t["N"], "K": t["K"],
+                    "us": round(us, 3), "weight_GBs": round(t["bytes"] / us / 1e3, 1),
+                    "frac_peak": round(t["bytes"] / us / 1e3 / PEAK_HBM_GBS, 4)})
+    return out
+
+
+def cpu_baseline(entries):
+    """The CPU oracle on the step's three GEMVs (all rows), median of 3."""
+    import numpy as np
+
+    import oracle
+    from quant_dequant_gemv_amd import synth
+    data = [(e["qtype"], synth.superblocks(e["qtype"], e["N"], e["K"], e["seed"]),
+             synth.activations(e["K"], 1, e["seed"]), e["K"]) for e in entries]
+    threads = oracle.default_threads()
+    oracle.load()
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        for qt, W, x, K in data:
+            oracle.gemv(qt, W, x, K, nthreads=threads)
+        times.append(time.perf_counter() - t0)
+    t = sorted(times)[1]
+    nbytes = sum(W.size for _, W, _, _ in data)
+    return {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full step (3 GEMVs, {nbytes} weight bytes), median of 3 runs, "
+                      f"{t:.2f} s per step",
+            "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def traffic_for(kernel, frac_bytes):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were
+    taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    v = t.get("per_launch_bytes", {}).get(kernel)
+    return v
+
+
+def run_stream(torch, launcher, warm=2):
+    """448 back-to-back GEMVs of one decode token, all weights resident:
+    event span of plain launches on one stream (the host enqueues the token
+    ahead of the GPU behind a spin kernel) and of one captured graph."""
+    from quant_dequant_gemv_amd import synth
+    entries = synth.decode_stream()
+    tensors = make_tensors(torch, entries)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def one_token():
+        for t in tensors:
+            launcher.gemv(t["qtype"], t["W"][0].data_ptr(), t["x"].data_ptr(), t["y"].data_ptr(),
+                          t["N"], t["K"], 1, sh)
+
+    for _ in range(warm):
+        one_token()
+    torch.cuda.synchronize()
+    spans = []
+    for _ in range(3):
+        torch.cuda._sleep(int(2e7))
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        one_token()
+        b.record(stream)
+        torch.cuda.synchronize()
+        spans.append(a.elapsed_time(b) * 1e-3)
+    span = sorted(spans)[1]
+    g = capture(torch, launcher, [(t, 0) for t in tensors])
+    gspan = graph_span(torch, g)
+    del g
+    nbytes = synth.weight_bytes(entries)
+    del tensors
+    torch.cuda.empty_cache()
+    return {"gemvs": len(entries), "weight_bytes": nbytes,
+            "launches": {"token_ms": round(span * 1e3, 4), "tok_s": round(1 / span, 2),
+                         "weight_GBs": round(nbytes / span / 1e9, 1)},
+            "graph": {"token_ms": round(gspan * 1e3, 4), "tok_s": round(1 / gspan, 2),
+                      "weight_GBs": round(nbytes / gspan / 1e9, 1)}}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-stream", action="store_true", help="skip the 448-GEMV decode stream")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(row sharding across GPUs is a design note, not an implementation). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from quant_dequant_gemv_amd import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    launcher = Launcher()
+
+    entries = synth.Q4K_PROJECTIONS
+    tensors = make_tensors(torch, entries)
+    copies = add_rotation(tensors)
+    step_bytes = sum(t["bytes"] for t in tensors)
+    step_alg = sum(algorithmic_bytes(t["qtype"], t["N"], t["K"]) for t in tensors)
+    # exactly K steps in one graph (step i reads rotation set i mod copies)
+    timed = capture(torch, launcher, [(t, i % copies) for i in range(args.steps) for t in tensors])
+    warm = capture(torch, launcher, [(t, i % copies) for i in range(max(1, args.warmup)) for t in tensors])
+    warm.replay()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    timed.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    span = e0.elapsed_time(e1) * 1e-3
+    value = args.steps * step_bytes / wall / 1e9
+    per_step = len(tensors)
+    launches = args.steps * per_step
+    # dominant kernel: every launch of the timed region is the Q4_K one-column GEMV
+    achieved = (step_alg / per_step) / (span / launches) / 1e9
+    del timed, warm
+
+    shapes = per_shape(torch, launcher, tensors, copies)
+    del tensors
+    torch.cuda.empty_cache()
+
+    mixed = make_tensors(torch, synth.MIXED)
+    mcopies = add_rotation(mixed)
+    mixed_out = per_shape(torch, launcher, mixed, mcopies)
+    del mixed
+    torch.cuda.empty_cache()
+
+    stream_out = None if args.no_stream else run_stream(torch, launcher)
+    cpu = None if args.no_cpu else cpu_baseline(entries)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "k-quant(u8) x f16 -> f32",
+        "data": "synthetic (seeded k-quant superblocks, x ~ N(0,1) fp16)",
+        "config": {"workload": "Q4_K one-column GEMV x3 per step: N=10240, 12288, 17408 at K=5120 "
+                               "(fused DeltaNet QKV, attention Q, FFN gate/up of a 5120-hidden decoder)",
+                   "ncols": 1, "weight_bytes_per_step": step_bytes, "rotation_copies": copies,
+                   "timing": "the K timed steps replayed from one HIP graph; wall clock around them"},
+        "roofline": {"bound": "hbm", "kernel": "gemv1_kernel<Q4_K>", "achieved": round(achieved, 1),
+                     "avg_launch_us": round(span / launches * 1e6, 3),
+                     "bytes_per_launch": round(step_alg / per_step),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for("gemv1_kernel<Q4_K>", None)},
+        "cpu_baseline": cpu,
+        "per_gemv": shapes,
+        "mixed_types": mixed_out,
+        "decode_stream": stream_out,
+        "event_span_ms_per_step": round(span / args.steps * 1e3, 5),
+        "kernel_hash": kernel_hash(),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
