@@ -277,6 +277,20 @@ def main():
     del mixed
     torch.cuda.empty_cache()
 
+    # few-column verify: Q4_K 17408 x 5120, weights read once per call
+    v = synth.VERIFY
+    verify_out = []
+    for nc in v["ncols"]:
+        vt = make_tensors(torch, [dict(name=f"verify_ncols{nc}", qtype=v["qtype"], N=v["N"], K=v["K"],
+                                       seed=v["seed"], ncols=nc)])
+        vc = add_rotation(vt)
+        r = per_shape(torch, launcher, vt, vc)[0]
+        r["ncols"] = nc
+        r["TFLOPs"] = round(2.0 * v["N"] * v["K"] * nc / r["us"] / 1e6, 2)
+        verify_out.append(r)
+        del vt
+        torch.cuda.empty_cache()
+
     stream_out = None if args.no_stream else run_stream(torch, launcher)
     cpu = None if args.no_cpu else cpu_baseline(entries)
 
@@ -305,6 +319,7 @@ def main():
         "cpu_baseline": cpu,
         "per_gemv": shapes,
         "mixed_types": mixed_out,
+        "verify": verify_out,
         "decode_stream": stream_out,
         "event_span_ms_per_step": round(span / args.steps * 1e3, 5),
         "kernel_hash": kernel_hash(),
