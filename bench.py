@@ -110,43 +110,54 @@ def graph_span(torch, g, reps=3):
     return sorted(spans)[len(spans) // 2]
 
 
-def per_shape(torch, launcher, tensors, copies):
-    """Average kernel duration per tensor: one graph of back-to-back launches
-    of that tensor alone (rotating its copies), event span / launches."""
+def per_shape(torch, launcher, tensors):
+    """Average kernel duration per tensor: its own rotation of >= 1.2 GB of
+    copies, one graph of back-to-back launches of that tensor alone, event
+    span / launches."""
     from quant_dequant_gemv_amd import synth
     out = []
     for t in tensors:
+        base = t["W"]
+        t["W"] = [base[0]]
+        copies = add_rotation([t])
         n = 4 * copies
         g = capture(torch, launcher, [(t, i % copies) for i in range(n)])
         us = graph_span(torch, g) / n * 1e6
         del g
+        t["W"] = base
+        torch.cuda.empty_cache()
         out.append({"name": t["name"], "type": synth.TYPE_NAMES[t["qtype"]], "N": t["N"], "K": t["K"],
                     "us": round(us, 3), "weight_GBs": round(t["bytes"] / us / 1e3, 1),
-                    "frac_peak": round(t["bytes"] / us / 1e3 / PEAK_HBM_GBS, 4)})
+                    "frac_peak": round(t["bytes"] / us / 1e3 / PEAK_HBM_GBS, 4), "rotation_copies": copies})
     return out
 
 
-def cpu_baseline(entries):
-    """The CPU oracle on the step's three GEMVs (all rows), median of 3."""
-    import numpy as np
-
+def cpu_baseline(entries, min_seconds=10.0):
+    """The CPU oracle on the step's three GEMVs (all rows), repeated until at
+    least `min_seconds` of wall time; plus one single-threaded step."""
     import oracle
     from quant_dequant_gemv_amd import synth
     data = [(e["qtype"], synth.superblocks(e["qtype"], e["N"], e["K"], e["seed"]),
              synth.activations(e["K"], 1, e["seed"]), e["K"]) for e in entries]
     threads = oracle.default_threads()
     oracle.load()
-    times = []
-    for _ in range(3):
-        t0 = time.perf_counter()
+    nbytes = sum(W.size for _, W, _, _ in data)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
         for qt, W, x, K in data:
             oracle.gemv(qt, W, x, K, nthreads=threads)
-        times.append(time.perf_counter() - t0)
-    t = sorted(times)[1]
-    nbytes = sum(W.size for _, W, _, _ in data)
-    return {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full step (3 GEMVs, {nbytes} weight bytes), median of 3 runs, "
-                      f"{t:.2f} s per step",
+        steps += 1
+        t = time.perf_counter() - t0
+        if t >= min_seconds and steps >= 3:
+            break
+    t1 = time.perf_counter()
+    for qt, W, x, K in data:
+        oracle.gemv(qt, W, x, K, nthreads=1)
+    one = time.perf_counter() - t1
+    return {"value": round(steps * nbytes / t / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} full steps (3 GEMVs, {nbytes} weight bytes each) in {t:.1f} s wall",
+            "one_thread_GBs": round(nbytes / one / 1e9, 4),
             "cpu": _cpu_model()}
 
 
@@ -267,13 +278,15 @@ def main():
     achieved = (step_alg / per_step) / (span / launches) / 1e9
     del timed, warm
 
-    shapes = per_shape(torch, launcher, tensors, copies)
+    for t in tensors:
+        t["W"] = t["W"][:1]
+    torch.cuda.empty_cache()
+    shapes = per_shape(torch, launcher, tensors)
     del tensors
     torch.cuda.empty_cache()
 
     mixed = make_tensors(torch, synth.MIXED)
-    mcopies = add_rotation(mixed)
-    mixed_out = per_shape(torch, launcher, mixed, mcopies)
+    mixed_out = per_shape(torch, launcher, mixed)
     del mixed
     torch.cuda.empty_cache()
 
@@ -283,8 +296,7 @@ def main():
     for nc in v["ncols"]:
         vt = make_tensors(torch, [dict(name=f"verify_ncols{nc}", qtype=v["qtype"], N=v["N"], K=v["K"],
                                        seed=v["seed"], ncols=nc)])
-        vc = add_rotation(vt)
-        r = per_shape(torch, launcher, vt, vc)[0]
+        r = per_shape(torch, launcher, vt)[0]
         r["ncols"] = nc
         r["TFLOPs"] = round(2.0 * v["N"] * v["K"] * nc / r["us"] / 1e6, 2)
         verify_out.append(r)

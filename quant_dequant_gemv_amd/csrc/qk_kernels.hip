@@ -134,19 +134,25 @@ __device__ __forceinline__ float unit_dot<Q6_K>(const Unit<Q6_K> &U, int q, cons
 // walked in segments of at most `useg` units.  Inside a segment lane
 // t < P*useg owns unit column uc = t % useg and row phase ph = t / useg: it
 // holds x of that unit in registers and visits rows r0+ph, r0+ph+P, ... ; a
-// wave therefore reads up to 16 consecutive superblocks of one row per load.
-// The lane's rows are streamed through a ring of D unit buffers (the math on
-// one row overlaps the loads of the next D).  Loads are unconditional, with
-// addresses clamped into the tensor past the end, so that the compiler keeps
-// exact counts of the loads in flight.  Each unit's partial sum goes to LDS;
-// at the end every row's partials are added in a fixed order.
+// wave reads up to 16 consecutive superblocks of one row per load.
+//
+// The rows of a lane are taken RL at a time, and the body for RL rows is
+// straight-line code: all RL units' loads are issued first, then the units
+// are computed in order.  There is no branch anywhere in it -- addresses past
+// the end are clamped into the tensor, invalid results are discarded with a
+// select and invalid partial sums go to a spare LDS slot -- so the compiler
+// knows exactly how many loads are in flight and waits for one unit at a
+// time: the math on the first rows overlaps the arrival of the later ones.
+// Each unit's partial sum goes to LDS; at the end every row's partials are
+// added in a fixed order.
 // ---------------------------------------------------------------------------
-template <int T, int D, bool NT>
-__global__ void __launch_bounds__(512, 4) gemv1_kernel(const uint8_t *__restrict__ W,
-                                                   const uint16_t *__restrict__ x,
-                                                   float *__restrict__ y, int N, int K, int useg, int P) {
-    extern __shared__ __attribute__((aligned(16))) float part[];  // [rows of this wg][useg]
+template <int T, int RL, int D, bool NT>
+__global__ void __launch_bounds__(1024) gemv1_kernel(const uint8_t *__restrict__ W,
+                                                      const uint16_t *__restrict__ x,
+                                                      float *__restrict__ y, int N, int K, int useg, int P) {
+    extern __shared__ __attribute__((aligned(16))) float part[];  // [rows of this wg][useg] + 1 spare
     constexpr int BB = Fmt<T>::bytes;
+    constexpr int DD = D < RL ? D : RL;  // units in flight
     const int tid = (int)threadIdx.x;
     const int r0 = (int)((int64_t)blockIdx.x * N / gridDim.x);
     const int r1 = (int)((int64_t)(blockIdx.x + 1) * N / gridDim.x);
@@ -155,7 +161,9 @@ __global__ void __launch_bounds__(512, 4) gemv1_kernel(const uint8_t *__restrict
     const size_t row_bytes = (size_t)(K >> 8) * BB;
     const int ph = tid / useg, uc = tid - ph * useg;
     const bool lane_ok = ph < P;
+    const int ph_c = lane_ok ? ph : 0;
     const int rows_lane = (R + P - 1) / P;  // same schedule for every lane
+    const int spare = R * useg;              // index of the spare slot
 
     for (int s0 = 0; s0 < U; s0 += useg) {
         const int ns = min(useg, U - s0);
@@ -166,25 +174,25 @@ __global__ void __launch_bounds__(512, 4) gemv1_kernel(const uint8_t *__restrict
         XReg<T> X;
         load_x<T>(X, x, u);
         const uint8_t *wcol = W + (size_t)(u >> 2) * BB;
-        const int ph_c = lane_ok ? ph : 0;
 
-        auto row_of = [&](int i) { return r0 + ph_c + P * i; };
-        Unit<T> buf[D];
+        for (int i0 = 0; i0 < rows_lane; i0 += RL) {
+            // straight line over RL rows with a ring of DD units in flight
+            Unit<T> buf[DD];
+            auto load_row = [&](Unit<T> &dst, int i) {
+                const int row = min(r0 + ph_c + P * (i0 + i), r1 - 1);
+                dst.template load<NT>(wcol + (size_t)row * row_bytes, q);
+            };
 #pragma unroll
-        for (int p = 0; p < D; ++p) buf[p].template load<NT>(wcol + (size_t)min(row_of(p), r1 - 1) * row_bytes, q);
-
-        for (int i0 = 0; i0 < rows_lane; i0 += D) {
+            for (int p = 0; p < DD; ++p) load_row(buf[p], p);
 #pragma unroll
-            for (int p = 0; p < D; ++p) {
+            for (int p = 0; p < RL; ++p) {
                 const int i = i0 + p;
-                const int row = row_of(i);
-                float v = 0.f;
-                if (col_ok && i < rows_lane && row < r1) v = unit_dot<T>(buf[p], q, sel, X);
-                buf[p].template load<NT>(wcol + (size_t)min(row_of(i + D), r1 - 1) * row_bytes, q);
-                if (col_ok && i < rows_lane && row < r1) {
-                    float *dst = part + (size_t)(row - r0) * useg + uc;
-                    *dst = s0 == 0 ? v : *dst + v;
-                }
+                const int row = r0 + ph_c + P * i;
+                const bool ok = col_ok && i < rows_lane && row < r1;
+                const float v = unit_dot<T>(buf[p % DD], q, sel, X);
+                if (p + DD < RL) load_row(buf[p % DD], p + DD);
+                const int slot = ok ? (row - r0) * useg + uc : spare;
+                part[slot] = (s0 == 0 ? 0.f : part[slot]) + v;
             }
         }
     }
@@ -315,17 +323,42 @@ static Geo geometry(int64_t N, int64_t K, int cus) {
     return g;
 }
 
-template <int T, int D, bool NT>
+template <int T, int RL, int D, bool NT>
 static hipError_t launch1(const void *W, const void *x, void *y, int64_t N, int64_t K, Geo geo, hipStream_t st) {
-    const size_t lds = (size_t)((N + geo.G - 1) / geo.G) * geo.useg * 4;
-    hipLaunchKernelGGL((gemv1_kernel<T, D, NT>), dim3(geo.G), dim3(geo.threads), lds, st,
+    const size_t lds = ((size_t)((N + geo.G - 1) / geo.G) * geo.useg + 1) * 4;
+    hipLaunchKernelGGL((gemv1_kernel<T, RL, D, NT>), dim3(geo.G), dim3(geo.threads), lds, st,
                        (const uint8_t *)W, (const uint16_t *)x, (float *)y, (int)N, (int)K, geo.useg, geo.P);
     return hipGetLastError();
 }
 
+// Rows per straight-line round and units kept in flight.  Q6_K units are the
+// largest (58 B of loads per lane), and one unit in flight per lane with two
+// row phases per CU streams them fastest; Q4_K/Q5_K keep two units in flight
+// and take up to 12 (Q4_K) or 2 (Q5_K) of a lane's rows per straight-line
+// round, the most that fits in 128 VGPRs without spilling.
 template <int T>
 static hipError_t gemv1_dispatch(const void *W, const void *x, void *y, int64_t N, int64_t K, hipStream_t st) {
-    return launch1<T, 2, false>(W, x, y, N, K, geometry(N, K, cu_count()), st);
+    Geo geo = geometry(N, K, cu_count());
+    const int64_t R = (N + geo.G - 1) / geo.G;
+    if constexpr (T == Q6_K) {
+        if (geo.P == 1 && R > 1 && 2 * geo.useg <= 1024) {
+            geo.P = 2;
+            geo.threads = (2 * geo.useg + 63) / 64 * 64;
+        }
+        return launch1<T, 1, 1, false>(W, x, y, N, K, geo, st);
+    } else {
+        const int64_t rows_lane = (R + geo.P - 1) / geo.P;
+        if (rows_lane <= 1) return launch1<T, 1, 1, false>(W, x, y, N, K, geo, st);
+        if constexpr (T == Q5_K) {
+            // a Q5_K unit holds 20 dwords: longer rounds would spill under 128 VGPRs
+            return launch1<T, 2, 2, false>(W, x, y, N, K, geo, st);
+        } else {
+            if (rows_lane <= 2) return launch1<T, 2, 2, false>(W, x, y, N, K, geo, st);
+            if (rows_lane <= 4) return launch1<T, 4, 2, false>(W, x, y, N, K, geo, st);
+            if (rows_lane <= 8) return launch1<T, 8, 2, false>(W, x, y, N, K, geo, st);
+            return launch1<T, 12, 2, false>(W, x, y, N, K, geo, st);
+        }
+    }
 }
 
 hipError_t launch_gemv1(int type, const void *W, const void *x, void *y, int64_t N, int64_t K, hipStream_t st) {
