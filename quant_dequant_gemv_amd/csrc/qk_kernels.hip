@@ -197,15 +197,26 @@ __global__ void __launch_bounds__(1024) gemv1_kernel(const uint8_t *__restrict__
         }
     }
     __syncthreads();
-    // y[row] = sum of its partials, 4 lanes per row, fixed order
-    const int cols = min(useg, U);
-    for (int rr = tid >> 2; rr < R; rr += (int)blockDim.x >> 2) {
-        const float *pr = part + (size_t)rr * useg;
+    // y[row] = sum of its partials in a fixed order: 16 lanes per row, each
+    // adding float4 groups c, c+16, ... (useg is a multiple of 4), then a
+    // butterfly over the 16 lanes.  Every lane runs the same number of rounds
+    // so the shuffles see whole groups.
+    const int c4 = min(useg, U) >> 2;
+    const int j = tid & 15;
+    for (int rr = tid >> 4; rr - (tid >> 4) < R; rr += (int)blockDim.x >> 4) {
+        const bool rok = rr < R;
+        const float4 *pr = reinterpret_cast<const float4 *>(part + (size_t)(rok ? rr : 0) * useg);
         float a = 0.f;
-        for (int c = (tid & 3); c < cols; c += 4) a += pr[c];
+#pragma unroll 4
+        for (int c = j; c < c4; c += 16) {
+            const float4 v = pr[c];
+            a += (v.x + v.y) + (v.z + v.w);
+        }
         a += __shfl_xor(a, 1);
         a += __shfl_xor(a, 2);
-        if ((tid & 3) == 0) y[r0 + rr] = a;
+        a += __shfl_xor(a, 4);
+        a += __shfl_xor(a, 8);
+        if (rok && j == 0) y[r0 + rr] = a;
     }
 }
 
@@ -282,7 +293,7 @@ __global__ void __launch_bounds__(WG) dequant_kernel(const uint8_t *__restrict__
 constexpr int LDS_PART = 96 * 1024;  // LDS for the per-unit partial sums
 
 // Launch geometry of the ncols = 1 kernel.
-struct Geo { int G, threads, useg, P; };
+struct Geo { int G, threads, useg, P, RL; };
 
 static int cu_count() {
     static int cus = 0;
@@ -297,11 +308,23 @@ static int cu_count() {
     return cus;
 }
 
+// Rows per straight-line round that each type is compiled for.  Q6_K units
+// are the largest (58 B of loads per lane): one unit in flight per lane
+// streams them fastest.  Q5_K units hold 20 dwords: rounds longer than two
+// rows would spill under 128 VGPRs.  Q4_K rounds go up to 12 rows.
+template <int T> struct RowRounds;
+template <> struct RowRounds<Q4_K> { static constexpr int n = 6, rl[n] = {1, 2, 4, 6, 8, 12}, max_threads = 512; };
+template <> struct RowRounds<Q5_K> { static constexpr int n = 2, rl[n] = {1, 2}, max_threads = 512; };
+template <> struct RowRounds<Q6_K> { static constexpr int n = 1, rl[n] = {1}, max_threads = 1024; };
+
 // Rows are split evenly over G workgroups (one per CU unless the partial
-// sums would not fit in LDS); within a workgroup P row phases of useg lanes
-// each, P chosen so that every lane gets the fewest rows with the fewest
-// waves.
+// sums would not fit in LDS).  Within a workgroup P row phases of useg lanes
+// each take every P-th row, RL rows per straight-line round.  P and RL are
+// chosen to waste the fewest row slots (P * rounds * RL - R), then for the
+// most lanes.
+template <int T>
 static Geo geometry(int64_t N, int64_t K, int cus) {
+    using RR = RowRounds<T>;
     Geo g;
     const int64_t U = K / 64;
     g.useg = (int)(U < 512 ? U : 512);
@@ -310,16 +333,19 @@ static Geo geometry(int64_t N, int64_t K, int cus) {
     if (G > N) G = N;
     g.G = (int)G;
     const int64_t R = (N + G - 1) / G;
-    const int pmax = 512 / g.useg;
-    int best_p = 1;
-    int64_t best_t = INT64_MAX;
+    const int pmax = RR::max_threads / g.useg > 0 ? RR::max_threads / g.useg : 1;
+    int64_t best = INT64_MAX;
+    g.P = 1;
+    g.RL = 1;
     for (int p = 1; p <= pmax; ++p) {
-        const int64_t t = (R + p - 1) / p;
-        if (t < best_t) { best_t = t; best_p = p; }
+        const int64_t rows = (R + p - 1) / p;
+        int rl = RR::rl[RR::n - 1];
+        for (int k = 0; k < RR::n; ++k)
+            if (RR::rl[k] >= rows) { rl = RR::rl[k]; break; }
+        const int64_t slots = (int64_t)p * ((rows + rl - 1) / rl) * rl;
+        if (slots <= best) { best = slots; g.P = p; g.RL = rl; }
     }
-    g.P = best_p;
-    const int lanes = g.P * g.useg;
-    g.threads = (lanes + 63) / 64 * 64;
+    g.threads = (g.P * g.useg + 63) / 64 * 64;
     return g;
 }
 
@@ -331,34 +357,20 @@ static hipError_t launch1(const void *W, const void *x, void *y, int64_t N, int6
     return hipGetLastError();
 }
 
-// Rows per straight-line round and units kept in flight.  Q6_K units are the
-// largest (58 B of loads per lane), and one unit in flight per lane with two
-// row phases per CU streams them fastest; Q4_K/Q5_K keep two units in flight
-// and take up to 12 (Q4_K) or 2 (Q5_K) of a lane's rows per straight-line
-// round, the most that fits in 128 VGPRs without spilling.
+// Two units in flight per lane, one for one-row rounds.
 template <int T>
 static hipError_t gemv1_dispatch(const void *W, const void *x, void *y, int64_t N, int64_t K, hipStream_t st) {
-    Geo geo = geometry(N, K, cu_count());
-    const int64_t R = (N + geo.G - 1) / geo.G;
-    if constexpr (T == Q6_K) {
-        if (geo.P == 1 && R > 1 && 2 * geo.useg <= 1024) {
-            geo.P = 2;
-            geo.threads = (2 * geo.useg + 63) / 64 * 64;
-        }
-        return launch1<T, 1, 1, false>(W, x, y, N, K, geo, st);
-    } else {
-        const int64_t rows_lane = (R + geo.P - 1) / geo.P;
-        if (rows_lane <= 1) return launch1<T, 1, 1, false>(W, x, y, N, K, geo, st);
-        if constexpr (T == Q5_K) {
-            // a Q5_K unit holds 20 dwords: longer rounds would spill under 128 VGPRs
-            return launch1<T, 2, 2, false>(W, x, y, N, K, geo, st);
-        } else {
-            if (rows_lane <= 2) return launch1<T, 2, 2, false>(W, x, y, N, K, geo, st);
-            if (rows_lane <= 4) return launch1<T, 4, 2, false>(W, x, y, N, K, geo, st);
-            if (rows_lane <= 8) return launch1<T, 8, 2, false>(W, x, y, N, K, geo, st);
-            return launch1<T, 12, 2, false>(W, x, y, N, K, geo, st);
-        }
+    const Geo geo = geometry<T>(N, K, cu_count());
+    switch (geo.RL) {
+    case 1: return launch1<T, 1, 1, false>(W, x, y, N, K, geo, st);
+    case 2: if constexpr (T != Q6_K) return launch1<T, 2, 2, false>(W, x, y, N, K, geo, st); break;
+    case 4: if constexpr (T == Q4_K) return launch1<T, 4, 2, false>(W, x, y, N, K, geo, st); break;
+    case 6: if constexpr (T == Q4_K) return launch1<T, 6, 2, false>(W, x, y, N, K, geo, st); break;
+    case 8: if constexpr (T == Q4_K) return launch1<T, 8, 2, false>(W, x, y, N, K, geo, st); break;
+    case 12: if constexpr (T == Q4_K) return launch1<T, 12, 2, false>(W, x, y, N, K, geo, st); break;
+    default: break;
     }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv1(int type, const void *W, const void *x, void *y, int64_t N, int64_t K, hipStream_t st) {

@@ -129,3 +129,18 @@ def test_gemv_stream_small_shapes(name, qt, N, K):
     y = gpu_gemv(qt, W, x, N, K)
     y_ref, S = oracle.gemv(qt, W, x, K)
     assert_row_bound(y, y_ref, S, name)
+
+
+# With 256 workgroups at K = 5120 these row counts give every lane 2, 4, 6, 12
+# and 12+12+12 rows (Q4_K), two-row rounds (Q5_K) and one-row rounds over two
+# and three row phases (Q6_K); N is not a multiple of 256, so workgroups differ
+# by one row.  Every row is checked.
+@pytest.mark.parametrize("qt,N", [(Q4, 3000), (Q4, 6000), (Q4, 9000), (Q4, 17000), (Q4, 25600),
+                                  (Q5, 3000), (Q5, 9000), (Q6, 3000), (Q6, 9000)],
+                         ids=lambda v: NAMES.get(v, str(v)))
+def test_gemv_row_rounds_all_rows(qt, N):
+    K = 5120
+    W, x = _case(qt, N, K, 500 + N)
+    y = gpu_gemv(qt, W, x, N, K)
+    y_ref, S = oracle.gemv(qt, W, x, K)
+    assert_row_bound(y, y_ref, S, f"{NAMES[qt]} {N}x{K}")
