@@ -186,45 +186,83 @@ def traffic_for(kernel, frac_bytes):
 
 
 def run_stream(torch, launcher, warm=2):
-    """448 back-to-back GEMVs of one decode token, all weights resident:
-    event span of plain launches on one stream (the host enqueues the token
-    ahead of the GPU behind a spin kernel) and of one captured graph."""
-    from quant_dequant_gemv_amd import synth
+    """448 GEMVs of one decode token, all weights resident, back to back on
+    one stream: one launch per GEMV, and one qk_gemv_batch launch per group of
+    projections that read the same activations (256 launches).  Each is timed
+    as plain launches enqueued ahead of the GPU (behind a spin kernel) and as
+    one captured graph; HIP-event spans."""
+    import ctypes
+
+    from quant_dequant_gemv_amd import binding, synth
     entries = synth.decode_stream()
+    groups = synth.decode_groups(entries)
     tensors = make_tensors(torch, entries)
+    for idx in groups:  # a group's projections read one activation vector
+        for i in idx[1:]:
+            tensors[i]["x"] = tensors[idx[0]]["x"]
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    lib = binding.load_library()
+    batches = []
+    for idx in groups:
+        arr = (binding.qk_gemv_item * len(idx))(*[
+            binding.qk_gemv_item(tensors[i]["qtype"], tensors[i]["W"][0].data_ptr(), tensors[i]["x"].data_ptr(),
+                                 tensors[i]["y"].data_ptr(), tensors[i]["N"], tensors[i]["K"]) for i in idx])
+        batches.append((arr, len(idx)))
 
     def one_token():
         for t in tensors:
             launcher.gemv(t["qtype"], t["W"][0].data_ptr(), t["x"].data_ptr(), t["y"].data_ptr(),
                           t["N"], t["K"], 1, sh)
 
-    for _ in range(warm):
-        one_token()
-    torch.cuda.synchronize()
-    spans = []
-    for _ in range(3):
-        torch.cuda._sleep(int(2e7))
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        one_token()
-        b.record(stream)
+    def one_token_batched(st=None):
+        h = sh if st is None else st
+        for arr, n in batches:
+            rc = lib.qk_gemv_batch(arr, n, h)
+            if rc != 0:
+                raise binding.QKError(rc, "qk_gemv_batch")
+
+    def spans_of(fn):
+        for _ in range(warm):
+            fn()
         torch.cuda.synchronize()
-        spans.append(a.elapsed_time(b) * 1e-3)
-    span = sorted(spans)[1]
+        spans = []
+        for _ in range(3):
+            torch.cuda._sleep(int(2e7))
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            spans.append(a.elapsed_time(b) * 1e-3)
+        return sorted(spans)[1]
+
+    def graph_of(fn):
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            fn(s.cuda_stream)
+        sp = graph_span(torch, g)
+        del g
+        return sp
+
+    span = spans_of(one_token)
     g = capture(torch, launcher, [(t, 0) for t in tensors])
     gspan = graph_span(torch, g)
     del g
+    bspan = spans_of(one_token_batched)
+    bgspan = graph_of(one_token_batched)
     nbytes = synth.weight_bytes(entries)
-    del tensors
+    del tensors, batches
     torch.cuda.empty_cache()
+
+    def rec(sp, launches):
+        return {"launches_per_token": launches, "token_ms": round(sp * 1e3, 4), "tok_s": round(1 / sp, 2),
+                "weight_GBs": round(nbytes / sp / 1e9, 1)}
     return {"gemvs": len(entries), "weight_bytes": nbytes,
-            "launches": {"token_ms": round(span * 1e3, 4), "tok_s": round(1 / span, 2),
-                         "weight_GBs": round(nbytes / span / 1e9, 1)},
-            "graph": {"token_ms": round(gspan * 1e3, 4), "tok_s": round(1 / gspan, 2),
-                      "weight_GBs": round(nbytes / gspan / 1e9, 1)}}
+            "launches": rec(span, len(entries)), "graph": rec(gspan, len(entries)),
+            "batched": rec(bspan, len(groups)), "batched_graph": rec(bgspan, len(groups))}
 
 
 def main():

@@ -96,6 +96,41 @@ int qk_gemv(int type, const void *W, const void *x, void *y,
  */
 int qk_dequant(int type, const void *W, void *out, int64_t N, int64_t K, void *stream);
 
+#define QK_MAX_BATCH 16
+
+/* One entry of qk_gemv_batch: a one-column GEMV, fields as for qk_gemv. */
+typedef struct qk_gemv_item {
+    int type;
+    const void *W;
+    const void *x;
+    void *y;
+    int64_t N;
+    int64_t K;
+} qk_gemv_item;
+
+/*
+ * qk_gemv_batch -- `count` independent one-column GEMVs in one launch:
+ * y_i = dequant(W_i) @ x_i for every entry i.  The merged launch for the
+ * projections that read the same activations (q/k/v, or gate and up, of one
+ * layer), or for any other set of GEMVs with no dependence between them: the
+ * B70 plan asks for the fewest practical device submissions ("Non-Negotiable
+ * Requirements" item 4) and puts the gap between its observed pass and the
+ * Q4 read floor on per-submission overhead ("Performance Model And North
+ * Star"; "Phase 2: Full Device Replay", "Phase 3: Maximum Useful Fusion").
+ *
+ *   items  host array of `count` entries, read during the call only
+ *   count  1..QK_MAX_BATCH
+ *   stream hipStream_t to enqueue on
+ *
+ * Entries may share W and x.  No entry's y may overlap any entry's W, x or y.
+ * Every y_i is bit-identical to what qk_gemv(type_i, W_i, x_i, y_i, N_i, K_i,
+ * 1, stream) writes; the accuracy bound is that of qk_gemv.  Every entry is
+ * checked before anything is enqueued, with qk_gemv's codes; a count outside
+ * 1..QK_MAX_BATCH or a NULL `items` gives QK_EINVAL_SHAPE.  Nothing is
+ * allocated: the entries travel in the kernel arguments.
+ */
+int qk_gemv_batch(const qk_gemv_item *items, int count, void *stream);
+
 /* Bytes per 256-weight superblock: 144 / 176 / 210, or -1 for a bad type. */
 int qk_block_bytes(int type);
 

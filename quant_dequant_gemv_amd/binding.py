@@ -17,8 +17,16 @@ LIB_PATH = os.path.join(HERE, "libqkgemv.so")
 Q4_K, Q5_K, Q6_K = 12, 13, 14
 QK_OK, QK_EINVAL_TYPE, QK_EINVAL_SHAPE, QK_EINVAL_PTR, QK_ELAUNCH = 0, -1, -2, -3, -4
 MAX_NCOLS = 8
+MAX_BATCH = 16
 
-EXPORTS = ("qk_gemv", "qk_dequant", "qk_block_bytes", "qk_row_bytes", "qk_strerror", "qk_version")
+EXPORTS = ("qk_gemv", "qk_gemv_batch", "qk_dequant", "qk_block_bytes", "qk_row_bytes", "qk_strerror",
+           "qk_version")
+
+
+class qk_gemv_item(ctypes.Structure):
+    """struct qk_gemv_item of include/qkgemv.h."""
+    _fields_ = [("type", ctypes.c_int), ("W", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
 
 
 class QKError(RuntimeError):
@@ -42,6 +50,8 @@ def load_library(path: str = LIB_PATH):
     P, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.qk_gemv.argtypes = [c_int, P, P, P, i64, i64, c_int, P]
     lib.qk_gemv.restype = c_int
+    lib.qk_gemv_batch.argtypes = [ctypes.POINTER(qk_gemv_item), c_int, P]
+    lib.qk_gemv_batch.restype = c_int
     lib.qk_dequant.argtypes = [c_int, P, P, i64, i64, P]
     lib.qk_dequant.restype = c_int
     lib.qk_block_bytes.argtypes = [c_int]
@@ -60,6 +70,12 @@ def load_library(path: str = LIB_PATH):
 
 def qk_gemv(qtype: int, W: int, x: int, y: int, N: int, K: int, ncols: int, stream: int = 0) -> int:
     return load_library().qk_gemv(qtype, W, x, y, N, K, ncols, stream)
+
+
+def qk_gemv_batch(items, stream: int = 0) -> int:
+    """items: sequence of (type, W, x, y, N, K) with integer device addresses."""
+    arr = (qk_gemv_item * max(1, len(items)))(*[qk_gemv_item(*it) for it in items])
+    return load_library().qk_gemv_batch(arr, len(items), stream)
 
 
 def qk_dequant(qtype: int, W: int, out: int, N: int, K: int, stream: int = 0) -> int:
@@ -107,6 +123,27 @@ def gemv(qtype: int, W, x, N: int, K: int, out=None, stream=None):
     if rc != QK_OK:
         raise QKError(rc, "qk_gemv")
     return out
+
+
+def gemv_batch(entries, stream=None):
+    """Independent one-column GEMVs in one launch.  entries: sequence of
+    (qtype, W, x, N, K) or (qtype, W, x, N, K, out) with torch device tensors
+    (W uint8, x float16 [K], out float32 [N]); returns the list of outputs."""
+    import torch
+    items, outs = [], []
+    for e in entries:
+        qtype, W, x, N, K = e[:5]
+        out = e[5] if len(e) > 5 else torch.empty(N, dtype=torch.float32, device=x.device)
+        if x.dtype != torch.float16 or out.dtype != torch.float32 or W.dtype != torch.uint8:
+            raise TypeError("W must be uint8, x float16, out float32")
+        if not (W.is_contiguous() and x.is_contiguous() and out.is_contiguous()):
+            raise ValueError("tensors must be contiguous")
+        items.append((qtype, W.data_ptr(), x.data_ptr(), out.data_ptr(), N, K))
+        outs.append(out)
+    rc = qk_gemv_batch(items, _stream_handle(stream))
+    if rc != QK_OK:
+        raise QKError(rc, "qk_gemv_batch")
+    return outs
 
 
 def dequant(qtype: int, W, N: int, K: int, out=None, stream=None):

@@ -65,6 +65,20 @@ int qk_gemv(int type, const void *W, const void *x, void *y, int64_t N, int64_t 
     return launched(qk::launch_gemv_multi(type, W, x, y, N, K, ncols, st));
 }
 
+int qk_gemv_batch(const qk_gemv_item *items, int count, void *stream) {
+    if (!items || count < 1 || count > QK_MAX_BATCH || count > qk::MAX_BATCH) return QK_EINVAL_SHAPE;
+    qk::BatchEntry e[qk::MAX_BATCH];
+    for (int i = 0; i < count; ++i) {
+        const qk_gemv_item &it = items[i];
+        const int rc = check_shape(it.type, it.N, it.K, 1);
+        if (rc) return rc;
+        if (!it.W || !it.x || !it.y || !aligned(it.W, 16) || !aligned(it.x, 16) || !aligned(it.y, 4))
+            return QK_EINVAL_PTR;
+        e[i] = qk::BatchEntry{it.type, it.W, it.x, it.y, it.N, it.K};
+    }
+    return launched(qk::launch_gemv_batch(e, count, (hipStream_t)stream));
+}
+
 int qk_dequant(int type, const void *W, void *out, int64_t N, int64_t K, void *stream) {
     const int rc = check_shape(type, N, K, 1);
     if (rc) return rc;

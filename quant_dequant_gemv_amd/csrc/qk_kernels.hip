@@ -20,6 +20,8 @@
 #include "qk_format.h"
 #include "qk_launch.h"
 
+#include <algorithm>
+
 namespace qk {
 
 constexpr int WG = 256;  // threads per workgroup
@@ -146,16 +148,18 @@ __device__ __forceinline__ float unit_dot<Q6_K>(const Unit<Q6_K> &U, int q, cons
 // Each unit's partial sum goes to LDS; at the end every row's partials are
 // added in a fixed order.
 // ---------------------------------------------------------------------------
+// Workgroup blk of nblk (nthr threads, a multiple of 64) takes rows
+// [blk*N/nblk, (blk+1)*N/nblk).
 template <int T, int RL, int D, bool NT>
-__global__ void __launch_bounds__(1024) gemv1_kernel(const uint8_t *__restrict__ W,
-                                                      const uint16_t *__restrict__ x,
-                                                      float *__restrict__ y, int N, int K, int useg, int P) {
+__device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const uint16_t *__restrict__ x,
+                                           float *__restrict__ y, int N, int K, int useg, int P, int blk,
+                                           int nblk, int nthr) {
     extern __shared__ __attribute__((aligned(16))) float part[];  // [rows of this wg][useg] + 1 spare
     constexpr int BB = Fmt<T>::bytes;
     constexpr int DD = D < RL ? D : RL;  // units in flight
     const int tid = (int)threadIdx.x;
-    const int r0 = (int)((int64_t)blockIdx.x * N / gridDim.x);
-    const int r1 = (int)((int64_t)(blockIdx.x + 1) * N / gridDim.x);
+    const int r0 = (int)((int64_t)blk * N / nblk);
+    const int r1 = (int)((int64_t)(blk + 1) * N / nblk);
     const int R = r1 - r0;
     const int U = K >> 6;
     const size_t row_bytes = (size_t)(K >> 8) * BB;
@@ -203,7 +207,7 @@ __global__ void __launch_bounds__(1024) gemv1_kernel(const uint8_t *__restrict__
     // so the shuffles see whole groups.
     const int c4 = min(useg, U) >> 2;
     const int j = tid & 15;
-    for (int rr = tid >> 4; rr - (tid >> 4) < R; rr += (int)blockDim.x >> 4) {
+    for (int rr = tid >> 4; rr - (tid >> 4) < R; rr += nthr >> 4) {
         const bool rok = rr < R;
         const float4 *pr = reinterpret_cast<const float4 *>(part + (size_t)(rok ? rr : 0) * useg);
         float a = 0.f;
@@ -218,6 +222,57 @@ __global__ void __launch_bounds__(1024) gemv1_kernel(const uint8_t *__restrict__
         a += __shfl_xor(a, 8);
         if (rok && j == 0) y[r0 + rr] = a;
     }
+}
+
+template <int T, int RL, int D, bool NT>
+__global__ void __launch_bounds__(1024) gemv1_kernel(const uint8_t *__restrict__ W,
+                                                      const uint16_t *__restrict__ x,
+                                                      float *__restrict__ y, int N, int K, int useg, int P) {
+    gemv1_body<T, RL, D, NT>(W, x, y, N, K, useg, P, (int)blockIdx.x, (int)gridDim.x, (int)blockDim.x);
+}
+
+// ---------------------------------------------------------------------------
+// Batched one-column GEMVs: independent (W, x, y) entries in one launch.
+// Entry i owns workgroups [first[i], first[i+1]) and runs exactly the body
+// and geometry its own launch would, so its y is bit-identical to that of a
+// single call.  Entries travel in the kernel arguments (no device memory).
+// A workgroup with more threads than its entry needs retires the surplus
+// waves at once (a retired wave does not hold up the barrier).
+// ---------------------------------------------------------------------------
+enum BodyCode { B_Q4_1, B_Q4_2, B_Q4_4, B_Q4_6, B_Q4_8, B_Q4_12, B_Q5_1, B_Q5_2, B_Q6_1 };
+
+struct BatchItem {
+    const uint8_t *W;
+    const uint16_t *x;
+    float *y;
+    int N, K, useg, P, threads, code;
+};
+struct BatchArgs {
+    int count;
+    int first[MAX_BATCH + 1];
+    BatchItem it[MAX_BATCH];
+};
+
+__global__ void __launch_bounds__(1024) gemv1_batch_kernel(const BatchArgs a) {
+    int i = 0;
+    while (i + 1 < a.count && (int)blockIdx.x >= a.first[i + 1]) ++i;
+    const BatchItem &e = a.it[i];
+    if ((int)threadIdx.x >= e.threads) return;
+    const int blk = (int)blockIdx.x - a.first[i], nblk = a.first[i + 1] - a.first[i];
+#define QK_BODY(T, RL, D) gemv1_body<T, RL, D, false>(e.W, e.x, e.y, e.N, e.K, e.useg, e.P, blk, nblk, e.threads)
+    switch (e.code) {
+    case B_Q4_1: QK_BODY(Q4_K, 1, 1); break;
+    case B_Q4_2: QK_BODY(Q4_K, 2, 2); break;
+    case B_Q4_4: QK_BODY(Q4_K, 4, 2); break;
+    case B_Q4_6: QK_BODY(Q4_K, 6, 2); break;
+    case B_Q4_8: QK_BODY(Q4_K, 8, 2); break;
+    case B_Q4_12: QK_BODY(Q4_K, 12, 2); break;
+    case B_Q5_1: QK_BODY(Q5_K, 1, 1); break;
+    case B_Q5_2: QK_BODY(Q5_K, 2, 2); break;
+    case B_Q6_1: QK_BODY(Q6_K, 1, 1); break;
+    default: break;
+    }
+#undef QK_BODY
 }
 
 // ---------------------------------------------------------------------------
@@ -349,9 +404,24 @@ static Geo geometry(int64_t N, int64_t K, int cus) {
     return g;
 }
 
+static size_t part_lds(int64_t N, const Geo &g) { return ((size_t)((N + g.G - 1) / g.G) * g.useg + 1) * 4; }
+
+// Dynamic LDS above the default 64 KB needs the kernel's opt-in (once per
+// kernel: the static is per template instance, i.e. per kernel).
+template <auto Kernel>
+static void allow_lds() {
+    static const bool done = [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, LDS_PART + 1024);
+        return true;
+    }();
+    (void)done;
+}
+
 template <int T, int RL, int D, bool NT>
 static hipError_t launch1(const void *W, const void *x, void *y, int64_t N, int64_t K, Geo geo, hipStream_t st) {
-    const size_t lds = ((size_t)((N + geo.G - 1) / geo.G) * geo.useg + 1) * 4;
+    const size_t lds = part_lds(N, geo);
+    allow_lds<gemv1_kernel<T, RL, D, NT>>();
     hipLaunchKernelGGL((gemv1_kernel<T, RL, D, NT>), dim3(geo.G), dim3(geo.threads), lds, st,
                        (const uint8_t *)W, (const uint16_t *)x, (float *)y, (int)N, (int)K, geo.useg, geo.P);
     return hipGetLastError();
@@ -380,6 +450,58 @@ hipError_t launch_gemv1(int type, const void *W, const void *x, void *y, int64_t
     case Q6_K: return gemv1_dispatch<Q6_K>(W, x, y, N, K, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+static Geo geometry_of(int type, int64_t N, int64_t K, int cus) {
+    switch (type) {
+    case Q4_K: return geometry<Q4_K>(N, K, cus);
+    case Q5_K: return geometry<Q5_K>(N, K, cus);
+    default: return geometry<Q6_K>(N, K, cus);
+    }
+}
+
+static int body_code(int type, int rl) {
+    if (type == Q4_K) {
+        switch (rl) {
+        case 1: return B_Q4_1;
+        case 2: return B_Q4_2;
+        case 4: return B_Q4_4;
+        case 6: return B_Q4_6;
+        case 8: return B_Q4_8;
+        case 12: return B_Q4_12;
+        default: return -1;
+        }
+    }
+    if (type == Q5_K) return rl == 1 ? B_Q5_1 : rl == 2 ? B_Q5_2 : -1;
+    if (type == Q6_K) return rl == 1 ? B_Q6_1 : -1;
+    return -1;
+}
+
+hipError_t launch_gemv_batch(const BatchEntry *in, int count, hipStream_t st) {
+    if (count < 1 || count > MAX_BATCH) return hipErrorInvalidValue;
+    BatchArgs a{};
+    a.count = count;
+    a.first[0] = 0;
+    size_t lds = 4;
+    int threads = 64;
+    int64_t total = 0;
+    const int cus = cu_count();
+    for (int i = 0; i < count; ++i) {
+        const BatchEntry &e = in[i];
+        const Geo g = geometry_of(e.type, e.N, e.K, cus);
+        const int code = body_code(e.type, g.RL);
+        if (code < 0) return hipErrorInvalidValue;
+        a.it[i] = BatchItem{(const uint8_t *)e.W, (const uint16_t *)e.x, (float *)e.y, (int)e.N, (int)e.K,
+                            g.useg, g.P, g.threads, code};
+        total += g.G;
+        if (total > INT32_MAX) return hipErrorInvalidValue;
+        a.first[i + 1] = (int)total;
+        lds = std::max(lds, part_lds(e.N, g));
+        threads = std::max(threads, g.threads);
+    }
+    allow_lds<gemv1_batch_kernel>();
+    hipLaunchKernelGGL(gemv1_batch_kernel, dim3((unsigned)total), dim3(threads), lds, st, a);
+    return hipGetLastError();
 }
 
 template <int T>

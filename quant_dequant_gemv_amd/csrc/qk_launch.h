@@ -11,6 +11,17 @@ namespace qk {
 hipError_t launch_gemv1(int type, const void *W, const void *x, void *y, int64_t N, int64_t K,
                         hipStream_t stream);
 
+// Independent one-column GEMVs in one launch (at most MAX_BATCH).
+constexpr int MAX_BATCH = 16;
+struct BatchEntry {
+    int type;
+    const void *W;
+    const void *x;
+    void *y;
+    int64_t N, K;
+};
+hipError_t launch_gemv_batch(const BatchEntry *entries, int count, hipStream_t stream);
+
 // ncols in 2..8: the few-column verify form (matrix cores).
 hipError_t launch_gemv_multi(int type, const void *W, const void *x, void *y, int64_t N, int64_t K,
                              int ncols, hipStream_t stream);

@@ -128,5 +128,24 @@ def decode_stream(n_layers: int = N_LAYERS):
     return out
 
 
+# Projections of one layer that read the same activations (the layer input,
+# the mixer output, the FFN input, the FFN hidden state) and so may share one
+# launch; entries of a group are adjacent in decode_stream order.
+X_GROUP = {"attn_qkv": "in", "ssm_alpha": "in", "ssm_beta": "in", "attn_q": "in", "attn_k": "in", "attn_v": "in",
+           "ssm_out": "mix", "attn_output": "mix", "ffn_gate": "ffn_in", "ffn_up": "ffn_in", "ffn_down": "ffn_mid"}
+
+
+def decode_groups(entries):
+    """Index lists of the adjacent entries that share a layer and an input."""
+    groups = []
+    for i, e in enumerate(entries):
+        key = (e["layer"], X_GROUP[e["name"]])
+        if groups and groups[-1][0] == key:
+            groups[-1][1].append(i)
+        else:
+            groups.append((key, [i]))
+    return [idx for _, idx in groups]
+
+
 def weight_bytes(entries) -> int:
     return sum(e["N"] * row_bytes(e["qtype"], e["K"]) for e in entries)

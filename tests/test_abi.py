@@ -83,3 +83,23 @@ def test_python_wrappers_raise_not_fallback():
         err = binding.qk_gemv(99, FAKE, FAKE, FAKE, 4, 256, 1, 0)
         raise binding.QKError(err, "qk_gemv")
     assert e.value.code == binding.QK_EINVAL_TYPE
+
+
+def test_batch_item_layout_matches_header():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct qk_gemv_item \{(.*?)\} qk_gemv_item;", text, flags=re.S).group(1)
+    fields = re.findall(r"(\w+);", body)
+    assert fields == [f for f, _ in binding.qk_gemv_item._fields_]
+    assert ctypes.sizeof(binding.qk_gemv_item) == 48
+    assert binding.MAX_BATCH == int(re.search(r"#define QK_MAX_BATCH (\d+)", text).group(1))
+
+
+def test_batch_validation_codes():
+    good = (binding.Q4_K, FAKE, FAKE, FAKE, 4, 256)
+    assert binding.qk_gemv_batch([], 0) == binding.QK_EINVAL_SHAPE
+    assert binding.qk_gemv_batch([good] * (binding.MAX_BATCH + 1), 0) == binding.QK_EINVAL_SHAPE
+    assert binding.load_library().qk_gemv_batch(None, 1, None) == binding.QK_EINVAL_SHAPE
+    assert binding.qk_gemv_batch([good, (99, FAKE, FAKE, FAKE, 4, 256)], 0) == binding.QK_EINVAL_TYPE
+    assert binding.qk_gemv_batch([good, (binding.Q6_K, FAKE, FAKE, FAKE, 4, 300)], 0) == binding.QK_EINVAL_SHAPE
+    assert binding.qk_gemv_batch([(binding.Q5_K, FAKE, FAKE + 2, FAKE, 4, 256), good], 0) == binding.QK_EINVAL_PTR
+    assert binding.qk_gemv_batch([good, (binding.Q4_K, FAKE, FAKE, 0, 4, 256)], 0) == binding.QK_EINVAL_PTR
