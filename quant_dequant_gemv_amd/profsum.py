@@ -1,0 +1,116 @@
+"""Summarise a rocprofv3 kernel trace of bench.py as the markdown kept with
+the profiles.
+
+    rocprofv3 --kernel-trace --output-format csv -d gpurun_out/prof_bench -o bench -- \\
+        python3 -u bench.py --no-stream --no-cpu > gpurun_out/prof_bench.json
+    python3 -m quant_dequant_gemv_amd.profsum gpurun_out/prof_bench/bench_kernel_trace.csv \\
+        gpurun_out/prof_bench.json profiles/<name>.md --command "<the rocprofv3 command>"
+
+Dispatches are grouped by kernel, workgroup size and grid size (one group per
+tensor shape, since shapes sharing a kernel instance differ in launch
+geometry).  The timed region of bench.py is the first warmup*3 + steps*3
+one-column Q4_K GEMV dispatches after the warm-up ones; their mean duration
+is set beside bench.py's own roofline.avg_launch_us from the same run.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+import re
+import statistics
+
+
+def short(name: str) -> str:
+    name = re.sub(r"^void ", "", name)
+    return re.sub(r"\(.*\)$", "", name)
+
+
+def load(trace: str):
+    rows = []
+    with open(trace, newline="") as f:
+        for r in csv.DictReader(f):
+            if r.get("Kind", "KERNEL_DISPATCH") != "KERNEL_DISPATCH":
+                continue
+            rows.append(dict(name=short(r["Kernel_Name"]), dispatch=int(r["Dispatch_Id"]),
+                             us=(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3,
+                             wg=int(r["Workgroup_Size_X"]), grid=int(r["Grid_Size_X"]),
+                             lds=int(r["LDS_Block_Size"]), vgpr=int(r["VGPR_Count"]),
+                             scratch=int(r["Scratch_Size"])))
+    rows.sort(key=lambda r: r["dispatch"])
+    return rows
+
+
+def _bench(path: str) -> dict:
+    with open(path) as f:
+        return json.loads(f.read().strip().splitlines()[-1])
+
+
+def summarise(trace: str, bench_json: str, command: str, plain_json: str | None = None) -> str:
+    rows = load(trace)
+    bench = _bench(bench_json)
+    total = sum(r["us"] for r in rows)
+    groups = {}
+    for r in rows:
+        groups.setdefault((r["name"], r["wg"], r["grid"]), []).append(r)
+    out = ["| kernel | threads/WG | WGs | calls | avg us | median us | min us | max us | share |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for (name, wg, grid), g in sorted(groups.items(), key=lambda kv: -sum(r["us"] for r in kv[1])):
+        d = [r["us"] for r in g]
+        out.append(f"| `{name}` | {wg} | {grid // max(wg, 1)} | {len(d)} | {statistics.mean(d):.3f} | "
+                   f"{statistics.median(d):.3f} | {min(d):.3f} | {max(d):.3f} | {100 * sum(d) / total:.1f}% |")
+    step = [r for r in rows if r["name"].startswith("qk::gemv1_kernel<12,")]
+    per_step = 3
+    w, k = int(bench["warmup"]), int(bench["steps"])
+    timed = step[w * per_step:(w + k) * per_step]
+    rl = bench["roofline"]
+    lines = [f"Command (run from the repository root on one MI355X):", "", f"    {command}", "",
+             "Every dispatch of the profiled run, grouped by kernel and launch geometry "
+             "(one group per tensor shape):", ""] + out
+    if timed:
+        avg = statistics.mean(r["us"] for r in timed)
+        achieved = rl["bytes_per_launch"] / (avg * 1e-6) / 1e9
+        lines += ["", "Timed region of bench.py (its warm-up and timed graphs are the first "
+                  f"{(w + k) * per_step} one-column Q4_K dispatches; the last {k * per_step} are timed):", "",
+                  f"- rocprofv3 mean duration of the {len(timed)} timed dispatches: {avg:.3f} us",
+                  f"- bench.py `roofline.avg_launch_us` of the same run (HIP-event span / launches): "
+                  f"{rl['avg_launch_us']:.3f} us (ratio {rl['avg_launch_us'] / avg:.3f})",
+                  f"- algorithmic bytes per launch {rl['bytes_per_launch']} -> {achieved:.1f} GB/s by rocprofv3, "
+                  f"{rl['achieved']:.1f} GB/s by bench.py = {rl['frac']:.3f} of {rl['peak']:.0f} GB/s",
+                  f"- bench.py `value` of the same run: {bench['value']} {bench['unit']}"]
+        if plain_json:
+            pb = _bench(plain_json)
+            prl = pb["roofline"]
+            lines += [f"- the same bench.py without the profiler, just before on the same GPU: "
+                      f"`roofline.avg_launch_us` {prl['avg_launch_us']:.3f} us (ratio {prl['avg_launch_us'] / avg:.3f} "
+                      f"to the traced kernel mean), achieved {prl['achieved']:.1f} GB/s = {prl['frac']:.3f}, "
+                      f"`value` {pb['value']} {pb['unit']}.  Tracing adds time between dispatches, which "
+                      f"the event span counts and the kernel durations do not."]
+    lines += ["", "Per-shape times reported by bench.py in the same run (graph of back-to-back launches of one "
+              "tensor over >= 1.2 GB of copies):", ""]
+    for sec in ("per_gemv", "mixed_types", "verify"):
+        for r in bench.get(sec, []):
+            extra = f", ncols {r['ncols']}" if "ncols" in r else ""
+            lines.append(f"- {r['name']} ({r['type']} {r['N']}x{r['K']}{extra}): {r['us']} us, "
+                         f"{r['weight_GBs']} GB/s")
+    lines.append(f"\nKernel source hash (bench.py `kernel_hash`): {bench.get('kernel_hash')}")
+    return "\n".join(lines) + "\n"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("trace")
+    ap.add_argument("bench_json")
+    ap.add_argument("out")
+    ap.add_argument("--command", required=True)
+    ap.add_argument("--plain", help="bench.py JSON of an unprofiled run on the same GPU")
+    ap.add_argument("--title", default="gemv1_kernel (one column): Q4_K projection step, rocprofv3 kernel trace")
+    a = ap.parse_args()
+    text = f"# {a.title}\n\n" + summarise(a.trace, a.bench_json, a.command, a.plain)
+    with open(a.out, "w") as f:
+        f.write(text)
+    print(text)
+
+
+if __name__ == "__main__":
+    main()
