@@ -67,9 +67,31 @@ enum {
 #define QK_MAX_NCOLS 8
 
 /*
+ * Row layout flag, OR'ed into a type argument: QK_Q4_K | QK_PLANAR names a
+ * Q4_K tensor whose rows are in the PLANAR layout that qk_repack writes.
+ * PLANAR keeps every byte of a GGUF row but groups them into planes so that
+ * the pieces consecutive lanes read are consecutive in memory (S = K/256
+ * superblocks, U = 4S units of 64 weights, unit u = 4s + q of superblock s):
+ *   Q4_K  H[S][16] (d, dmin, scales[12] of superblock s)
+ *         A[U][16] = qs[32q .. 32q+15]   B[U][16] = qs[32q+16 .. 32q+31]
+ *   Q5_K  H[S][16]  QH0[S][16] = qh[0..15]  QH1[S][16] = qh[16..31]  A[U][16]  B[U][16]
+ *   Q6_K  A[U][16] = ql[64n+16b ..]  B[U][16] = ql[64n+32+16b ..]  C[U][16] = qh[32n+16b ..]
+ *         SC[U][4] = scales[8n+b], scales[8n+2+b], scales[8n+4+b], scales[8n+6+b]
+ *         D[S][2] = d;  (q = 2n+b), then zero padding to a multiple of 16 bytes
+ * Planes follow one another in the order listed; rows are
+ * qk_row_bytes(type | QK_PLANAR, K) bytes apart.  This is a repack for this
+ * GPU, not a format of the pages; the pages' B70 plan lists "B70-native weight
+ * packs" among what may be built and kept resident ("Non-Negotiable
+ * Requirements" item 7).  qk_gemv (ncols = 1), qk_gemv_batch and qk_dequant
+ * accept it; qk_gemv with ncols > 1 does not (QK_EINVAL_TYPE).
+ */
+#define QK_PLANAR 0x100
+
+/*
  * qk_gemv -- y[n][c] = sum_k dequant(W)[n][k] * x[k][c], fp32 accumulation.
  *
- *   type   QK_Q4_K, QK_Q5_K or QK_Q6_K (one flag for the whole tensor)
+ *   type   QK_Q4_K, QK_Q5_K or QK_Q6_K (one flag for the whole tensor),
+ *          optionally | QK_PLANAR (then ncols must be 1)
  *   W      device pointer to N rows of K/256 superblocks, 16-byte aligned
  *   x      device pointer to K*ncols fp16 values, 16-byte aligned
  *   y      device pointer to N*ncols fp32 values, 4-byte aligned (written)
@@ -131,11 +153,25 @@ typedef struct qk_gemv_item {
  */
 int qk_gemv_batch(const qk_gemv_item *items, int count, void *stream);
 
+/*
+ * qk_repack -- rewrite N GGUF rows of `type` (no flag) as PLANAR rows: Wp is
+ * then a valid QK_PLANAR tensor with the same weights.  One-time, outside the
+ * decode loop; every y and every dequantised weight computed from Wp is
+ * bit-identical to the one computed from W.
+ *
+ *   W      device pointer to N GGUF rows, 16-byte aligned (read)
+ *   Wp     device pointer to N * qk_row_bytes(type | QK_PLANAR, K) bytes,
+ *          16-byte aligned, not overlapping W (written)
+ * Errors as for qk_dequant; overlapping W and Wp give QK_EINVAL_PTR.
+ */
+int qk_repack(int type, const void *W, void *Wp, int64_t N, int64_t K, void *stream);
+
 /* Bytes per 256-weight superblock: 144 / 176 / 210, or -1 for a bad type. */
 int qk_block_bytes(int type);
 
-/* Bytes per row of K weights, (K/256) * qk_block_bytes(type), or -1 for a bad
- * type or a K that is not a positive multiple of 256. */
+/* Bytes per row of K weights: (K/256) * qk_block_bytes(type) for a GGUF type;
+ * for type | QK_PLANAR the PLANAR row (the same, rounded up to 16 bytes for
+ * Q6_K); -1 for a bad type or a K that is not a positive multiple of 256. */
 int64_t qk_row_bytes(int type, int64_t K);
 
 /* Static description of a return code; for QK_ELAUNCH the HIP error text of

@@ -18,9 +18,10 @@ Q4_K, Q5_K, Q6_K = 12, 13, 14
 QK_OK, QK_EINVAL_TYPE, QK_EINVAL_SHAPE, QK_EINVAL_PTR, QK_ELAUNCH = 0, -1, -2, -3, -4
 MAX_NCOLS = 8
 MAX_BATCH = 16
+PLANAR = 0x100  # QK_PLANAR: layout flag OR'ed into a type
 
-EXPORTS = ("qk_gemv", "qk_gemv_batch", "qk_dequant", "qk_block_bytes", "qk_row_bytes", "qk_strerror",
-           "qk_version")
+EXPORTS = ("qk_gemv", "qk_gemv_batch", "qk_dequant", "qk_repack", "qk_block_bytes", "qk_row_bytes",
+           "qk_strerror", "qk_version")
 
 
 class qk_gemv_item(ctypes.Structure):
@@ -54,6 +55,8 @@ def load_library(path: str = LIB_PATH):
     lib.qk_gemv_batch.restype = c_int
     lib.qk_dequant.argtypes = [c_int, P, P, i64, i64, P]
     lib.qk_dequant.restype = c_int
+    lib.qk_repack.argtypes = [c_int, P, P, i64, i64, P]
+    lib.qk_repack.restype = c_int
     lib.qk_block_bytes.argtypes = [c_int]
     lib.qk_block_bytes.restype = c_int
     lib.qk_row_bytes.argtypes = [c_int, i64]
@@ -80,6 +83,10 @@ def qk_gemv_batch(items, stream: int = 0) -> int:
 
 def qk_dequant(qtype: int, W: int, out: int, N: int, K: int, stream: int = 0) -> int:
     return load_library().qk_dequant(qtype, W, out, N, K, stream)
+
+
+def qk_repack(qtype: int, W: int, Wp: int, N: int, K: int, stream: int = 0) -> int:
+    return load_library().qk_repack(qtype, W, Wp, N, K, stream)
 
 
 def qk_block_bytes(qtype: int) -> int:
@@ -154,4 +161,17 @@ def dequant(qtype: int, W, N: int, K: int, out=None, stream=None):
     rc = qk_dequant(qtype, W.data_ptr(), out.data_ptr(), N, K, _stream_handle(stream))
     if rc != QK_OK:
         raise QKError(rc, "qk_dequant")
+    return out
+
+
+def repack(qtype: int, W, N: int, K: int, out=None, stream=None):
+    """GGUF rows -> PLANAR rows on the GPU; returns the uint8 device tensor to
+    pass with type ``qtype | PLANAR``."""
+    import torch
+    nbytes = N * qk_row_bytes(qtype | PLANAR, K)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    rc = qk_repack(qtype, W.data_ptr(), out.data_ptr(), N, K, _stream_handle(stream))
+    if rc != QK_OK:
+        raise QKError(rc, "qk_repack")
     return out

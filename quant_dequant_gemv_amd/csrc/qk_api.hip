@@ -14,6 +14,8 @@ namespace {
 
 thread_local char g_launch_msg[256] = "launch failed";
 
+static_assert(QK_PLANAR == qk::PLANAR_FLAG, "layout flag of the C ABI and the kernels");
+
 int block_bytes(int type) {
     switch (type) {
     case QK_Q4_K: return 144;
@@ -25,14 +27,23 @@ int block_bytes(int type) {
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// Bytes of one row in the layout the type flags name, or -1.
+int64_t row_bytes_of(int type, int64_t K) {
+    const int bb = block_bytes(type & ~QK_PLANAR);
+    if (bb < 0 || (type & ~(QK_PLANAR | 0xff)) != 0 || K < 256 || (K % 256) != 0) return -1;
+    const int64_t b = (K / 256) * bb;
+    return (type & QK_PLANAR) ? (b + 15) / 16 * 16 : b;
+}
+
 // Shared shape check.  Rows and columns must keep every byte offset inside
 // int64 and every per-launch index inside the kernels' 32-bit ranges.
 int check_shape(int type, int64_t N, int64_t K, int ncols) {
-    if (block_bytes(type) < 0) return QK_EINVAL_TYPE;
+    if (block_bytes(type & ~QK_PLANAR) < 0 || (type & ~(QK_PLANAR | 0xff)) != 0) return QK_EINVAL_TYPE;
     if (N < 1 || K < 256 || (K % 256) != 0) return QK_EINVAL_SHAPE;
     if (ncols < 1 || ncols > QK_MAX_NCOLS) return QK_EINVAL_SHAPE;
+    if ((type & QK_PLANAR) && ncols != 1) return QK_EINVAL_TYPE;
     if (K > (int64_t)1 << 30 || N > ((int64_t)1 << 31) - 1) return QK_EINVAL_SHAPE;
-    const int64_t row_bytes = (K / 256) * block_bytes(type);
+    const int64_t row_bytes = row_bytes_of(type, K);
     if (N > INT64_MAX / row_bytes) return QK_EINVAL_SHAPE;
     if (N > INT64_MAX / ((int64_t)K * 4)) return QK_EINVAL_SHAPE;
     return QK_OK;
@@ -50,11 +61,7 @@ extern "C" {
 
 int qk_block_bytes(int type) { return block_bytes(type); }
 
-int64_t qk_row_bytes(int type, int64_t K) {
-    const int bb = block_bytes(type);
-    if (bb < 0 || K < 256 || (K % 256) != 0) return -1;
-    return (K / 256) * bb;
-}
+int64_t qk_row_bytes(int type, int64_t K) { return row_bytes_of(type, K); }
 
 int qk_gemv(int type, const void *W, const void *x, void *y, int64_t N, int64_t K, int ncols, void *stream) {
     const int rc = check_shape(type, N, K, ncols);
@@ -86,10 +93,23 @@ int qk_dequant(int type, const void *W, void *out, int64_t N, int64_t K, void *s
     return launched(qk::launch_dequant(type, W, out, N, K, (hipStream_t)stream));
 }
 
+int qk_repack(int type, const void *W, void *Wp, int64_t N, int64_t K, void *stream) {
+    if (type & QK_PLANAR) return QK_EINVAL_TYPE;
+    const int rc = check_shape(type, N, K, 1);
+    if (rc) return rc;
+    if (!W || !Wp || !aligned(W, 16) || !aligned(Wp, 16)) return QK_EINVAL_PTR;
+    const uintptr_t a0 = (uintptr_t)W, a1 = a0 + (uintptr_t)(N * row_bytes_of(type, K));
+    const uintptr_t b0 = (uintptr_t)Wp, b1 = b0 + (uintptr_t)(N * row_bytes_of(type | QK_PLANAR, K));
+    if (a0 < b1 && b0 < a1) return QK_EINVAL_PTR;
+    return launched(qk::launch_repack(type, W, Wp, N, K, (hipStream_t)stream));
+}
+
 const char *qk_strerror(int code) {
     switch (code) {
     case QK_OK: return "ok";
-    case QK_EINVAL_TYPE: return "invalid type: expected QK_Q4_K (12), QK_Q5_K (13) or QK_Q6_K (14)";
+    case QK_EINVAL_TYPE:
+        return "invalid type: expected QK_Q4_K (12), QK_Q5_K (13) or QK_Q6_K (14), optionally | QK_PLANAR "
+               "(0x100) with ncols = 1 (qk_repack takes the type without the flag)";
     case QK_EINVAL_SHAPE: return "invalid shape: need N >= 1, K a positive multiple of 256, 1 <= ncols <= 8";
     case QK_EINVAL_PTR: return "invalid pointer: NULL, or W/x not 16-byte aligned, or y/out not 4-byte aligned";
     case QK_ELAUNCH: return g_launch_msg;

@@ -40,6 +40,66 @@ template <> struct Fmt<Q4_K> { static constexpr int bytes = 144; static constexp
 template <> struct Fmt<Q5_K> { static constexpr int bytes = 176; static constexpr int group = 32; };
 template <> struct Fmt<Q6_K> { static constexpr int bytes = 210; static constexpr int group = 16; };
 
+// ---------------------------------------------------------------------------
+// Row layouts.  GGUF: a row is K/256 superblocks back to back, as in the file.
+// PLANAR: the same bytes of a row regrouped into planes, so that the pieces
+// the 64 lanes of a wave read for 64 consecutive units are consecutive in
+// memory (whole 1 KB per load instruction instead of 16-byte pieces at the
+// superblock stride).  S = K/256 superblocks, U = 4S units, unit u = 4s + q:
+//   Q4_K: H[S][16] (d, dmin, scales)  A[U][16] = qs[32q..32q+15] of unit u
+//         B[U][16] = qs[32q+16..32q+31]                         = 144 S bytes
+//   Q5_K: H[S][16]  QH0[S][16] = qh[0..15]  QH1[S][16] = qh[16..31]
+//         A[U][16]  B[U][16] (qs halves as for Q4_K)             = 176 S bytes
+//   Q6_K: A[U][16] = ql[64n+16b..]  B[U][16] = ql[64n+32+16b..]
+//         C[U][16] = qh[32n+16b..]  SC[U][4] = scales[8n+2t+b], t = 0..3
+//         D[S][2] = d                       (q = 2n+b)          = 210 S bytes,
+//         row padded to a multiple of 16 bytes.
+// ---------------------------------------------------------------------------
+enum : int { GGUF = 0, PLANAR = 1 };
+
+__host__ __device__ constexpr int64_t layout_row_bytes(int T, int L, int64_t K) {
+    const int64_t S = K / 256;
+    const int64_t b = S * (T == Q4_K ? 144 : T == Q5_K ? 176 : 210);
+    return (L == PLANAR && T == Q6_K) ? (b + 15) / 16 * 16 : b;
+}
+
+// Byte offsets, within a row, of the pieces unit u reads (S superblocks per row).
+template <int T, int L> struct UnitAddr;
+template <> struct UnitAddr<Q4_K, GGUF> {
+    uint32_t h, a, b;
+    __host__ __device__ UnitAddr(int /*S*/, int u) : h(144u * (u >> 2)), a(h + 16u + 32u * (u & 3)), b(a + 16u) {}
+};
+template <> struct UnitAddr<Q4_K, PLANAR> {
+    uint32_t h, a, b;
+    __host__ __device__ UnitAddr(int S, int u) : h(16u * (u >> 2)), a(16u * S + 16u * u), b(80u * S + 16u * u) {}
+};
+template <> struct UnitAddr<Q5_K, GGUF> {
+    uint32_t h, qh0, qh1, a, b;
+    __host__ __device__ UnitAddr(int /*S*/, int u)
+        : h(176u * (u >> 2)), qh0(h + 16u), qh1(h + 32u), a(h + 48u + 32u * (u & 3)), b(a + 16u) {}
+};
+template <> struct UnitAddr<Q5_K, PLANAR> {
+    uint32_t h, qh0, qh1, a, b;
+    __host__ __device__ UnitAddr(int S, int u)
+        : h(16u * (u >> 2)), qh0(16u * S + h), qh1(32u * S + h), a(48u * S + 16u * u), b(112u * S + 16u * u) {}
+};
+template <> struct UnitAddr<Q6_K, GGUF> {
+    uint32_t a, b, c, sc, d;
+    __host__ __device__ UnitAddr(int /*S*/, int u) {
+        const uint32_t sb = 210u * (u >> 2), n = (u >> 1) & 1, bb = u & 1;
+        a = sb + 64u * n + 16u * bb;
+        b = a + 32u;
+        c = sb + 128u + 32u * n + 16u * bb;
+        sc = sb + 192u + 8u * n;
+        d = sb + 208u;
+    }
+};
+template <> struct UnitAddr<Q6_K, PLANAR> {
+    uint32_t a, b, c, sc, d;
+    __host__ __device__ UnitAddr(int S, int u)
+        : a(16u * u), b(64u * S + 16u * u), c(128u * S + 16u * u), sc(192u * S + 4u * u), d(208u * S + 2u * (u >> 2)) {}
+};
+
 // fp32 += a.lo*b.lo + a.hi*b.hi with fp16 operands (v_dot2_f32_f16).
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
@@ -74,6 +134,11 @@ __device__ __forceinline__ uint2 ld8(const uint8_t *p) {
     } else {
         return *reinterpret_cast<const uint2 *>(p);
     }
+}
+template <bool NT>
+__device__ __forceinline__ uint32_t ld4(const uint8_t *p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+    else return *reinterpret_cast<const uint32_t *>(p);
 }
 template <bool NT>
 __device__ __forceinline__ uint32_t ld2(const uint8_t *p) {
@@ -136,11 +201,11 @@ template <int T> struct Unit;
 //   p[2] = high-sub-block pair A (s = 16)   p[3] = high pair B (s = 16)
 template <> struct Unit<Q4_K> {
     uint4 h, a, b;
-    template <bool NT>
-    __device__ __forceinline__ void load(const uint8_t *sb, int q) {
-        h = ld16<NT>(sb);
-        a = ld16<NT>(sb + 16 + 32 * q);
-        b = ld16<NT>(sb + 32 + 32 * q);
+    template <bool NT, int L>
+    __device__ __forceinline__ void load(const uint8_t *row, const UnitAddr<Q4_K, L> &o) {
+        h = ld16<NT>(row + o.h);
+        a = ld16<NT>(row + o.a);
+        b = ld16<NT>(row + o.b);
     }
     __device__ __forceinline__ uint4 header() const { return h; }
     __device__ __forceinline__ uint32_t qword(int i) const { return i < 4 ? word(a, i) : word(b, i - 4); }
@@ -158,13 +223,13 @@ template <> struct Unit<Q4_K> {
 // byte are bits 2q (low sub-block) and 2q+1 (high sub-block).
 template <> struct Unit<Q5_K> {
     uint4 h, qh0, qh1, a, b;
-    template <bool NT>
-    __device__ __forceinline__ void load(const uint8_t *sb, int q) {
-        h = ld16<NT>(sb);
-        qh0 = ld16<NT>(sb + 16);
-        qh1 = ld16<NT>(sb + 32);
-        a = ld16<NT>(sb + 48 + 32 * q);
-        b = ld16<NT>(sb + 64 + 32 * q);
+    template <bool NT, int L>
+    __device__ __forceinline__ void load(const uint8_t *row, const UnitAddr<Q5_K, L> &o) {
+        h = ld16<NT>(row + o.h);
+        qh0 = ld16<NT>(row + o.qh0);
+        qh1 = ld16<NT>(row + o.qh1);
+        a = ld16<NT>(row + o.a);
+        b = ld16<NT>(row + o.b);
     }
     __device__ __forceinline__ uint4 header() const { return h; }
     __device__ __forceinline__ uint32_t qword(int i) const { return i < 4 ? word(a, i) : word(b, i - 4); }
@@ -187,16 +252,16 @@ template <> struct Unit<Q5_K> {
 //   p[2t] = quarter t pair A, p[2t+1] = quarter t pair B;  s = 1 for t < 2, 16 for t >= 2.
 template <> struct Unit<Q6_K> {
     uint4 a, b, c;
-    uint2 sc;      // scales[8n .. 8n+7]
+    uint2 sc;      // GGUF: scales[8n .. 8n+7];  PLANAR: .x = this unit's 4 scales, quarter order
     uint32_t d;    // fp16 d in the low half
-    template <bool NT>
-    __device__ __forceinline__ void load(const uint8_t *sb, int q) {
-        const int n = q >> 1, bb = q & 1;
-        a = ld16<NT>(sb + 64 * n + 16 * bb);
-        b = ld16<NT>(sb + 64 * n + 32 + 16 * bb);
-        c = ld16<NT>(sb + 128 + 32 * n + 16 * bb);
-        sc = ld8<NT>(sb + 192 + 8 * n);
-        d = ld2<NT>(sb + 208);
+    template <bool NT, int L>
+    __device__ __forceinline__ void load(const uint8_t *row, const UnitAddr<Q6_K, L> &o) {
+        a = ld16<NT>(row + o.a);
+        b = ld16<NT>(row + o.b);
+        c = ld16<NT>(row + o.c);
+        if constexpr (L == PLANAR) sc = make_uint2(ld4<NT>(row + o.sc), 0u);
+        else sc = ld8<NT>(row + o.sc);
+        d = ld2<NT>(row + o.d);
     }
     __device__ __forceinline__ void patterns(int i, int /*q*/, uint32_t p[8]) const {
         const uint32_t A = word(a, i), B = word(b, i), C = word(c, i);
@@ -212,7 +277,9 @@ template <> struct Unit<Q6_K> {
         p[7] = (B8 & 0x00f000f0u) | (c2b & 0x03000300u);
     }
     // signed scale of quarter t for this unit (b = q & 1): scales[8n + 2t + b]
+    template <int L = GGUF>
     __device__ __forceinline__ int scale(int t, int q) const {
+        if constexpr (L == PLANAR) return (int)(int8_t)(uint8_t)(sc.x >> (8 * t));
         const int idx = 2 * t + (q & 1);
         const uint32_t wv = idx < 4 ? sc.x : sc.y;
         return (int)(int8_t)(uint8_t)(wv >> (8 * (idx & 3)));

@@ -84,30 +84,8 @@ __device__ __forceinline__ void load_x(XReg<T> &X, const uint16_t *__restrict__ 
     }
 }
 
-// Dot of one unit with the register-held x of the same unit column.
-template <int T>
-__device__ __forceinline__ float unit_dot(const Unit<T> &U, int q, const KScaleSel &sel, const XReg<T> &X) {
-    float aL = 0.f, aH = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t p[4];
-        U.patterns(i, q, p);
-        aL = dot2(p[0], X.xr[2 * i], aL);
-        aL = dot2(p[1], X.xr[2 * i + 1], aL);
-        aH = dot2(p[2], X.xr[16 + 2 * i], aH);
-        aH = dot2(p[3], X.xr[17 + 2 * i], aH);
-    }
-    const uint4 h = U.header();
-    const KScales s = k_scales(h, sel);
-    const float d = f16_lo(h.x), dmin = f16_hi(h.x);
-    // patterns hold q * 2^-24 (low sub-block) and 16q * 2^-24 (high)
-    const float fl = d * (float)s.sc_lo * 0x1p24f;
-    const float fh = d * (float)s.sc_hi * 0x1p20f;
-    return fl * aL + fh * aH - dmin * ((float)s.m_lo * X.xsum[0] + (float)s.m_hi * X.xsum[1]);
-}
-
-template <>
-__device__ __forceinline__ float unit_dot<Q6_K>(const Unit<Q6_K> &U, int q, const KScaleSel &, const XReg<Q6_K> &X) {
+template <int L>
+__device__ __forceinline__ float unit_dot_q6(const Unit<Q6_K> &U, int q, const XReg<Q6_K> &X) {
     float R[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -123,10 +101,37 @@ __device__ __forceinline__ float unit_dot<Q6_K>(const Unit<Q6_K> &U, int q, cons
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const float k = t < 2 ? 0x1p24f : 0x1p20f;  // patterns hold s*q*2^-24, s = 1 or 16
-        acc += (float)U.scale(t, q) * (R[t] * k - 32.f * X.xsum[t]);
+        acc += (float)U.template scale<L>(t, q) * (R[t] * k - 32.f * X.xsum[t]);
     }
     return f16_lo(U.d) * acc;
 }
+
+// Dot of one unit with the register-held x of the same unit column.
+template <int T, int L>
+__device__ __forceinline__ float unit_dot(const Unit<T> &U, int q, const KScaleSel &sel, const XReg<T> &X) {
+    if constexpr (T == Q6_K) {
+        return unit_dot_q6<L>(U, q, X);
+    } else {
+        float aL = 0.f, aH = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t p[4];
+            U.patterns(i, q, p);
+            aL = dot2(p[0], X.xr[2 * i], aL);
+            aL = dot2(p[1], X.xr[2 * i + 1], aL);
+            aH = dot2(p[2], X.xr[16 + 2 * i], aH);
+            aH = dot2(p[3], X.xr[17 + 2 * i], aH);
+        }
+        const uint4 h = U.header();
+        const KScales s = k_scales(h, sel);
+        const float d = f16_lo(h.x), dmin = f16_hi(h.x);
+        // patterns hold q * 2^-24 (low sub-block) and 16q * 2^-24 (high)
+        const float fl = d * (float)s.sc_lo * 0x1p24f;
+        const float fh = d * (float)s.sc_hi * 0x1p20f;
+        return fl * aL + fh * aH - dmin * ((float)s.m_lo * X.xsum[0] + (float)s.m_hi * X.xsum[1]);
+    }
+}
+
 
 // ---------------------------------------------------------------------------
 // One column, x-stationary and row-balanced.
@@ -150,7 +155,7 @@ __device__ __forceinline__ float unit_dot<Q6_K>(const Unit<Q6_K> &U, int q, cons
 // ---------------------------------------------------------------------------
 // Workgroup blk of nblk (nthr threads, a multiple of 64) takes rows
 // [blk*N/nblk, (blk+1)*N/nblk).
-template <int T, int RL, int D, bool NT>
+template <int T, int L, int RL, int D, bool NT>
 __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const uint16_t *__restrict__ x,
                                            float *__restrict__ y, int N, int K, int useg, int P, int blk,
                                            int nblk, int nthr) {
@@ -162,7 +167,7 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     const int r1 = (int)((int64_t)(blk + 1) * N / nblk);
     const int R = r1 - r0;
     const int U = K >> 6;
-    const size_t row_bytes = (size_t)(K >> 8) * BB;
+    const size_t row_bytes = (size_t)layout_row_bytes(T, L, K);
     const int ph = tid / useg, uc = tid - ph * useg;
     const bool lane_ok = ph < P;
     const int ph_c = lane_ok ? ph : 0;
@@ -177,14 +182,14 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
         const KScaleSel sel(q);
         XReg<T> X;
         load_x<T>(X, x, u);
-        const uint8_t *wcol = W + (size_t)(u >> 2) * BB;
+        const UnitAddr<T, L> ua(K >> 8, u);
 
         for (int i0 = 0; i0 < rows_lane; i0 += RL) {
             // straight line over RL rows with a ring of DD units in flight
             Unit<T> buf[DD];
             auto load_row = [&](Unit<T> &dst, int i) {
                 const int row = min(r0 + ph_c + P * (i0 + i), r1 - 1);
-                dst.template load<NT>(wcol + (size_t)row * row_bytes, q);
+                dst.template load<NT, L>(W + (size_t)row * row_bytes, ua);
             };
 #pragma unroll
             for (int p = 0; p < DD; ++p) load_row(buf[p], p);
@@ -193,7 +198,7 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
                 const int i = i0 + p;
                 const int row = r0 + ph_c + P * i;
                 const bool ok = col_ok && i < rows_lane && row < r1;
-                const float v = unit_dot<T>(buf[p % DD], q, sel, X);
+                const float v = unit_dot<T, L>(buf[p % DD], q, sel, X);
                 if (p + DD < RL) load_row(buf[p % DD], p + DD);
                 const int slot = ok ? (row - r0) * useg + uc : spare;
                 part[slot] = (s0 == 0 ? 0.f : part[slot]) + v;
@@ -224,11 +229,11 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     }
 }
 
-template <int T, int RL, int D, bool NT>
+template <int T, int L, int RL, int D, bool NT>
 __global__ void __launch_bounds__(1024) gemv1_kernel(const uint8_t *__restrict__ W,
                                                       const uint16_t *__restrict__ x,
                                                       float *__restrict__ y, int N, int K, int useg, int P) {
-    gemv1_body<T, RL, D, NT>(W, x, y, N, K, useg, P, (int)blockIdx.x, (int)gridDim.x, (int)blockDim.x);
+    gemv1_body<T, L, RL, D, NT>(W, x, y, N, K, useg, P, (int)blockIdx.x, (int)gridDim.x, (int)blockDim.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -239,7 +244,8 @@ __global__ void __launch_bounds__(1024) gemv1_kernel(const uint8_t *__restrict__
 // A workgroup with more threads than its entry needs retires the surplus
 // waves at once (a retired wave does not hold up the barrier).
 // ---------------------------------------------------------------------------
-enum BodyCode { B_Q4_1, B_Q4_2, B_Q4_4, B_Q4_6, B_Q4_8, B_Q4_12, B_Q5_1, B_Q5_2, B_Q6_1 };
+enum BodyCode { B_Q4_1, B_Q4_2, B_Q4_4, B_Q4_6, B_Q4_8, B_Q4_12, B_Q5_1, B_Q5_2, B_Q6_1, B_COUNT };
+// code + B_COUNT: the same body on the PLANAR layout
 
 struct BatchItem {
     const uint8_t *W;
@@ -259,7 +265,8 @@ __global__ void __launch_bounds__(1024) gemv1_batch_kernel(const BatchArgs a) {
     const BatchItem &e = a.it[i];
     if ((int)threadIdx.x >= e.threads) return;
     const int blk = (int)blockIdx.x - a.first[i], nblk = a.first[i + 1] - a.first[i];
-#define QK_BODY(T, RL, D) gemv1_body<T, RL, D, false>(e.W, e.x, e.y, e.N, e.K, e.useg, e.P, blk, nblk, e.threads)
+#define QK_BODY(T, RL, D) gemv1_body<T, GGUF, RL, D, false>(e.W, e.x, e.y, e.N, e.K, e.useg, e.P, blk, nblk, e.threads)
+#define QK_BODYP(T, RL, D) gemv1_body<T, PLANAR, RL, D, false>(e.W, e.x, e.y, e.N, e.K, e.useg, e.P, blk, nblk, e.threads)
     switch (e.code) {
     case B_Q4_1: QK_BODY(Q4_K, 1, 1); break;
     case B_Q4_2: QK_BODY(Q4_K, 2, 2); break;
@@ -270,8 +277,18 @@ __global__ void __launch_bounds__(1024) gemv1_batch_kernel(const BatchArgs a) {
     case B_Q5_1: QK_BODY(Q5_K, 1, 1); break;
     case B_Q5_2: QK_BODY(Q5_K, 2, 2); break;
     case B_Q6_1: QK_BODY(Q6_K, 1, 1); break;
+    case B_COUNT + B_Q4_1: QK_BODYP(Q4_K, 1, 1); break;
+    case B_COUNT + B_Q4_2: QK_BODYP(Q4_K, 2, 2); break;
+    case B_COUNT + B_Q4_4: QK_BODYP(Q4_K, 4, 2); break;
+    case B_COUNT + B_Q4_6: QK_BODYP(Q4_K, 6, 2); break;
+    case B_COUNT + B_Q4_8: QK_BODYP(Q4_K, 8, 2); break;
+    case B_COUNT + B_Q4_12: QK_BODYP(Q4_K, 12, 2); break;
+    case B_COUNT + B_Q5_1: QK_BODYP(Q5_K, 1, 1); break;
+    case B_COUNT + B_Q5_2: QK_BODYP(Q5_K, 2, 2); break;
+    case B_COUNT + B_Q6_1: QK_BODYP(Q6_K, 1, 1); break;
     default: break;
     }
+#undef QK_BODYP
 #undef QK_BODY
 }
 
@@ -283,20 +300,18 @@ __global__ void __launch_bounds__(1024) gemv1_batch_kernel(const BatchArgs a) {
 __device__ __forceinline__ uint32_t pat_lo(uint32_t p, int shift) { return (p & 0xffffu) >> shift; }
 __device__ __forceinline__ uint32_t pat_hi(uint32_t p, int shift) { return (p >> 16) >> shift; }
 
-template <int T>
+template <int T, int L>
 __global__ void __launch_bounds__(WG) dequant_kernel(const uint8_t *__restrict__ W, float *__restrict__ out,
                                                      int64_t N, int K) {
-    constexpr int BB = Fmt<T>::bytes;
     const int64_t unit = (int64_t)blockIdx.x * WG + threadIdx.x;
     const int upr = K >> 6;
     if (unit >= N * upr) return;
     const int64_t row = unit / upr;
     const int u = (int)(unit - row * upr);
     const int s = u >> 2, q = u & 3;
-    const uint8_t *sb = W + ((size_t)row * (size_t)(K >> 8) + (size_t)s) * BB;
     float *o = out + (size_t)row * (size_t)K + 256 * s;
     Unit<T> U;
-    U.template load<false>(sb, q);
+    U.template load<false, L>(W + (size_t)row * (size_t)layout_row_bytes(T, L, K), UnitAddr<T, L>(K >> 8, u));
     if constexpr (T == Q6_K) {
         const float d = f16_lo(U.d);
         const int kb = 128 * (q >> 1) + 16 * (q & 1);
@@ -307,7 +322,7 @@ __global__ void __launch_bounds__(WG) dequant_kernel(const uint8_t *__restrict__
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int sh = t < 2 ? 0 : 4;
-                const int sc = U.scale(t, q);
+                const int sc = U.template scale<L>(t, q);
                 const uint32_t pa = p[2 * t], pb = p[2 * t + 1];
                 float4 w;
                 w.x = d * (float)(sc * ((int)pat_lo(pa, sh) - 32));
@@ -343,7 +358,65 @@ __global__ void __launch_bounds__(WG) dequant_kernel(const uint8_t *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Launchers.
+// GGUF -> PLANAR repack, one superblock per thread: the same bytes moved to
+// the planes (qk_format.h); the Q6_K row padding is written as zeros.
+// ---------------------------------------------------------------------------
+template <int T>
+__global__ void __launch_bounds__(WG) repack_kernel(const uint8_t *__restrict__ W, uint8_t *__restrict__ Wp,
+                                                    int64_t N, int K) {
+    constexpr int BB = Fmt<T>::bytes;
+    const int S = K >> 8;
+    const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;
+    if (i >= N * S) return;
+    const int64_t row = i / S;
+    const int s = (int)(i - row * S);
+    const uint8_t *sb = W + ((size_t)row * S + s) * BB;
+    const size_t prow = (size_t)layout_row_bytes(T, PLANAR, K);
+    uint8_t *rp = Wp + (size_t)row * prow;
+    auto cp16 = [](uint8_t *dst, const uint8_t *src) {
+        *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+    };
+    if constexpr (T == Q6_K) {
+        // scales[16] at 192 and d at 208; superblocks are only 2-byte aligned
+        uint8_t sc[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) sc[k] = sb[192 + k];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const UnitAddr<Q6_K, GGUF> g(0, q);
+            const UnitAddr<Q6_K, PLANAR> o(S, 4 * s + q);
+            cp16(rp + o.a, sb + g.a);
+            cp16(rp + o.b, sb + g.b);
+            cp16(rp + o.c, sb + g.c);
+            const int n = q >> 1, b = q & 1;
+            uint32_t v = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v |= (uint32_t)sc[8 * n + 2 * t + b] << (8 * t);
+            *reinterpret_cast<uint32_t *>(rp + o.sc) = v;
+        }
+        *reinterpret_cast<uint16_t *>(rp + UnitAddr<Q6_K, PLANAR>(S, 4 * s).d) =
+            *reinterpret_cast<const uint16_t *>(sb + 208);
+        if (s == S - 1)
+            for (size_t k = (size_t)210 * S; k < prow; ++k) rp[k] = 0;
+    } else {
+        const UnitAddr<T, PLANAR> o0(S, 4 * s);
+        cp16(rp + o0.h, sb);
+        if constexpr (T == Q5_K) {
+            cp16(rp + o0.qh0, sb + 16);
+            cp16(rp + o0.qh1, sb + 32);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const UnitAddr<T, GGUF> g(0, q);
+            const UnitAddr<T, PLANAR> o(S, 4 * s + q);
+            cp16(rp + o.a, sb + g.a);
+            cp16(rp + o.b, sb + g.b);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.  The type argument carries the PLANAR_FLAG bit of the C ABI.
 // ---------------------------------------------------------------------------
 constexpr int LDS_PART = 96 * 1024;  // LDS for the per-unit partial sums
 
@@ -418,26 +491,26 @@ static void allow_lds() {
     (void)done;
 }
 
-template <int T, int RL, int D, bool NT>
+template <int T, int L, int RL, int D, bool NT>
 static hipError_t launch1(const void *W, const void *x, void *y, int64_t N, int64_t K, Geo geo, hipStream_t st) {
     const size_t lds = part_lds(N, geo);
-    allow_lds<gemv1_kernel<T, RL, D, NT>>();
-    hipLaunchKernelGGL((gemv1_kernel<T, RL, D, NT>), dim3(geo.G), dim3(geo.threads), lds, st,
+    allow_lds<gemv1_kernel<T, L, RL, D, NT>>();
+    hipLaunchKernelGGL((gemv1_kernel<T, L, RL, D, NT>), dim3(geo.G), dim3(geo.threads), lds, st,
                        (const uint8_t *)W, (const uint16_t *)x, (float *)y, (int)N, (int)K, geo.useg, geo.P);
     return hipGetLastError();
 }
 
 // Two units in flight per lane, one for one-row rounds.
-template <int T>
+template <int T, int L>
 static hipError_t gemv1_dispatch(const void *W, const void *x, void *y, int64_t N, int64_t K, hipStream_t st) {
     const Geo geo = geometry<T>(N, K, cu_count());
     switch (geo.RL) {
-    case 1: return launch1<T, 1, 1, false>(W, x, y, N, K, geo, st);
-    case 2: if constexpr (T != Q6_K) return launch1<T, 2, 2, false>(W, x, y, N, K, geo, st); break;
-    case 4: if constexpr (T == Q4_K) return launch1<T, 4, 2, false>(W, x, y, N, K, geo, st); break;
-    case 6: if constexpr (T == Q4_K) return launch1<T, 6, 2, false>(W, x, y, N, K, geo, st); break;
-    case 8: if constexpr (T == Q4_K) return launch1<T, 8, 2, false>(W, x, y, N, K, geo, st); break;
-    case 12: if constexpr (T == Q4_K) return launch1<T, 12, 2, false>(W, x, y, N, K, geo, st); break;
+    case 1: return launch1<T, L, 1, 1, false>(W, x, y, N, K, geo, st);
+    case 2: if constexpr (T != Q6_K) return launch1<T, L, 2, 2, false>(W, x, y, N, K, geo, st); break;
+    case 4: if constexpr (T == Q4_K) return launch1<T, L, 4, 2, false>(W, x, y, N, K, geo, st); break;
+    case 6: if constexpr (T == Q4_K) return launch1<T, L, 6, 2, false>(W, x, y, N, K, geo, st); break;
+    case 8: if constexpr (T == Q4_K) return launch1<T, L, 8, 2, false>(W, x, y, N, K, geo, st); break;
+    case 12: if constexpr (T == Q4_K) return launch1<T, L, 12, 2, false>(W, x, y, N, K, geo, st); break;
     default: break;
     }
     return hipErrorInvalidValue;
@@ -445,22 +518,33 @@ static hipError_t gemv1_dispatch(const void *W, const void *x, void *y, int64_t 
 
 hipError_t launch_gemv1(int type, const void *W, const void *x, void *y, int64_t N, int64_t K, hipStream_t st) {
     switch (type) {
-    case Q4_K: return gemv1_dispatch<Q4_K>(W, x, y, N, K, st);
-    case Q5_K: return gemv1_dispatch<Q5_K>(W, x, y, N, K, st);
-    case Q6_K: return gemv1_dispatch<Q6_K>(W, x, y, N, K, st);
+    case Q4_K: return gemv1_dispatch<Q4_K, GGUF>(W, x, y, N, K, st);
+    case Q5_K: return gemv1_dispatch<Q5_K, GGUF>(W, x, y, N, K, st);
+    case Q6_K: return gemv1_dispatch<Q6_K, GGUF>(W, x, y, N, K, st);
+    case Q4_K | PLANAR_FLAG: return gemv1_dispatch<Q4_K, PLANAR>(W, x, y, N, K, st);
+    case Q5_K | PLANAR_FLAG: return gemv1_dispatch<Q5_K, PLANAR>(W, x, y, N, K, st);
+    case Q6_K | PLANAR_FLAG: return gemv1_dispatch<Q6_K, PLANAR>(W, x, y, N, K, st);
     default: return hipErrorInvalidValue;
     }
 }
 
 static Geo geometry_of(int type, int64_t N, int64_t K, int cus) {
-    switch (type) {
+    switch (type & ~PLANAR_FLAG) {
     case Q4_K: return geometry<Q4_K>(N, K, cus);
     case Q5_K: return geometry<Q5_K>(N, K, cus);
     default: return geometry<Q6_K>(N, K, cus);
     }
 }
 
-static int body_code(int type, int rl) {
+static int body_code_gguf(int type, int rl);
+
+static int body_code(int type_flags, int rl) {
+    const int type = type_flags & ~PLANAR_FLAG, plane = (type_flags & PLANAR_FLAG) ? B_COUNT : 0;
+    const int c = body_code_gguf(type, rl);
+    return c < 0 ? -1 : c + plane;
+}
+
+static int body_code_gguf(int type, int rl) {
     if (type == Q4_K) {
         switch (rl) {
         case 1: return B_Q4_1;
@@ -504,19 +588,40 @@ hipError_t launch_gemv_batch(const BatchEntry *in, int count, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int T>
+template <int T, int L>
 static hipError_t launch_deq(const void *W, void *out, int64_t N, int64_t K, hipStream_t st) {
     const int64_t units = N * (K / 64);
     const unsigned grid = (unsigned)((units + WG - 1) / WG);
-    hipLaunchKernelGGL((dequant_kernel<T>), dim3(grid), dim3(WG), 0, st, (const uint8_t *)W, (float *)out, N, (int)K);
+    hipLaunchKernelGGL((dequant_kernel<T, L>), dim3(grid), dim3(WG), 0, st, (const uint8_t *)W, (float *)out, N,
+                       (int)K);
     return hipGetLastError();
 }
 
 hipError_t launch_dequant(int type, const void *W, void *out, int64_t N, int64_t K, hipStream_t st) {
     switch (type) {
-    case Q4_K: return launch_deq<Q4_K>(W, out, N, K, st);
-    case Q5_K: return launch_deq<Q5_K>(W, out, N, K, st);
-    case Q6_K: return launch_deq<Q6_K>(W, out, N, K, st);
+    case Q4_K: return launch_deq<Q4_K, GGUF>(W, out, N, K, st);
+    case Q5_K: return launch_deq<Q5_K, GGUF>(W, out, N, K, st);
+    case Q6_K: return launch_deq<Q6_K, GGUF>(W, out, N, K, st);
+    case Q4_K | PLANAR_FLAG: return launch_deq<Q4_K, PLANAR>(W, out, N, K, st);
+    case Q5_K | PLANAR_FLAG: return launch_deq<Q5_K, PLANAR>(W, out, N, K, st);
+    case Q6_K | PLANAR_FLAG: return launch_deq<Q6_K, PLANAR>(W, out, N, K, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int T>
+static hipError_t launch_rp(const void *W, void *Wp, int64_t N, int64_t K, hipStream_t st) {
+    const int64_t sbs = N * (K / 256);
+    const unsigned grid = (unsigned)((sbs + WG - 1) / WG);
+    hipLaunchKernelGGL((repack_kernel<T>), dim3(grid), dim3(WG), 0, st, (const uint8_t *)W, (uint8_t *)Wp, N, (int)K);
+    return hipGetLastError();
+}
+
+hipError_t launch_repack(int type, const void *W, void *Wp, int64_t N, int64_t K, hipStream_t st) {
+    switch (type) {
+    case Q4_K: return launch_rp<Q4_K>(W, Wp, N, K, st);
+    case Q5_K: return launch_rp<Q5_K>(W, Wp, N, K, st);
+    case Q6_K: return launch_rp<Q6_K>(W, Wp, N, K, st);
     default: return hipErrorInvalidValue;
     }
 }

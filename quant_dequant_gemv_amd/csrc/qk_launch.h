@@ -7,6 +7,9 @@
 
 namespace qk {
 
+// Layout flag carried in the type argument (QK_PLANAR of the C ABI).
+constexpr int PLANAR_FLAG = 0x100;
+
 // ncols == 1: the streaming GEMV.
 hipError_t launch_gemv1(int type, const void *W, const void *x, void *y, int64_t N, int64_t K,
                         hipStream_t stream);
@@ -26,7 +29,10 @@ hipError_t launch_gemv_batch(const BatchEntry *entries, int count, hipStream_t s
 hipError_t launch_gemv_multi(int type, const void *W, const void *x, void *y, int64_t N, int64_t K,
                              int ncols, hipStream_t stream);
 
-// fp32 dequantisation of the whole tensor.
+// fp32 dequantisation of the whole tensor (either layout).
 hipError_t launch_dequant(int type, const void *W, void *out, int64_t N, int64_t K, hipStream_t stream);
+
+// GGUF rows -> PLANAR rows (type without the flag).
+hipError_t launch_repack(int type, const void *W, void *Wp, int64_t N, int64_t K, hipStream_t stream);
 
 }  // namespace qk

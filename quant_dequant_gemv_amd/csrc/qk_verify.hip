@@ -213,9 +213,10 @@ __global__ void __launch_bounds__(512) verify_kernel(const uint8_t *__restrict__
         };
         const int qq = blk & 3;  // unit index within the superblock (u & 3 == blk & 3)
         const KScaleSel sel(qq);
+        const UnitAddr<T, GGUF> ua(0, qq);  // offsets from the superblock start
         Unit<T> buf[2];
-        buf[0].template load<false>(addr(i0), qq);
-        buf[1].template load<false>(addr(i0 + 1), qq);
+        buf[0].template load<false, GGUF>(addr(i0), ua);
+        buf[1].template load<false, GGUF>(addr(i0 + 1), ua);
 
         float acc[4 * NCB];
 #pragma unroll
@@ -257,7 +258,7 @@ __global__ void __launch_bounds__(512) verify_kernel(const uint8_t *__restrict__
                         run_step = -1;
                     }
                 }
-                buf[p].template load<false>(addr(item + 2), qq);
+                buf[p].template load<false, GGUF>(addr(item + 2), ua);
             }
         }
     }

@@ -103,3 +103,26 @@ def test_batch_validation_codes():
     assert binding.qk_gemv_batch([good, (binding.Q6_K, FAKE, FAKE, FAKE, 4, 300)], 0) == binding.QK_EINVAL_SHAPE
     assert binding.qk_gemv_batch([(binding.Q5_K, FAKE, FAKE + 2, FAKE, 4, 256), good], 0) == binding.QK_EINVAL_PTR
     assert binding.qk_gemv_batch([good, (binding.Q4_K, FAKE, FAKE, 0, 4, 256)], 0) == binding.QK_EINVAL_PTR
+
+
+def test_planar_row_bytes_and_flag_validation():
+    P = binding.PLANAR
+    assert binding.qk_row_bytes(binding.Q4_K | P, 5120) == 20 * 144
+    assert binding.qk_row_bytes(binding.Q5_K | P, 6144) == 24 * 176
+    assert binding.qk_row_bytes(binding.Q6_K | P, 17408) == 14288  # 68 * 210 rounded up to 16
+    assert binding.qk_row_bytes(binding.Q6_K | P, 2048) == 8 * 210 == 1680
+    assert binding.qk_row_bytes(binding.Q4_K | 0x200, 5120) == -1
+    assert binding.qk_gemv(binding.Q4_K | P, FAKE, FAKE, FAKE, 4, 256, 2, 0) == binding.QK_EINVAL_TYPE
+    assert binding.qk_gemv(binding.Q4_K | 0x200, FAKE, FAKE, FAKE, 4, 256, 1, 0) == binding.QK_EINVAL_TYPE
+    assert binding.qk_dequant(binding.Q5_K | P, FAKE, FAKE, 4, 300, 0) == binding.QK_EINVAL_SHAPE
+    assert binding.qk_gemv_batch([(binding.Q6_K | P, FAKE, FAKE, FAKE + 2, 4, 256)], 0) == binding.QK_EINVAL_PTR
+
+
+def test_repack_validation_codes():
+    P = binding.PLANAR
+    assert binding.qk_repack(binding.Q4_K | P, FAKE, 4 * FAKE, 4, 256, 0) == binding.QK_EINVAL_TYPE
+    assert binding.qk_repack(99, FAKE, 4 * FAKE, 4, 256, 0) == binding.QK_EINVAL_TYPE
+    assert binding.qk_repack(binding.Q4_K, FAKE, 4 * FAKE, 4, 300, 0) == binding.QK_EINVAL_SHAPE
+    assert binding.qk_repack(binding.Q4_K, FAKE + 8, 4 * FAKE, 4, 256, 0) == binding.QK_EINVAL_PTR
+    assert binding.qk_repack(binding.Q4_K, FAKE, 4 * FAKE + 4, 4, 256, 0) == binding.QK_EINVAL_PTR
+    assert binding.qk_repack(binding.Q6_K, FAKE, FAKE + 16 * 210, 32, 256, 0) == binding.QK_EINVAL_PTR  # overlap

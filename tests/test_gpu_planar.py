@@ -1,0 +1,91 @@
+"""GPU parity of the PLANAR row layout (qk_repack, QK_PLANAR) through the C
+ABI: the repack matches the test-side packer byte for byte; dequantising the
+repacked tensor is bit-exact against the oracle's GGUF dequantisation; the
+GEMV on it is within the oracle's row bound and bit-identical to the GEMV on
+the GGUF tensor (same units, same geometry, same summation order)."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_row_bound, dev, gpu_gemv, needs_gpu, same_f32, torch
+from kquant_planar import pack
+from quant_dequant_gemv_amd import binding, synth
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+Q4, Q5, Q6 = synth.Q4_K, synth.Q5_K, synth.Q6_K
+TYPES = [Q4, Q5, Q6]
+NAMES = {Q4: "Q4_K", Q5: "Q5_K", Q6: "Q6_K"}
+P = binding.PLANAR
+# K = 2048 (8 superblocks: Q6_K rows need no pad), 1280 and 17408 (Q6_K rows padded)
+SHAPES = [(1, 256), (5, 1280), (47, 2048), (130, 5120), (37, 17408), (3000, 5120)]
+
+
+def _repacked(qt, W, N, K):
+    Wp = binding.repack(qt, dev(W.reshape(-1)), N, K)
+    torch.cuda.synchronize()
+    return Wp
+
+
+@pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_repack_matches_packer(qt, N, K):
+    W = synth.superblocks(qt, N, K, 40 + N)
+    Wp = _repacked(qt, W, N, K).cpu().numpy().reshape(N, -1)
+    assert np.array_equal(Wp, pack(qt, W, K))
+
+
+@pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
+@pytest.mark.parametrize("N,K", SHAPES[:5])
+def test_planar_dequant_bit_exact(qt, N, K):
+    W = synth.superblocks(qt, N, K, 50 + N)
+    Wp = _repacked(qt, W, N, K)
+    out = binding.dequant(qt | P, Wp, N, K)
+    torch.cuda.synchronize()
+    assert same_f32(out.cpu().numpy(), oracle.dequant(qt, W, K))
+
+
+@pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_planar_gemv_bound_and_identical_to_gguf(qt, N, K):
+    W = synth.superblocks(qt, N, K, 60 + N)
+    x = synth.activations(K, 1, 60 + N)
+    Wp = _repacked(qt, W, N, K)
+    xd = dev(x).reshape(-1)
+    yp = binding.gemv(qt | P, Wp, xd, N, K).cpu().numpy().reshape(-1)
+    yg = gpu_gemv(qt, W, x, N, K).reshape(-1)
+    assert np.array_equal(yp.view(np.uint32), yg.view(np.uint32)), "planar != GGUF"
+    y_ref, S = oracle.gemv(qt, W, x, K)
+    assert_row_bound(yp, y_ref, S, f"{NAMES[qt]} planar {N}x{K}")
+
+
+@pytest.mark.parametrize("case", synth.Q4K_PROJECTIONS + synth.MIXED, ids=lambda c: c["name"])
+def test_planar_full_shapes_sampled(case):
+    qt, N, K = case["qtype"], case["N"], case["K"]
+    W = synth.superblocks(qt, N, K, case["seed"])
+    x = synth.activations(K, 1, case["seed"])
+    Wp = _repacked(qt, W, N, K)
+    y = binding.gemv(qt | P, Wp, dev(x).reshape(-1), N, K).cpu().numpy().reshape(-1)
+    rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(7).integers(0, N, 160)]))
+    y_ref, S = oracle.gemv(qt, W[rows], x, K)
+    assert_row_bound(y[rows], y_ref, S, f"{case['name']} planar")
+    assert np.isfinite(y).all()
+
+
+def test_planar_batch_mixed_layouts():
+    ents, host = [], []
+    for qt, N, K, seed, planar in [(Q4, 1000, 5120, 1, True), (Q6, 48, 5120, 2, True), (Q5, 300, 6144, 3, False),
+                                   (Q6, 200, 17408, 4, True), (Q4, 77, 2048, 5, False)]:
+        W = synth.superblocks(qt, N, K, seed)
+        x = synth.activations(K, 1, seed)
+        Wd = _repacked(qt, W, N, K) if planar else dev(W.reshape(-1))
+        ents.append((qt | (P if planar else 0), Wd, dev(x).reshape(-1), N, K))
+        host.append((qt, W, x, N, K))
+    ys = binding.gemv_batch(ents)
+    torch.cuda.synchronize()
+    for (qt, W, x, N, K), e, y in zip(host, ents, ys):
+        y1 = binding.gemv(*e).cpu().numpy().reshape(-1)
+        yb = y.cpu().numpy()
+        assert np.array_equal(yb.view(np.uint32), y1.view(np.uint32))
+        y_ref, S = oracle.gemv(qt, W, x, K)
+        assert_row_bound(yb, y_ref, S, f"batch type {e[0]:#x}")
