@@ -201,11 +201,12 @@ template <int T> struct Unit;
 //   p[2] = high-sub-block pair A (s = 16)   p[3] = high pair B (s = 16)
 template <> struct Unit<Q4_K> {
     uint4 h, a, b;
+    // base: uniform pointer; off: byte offset of the row from base (< 2^31)
     template <bool NT, int L>
-    __device__ __forceinline__ void load(const uint8_t *row, const UnitAddr<Q4_K, L> &o) {
-        h = ld16<NT>(row + o.h);
-        a = ld16<NT>(row + o.a);
-        b = ld16<NT>(row + o.b);
+    __device__ __forceinline__ void load(const uint8_t *base, uint32_t off, const UnitAddr<Q4_K, L> &o) {
+        h = ld16<NT>(base + (off + o.h));
+        a = ld16<NT>(base + (off + o.a));
+        b = ld16<NT>(base + (off + o.b));
     }
     __device__ __forceinline__ uint4 header() const { return h; }
     __device__ __forceinline__ uint32_t qword(int i) const { return i < 4 ? word(a, i) : word(b, i - 4); }
@@ -224,12 +225,12 @@ template <> struct Unit<Q4_K> {
 template <> struct Unit<Q5_K> {
     uint4 h, qh0, qh1, a, b;
     template <bool NT, int L>
-    __device__ __forceinline__ void load(const uint8_t *row, const UnitAddr<Q5_K, L> &o) {
-        h = ld16<NT>(row + o.h);
-        qh0 = ld16<NT>(row + o.qh0);
-        qh1 = ld16<NT>(row + o.qh1);
-        a = ld16<NT>(row + o.a);
-        b = ld16<NT>(row + o.b);
+    __device__ __forceinline__ void load(const uint8_t *base, uint32_t off, const UnitAddr<Q5_K, L> &o) {
+        h = ld16<NT>(base + (off + o.h));
+        qh0 = ld16<NT>(base + (off + o.qh0));
+        qh1 = ld16<NT>(base + (off + o.qh1));
+        a = ld16<NT>(base + (off + o.a));
+        b = ld16<NT>(base + (off + o.b));
     }
     __device__ __forceinline__ uint4 header() const { return h; }
     __device__ __forceinline__ uint32_t qword(int i) const { return i < 4 ? word(a, i) : word(b, i - 4); }
@@ -255,13 +256,13 @@ template <> struct Unit<Q6_K> {
     uint2 sc;      // GGUF: scales[8n .. 8n+7];  PLANAR: .x = this unit's 4 scales, quarter order
     uint32_t d;    // fp16 d in the low half
     template <bool NT, int L>
-    __device__ __forceinline__ void load(const uint8_t *row, const UnitAddr<Q6_K, L> &o) {
-        a = ld16<NT>(row + o.a);
-        b = ld16<NT>(row + o.b);
-        c = ld16<NT>(row + o.c);
-        if constexpr (L == PLANAR) sc = make_uint2(ld4<NT>(row + o.sc), 0u);
-        else sc = ld8<NT>(row + o.sc);
-        d = ld2<NT>(row + o.d);
+    __device__ __forceinline__ void load(const uint8_t *base, uint32_t off, const UnitAddr<Q6_K, L> &o) {
+        a = ld16<NT>(base + (off + o.a));
+        b = ld16<NT>(base + (off + o.b));
+        c = ld16<NT>(base + (off + o.c));
+        if constexpr (L == PLANAR) sc = make_uint2(ld4<NT>(base + (off + o.sc)), 0u);
+        else sc = ld8<NT>(base + (off + o.sc));
+        d = ld2<NT>(base + (off + o.d));
     }
     __device__ __forceinline__ void patterns(int i, int /*q*/, uint32_t p[8]) const {
         const uint32_t A = word(a, i), B = word(b, i), C = word(c, i);

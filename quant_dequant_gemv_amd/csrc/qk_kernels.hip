@@ -79,9 +79,15 @@ __device__ __forceinline__ void load_x(XReg<T> &X, const uint16_t *__restrict__ 
         const float s1 = x_pairs16(v[2], v[3], X.xr + 8);
         const float s2 = x_pairs16(v[4], v[5], X.xr + 16);
         const float s3 = x_pairs16(v[6], v[7], X.xr + 24);
-        X.xsum[0] = s0 + s1;
-        X.xsum[1] = s2 + s3;
+        X.xsum[0] = (s0 + s1) * 0x1p-24f;  // Q4_K/Q5_K partials are kept in units of 2^-48
+        X.xsum[1] = (s2 + s3) * 0x1p-24f;
     }
+}
+
+// a from the lane that the DPP control names (a full-rate VALU move)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float a) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), CTRL, 0xf, 0xf, false));
 }
 
 template <int L>
@@ -112,23 +118,35 @@ __device__ __forceinline__ float unit_dot(const Unit<T> &U, int q, const KScaleS
     if constexpr (T == Q6_K) {
         return unit_dot_q6<L>(U, q, X);
     } else {
-        float aL = 0.f, aH = 0.f;
+        uint32_t p[4];
+        U.patterns(0, q, p);
+        float aL = dot2(p[0], X.xr[0], 0.f), aH = dot2(p[2], X.xr[16], 0.f);
+        aL = dot2(p[1], X.xr[1], aL);
+        aH = dot2(p[3], X.xr[17], aH);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t p[4];
+        for (int i = 1; i < 8; ++i) {
             U.patterns(i, q, p);
             aL = dot2(p[0], X.xr[2 * i], aL);
             aL = dot2(p[1], X.xr[2 * i + 1], aL);
             aH = dot2(p[2], X.xr[16 + 2 * i], aH);
             aH = dot2(p[3], X.xr[17 + 2 * i], aH);
         }
+        // In units of 2^-48.  aL = 2^-24 * sum q*x (low sub-block), aH = 2^-20 * sum q*x
+        // (high: patterns hold 16q); the 6-bit sc / m read as fp16 bit patterns
+        // are sc*2^-24 / m*2^-24, and the x sums are held times 2^-24.  Every
+        // half x float product below is one mixed-precision instruction.
         const uint4 h = U.header();
         const KScales s = k_scales(h, sel);
-        const float d = f16_lo(h.x), dmin = f16_hi(h.x);
-        // patterns hold q * 2^-24 (low sub-block) and 16q * 2^-24 (high)
-        const float fl = d * (float)s.sc_lo * 0x1p24f;
-        const float fh = d * (float)s.sc_hi * 0x1p20f;
-        return fl * aL + fh * aH - dmin * ((float)s.m_lo * X.xsum[0] + (float)s.m_hi * X.xsum[1]);
+        const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)h.x);
+        const _Float16 dmin = __builtin_bit_cast(_Float16, (uint16_t)(h.x >> 16));
+        // (fma with a +0 addend is not a multiply for the compiler: it stays one
+        // mixed-precision fma, with the half operand converted for free)
+        auto pat = [](uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)v); };
+        float acc = __builtin_fmaf(pat(s.sc_lo), aL, 0.f);
+        acc = __builtin_fmaf(pat(s.sc_hi), aH * 0x1p-4f, acc);
+        float mn = __builtin_fmaf(pat(s.m_lo), X.xsum[0], 0.f);
+        mn = __builtin_fmaf(pat(s.m_hi), X.xsum[1], mn);
+        return __builtin_fmaf((float)d, acc, -__builtin_fmaf((float)dmin, mn, 0.f));
     }
 }
 
@@ -144,14 +162,14 @@ __device__ __forceinline__ float unit_dot(const Unit<T> &U, int q, const KScaleS
 // wave reads up to 16 consecutive superblocks of one row per load.
 //
 // The rows of a lane are taken RL at a time, and the body for RL rows is
-// straight-line code: all RL units' loads are issued first, then the units
-// are computed in order.  There is no branch anywhere in it -- addresses past
-// the end are clamped into the tensor, invalid results are discarded with a
-// select and invalid partial sums go to a spare LDS slot -- so the compiler
-// knows exactly how many loads are in flight and waits for one unit at a
-// time: the math on the first rows overlaps the arrival of the later ones.
-// Each unit's partial sum goes to LDS; at the end every row's partials are
-// added in a fixed order.
+// straight-line code with a ring of D units in flight.  There is no branch
+// in it: row offsets past the workgroup's last row are clamped to it, and
+// every lane (also a lane past the last row, or a tail lane of the last wave)
+// writes its partial sum to a slot of its own, which the final reduction
+// reads only for real rows -- so the compiler knows exactly how many loads
+// are in flight and waits for one unit at a time: the math on the first rows
+// overlaps the arrival of the later ones.  At the end every row's partials
+// are added in a fixed order.
 // ---------------------------------------------------------------------------
 // Workgroup blk of nblk (nthr threads, a multiple of 64) takes rows
 // [blk*N/nblk, (blk+1)*N/nblk).
@@ -159,7 +177,7 @@ template <int T, int L, int RL, int D, bool NT>
 __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const uint16_t *__restrict__ x,
                                            float *__restrict__ y, int N, int K, int useg, int P, int blk,
                                            int nblk, int nthr) {
-    extern __shared__ __attribute__((aligned(16))) float part[];  // [rows of this wg][useg] + 1 spare
+    extern __shared__ __attribute__((aligned(16))) float part[];  // partial sums, slot rows of useg floats
     constexpr int BB = Fmt<T>::bytes;
     constexpr int DD = D < RL ? D : RL;  // units in flight
     const int tid = (int)threadIdx.x;
@@ -172,7 +190,12 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     const bool lane_ok = ph < P;
     const int ph_c = lane_ok ? ph : 0;
     const int rows_lane = (R + P - 1) / P;  // same schedule for every lane
-    const int spare = R * useg;              // index of the spare slot
+    // Partial sums: the lane of phase ph (tail lanes ph >= P included) writes
+    // its i-th row to slot row i*PT + ph, PT = phases incl. the tail, so every
+    // lane owns a distinct slot and no write needs a guard.  Row r of the
+    // workgroup is slot row (r / P) * PT + r % P.
+    const int PT = (nthr + useg - 1) / useg;
+    const int slot0 = ph * useg + uc, slot_step = PT * useg;
 
     for (int s0 = 0; s0 < U; s0 += useg) {
         const int ns = min(useg, U - s0);
@@ -187,21 +210,22 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
         for (int i0 = 0; i0 < rows_lane; i0 += RL) {
             // straight line over RL rows with a ring of DD units in flight
             Unit<T> buf[DD];
+            // lane rows past the workgroup's last row re-read the last row.
+            // (64-bit row pointers: loads addressed as a uniform base plus a
+            // 32-bit lane offset measured 10-30% slower)
             auto load_row = [&](Unit<T> &dst, int i) {
                 const int row = min(r0 + ph_c + P * (i0 + i), r1 - 1);
-                dst.template load<NT, L>(W + (size_t)row * row_bytes, ua);
+                dst.template load<NT, L>(W + (size_t)row * row_bytes, 0u, ua);
             };
 #pragma unroll
             for (int p = 0; p < DD; ++p) load_row(buf[p], p);
 #pragma unroll
             for (int p = 0; p < RL; ++p) {
-                const int i = i0 + p;
-                const int row = r0 + ph_c + P * i;
-                const bool ok = col_ok && i < rows_lane && row < r1;
                 const float v = unit_dot<T, L>(buf[p % DD], q, sel, X);
                 if (p + DD < RL) load_row(buf[p % DD], p + DD);
-                const int slot = ok ? (row - r0) * useg + uc : spare;
-                part[slot] = (s0 == 0 ? 0.f : part[slot]) + v;
+                float *slot = part + slot0 + (i0 + p) * slot_step;
+                if (s0 == 0) *slot = v;
+                else *slot += col_ok ? v : 0.f;  // a short last segment: lanes past it add nothing
             }
         }
     }
@@ -212,20 +236,25 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     // so the shuffles see whole groups.
     const int c4 = min(useg, U) >> 2;
     const int j = tid & 15;
+    const uint32_t inv_p = 0xffffffffu / (uint32_t)P + 1u;  // rr / P = umulhi(rr, inv_p) for rr < 2^20
     for (int rr = tid >> 4; rr - (tid >> 4) < R; rr += nthr >> 4) {
         const bool rok = rr < R;
-        const float4 *pr = reinterpret_cast<const float4 *>(part + (size_t)(rok ? rr : 0) * useg);
+        const int ri = (int)__umulhi((uint32_t)rr, inv_p);
+        const int sr = rok ? ri * PT + (rr - ri * P) : 0;
+        const float4 *pr = reinterpret_cast<const float4 *>(part + (size_t)sr * useg);
         float a = 0.f;
 #pragma unroll 4
         for (int c = j; c < c4; c += 16) {
             const float4 v = pr[c];
             a += (v.x + v.y) + (v.z + v.w);
         }
-        a += __shfl_xor(a, 1);
-        a += __shfl_xor(a, 2);
-        a += __shfl_xor(a, 4);
-        a += __shfl_xor(a, 8);
-        if (rok && j == 0) y[r0 + rr] = a;
+        // sum over the 16-lane row with DPP (no LDS round trips): pairs, quads,
+        // the two quads of each half-row, the two half-rows
+        a += dpp_f32<0xb1>(a);   // quad_perm [1,0,3,2]
+        a += dpp_f32<0x4e>(a);   // quad_perm [2,3,0,1]
+        a += dpp_f32<0x141>(a);  // row_half_mirror
+        a += dpp_f32<0x140>(a);  // row_mirror
+        if (rok && j == 0) y[r0 + rr] = a * (T == Q6_K ? 1.f : 0x1p48f);
     }
 }
 
@@ -311,7 +340,7 @@ __global__ void __launch_bounds__(WG) dequant_kernel(const uint8_t *__restrict__
     const int s = u >> 2, q = u & 3;
     float *o = out + (size_t)row * (size_t)K + 256 * s;
     Unit<T> U;
-    U.template load<false, L>(W + (size_t)row * (size_t)layout_row_bytes(T, L, K), UnitAddr<T, L>(K >> 8, u));
+    U.template load<false, L>(W + (size_t)row * (size_t)layout_row_bytes(T, L, K), 0u, UnitAddr<T, L>(K >> 8, u));
     if constexpr (T == Q6_K) {
         const float d = f16_lo(U.d);
         const int kb = 128 * (q >> 1) + 16 * (q & 1);
@@ -445,6 +474,13 @@ template <> struct RowRounds<Q4_K> { static constexpr int n = 6, rl[n] = {1, 2, 
 template <> struct RowRounds<Q5_K> { static constexpr int n = 2, rl[n] = {1, 2}, max_threads = 512; };
 template <> struct RowRounds<Q6_K> { static constexpr int n = 1, rl[n] = {1}, max_threads = 1024; };
 
+// LDS of one workgroup: ceil(R / P) slot rows per phase, tail phase included.
+static size_t part_lds(int64_t N, const Geo &g) {
+    const int64_t R = (N + g.G - 1) / g.G, rows_lane = (R + g.P - 1) / g.P;
+    const int64_t PT = (g.threads + g.useg - 1) / g.useg;
+    return (size_t)(rows_lane * PT * g.useg) * 4;
+}
+
 // Rows are split evenly over G workgroups (one per CU unless the partial
 // sums would not fit in LDS).  Within a workgroup P row phases of useg lanes
 // each take every P-th row, RL rows per straight-line round.  P and RL are
@@ -456,28 +492,28 @@ static Geo geometry(int64_t N, int64_t K, int cus) {
     Geo g;
     const int64_t U = K / 64;
     g.useg = (int)(U < 512 ? U : 512);
-    int64_t G = N < cus ? N : cus;
-    while ((N + G - 1) / G * g.useg * 4 > LDS_PART) G *= 2;
-    if (G > N) G = N;
-    g.G = (int)G;
-    const int64_t R = (N + G - 1) / G;
     const int pmax = RR::max_threads / g.useg > 0 ? RR::max_threads / g.useg : 1;
-    int64_t best = INT64_MAX;
-    g.P = 1;
-    g.RL = 1;
-    for (int p = 1; p <= pmax; ++p) {
-        const int64_t rows = (R + p - 1) / p;
-        int rl = RR::rl[RR::n - 1];
-        for (int k = 0; k < RR::n; ++k)
-            if (RR::rl[k] >= rows) { rl = RR::rl[k]; break; }
-        const int64_t slots = (int64_t)p * ((rows + rl - 1) / rl) * rl;
-        if (slots <= best) { best = slots; g.P = p; g.RL = rl; }
+    for (int64_t G = N < cus ? N : cus;; G *= 2) {
+        if (G > N) G = N;
+        g.G = (int)G;
+        const int64_t R = (N + G - 1) / G;
+        int64_t best = INT64_MAX;
+        g.P = 1;
+        g.RL = 1;
+        for (int p = 1; p <= pmax; ++p) {
+            const int64_t rows = (R + p - 1) / p;
+            int rl = RR::rl[RR::n - 1];
+            for (int k = 0; k < RR::n; ++k)
+                if (RR::rl[k] >= rows) { rl = RR::rl[k]; break; }
+            const int64_t slots = (int64_t)p * ((rows + rl - 1) / rl) * rl;
+            if (slots <= best) { best = slots; g.P = p; g.RL = rl; }
+        }
+        g.threads = (g.P * g.useg + 63) / 64 * 64;
+        if (G == N || part_lds(N, g) <= (size_t)LDS_PART) break;  // the partial sums fit in LDS
     }
-    g.threads = (g.P * g.useg + 63) / 64 * 64;
     return g;
 }
 
-static size_t part_lds(int64_t N, const Geo &g) { return ((size_t)((N + g.G - 1) / g.G) * g.useg + 1) * 4; }
 
 // Dynamic LDS above the default 64 KB needs the kernel's opt-in (once per
 // kernel: the static is per template instance, i.e. per kernel).

@@ -215,8 +215,8 @@ __global__ void __launch_bounds__(512) verify_kernel(const uint8_t *__restrict__
         const KScaleSel sel(qq);
         const UnitAddr<T, GGUF> ua(0, qq);  // offsets from the superblock start
         Unit<T> buf[2];
-        buf[0].template load<false, GGUF>(addr(i0), ua);
-        buf[1].template load<false, GGUF>(addr(i0 + 1), ua);
+        buf[0].template load<false, GGUF>(addr(i0), 0u, ua);
+        buf[1].template load<false, GGUF>(addr(i0 + 1), 0u, ua);
 
         float acc[4 * NCB];
 #pragma unroll
@@ -258,7 +258,7 @@ __global__ void __launch_bounds__(512) verify_kernel(const uint8_t *__restrict__
                         run_step = -1;
                     }
                 }
-                buf[p].template load<false, GGUF>(addr(item + 2), ua);
+                buf[p].template load<false, GGUF>(addr(item + 2), 0u, ua);
             }
         }
     }
