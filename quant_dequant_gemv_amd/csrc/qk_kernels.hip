@@ -56,25 +56,73 @@ __device__ __forceinline__ float x_pairs16(const uint4 &v0, const uint4 &v1, uin
     return s;
 }
 
-// Load the x of unit u (superblock s = u/4, q = u%4) of a row.
-template <int T>
-__device__ __forceinline__ void load_x(XReg<T> &X, const uint16_t *__restrict__ x, int u) {
+// x of one segment is staged in LDS with every 64-weight unit's 128 bytes at
+// a 144-byte stride: 16-byte chunk c of the segment sits at 144*(c/8) +
+// 16*(c%8).  The pad puts the eight 16-byte reads of the lanes of a wave
+// (each of its own unit) on distinct banks.
+constexpr int XSTRIDE = 144;
+
+__device__ __forceinline__ uint4 x_chunk(const uint8_t *xl, int c) {
+    return *reinterpret_cast<const uint4 *>(xl + XSTRIDE * (c >> 3) + 16 * (c & 7));
+}
+
+// Stage x[64*s0 .. 64*(s0+ns)) into LDS: coalesced 16-byte global reads, four
+// per thread per round, issued together (indices clamped: repeats rewrite the
+// same bytes), then written to the padded layout.
+__device__ __forceinline__ void stage_x(uint8_t *xl, const uint16_t *__restrict__ x, int s0, int ns, int tid,
+                                        int nthr) {
+    const uint4 *xg = reinterpret_cast<const uint4 *>(x) + (size_t)s0 * 8;
+    const int nch = ns * 8;
+    for (int b = 0; b < nch; b += 4 * nthr) {
+        uint4 v[4];
+        int c[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            c[k] = min(b + tid + k * nthr, nch - 1);
+            v[k] = xg[c[k]];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            *reinterpret_cast<uint4 *>(xl + XSTRIDE * (c[k] >> 3) + 16 * (c[k] & 7)) = v[k];
+    }
+}
+
+// Q6_K: the lane's x straight from global memory (unit u of the row).  A
+// Q6_K segment's x is up to 3.4x larger per weight byte than Q4_K's, and with
+// one unit in flight per lane the copy's barrier delays the first weights:
+// the direct loads measured faster for it.
+__device__ __forceinline__ void load_x_q6(XReg<Q6_K> &X, const uint16_t *__restrict__ x, int u) {
     const uint4 *xv = reinterpret_cast<const uint4 *>(x);  // 8 halves per vector
+    const int s = u >> 2, n = (u >> 1) & 1, b = u & 1;
+    uint4 v[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int k = 256 * s + 128 * n + 32 * t + 16 * b;  // first weight of quarter t
+        v[2 * t] = xv[k >> 3];
+        v[2 * t + 1] = xv[(k >> 3) + 1];
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) X.xsum[t] = x_pairs16(v[2 * t], v[2 * t + 1], X.xr + 8 * t);
+}
+
+// The lane's x from the staged copy; ul is the unit index within the segment
+// (segments start on superblock boundaries, so ul % 4 == u % 4).
+template <int T>
+__device__ __forceinline__ void load_x(XReg<T> &X, const uint8_t *xl, int ul) {
+    uint4 v[8];
     if constexpr (T == Q6_K) {
-        const int s = u >> 2, n = (u >> 1) & 1, b = u & 1;
-        uint4 v[8];
+        const int s = ul >> 2, n = (ul >> 1) & 1, b = ul & 1;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int k = 256 * s + 128 * n + 32 * t + 16 * b;  // first weight of quarter t
-            v[2 * t] = xv[k >> 3];
-            v[2 * t + 1] = xv[(k >> 3) + 1];
+            const int c = 32 * s + 16 * n + 4 * t + 2 * b;  // first chunk of quarter t
+            v[2 * t] = x_chunk(xl, c);
+            v[2 * t + 1] = x_chunk(xl, c + 1);
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) X.xsum[t] = x_pairs16(v[2 * t], v[2 * t + 1], X.xr + 8 * t);
     } else {
-        uint4 v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = xv[8 * u + j];  // weights 64u .. 64u+63
+        for (int j = 0; j < 8; ++j) v[j] = x_chunk(xl, 8 * ul + j);
         const float s0 = x_pairs16(v[0], v[1], X.xr + 0);
         const float s1 = x_pairs16(v[2], v[3], X.xr + 8);
         const float s2 = x_pairs16(v[4], v[5], X.xr + 16);
@@ -196,6 +244,7 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     // workgroup is slot row (r / P) * PT + r % P.
     const int PT = (nthr + useg - 1) / useg;
     const int slot0 = ph * useg + uc, slot_step = PT * useg;
+    uint8_t *xl = reinterpret_cast<uint8_t *>(part + rows_lane * PT * useg);  // the segment's x
 
     for (int s0 = 0; s0 < U; s0 += useg) {
         const int ns = min(useg, U - s0);
@@ -204,7 +253,14 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
         const int q = u & 3;
         const KScaleSel sel(q);
         XReg<T> X;
-        load_x<T>(X, x, u);
+        if constexpr (T == Q6_K) {
+            load_x_q6(X, x, u);
+        } else {
+            if (s0 > 0) __syncthreads();  // every lane holds the previous segment's x in registers
+            stage_x(xl, x, s0, ns, tid, nthr);
+            __syncthreads();
+            load_x<T>(X, xl, u - s0);
+        }
         const UnitAddr<T, L> ua(K >> 8, u);
 
         for (int i0 = 0; i0 < rows_lane; i0 += RL) {
@@ -447,7 +503,8 @@ __global__ void __launch_bounds__(WG) repack_kernel(const uint8_t *__restrict__ 
 // ---------------------------------------------------------------------------
 // Launchers.  The type argument carries the PLANAR_FLAG bit of the C ABI.
 // ---------------------------------------------------------------------------
-constexpr int LDS_PART = 96 * 1024;  // LDS for the per-unit partial sums
+constexpr int LDS_PART = 128 * 1024;  // LDS budget of one workgroup: partial sums and the x copy
+constexpr int LDS_MAX = 160 * 1024;   // gfx950: the most one workgroup may take
 
 // Launch geometry of the ncols = 1 kernel.
 struct Geo { int G, threads, useg, P, RL; };
@@ -478,7 +535,7 @@ template <> struct RowRounds<Q6_K> { static constexpr int n = 1, rl[n] = {1}, ma
 static size_t part_lds(int64_t N, const Geo &g) {
     const int64_t R = (N + g.G - 1) / g.G, rows_lane = (R + g.P - 1) / g.P;
     const int64_t PT = (g.threads + g.useg - 1) / g.useg;
-    return (size_t)(rows_lane * PT * g.useg) * 4;
+    return (size_t)(rows_lane * PT * g.useg) * 4 + (size_t)g.useg * XSTRIDE;  // partial sums + x copy (Q4_K/Q5_K)
 }
 
 // Rows are split evenly over G workgroups (one per CU unless the partial
@@ -521,7 +578,7 @@ template <auto Kernel>
 static void allow_lds() {
     static const bool done = [] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, LDS_PART + 1024);
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, LDS_MAX);
         return true;
     }();
     (void)done;
