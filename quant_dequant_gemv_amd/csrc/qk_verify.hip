@@ -5,28 +5,35 @@
 // "MTP Verify Plan"; B70 plan, Phase 3 item 7 and Phase 4 "True Xe2 Batched
 // Verification").  W is read from HBM once per call whatever ncols is.
 //
-// Matrix-core mapping (v_mfma_f32_4x4x4_16b_f16: 16 independent 4x4x4
-// blocks, block = 4 consecutive lanes; lane 4b+j supplies row j of A and
-// column j of B and receives D[0..3][j]):
-//   B column j = W row (4*quad + j): the quant patterns of one 32-bit quant
-//                word (pairs A and B, weights (l, l+2, l+1, l+3)) -- exact
-//                fp16 values p * 2^-24, as in the one-column kernel;
-//   A row j    = x column (4*cb + j) at the same four weights, from LDS;
-//   D[i][j]    = sum over the word of x_i * q_j, accumulated in fp32 over a
-//                sub-block (8 words), then scaled per row by d*sc (and the
-//                min term dmin*m*sum(x) subtracted) in fp32.
-// So a lane ends up with all columns of its own row.  The 16 blocks of a
-// wave are 16 consecutive units of the same four rows; their partial sums are
-// reduced across the blocks at the end of each work item.
+// Same skeleton as the one-column kernel (x-stationary, rows balanced over
+// the CUs, a ring of units in flight, partial sums in LDS, a fixed-order
+// final sum), with the column products on the matrix cores:
+//   v_mfma_f32_4x4x4_16b_f16 runs 16 independent 4x4x4 blocks; block b is
+//   the 4 lanes 4b..4b+3, lane 4b+j supplies row j of A and column j of B and
+//   receives D[0..3][j].  Here block b is one unit column (64 weights of a
+//   superblock) of four rows, lane j being row j of a row quad:
+//     B column j = the quant patterns of row j for one 32-bit quant word
+//                  (exact fp16 values s*q*2^-24, weights (l, l+2, l+1, l+3)),
+//     A row i    = x column 4*cb + i at the same four weights, held in
+//                  registers by lane i of the block for the whole segment,
+//     D[i][j]    = sum over the word of x_i * q_j.
+//   D is accumulated over a scale group, then each lane scales its own row's
+//   four columns by d*sc (and subtracts the min term) in fp32.
+// A wave covers 16 consecutive unit columns of a row quad; the unit columns
+// of one K segment form a phase of useg/16 waves, and P phases take the row
+// quads of the workgroup in turn.  Per row quad the 16 blocks of a wave are
+// folded with DPP rotations inside each 16-lane row and the 4 results per
+// wave and column go to LDS; at the end each (row, column) adds its slots in
+// a fixed order.
 #include "qk_format.h"
 #include "qk_launch.h"
+
+#include <algorithm>
 
 namespace qk {
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
-
-constexpr int VSLOT = 36;  // dwords per unit slot: 32 of x pairs + 4 of padding
 
 __device__ __forceinline__ float4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, float4_t c) {
     const half4_t a = __builtin_bit_cast(half4_t, make_uint2(a0, a1));
@@ -34,251 +41,281 @@ __device__ __forceinline__ float4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0,
     return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 0, 0, 0);
 }
 
-template <int T>
-__host__ __device__ constexpr int groups_per_unit() { return T == Q6_K ? 4 : 2; }
-
-// Position of weight k (tile-relative, k < kt) in the LDS x planes: unit slot
-// u and half index within the slot.  Q4_K/Q5_K: unit u = weights 64u..64u+63
-// in order; Q6_K: unit 4s+2n+b holds quarter t at halves 16t..16t+15.  Groups
-// of four halves are stored in the order (0, 2, 1, 3).  g = scale group.
-template <int T>
-__device__ __forceinline__ void x_place(int k, int &u, int &pos, int &g) {
-    int r, base;
-    if constexpr (T == Q6_K) {
-        const int s = k >> 8, kk = k & 255;
-        const int n = kk >> 7, t = (kk >> 5) & 3, b = (kk >> 4) & 1, l = kk & 15;
-        u = 4 * s + 2 * n + b;
-        base = 16 * t + (l & ~3);
-        r = l & 3;
-        g = t;
-    } else {
-        u = k >> 6;
-        const int kk = k & 63;
-        base = kk & ~3;
-        r = kk & 3;
-        g = kk >> 5;
-    }
-    const int perm = (r == 0) ? 0 : (r == 1) ? 2 : (r == 2) ? 1 : 3;
-    pos = base + perm;
+// a from the lane that the DPP control names
+template <int CTRL>
+__device__ __forceinline__ float vdpp(float a) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), CTRL, 0xf, 0xf, false));
 }
 
-// Stage x[k0 .. k0+kt)[0..nc) into per-column planes of unit slots, then the
-// fp32 sums of each scale group (fixed order).  planes: nc * units * VSLOT
-// dwords; sums: nc * units * G floats.
+// Largest workgroup: 12 waves (3 per SIMD, 168 registers each) for one
+// column block; 8 waves (2 per SIMD, 256 registers) for two, whose x alone
+// takes 64 registers.
+template <int NCB>
+__host__ __device__ constexpr int v_max_threads() { return NCB == 1 ? 768 : 512; }
+constexpr int V_RAW_BUDGET = 96 * 1024;  // LDS for the x copy of one segment
+constexpr int V_LDS_MAX = 160 * 1024;
+
 template <int T>
-__device__ void stage_xv(const uint16_t *__restrict__ x, int k0, int kt, int nc, uint32_t *planes, float *sums) {
-    const int units = kt >> 6;
-    uint16_t *ph = reinterpret_cast<uint16_t *>(planes);
-    for (int e = (int)threadIdx.x; e < kt * nc; e += (int)blockDim.x) {
-        const int k = e / nc, c = e - k * nc;
-        int u, pos, g;
-        x_place<T>(k, u, pos, g);
-        ph[2 * VSLOT * (c * units + u) + pos] = x[(size_t)(k0 + k) * nc + c];
-    }
-    __syncthreads();
-    constexpr int G = groups_per_unit<T>();
-    constexpr int GW = 64 / G;  // weights per group
-    for (int e = (int)threadIdx.x; e < nc * units * G; e += (int)blockDim.x) {
-        const int c = e / (units * G), rem = e - c * units * G, u = rem / G, g = rem - u * G;
-        const uint32_t *src = planes + VSLOT * (c * units + u) + (GW / 2) * g;
+__host__ __device__ constexpr int vgroups() { return T == Q6_K ? 4 : 2; }  // scale groups per unit
+
+// x of one K segment in LDS: the 64 rows k of x ([k][nc] fp16, as in memory)
+// of every 64-weight block kb of the segment at kb * xs bytes, xs = 128*nc +
+// 16 (the pad puts the 16 unit columns of a wave on different banks).
+__device__ __forceinline__ uint32_t xh(const uint8_t *raw, int xs, int nc, int k, int c) {
+    return *reinterpret_cast<const uint16_t *>(raw + (size_t)(k >> 6) * xs + 2 * ((k & 63) * nc + c));
+}
+
+// Column c of x at the unit's 64 weights (segment-relative unit ul), in the
+// register order of the quant patterns: groups of four halves as pairs
+// (0, 2), (1, 3); plus the fp32 sum of each scale group.
+template <int T>
+__device__ __forceinline__ void gather_x(const uint8_t *raw, int xs, int nc, int ul, int c, uint32_t *xr,
+                                         float *sums) {
+    constexpr int G = vgroups<T>(), GW = 64 / G;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        // first k of scale group g: Q4_K/Q5_K 32 consecutive weights; Q6_K quarter t = g
+        // of unit 4s + 2n + b is the 16 weights 256s + 128n + 32t + 16b + (0..15)
+        const int k0 =
+            T == Q6_K ? 256 * (ul >> 2) + 128 * ((ul >> 1) & 1) + 32 * g + 16 * (ul & 1) : 64 * ul + 32 * g;
         float s = 0.f;
-        for (int i = 0; i < GW / 2; ++i) s += f16_lo(src[i]) + f16_hi(src[i]);
-        sums[(c * units + u) * G + g] = s;
+#pragma unroll
+        for (int m = 0; m < GW / 4; ++m) {
+            const int k = k0 + 4 * m;
+            const uint32_t h0 = xh(raw, xs, nc, k, c), h1 = xh(raw, xs, nc, k + 1, c);
+            const uint32_t h2 = xh(raw, xs, nc, k + 2, c), h3 = xh(raw, xs, nc, k + 3, c);
+            xr[(GW / 2) * g + 2 * m] = h0 | (h2 << 16);
+            xr[(GW / 2) * g + 2 * m + 1] = h1 | (h3 << 16);
+            s += (f16_lo(h0) + f16_lo(h2)) + (f16_lo(h1) + f16_lo(h3));
+        }
+        sums[g] = s;
     }
-    __syncthreads();
 }
 
-// One work item = (row quad, step of 16 units).  Accumulates this lane's
-// contribution for its row into acc[4*NCB] (columns 4*cb + i in acc[4*cb+i]).
-template <int T, int NCB>
-__device__ __forceinline__ void item_dot(const Unit<T> &U, int q, const KScaleSel &sel, const uint32_t *planes,
-                                         const float *sums, int units, int u, int j, int nc, float *acc) {
-    constexpr int G = groups_per_unit<T>();
-    // A operands come from the planes of columns 4*cb + j (zero when past nc)
-    const uint32_t *xa[NCB];
-    bool colok[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-        const int c = 4 * cb + j;
-        colok[cb] = c < nc;
-        xa[cb] = planes + VSLOT * ((colok[cb] ? c : 0) * units + u);
-    }
-    if constexpr (T == Q6_K) {
-        float4_t D[NCB][4];
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) D[cb][t] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t p[8];
-            U.patterns(i, q, p);
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    const uint2 xv = *reinterpret_cast<const uint2 *>(xa[cb] + 8 * t + 2 * i);
-                    const uint32_t a0 = colok[cb] ? xv.x : 0u, a1 = colok[cb] ? xv.y : 0u;
-                    D[cb][t] = mfma4(a0, a1, p[2 * t], p[2 * t + 1], D[cb][t]);
-                }
+// DPP quad_perm broadcast of lane J of each quad (J = 0..3)
+template <int J>
+__device__ __forceinline__ float quad_bcast(float a) { return vdpp<J | (J << 2) | (J << 4) | (J << 6)>(a); }
+
+template <int T, int NCB, int RL, int D>
+__global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint8_t *__restrict__ W,
+                                                               const uint16_t *__restrict__ x,
+                                                               float *__restrict__ y, int N, int K, int nc,
+                                                               int useg, int P) {
+    extern __shared__ __attribute__((aligned(16))) float vsm[];
+    constexpr int G = vgroups<T>(), NC = 4 * NCB;
+    constexpr int DD = D < RL ? D : RL;
+    const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int blk = lane >> 2, j = lane & 3;
+    const int wpp = useg >> 4;  // waves per phase
+    const int ph = wave / wpp, wip = wave - ph * wpp;
+    const int uc = 16 * wip + blk;  // unit column within the segment
+    const int r0 = (int)((int64_t)blockIdx.x * N / gridDim.x);
+    const int r1 = (int)((int64_t)(blockIdx.x + 1) * N / gridDim.x);
+    const int R = r1 - r0, Q = (R + 3) >> 2;
+    const int quads_lane = (Q + P - 1) / P;
+    const int U = K >> 6;
+    const size_t row_bytes = (size_t)(K >> 8) * Fmt<T>::bytes;
+    const int nslot = 4 * wpp;  // partial slots per (row, column): 4 per wave of a phase
+    // LDS: partial sums [row][slot][NC] (rows of every quad a phase visits),
+    // then the raw x copy of a segment
+    float *part = vsm;
+    uint8_t *raw = reinterpret_cast<uint8_t *>(vsm + (size_t)quads_lane * P * 4 * nslot * NC);
+    const int xs = 128 * nc + 16;
+    const int slot = 4 * wip + (blk >> 2);  // this lane's slot if it writes (blk % 4 == 0)
+
+    for (int s0 = 0; s0 < U; s0 += useg) {
+        const int ns = min(useg, U - s0);
+        const bool col_ok = uc < ns;
+        const int u = s0 + min(uc, ns - 4 + (uc & 3));  // clamped, same q
+        const int q = u & 3;
+        const KScaleSel sel(q);
+
+        // raw x of the segment: coalesced 16-byte copies
+        if (s0 > 0) __syncthreads();  // the previous segment's x is in registers everywhere
+        {
+            const uint4 *xg = reinterpret_cast<const uint4 *>(x + (size_t)s0 * 64 * nc);
+            const int per_block = 8 * nc, nch = ns * per_block;
+            for (int c = tid; c < nch; c += (int)blockDim.x) {
+                const int kb = c / per_block;
+                *reinterpret_cast<uint4 *>(raw + (size_t)kb * xs + 16 * (c - kb * per_block)) = xg[c];
+            }
         }
-        const float d = f16_lo(U.d);
+        __syncthreads();
+        // this lane's columns j, j+4 in registers; group sums of all columns of the unit
+        uint32_t xr[NCB][32];
+        float xsum[NC][G];
+        {
+            float own[NCB][G];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const float ds = d * (float)U.scale(t, q);
-            const float k = t < 2 ? 0x1p24f : 0x1p20f;
+            for (int cb = 0; cb < NCB; ++cb) {
+                const int c = 4 * cb + j;
+                if (c < nc) {
+                    gather_x<T>(raw, xs, nc, u - s0, c, xr[cb], own[cb]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) xr[cb][i] = 0u;
+#pragma unroll
+                    for (int g = 0; g < G; ++g) own[cb][g] = 0.f;
+                }
+            }
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int c = 4 * cb + i;
-                    const float xs = c < nc ? sums[(c * units + u) * G + t] : 0.f;
-                    acc[4 * cb + i] += ds * (D[cb][t][i] * k - 32.f * xs);
+                for (int g = 0; g < G; ++g) {
+                    // pre-scaled for the 2^-48 units of the Q4_K/Q5_K partials
+                    const float v = T == Q6_K ? own[cb][g] : own[cb][g] * 0x1p-24f;
+                    xsum[4 * cb + 0][g] = quad_bcast<0>(v);
+                    xsum[4 * cb + 1][g] = quad_bcast<1>(v);
+                    xsum[4 * cb + 2][g] = quad_bcast<2>(v);
+                    xsum[4 * cb + 3][g] = quad_bcast<3>(v);
                 }
         }
-    } else {
-        float4_t Dl[NCB], Dh[NCB];
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) Dl[cb] = Dh[cb] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t p[4];
-            U.patterns(i, q, p);
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                const uint2 xl = *reinterpret_cast<const uint2 *>(xa[cb] + 2 * i);
-                const uint2 xh = *reinterpret_cast<const uint2 *>(xa[cb] + 16 + 2 * i);
-                Dl[cb] = mfma4(colok[cb] ? xl.x : 0u, colok[cb] ? xl.y : 0u, p[0], p[1], Dl[cb]);
-                Dh[cb] = mfma4(colok[cb] ? xh.x : 0u, colok[cb] ? xh.y : 0u, p[2], p[3], Dh[cb]);
-            }
-        }
-        const uint4 h = U.header();
-        const KScales s = k_scales(h, sel);
-        const float d = f16_lo(h.x), dmin = f16_hi(h.x);
-        const float fl = d * (float)s.sc_lo * 0x1p24f, fh = d * (float)s.sc_hi * 0x1p20f;
-        const float ml = dmin * (float)s.m_lo, mh = dmin * (float)s.m_hi;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int c = 4 * cb + i;
-                const float2 xs = c < nc ? *reinterpret_cast<const float2 *>(sums + (c * units + u) * 2)
-                                         : make_float2(0.f, 0.f);
-                acc[4 * cb + i] += fl * Dl[cb][i] + fh * Dh[cb][i] - (ml * xs.x + mh * xs.y);
-            }
-    }
-}
+        const UnitAddr<T, GGUF> ua(K >> 8, u);
 
-// Work items of a workgroup: rows [r0, r1) in quads of 4, each row's units in
-// steps of 16 (one unit per block).  Wave w takes the contiguous item range
-// [w*per, (w+1)*per): consecutive items are consecutive steps of one quad, so
-// the lane accumulates its row's sums across them and the 16 blocks are
-// reduced only when the quad changes.  The run total goes to LDS at
-// part[(row*nc + c)*steps_max + first step of the run] (other slots stay 0);
-// at the end each (row, c) adds its slots in step order.  Loads go through a
-// two-deep ring, unconditional with clamped addresses (exact load counting).
-template <int T, int NCB>
-__global__ void __launch_bounds__(512) verify_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ x,
-                                                    float *__restrict__ y, int N, int K, int nc, int KT, int steps_max) {
-    extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
-    constexpr int BB = Fmt<T>::bytes, G = groups_per_unit<T>();
-    const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = (int)blockDim.x >> 6;
-    const int blk = lane >> 2, j = lane & 3;
-    const int r0 = (int)((int64_t)blockIdx.x * N / gridDim.x);
-    const int r1 = (int)((int64_t)(blockIdx.x + 1) * N / gridDim.x);
-    const int R = r1 - r0, quads = (R + 3) >> 2;
-    const size_t row_bytes = (size_t)(K >> 8) * BB;
-    const int units_kt = KT >> 6;
-    float *part = reinterpret_cast<float *>(smem);  // [R][nc][steps_max]
-    uint32_t *planes = smem + (size_t)R * nc * steps_max;
-    float *sums = reinterpret_cast<float *>(planes + (size_t)nc * units_kt * VSLOT);
-    for (int e = tid; e < R * nc * steps_max; e += (int)blockDim.x) part[e] = 0.f;
-
-    for (int k0 = 0; k0 < K; k0 += KT) {
-        const int kt = min(KT, K - k0), units = kt >> 6, ub = k0 >> 6;
-        const int steps = (units + 15) >> 4;
-        const int items = quads * steps;
-        const int per = (items + nwaves - 1) / nwaves;
-        const int i0 = min(wave * per, items), i1 = min(i0 + per, items);
-        if (k0 > 0) __syncthreads();
-        stage_xv<T>(x, k0, kt, nc, planes, sums);  // ends with a barrier
-
-        auto addr = [&](int item) {
-            const int it = min(item, items - 1);
-            const int quad = it / steps, step = it - quad * steps;
-            const int row = min(4 * quad + j, R - 1);
-            const int u_raw = 16 * step + blk;
-            const int u = min(u_raw, units - 4 + (u_raw & 3));
-            return W + (size_t)(r0 + row) * row_bytes + (size_t)((ub + u) >> 2) * BB;
-        };
-        const int qq = blk & 3;  // unit index within the superblock (u & 3 == blk & 3)
-        const KScaleSel sel(qq);
-        const UnitAddr<T, GGUF> ua(0, qq);  // offsets from the superblock start
-        Unit<T> buf[2];
-        buf[0].template load<false, GGUF>(addr(i0), 0u, ua);
-        buf[1].template load<false, GGUF>(addr(i0 + 1), 0u, ua);
-
-        float acc[4 * NCB];
+        for (int i0 = 0; i0 < quads_lane; i0 += RL) {
+            Unit<T> buf[DD];
+            auto load_quad = [&](Unit<T> &dst, int i) {
+                const int row = min(r0 + 4 * (ph + P * (i0 + i)) + j, r1 - 1);
+                dst.template load<false, GGUF>(W + (size_t)row * row_bytes, 0u, ua);
+            };
 #pragma unroll
-        for (int i = 0; i < 4 * NCB; ++i) acc[i] = 0.f;
-        int run_step = -1;
-        for (int item0 = i0; item0 < i1; item0 += 2) {
+            for (int p = 0; p < DD; ++p) load_quad(buf[p], p);
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const int item = item0 + p;
-                if (item < i1) {
-                    const int quad = item / steps, step = item - quad * steps;
-                    const int row = 4 * quad + j;
-                    const int u_raw = 16 * step + blk;
-                    if (run_step < 0) run_step = step;
-                    // every lane runs the matrix-core path (a block reads the A rows of
-                    // all four lanes); lanes past the rows or units only drop the result
-                    const int u_c = min(u_raw, units - 4 + (u_raw & 3));
-                    float tmp[4 * NCB];
+            for (int p = 0; p < RL; ++p) {
+                const Unit<T> &Un = buf[p % DD];
+                float val[NC];
+                // one column block at a time: its accumulators only (the quant
+                // patterns are recomputed per block, cheaper than the registers)
+                if constexpr (T == Q6_K) {
+                    const float d = f16_lo(Un.d);
+                    float f[4];
 #pragma unroll
-                    for (int i = 0; i < 4 * NCB; ++i) tmp[i] = 0.f;
-                    item_dot<T, NCB>(buf[p], qq, sel, planes, sums, units, u_c, j, nc, tmp);
-                    const bool ok = row < R && u_raw < units;
+                    for (int t = 0; t < 4; ++t) f[t] = d * (float)Un.scale(t, q);
 #pragma unroll
-                    for (int i = 0; i < 4 * NCB; ++i) acc[i] += ok ? tmp[i] : 0.f;
-                    // end of a run: next item is another quad, or the range ends
-                    const bool last = item + 1 >= i1 || (item + 1) / steps != quad;
-                    if (last) {
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        float4_t Dq[4];
 #pragma unroll
-                        for (int i = 0; i < 4 * NCB; ++i) {
-                            float v = acc[i];
-                            v += __shfl_xor(v, 4);
-                            v += __shfl_xor(v, 8);
-                            v += __shfl_xor(v, 16);
-                            v += __shfl_xor(v, 32);
-                            acc[i] = 0.f;
-                            if (blk == 0 && row < R && i < nc)
-                                part[((size_t)row * nc + i) * steps_max + (k0 >> 10) + run_step] = v;
+                        for (int t = 0; t < 4; ++t) Dq[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            uint32_t pt[8];
+                            Un.patterns(i, q, pt);
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)
+                                Dq[t] = mfma4(xr[cb][8 * t + 2 * i], xr[cb][8 * t + 2 * i + 1], pt[2 * t], pt[2 * t + 1],
+                                              Dq[t]);
                         }
-                        run_step = -1;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            float a = 0.f;
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)  // patterns hold q*2^-24 (t < 2) or 16q*2^-24
+                                a = __builtin_fmaf(f[t],
+                                                   Dq[t][i] * (t < 2 ? 0x1p24f : 0x1p20f) - 32.f * xsum[4 * cb + i][t],
+                                                   a);
+                            val[4 * cb + i] = a;
+                        }
+                    }
+                } else {
+                    // units of 2^-48, as in the one-column kernel: sc and m read as fp16
+                    // patterns are sc*2^-24 and m*2^-24; the x sums are held times 2^-24
+                    const uint4 h = Un.header();
+                    const KScales sk = k_scales(h, sel);
+                    auto pat = [](uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)v); };
+                    const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)h.x);
+                    const float dmin = (float)__builtin_bit_cast(_Float16, (uint16_t)(h.x >> 16));
+                    const float fl = __builtin_fmaf(d, pat(sk.sc_lo), 0.f);
+                    const float fh = __builtin_fmaf(d, pat(sk.sc_hi), 0.f) * 0x1p-4f;
+                    const float ml = __builtin_fmaf(dmin, pat(sk.m_lo), 0.f);
+                    const float mh = __builtin_fmaf(dmin, pat(sk.m_hi), 0.f);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        float4_t Dl = float4_t{0.f, 0.f, 0.f, 0.f}, Dh = Dl;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            uint32_t pt[4];
+                            Un.patterns(i, q, pt);
+                            Dl = mfma4(xr[cb][2 * i], xr[cb][2 * i + 1], pt[0], pt[1], Dl);
+                            Dh = mfma4(xr[cb][16 + 2 * i], xr[cb][17 + 2 * i], pt[2], pt[3], Dh);
+                        }
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float mn = __builtin_fmaf(ml, xsum[4 * cb + i][0], mh * xsum[4 * cb + i][1]);
+                            val[4 * cb + i] = __builtin_fmaf(fl, Dl[i], __builtin_fmaf(fh, Dh[i], -mn));
+                        }
                     }
                 }
-                buf[p].template load<false, GGUF>(addr(item + 2), 0u, ua);
+                if (p + DD < RL) load_quad(buf[p % DD], p + DD);
+                // fold the 4 blocks of each 16-lane row (same row j, consecutive units)
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    float v = col_ok ? val[c] : 0.f;
+                    v += vdpp<0x124>(v);  // row_ror:4
+                    v += vdpp<0x128>(v);  // row_ror:8
+                    val[c] = v;
+                }
+                if ((blk & 3) == 0) {
+                    const int row = 4 * (ph + P * (i0 + p)) + j;  // slot row (rows >= R are never read)
+                    float4 *d4 = reinterpret_cast<float4 *>(part + ((size_t)row * nslot + slot) * NC);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        const float4 v = make_float4(val[4 * cb], val[4 * cb + 1], val[4 * cb + 2], val[4 * cb + 3]);
+                        if (s0 == 0) {
+                            d4[cb] = v;
+                        } else {
+                            const float4 o = d4[cb];
+                            d4[cb] = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+                        }
+                    }
+                }
             }
         }
     }
     __syncthreads();
-    const int total_steps = ((K >> 6) + 15) >> 4;
-    for (int e = tid; e < R * nc; e += (int)blockDim.x) {
-        const float *pp = part + (size_t)e * steps_max;
-        float s = 0.f;
-        for (int i = 0; i < total_steps; ++i) s += pp[i];
-        const int row = e / nc, c = e - row * nc;
-        y[(size_t)(r0 + row) * nc + c] = s;
+    // y[row][c] = sum over the slots, fixed order: 16 lanes per row, lane s
+    // adds slots s, s+16, ..., then a DPP fold of the 16 lanes per column
+    const int s16 = tid & 15;
+    const float oscale = T == Q6_K ? 1.f : 0x1p48f;
+    for (int rr = tid >> 4; rr - (tid >> 4) < R; rr += (int)blockDim.x >> 4) {
+        const bool rok = rr < R;
+        const float *pr = part + (size_t)(rok ? rr : 0) * nslot * NC;
+        float a[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) a[c] = 0.f;
+        for (int sl = s16; sl < nslot; sl += 16) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const float4 v = reinterpret_cast<const float4 *>(pr + (size_t)sl * NC)[cb];
+                a[4 * cb] += v.x;
+                a[4 * cb + 1] += v.y;
+                a[4 * cb + 2] += v.z;
+                a[4 * cb + 3] += v.w;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            float v = a[c];
+            v += vdpp<0xb1>(v);   // quad_perm [1,0,3,2]
+            v += vdpp<0x4e>(v);   // quad_perm [2,3,0,1]
+            v += vdpp<0x141>(v);  // row_half_mirror
+            v += vdpp<0x140>(v);  // row_mirror
+            a[c] = v;
+        }
+        if (rok && s16 == 0)
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                if (c < nc) y[(size_t)(r0 + rr) * nc + c] = a[c] * oscale;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Launch: one workgroup per CU (more if the per-row partial sums would not fit
-// in LDS); waves per workgroup chosen so every wave gets the same number of
-// (quad, step) items; K tiled so that the x planes fit next to the partials.
+// Launch geometry.  useg: unit columns per segment, a multiple of 16 (one
+// wave per 16), at most 192 and with the raw x copy within its budget; the
+// segments of K are made as even as possible.  G: one workgroup per CU unless
+// the LDS does not fit.  P phases and RL quads per straight-line round are
+// chosen to waste the fewest quad slots, then for the most phases.
 // ---------------------------------------------------------------------------
-constexpr size_t VLDS = 160 * 1024;
+struct VGeo { int G, useg, P, RL, threads; size_t lds; };
 
 static int cus_v() {
     static int cus = 0;
@@ -293,55 +330,91 @@ static int cus_v() {
     return cus;
 }
 
-template <int T, int NCB>
-static hipError_t launch_v(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, hipStream_t st) {
-    const int U = (int)(K / 64);
-    const int steps_max = (U + 15) / 16;
-    int64_t G = N < cus_v() ? N : cus_v();
-    const size_t part_budget = 64 * 1024;
-    while ((size_t)((N + G - 1) / G) * nc * steps_max * 4 > part_budget && G < N) G *= 2;
-    if (G > N) G = N;
-    const int64_t R = (N + G - 1) / G;
-    const size_t part_bytes = (size_t)R * nc * steps_max * 4;
-    // x planes + sums per unit of the tile
-    const size_t per_unit = (size_t)nc * (VSLOT * 4 + groups_per_unit<T>() * 4);
-    int KT = (int)(((VLDS - part_bytes) / per_unit) * 64);
-    KT -= KT % 1024;  // whole 16-unit steps
-    if (KT <= 0) return hipErrorInvalidValue;
-    if (KT > K) KT = (int)K;
-    const size_t lds = part_bytes + (size_t)(KT / 64) * per_unit;
-    // waves: the fewest items per wave, then the fewest waves
-    const int64_t items = ((R + 3) / 4) * ((KT / 64 + 15) / 16);
-    int best_w = 8;
-    int64_t best_t = INT64_MAX;
-    for (int w = 1; w <= 8; ++w) {
-        const int64_t t = (items + w - 1) / w;
-        if (t < best_t) { best_t = t; best_w = w; }
+static bool vgeo(int64_t N, int64_t K, int nc, int ncb, VGeo &g) {
+    const int64_t U = K / 64;
+    const int64_t xs = 128 * nc + 16;
+    const int max_waves = (ncb == 1 ? v_max_threads<1>() : v_max_threads<2>()) / 64;
+    const int cap = (int)std::min<int64_t>(16 * max_waves, V_RAW_BUDGET / xs) / 16 * 16;
+    if (cap < 16) return false;
+    const int64_t nseg = (U + cap - 1) / cap;
+    g.useg = (int)(((U + nseg - 1) / nseg + 15) / 16 * 16);
+    const int wpp = g.useg / 16;
+    const int pmax = std::max(1, ((ncb == 1 ? v_max_threads<1>() : v_max_threads<2>()) / 64) / wpp);
+    static const int RLS[] = {1, 2, 3, 4};
+    for (int64_t G = std::min<int64_t>(N, cus_v());; G *= 2) {
+        if (G > N) G = N;
+        g.G = (int)G;
+        const int64_t R = (N + G - 1) / G, Q = (R + 3) / 4;
+        // the fewest quad slots per lane (its chain of dependent rounds), then
+        // the fewest wasted slots, then the most phases
+        int64_t best_lane = INT64_MAX, best_slots = INT64_MAX;
+        for (int p = 1; p <= pmax; ++p) {
+            const int64_t ql = (Q + p - 1) / p;
+            // rounds of at least 2 quads keep two units in flight per lane
+            int rl = 1;
+            int64_t lane = ql;
+            if (ql > 1) {
+                lane = INT64_MAX;
+                for (int r : RLS) {
+                    if (r < 2) continue;
+                    const int64_t l = (ql + r - 1) / r * r;
+                    if (l < lane || (l == lane && r > rl)) { lane = l; rl = r; }
+                }
+            }
+            const int64_t slots = (int64_t)p * lane;
+            if (lane < best_lane || (lane == best_lane && slots <= best_slots)) {
+                best_lane = lane; best_slots = slots; g.P = p; g.RL = rl;
+            }
+        }
+        const int64_t ql = (Q + g.P - 1) / g.P;
+        g.threads = g.P * wpp * 64;
+        g.lds = (size_t)(ql * g.P * 4 * (4 * wpp) * (4 * ncb)) * 4 + (size_t)g.useg * xs;
+        if (g.lds <= (size_t)V_LDS_MAX) return true;
+        if (G == N) return false;
     }
-    static bool lds_opt_in = false;  // allow more than 64 KB of dynamic LDS
-    if (!lds_opt_in) {
-        const hipError_t e = hipFuncSetAttribute((const void *)verify_kernel<T, NCB>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)VLDS);
-        if (e != hipSuccess) return e;
-        lds_opt_in = true;
-    }
-    hipLaunchKernelGGL((verify_kernel<T, NCB>), dim3((unsigned)G), dim3(64 * best_w), lds, st,
-                       (const uint8_t *)W, (const uint16_t *)x, (float *)y, (int)N, (int)K, nc, KT, steps_max);
+}
+
+template <auto Kernel>
+static hipError_t v_allow_lds() {
+    static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, V_LDS_MAX);
+    return e;
+}
+
+template <int T, int NCB, int RL>
+static hipError_t launch_v(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, const VGeo &g,
+                           hipStream_t st) {
+    constexpr int D = 2;
+    const hipError_t e = v_allow_lds<verify_kernel<T, NCB, RL, D>>();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((verify_kernel<T, NCB, RL, D>), dim3((unsigned)g.G), dim3(g.threads), g.lds, st,
+                       (const uint8_t *)W, (const uint16_t *)x, (float *)y, (int)N, (int)K, nc, g.useg, g.P);
     return hipGetLastError();
 }
 
-template <int T>
-static hipError_t verify_dispatch(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, hipStream_t st) {
-    if (nc <= 4) return launch_v<T, 1>(W, x, y, N, K, nc, st);
-    return launch_v<T, 2>(W, x, y, N, K, nc, st);
+template <int T, int NCB>
+static hipError_t verify_dispatch(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
+                                  hipStream_t st) {
+    VGeo g;
+    if (!vgeo(N, K, nc, NCB, g)) return hipErrorInvalidValue;
+    switch (g.RL) {
+    case 1: return launch_v<T, NCB, 1>(W, x, y, N, K, nc, g, st);
+    case 2: return launch_v<T, NCB, 2>(W, x, y, N, K, nc, g, st);
+    case 3: return launch_v<T, NCB, 3>(W, x, y, N, K, nc, g, st);
+    default: return launch_v<T, NCB, 4>(W, x, y, N, K, nc, g, st);
+    }
 }
 
 hipError_t launch_gemv_multi(int type, const void *W, const void *x, void *y, int64_t N, int64_t K, int ncols,
                              hipStream_t stream) {
+    const bool two = ncols > 4;
     switch (type) {
-    case Q4_K: return verify_dispatch<Q4_K>(W, x, y, N, K, ncols, stream);
-    case Q5_K: return verify_dispatch<Q5_K>(W, x, y, N, K, ncols, stream);
-    case Q6_K: return verify_dispatch<Q6_K>(W, x, y, N, K, ncols, stream);
+    case Q4_K: return two ? verify_dispatch<Q4_K, 2>(W, x, y, N, K, ncols, stream)
+                          : verify_dispatch<Q4_K, 1>(W, x, y, N, K, ncols, stream);
+    case Q5_K: return two ? verify_dispatch<Q5_K, 2>(W, x, y, N, K, ncols, stream)
+                          : verify_dispatch<Q5_K, 1>(W, x, y, N, K, ncols, stream);
+    case Q6_K: return two ? verify_dispatch<Q6_K, 2>(W, x, y, N, K, ncols, stream)
+                          : verify_dispatch<Q6_K, 1>(W, x, y, N, K, ncols, stream);
     default: return hipErrorInvalidValue;
     }
 }
