@@ -52,43 +52,90 @@ __device__ __forceinline__ float vdpp(float a) {
 // takes 64 registers.
 template <int NCB>
 __host__ __device__ constexpr int v_max_threads() { return NCB == 1 ? 768 : 512; }
-constexpr int V_RAW_BUDGET = 96 * 1024;  // LDS for the x copy of one segment
+constexpr int V_RAW_BUDGET = 96 * 1024;  // LDS for the x planes of one segment
 constexpr int V_LDS_MAX = 160 * 1024;
 
 template <int T>
 __host__ __device__ constexpr int vgroups() { return T == Q6_K ? 4 : 2; }  // scale groups per unit
 
-// x of one K segment in LDS: the 64 rows k of x ([k][nc] fp16, as in memory)
-// of every 64-weight block kb of the segment at kb * xs bytes, xs = 128*nc +
-// 16 (the pad puts the 16 unit columns of a wave on different banks).
-__device__ __forceinline__ uint32_t xh(const uint8_t *raw, int xs, int nc, int k, int c) {
-    return *reinterpret_cast<const uint16_t *>(raw + (size_t)(k >> 6) * xs + 2 * ((k & 63) * nc + c));
+// x of one K segment in LDS, transposed into one plane per column: the 64
+// x values unit ul of the segment multiplies sit in block ul of column c's
+// plane, at c*ps + ul*144 (128 bytes + a 16-byte pad per block, so the 16
+// unit columns of a wave read different banks).  For Q4_K and Q5_K that is
+// k = 64*ul .. 64*ul+63 in order; for Q6_K the unit's four 16-value quarters.
+constexpr int VXSTRIDE = 144;
+
+__device__ __forceinline__ uint4 xplane16(const uint8_t *pl, int kb, int off) {
+    return *reinterpret_cast<const uint4 *>(pl + kb * VXSTRIDE + off);
 }
 
-// Column c of x at the unit's 64 weights (segment-relative unit ul), in the
-// register order of the quant patterns: groups of four halves as pairs
-// (0, 2), (1, 3); plus the fp32 sum of each scale group.
+// Sixteen halves (two 16-byte vectors) -> 8 pair dwords in the pattern order
+// (0, 2), (1, 3) per group of four, + their fp32 sum.
+__device__ __forceinline__ float vx_pairs16(const uint4 &v0, const uint4 &v1, uint32_t *o) {
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        o[2 * g] = (w[2 * g] & 0xffffu) | (w[2 * g + 1] << 16);
+        o[2 * g + 1] = (w[2 * g] >> 16) | (w[2 * g + 1] & 0xffff0000u);
+        s += (f16_lo(w[2 * g]) + f16_hi(w[2 * g])) + (f16_lo(w[2 * g + 1]) + f16_hi(w[2 * g + 1]));
+    }
+    return s;
+}
+
+// Column plane pl at the unit's 64 weights (segment-relative unit ul), in
+// the register order of the quant patterns; plus the fp32 sum of each scale
+// group (16 weights for Q6_K, 32 otherwise).
 template <int T>
-__device__ __forceinline__ void gather_x(const uint8_t *raw, int xs, int nc, int ul, int c, uint32_t *xr,
-                                         float *sums) {
-    constexpr int G = vgroups<T>(), GW = 64 / G;
+__device__ __forceinline__ void gather_x(const uint8_t *pl, int ul, uint32_t *xr, float *sums) {
+    float s[4];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        // first k of scale group g: Q4_K/Q5_K 32 consecutive weights; Q6_K quarter t = g
-        // of unit 4s + 2n + b is the 16 weights 256s + 128n + 32t + 16b + (0..15)
-        const int k0 =
-            T == Q6_K ? 256 * (ul >> 2) + 128 * ((ul >> 1) & 1) + 32 * g + 16 * (ul & 1) : 64 * ul + 32 * g;
-        float s = 0.f;
+    for (int m = 0; m < 4; ++m) s[m] = vx_pairs16(xplane16(pl, ul, 32 * m), xplane16(pl, ul, 32 * m + 16), xr + 8 * m);
+    if constexpr (T == Q6_K) {
 #pragma unroll
-        for (int m = 0; m < GW / 4; ++m) {
-            const int k = k0 + 4 * m;
-            const uint32_t h0 = xh(raw, xs, nc, k, c), h1 = xh(raw, xs, nc, k + 1, c);
-            const uint32_t h2 = xh(raw, xs, nc, k + 2, c), h3 = xh(raw, xs, nc, k + 3, c);
-            xr[(GW / 2) * g + 2 * m] = h0 | (h2 << 16);
-            xr[(GW / 2) * g + 2 * m + 1] = h1 | (h3 << 16);
-            s += (f16_lo(h0) + f16_lo(h2)) + (f16_lo(h1) + f16_lo(h3));
+        for (int m = 0; m < 4; ++m) sums[m] = s[m];
+    } else {
+        sums[0] = s[0] + s[1];
+        sums[1] = s[2] + s[3];
+    }
+}
+
+// Copy ns blocks of 64 rows of x (NCV columns, row-major) into the column
+// planes: each task takes 8 rows, contiguous in x (NCV 16-byte loads),
+// transposes them in registers and writes one 16-byte vector per column.
+// For Q6_K the plane block of unit ul holds the unit's four quarters in
+// order instead (the same 16-byte reads then serve every type).
+template <int T, int NCV>
+__device__ __forceinline__ void stage_planes(const uint8_t *xg, uint8_t *planes, int ps, int ns, int tid) {
+    const int ntask = ns * 8;
+    for (int t = tid; t < ntask; t += (int)blockDim.x) {
+        uint32_t h[4 * NCV];
+#pragma unroll
+        for (int i = 0; i < NCV; ++i) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(xg + ((size_t)t * NCV + i) * 16);
+            h[4 * i] = v.x; h[4 * i + 1] = v.y; h[4 * i + 2] = v.z; h[4 * i + 3] = v.w;
         }
-        sums[g] = s;
+        // half e of the task is x[8t + e / NCV][e % NCV]
+        auto half = [&](int e) -> uint32_t { return (h[e >> 1] >> (16 * (e & 1))) & 0xffffu; };
+        int off;
+        if constexpr (T == Q6_K) {
+            // rows 8t..8t+7: superblock t/32, 16-row group g = (t/2)%16 of it
+            // (quarter (g/2)%4 of unit 4*(t/32) + 2*(g/8) + g%2), half t%2 of the group
+            const int g = (t >> 1) & 15;
+            off = (4 * (t >> 5) + 2 * (g >> 3) + (g & 1)) * VXSTRIDE + 32 * ((g >> 1) & 3) + 16 * (t & 1);
+        } else {
+            off = (t >> 3) * VXSTRIDE + 16 * (t & 7);
+        }
+        uint8_t *dst = planes + off;
+#pragma unroll
+        for (int c = 0; c < NCV; ++c) {
+            uint4 o;
+            o.x = half(0 * NCV + c) | (half(1 * NCV + c) << 16);
+            o.y = half(2 * NCV + c) | (half(3 * NCV + c) << 16);
+            o.z = half(4 * NCV + c) | (half(5 * NCV + c) << 16);
+            o.w = half(6 * NCV + c) | (half(7 * NCV + c) << 16);
+            *reinterpret_cast<uint4 *>(dst + c * ps) = o;
+        }
     }
 }
 
@@ -117,10 +164,10 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
     const size_t row_bytes = (size_t)(K >> 8) * Fmt<T>::bytes;
     const int nslot = 4 * wpp;  // partial slots per (row, column): 4 per wave of a phase
     // LDS: partial sums [row][slot][NC] (rows of every quad a phase visits),
-    // then the raw x copy of a segment
+    // then the x planes of a segment
     float *part = vsm;
-    uint8_t *raw = reinterpret_cast<uint8_t *>(vsm + (size_t)quads_lane * P * 4 * nslot * NC);
-    const int xs = 128 * nc + 16;
+    uint8_t *planes = reinterpret_cast<uint8_t *>(vsm + (size_t)quads_lane * P * 4 * nslot * NC);
+    const int ps = useg * VXSTRIDE;  // bytes per column plane
     const int slot = 4 * wip + (blk >> 2);  // this lane's slot if it writes (blk % 4 == 0)
 
     for (int s0 = 0; s0 < U; s0 += useg) {
@@ -130,14 +177,18 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
         const int q = u & 3;
         const KScaleSel sel(q);
 
-        // raw x of the segment: coalesced 16-byte copies
+        // x of the segment into the column planes
         if (s0 > 0) __syncthreads();  // the previous segment's x is in registers everywhere
         {
-            const uint4 *xg = reinterpret_cast<const uint4 *>(x + (size_t)s0 * 64 * nc);
-            const int per_block = 8 * nc, nch = ns * per_block;
-            for (int c = tid; c < nch; c += (int)blockDim.x) {
-                const int kb = c / per_block;
-                *reinterpret_cast<uint4 *>(raw + (size_t)kb * xs + 16 * (c - kb * per_block)) = xg[c];
+            const uint8_t *xg = reinterpret_cast<const uint8_t *>(x + (size_t)s0 * 64 * nc);
+            switch (nc) {
+            case 2: stage_planes<T, 2>(xg, planes, ps, ns, tid); break;
+            case 3: if constexpr (NC >= 4) stage_planes<T, 3>(xg, planes, ps, ns, tid); break;
+            case 4: if constexpr (NC >= 4) stage_planes<T, 4>(xg, planes, ps, ns, tid); break;
+            case 5: if constexpr (NC >= 8) stage_planes<T, 5>(xg, planes, ps, ns, tid); break;
+            case 6: if constexpr (NC >= 8) stage_planes<T, 6>(xg, planes, ps, ns, tid); break;
+            case 7: if constexpr (NC >= 8) stage_planes<T, 7>(xg, planes, ps, ns, tid); break;
+            default: if constexpr (NC >= 8) stage_planes<T, 8>(xg, planes, ps, ns, tid); break;
             }
         }
         __syncthreads();
@@ -150,7 +201,7 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
             for (int cb = 0; cb < NCB; ++cb) {
                 const int c = 4 * cb + j;
                 if (c < nc) {
-                    gather_x<T>(raw, xs, nc, u - s0, c, xr[cb], own[cb]);
+                    gather_x<T>(planes + c * ps, u - s0, xr[cb], own[cb]);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 32; ++i) xr[cb][i] = 0u;
@@ -310,7 +361,7 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
 
 // ---------------------------------------------------------------------------
 // Launch geometry.  useg: unit columns per segment, a multiple of 16 (one
-// wave per 16), at most 192 and with the raw x copy within its budget; the
+// wave per 16), at most 192 and with the x planes within their budget; the
 // segments of K are made as even as possible.  G: one workgroup per CU unless
 // the LDS does not fit.  P phases and RL quads per straight-line round are
 // chosen to waste the fewest quad slots, then for the most phases.
@@ -332,7 +383,7 @@ static int cus_v() {
 
 static bool vgeo(int64_t N, int64_t K, int nc, int ncb, VGeo &g) {
     const int64_t U = K / 64;
-    const int64_t xs = 128 * nc + 16;
+    const int64_t xs = (int64_t)VXSTRIDE * nc;  // plane bytes per unit column
     const int max_waves = (ncb == 1 ? v_max_threads<1>() : v_max_threads<2>()) / 64;
     const int cap = (int)std::min<int64_t>(16 * max_waves, V_RAW_BUDGET / xs) / 16 * 16;
     if (cap < 16) return false;
