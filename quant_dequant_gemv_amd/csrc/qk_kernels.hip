@@ -279,9 +279,13 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
             for (int p = 0; p < RL; ++p) {
                 const float v = unit_dot<T, L>(buf[p % DD], q, sel, X);
                 if (p + DD < RL) load_row(buf[p % DD], p + DD);
-                float *slot = part + slot0 + (i0 + p) * slot_step;
-                if (s0 == 0) *slot = v;
-                else *slot += col_ok ? v : 0.f;  // a short last segment: lanes past it add nothing
+                // the round's rows past rows_lane (RL need not divide it) have
+                // no slot: the partial-sum region ends there
+                if (i0 + p < rows_lane) {
+                    float *slot = part + slot0 + (i0 + p) * slot_step;
+                    if (s0 == 0) *slot = v;
+                    else *slot += col_ok ? v : 0.f;  // a short last segment: lanes past it add nothing
+                }
             }
         }
     }

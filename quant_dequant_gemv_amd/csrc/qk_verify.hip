@@ -52,6 +52,7 @@ __device__ __forceinline__ float vdpp(float a) {
 // takes 64 registers.
 template <int NCB>
 __host__ __device__ constexpr int v_max_threads() { return NCB == 1 ? 768 : 512; }
+constexpr int V_MAX_RL = 8;  // quads per straight-line round, at most
 constexpr int V_RAW_BUDGET = 96 * 1024;  // LDS for the x planes of one segment
 constexpr int V_LDS_MAX = 160 * 1024;
 
@@ -305,7 +306,8 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
                     v += vdpp<0x128>(v);  // row_ror:8
                     val[c] = v;
                 }
-                if ((blk & 3) == 0) {
+                // quads past quads_lane (RL need not divide it) have no slot rows
+                if ((blk & 3) == 0 && i0 + p < quads_lane) {
                     const int row = 4 * (ph + P * (i0 + p)) + j;  // slot row (rows >= R are never read)
                     float4 *d4 = reinterpret_cast<float4 *>(part + ((size_t)row * nslot + slot) * NC);
 #pragma unroll
@@ -363,8 +365,8 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
 // Launch geometry.  useg: unit columns per segment, a multiple of 16 (one
 // wave per 16), at most 192 and with the x planes within their budget; the
 // segments of K are made as even as possible.  G: one workgroup per CU unless
-// the LDS does not fit.  P phases and RL quads per straight-line round are
-// chosen to waste the fewest quad slots, then for the most phases.
+// the LDS does not fit.  P phases and RL quads per straight-line round as
+// ranked below.
 // ---------------------------------------------------------------------------
 struct VGeo { int G, useg, P, RL, threads; size_t lds; };
 
@@ -391,30 +393,27 @@ static bool vgeo(int64_t N, int64_t K, int nc, int ncb, VGeo &g) {
     g.useg = (int)(((U + nseg - 1) / nseg + 15) / 16 * 16);
     const int wpp = g.useg / 16;
     const int pmax = std::max(1, ((ncb == 1 ? v_max_threads<1>() : v_max_threads<2>()) / 64) / wpp);
-    static const int RLS[] = {1, 2, 3, 4};
     for (int64_t G = std::min<int64_t>(N, cus_v());; G *= 2) {
         if (G > N) G = N;
         g.G = (int)G;
         const int64_t R = (N + G - 1) / G, Q = (R + 3) / 4;
-        // the fewest quad slots per lane (its chain of dependent rounds), then
-        // the fewest wasted slots, then the most phases
-        int64_t best_lane = INT64_MAX, best_slots = INT64_MAX;
+        // Each lane's quads run in straight-line rounds of RL <= V_MAX_RL; a
+        // round starts with an empty load ring, so the fewest rounds come
+        // first, then the fewest quad slots in all (P lanes' worth, the
+        // wasted ones included), then the fewest per lane.  Fewer than 4
+        // waves leave SIMDs idle: avoided wherever the segment allows.
+        const int min_waves = std::min(4, pmax * wpp);
+        int64_t best[4] = {INT64_MAX, INT64_MAX, INT64_MAX, INT64_MAX};
         for (int p = 1; p <= pmax; ++p) {
             const int64_t ql = (Q + p - 1) / p;
-            // rounds of at least 2 quads keep two units in flight per lane
-            int rl = 1;
-            int64_t lane = ql;
-            if (ql > 1) {
-                lane = INT64_MAX;
-                for (int r : RLS) {
-                    if (r < 2) continue;
-                    const int64_t l = (ql + r - 1) / r * r;
-                    if (l < lane || (l == lane && r > rl)) { lane = l; rl = r; }
-                }
-            }
-            const int64_t slots = (int64_t)p * lane;
-            if (lane < best_lane || (lane == best_lane && slots <= best_slots)) {
-                best_lane = lane; best_slots = slots; g.P = p; g.RL = rl;
+            const int64_t rounds = (ql + V_MAX_RL - 1) / V_MAX_RL;
+            const int rl = (int)((ql + rounds - 1) / rounds);
+            const int64_t lane = rounds * rl;
+            const int64_t key[4] = {p * wpp < min_waves ? 1 : 0, rounds, p * lane, lane};
+            if (std::lexicographical_compare(key, key + 4, best, best + 4)) {
+                std::copy(key, key + 4, best);
+                g.P = p;
+                g.RL = rl;
             }
         }
         const int64_t ql = (Q + g.P - 1) / g.P;
@@ -452,7 +451,11 @@ static hipError_t verify_dispatch(const void *W, const void *x, void *y, int64_t
     case 1: return launch_v<T, NCB, 1>(W, x, y, N, K, nc, g, st);
     case 2: return launch_v<T, NCB, 2>(W, x, y, N, K, nc, g, st);
     case 3: return launch_v<T, NCB, 3>(W, x, y, N, K, nc, g, st);
-    default: return launch_v<T, NCB, 4>(W, x, y, N, K, nc, g, st);
+    case 4: return launch_v<T, NCB, 4>(W, x, y, N, K, nc, g, st);
+    case 5: return launch_v<T, NCB, 5>(W, x, y, N, K, nc, g, st);
+    case 6: return launch_v<T, NCB, 6>(W, x, y, N, K, nc, g, st);
+    case 7: return launch_v<T, NCB, 7>(W, x, y, N, K, nc, g, st);
+    default: return launch_v<T, NCB, 8>(W, x, y, N, K, nc, g, st);
     }
 }
 

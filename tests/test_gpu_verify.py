@@ -82,3 +82,30 @@ def test_verify_mixed_shapes_sampled(case):
     rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(1).integers(0, N, 96)]))
     y_ref, S = oracle.gemv(qt, W[rows], x, K)
     assert_row_bound(y[rows], y_ref, S, f"{case['name']} ncols=4")
+
+
+# Row counts at which each workgroup's quads (4 rows) per lane take straight-
+# line rounds of every length 1..8 (the launch picks the length from the rows
+# per workgroup and the phases), for one and two column blocks.
+ROUND_CASES = [(1, 256, 2), (12328, 256, 2), (14365, 256, 2), (27654, 256, 2), (24647, 256, 2),
+               (10291, 5120, 2), (6217, 5120, 2), (14365, 5120, 2),
+               (8254, 256, 8), (14365, 256, 8), (18439, 256, 8), (24647, 256, 8), (35899, 256, 8),
+               (6217, 5120, 8), (7187, 5120, 8)]
+
+
+@pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
+@pytest.mark.parametrize("N,K,ncols", ROUND_CASES)
+def test_verify_round_lengths_sampled(qt, N, K, ncols):
+    """Sampled rows (both ends of many workgroups' row ranges) of shapes that
+    reach every round length, including rounds that run past the lane's last
+    quad."""
+    W = synth.superblocks(qt, N, K, 900 + N)
+    x = synth.activations(K, ncols, 900 + N)
+    y = gpu_gemv(qt, W, x, N, K)
+    G = min(N, 256)
+    edges = [b * N // G for b in range(0, G, 7)]
+    rows = np.unique(np.clip(np.concatenate([[0, N - 1], edges, np.array(edges) - 1,
+                                             np.random.default_rng(N).integers(0, N, 64)]), 0, N - 1))
+    y_ref, S = oracle.gemv(qt, W[rows], x, K)
+    assert_row_bound(y[rows], y_ref, S, f"{NAMES[qt]} N={N} K={K} ncols={ncols}")
+    assert np.isfinite(y).all()
