@@ -80,9 +80,9 @@ enum {
  *         D[S][2] = d;  (q = 2n+b), then zero padding to a multiple of 16 bytes
  * Planes follow one another in the order listed; rows are
  * qk_row_bytes(type | QK_PLANAR, K) bytes apart.  This is a repack for this
- * GPU, not a format of the pages; the pages' B70 plan lists "B70-native weight
- * packs" among what may be built and kept resident ("Non-Negotiable
- * Requirements" item 7).  qk_gemv (ncols = 1), qk_gemv_batch and qk_dequant
+ * GPU, not a format of the pages; the B70 plan ("Qwen3.6 27B Single-B70
+ * Maximum-Speed Requirements And Execution Plan", Non-Negotiable Requirements,
+ * item 7) allows GPU-native weight packs that are built once and kept resident.  qk_gemv (ncols = 1), qk_gemv_batch and qk_dequant
  * accept it; qk_gemv with ncols > 1 does not (QK_EINVAL_TYPE).
  */
 #define QK_PLANAR 0x100
