@@ -61,7 +61,8 @@ enum {
                              or a size whose byte count overflows int64          */
     QK_EINVAL_PTR = -3,   /* a NULL pointer, W or x not 16-byte aligned, or y /
                              out not 4-byte aligned                               */
-    QK_ELAUNCH = -4       /* the HIP launch failed (message via qk_strerror)      */
+    QK_ELAUNCH = -4,      /* the HIP launch failed (message via qk_strerror)      */
+    QK_EINVAL_FLAGS = -5  /* an epilogue flag other than QK_Y_F16                 */
 };
 
 #define QK_MAX_NCOLS 8
@@ -106,6 +107,63 @@ enum {
  */
 int qk_gemv(int type, const void *W, const void *x, void *y,
             int64_t N, int64_t K, int ncols, void *stream);
+
+/* Epilogue flag: y is written as fp16 (the fp32 result rounded to nearest
+ * even; beyond the fp16 range it becomes +-inf) -- the fp16 y of the T4
+ * kernel prompt's SPEC, for a consumer that reads fp16. */
+#define QK_Y_F16 0x1
+
+/*
+ * qk_gemv_ex -- qk_gemv with a fused epilogue at the store of y:
+ *
+ *   y[n][c] = residual[n][c] + sum_k dequant(W)[n][k] * x[k][c]
+ *
+ * the output projection with its residual add in one pass (the B70 plan,
+ * "Phase 3: Maximum Useful Fusion", family 1: attention / DeltaNet output and
+ * FFN down with a residual epilogue).  W is still read once; the epilogue
+ * adds N*ncols reads and nothing else.
+ *
+ *   residual  NULL, or device pointer to N*ncols fp32 values, 4-byte
+ *             aligned, row-major like y.  It may be y itself (y += W x in
+ *             place) when y is fp32; any other overlap with y is
+ *             QK_EINVAL_PTR.
+ *   flags     0 or QK_Y_F16 (y is then N*ncols fp16 values, 2-byte aligned)
+ *   others    as for qk_gemv (PLANAR types with ncols = 1)
+ *
+ * The residual is added in fp32 to the fp32 dot product (one rounding),
+ * then y is stored.  Accuracy: |y - (residual + y_exact)| <=
+ * 1e-4 * sum_k |w * x| + 2^-24 |y| (fp32 y) or + 2^-11 |y| + 2^-25 (fp16 y,
+ * its rounding).  qk_gemv(...) is qk_gemv_ex(..., NULL, 0, stream).
+ */
+int qk_gemv_ex(int type, const void *W, const void *x, void *y,
+               int64_t N, int64_t K, int ncols,
+               const void *residual, int flags, void *stream);
+
+/*
+ * qk_gemv_swiglu -- the gate and up projections with the SiLU gating fused,
+ * in one launch:
+ *
+ *   g = dequant(Wg) @ x,  u = dequant(Wu) @ x,  y[n][c] = silu(g[n][c]) * u[n][c]
+ *   silu(z) = z / (1 + e^-z)
+ *
+ * (the B70 plan, "Phase 3: Maximum Useful Fusion", family 3: the combined
+ * gate/up projection with SiLU and the multiply fused; family 7 asks for the
+ * same at verifier widths, hence ncols 1..8).  Every workgroup streams the
+ * same rows of both tensors, so g and u never leave the chip.
+ *
+ *   type   one type (and layout) for both tensors, as for qk_gemv
+ *   Wg, Wu device pointers to the gate and up tensors, N x K each, 16-byte
+ *          aligned (they may be the same tensor)
+ *   x, y, N, K, ncols, stream   as for qk_gemv; flags 0 or QK_Y_F16
+ *
+ * g and u are each the fp32 GEMV of qk_gemv (within 1e-4 * S_g and 1e-4 *
+ * S_u of their exact values, S = sum_k |w * x|); silu uses fp32 expf.  Since
+ * |silu'| <= 1.1, |y - silu(g_exact) * u_exact| <= 1.1e-4 S_g (|u| + 1e-4
+ * S_u) + 1e-4 S_u (|silu(g)| + 1.1e-4 S_g) + 2^-20 |y|, plus the fp16
+ * rounding with QK_Y_F16.
+ */
+int qk_gemv_swiglu(int type, const void *Wg, const void *Wu, const void *x, void *y,
+                   int64_t N, int64_t K, int ncols, int flags, void *stream);
 
 /*
  * qk_dequant -- out[n][k] = dequant(W)[n][k] as fp32, bit-exact: for Q4_K and

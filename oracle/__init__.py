@@ -13,9 +13,14 @@ and from which passage of the pages, is written at the top of that file:
 * ``gemv``     -- the f64 reference ``y = sum_k w*x`` in ascending k, plus
   ``S = sum_k |w*x|`` for the per-row tolerance;
 * ``half_to_float``, ``k_scale_min``, ``quant``, ``q6k_scale`` -- the field
-  readers, exposed so the tests can pin each one on its own.
+  readers, exposed so the tests can pin each one on its own;
+* ``silu``, ``gemv_residual``, ``swiglu`` -- the fused epilogues, in f64 numpy
+  on top of ``gemv``; ``residual_bound`` / ``swiglu_bound``, the tolerances
+  that the row bound 1e-4 * sum|w*x| implies for them, and ``within``, the
+  acceptance test (with the fp16 overflow rule).
 
-Every function is pinned by ``tests/test_oracle_pins.py``; none is unpinned.
+Every function is pinned by ``tests/test_oracle_pins.py`` or
+``tests/test_oracle_epilogue.py``; none is unpinned.
 """
 from __future__ import annotations
 
@@ -193,3 +198,88 @@ def within_row_bound(y_test, y_ref, S, rel: float = 1e-4) -> np.ndarray:
     y_test = np.asarray(y_test, dtype=np.float64)
     err = np.abs(y_test - np.asarray(y_ref, dtype=np.float64))
     return err <= rel * np.asarray(S, dtype=np.float64)
+
+
+# ---------------------------------------------------------------- epilogues
+# The B70 plan ("Qwen3.6 27B Single-B70 Maximum-Speed Requirements And
+# Execution Plan", "Phase 3: Maximum Useful Fusion") fuses into the weight
+# streaming pass a residual add after the output projections (family 1) and
+# the SiLU gate times the up projection (family 3).  Their definitions, in
+# f64 on the f64 GEMV above:
+
+def silu(z):
+    """silu(z) = z * sigmoid(z) = z / (1 + exp(-z)) in f64 (-0 for z -> -inf)."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def gemv_residual(qtype, W, x, K, residual, nthreads=None):
+    """(y, S): y = residual + dequant(W) @ x in f64, S = sum_k |w*x| as in gemv."""
+    y, S = gemv(qtype, W, x, K, nthreads)
+    r = np.asarray(residual, dtype=np.float64).reshape(y.shape)
+    return y + r, S
+
+
+def swiglu(qtype, Wg, Wu, x, K, nthreads=None):
+    """(y, g, Sg, u, Su): y = silu(g) * u with g = dequant(Wg) @ x and
+    u = dequant(Wu) @ x, all f64."""
+    g, Sg = gemv(qtype, Wg, x, K, nthreads)
+    u, Su = gemv(qtype, Wu, x, K, nthreads)
+    return silu(g) * u, g, Sg, u, Su
+
+
+# Largest |silu'(z)| over the reals: silu'(z) = s(z) (1 + z (1 - s(z))),
+# s = sigmoid; its maximum is about 1.0998 (near z = 2.4).
+SILU_SLOPE = 1.1
+
+
+def _f16_rounding(y_ref, err):
+    """Half an fp16 ulp of a value within err of y_ref, plus half the
+    smallest subnormal."""
+    return 2.0 ** -11 * (np.abs(y_ref) + err) + 2.0 ** -25
+
+
+# Round to nearest even takes an fp32 value to fp16 infinity from
+# 65504 + half an ulp (16) on: |v| >= 65520.
+F16_OVERFLOW = 65520.0
+
+
+def within(y_test, y_ref, tol, f16=False) -> np.ndarray:
+    """Acceptance of an epilogue result: |y_test - y_ref| <= tol elementwise;
+    for an fp16 y also the infinity of y_ref's sign wherever a value within
+    tol of y_ref would round past the fp16 range."""
+    y = np.asarray(y_test, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    tol = np.asarray(tol, dtype=np.float64)
+    with np.errstate(invalid="ignore"):
+        ok = np.abs(y - y_ref) <= tol
+    if f16:
+        ok |= np.isinf(y) & (np.sign(y) == np.sign(y_ref)) & (np.abs(y_ref) + tol >= F16_OVERFLOW)
+    return ok
+
+
+def residual_bound(y_ref, S, f16=False, rel=1e-4):
+    """Tolerance of y = residual + W x: the GEMV's rel*S, the fp32 rounding of
+    the add (2^-24 |y|, with |y| <= |y_ref| + rel*S), and with f16 the fp16
+    rounding of the stored value."""
+    y_ref = np.abs(np.asarray(y_ref, dtype=np.float64))
+    e = rel * np.asarray(S, dtype=np.float64)
+    e = e + 2.0 ** -24 * (y_ref + e)
+    return e + _f16_rounding(y_ref, e) if f16 else e
+
+
+def swiglu_bound(y_ref, g, Sg, u, Su, f16=False, rel=1e-4):
+    """Tolerance of y = silu(g) * u when g and u are each within rel*S of
+    their exact values: with eg, eu those errors and |silu'| <= SILU_SLOPE,
+    |silu(g+eg)(u+eu) - silu(g)u| <= SILU_SLOPE |eg| (|u| + |eu|) + |silu(g)| |eu|;
+    plus 2^-20 |y| for the fp32 evaluation (expf, the add, the quotient, the
+    product: a few ulps) and with f16 the fp16 rounding."""
+    eg = rel * np.asarray(Sg, dtype=np.float64)
+    eu = rel * np.asarray(Su, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    u = np.abs(np.asarray(u, dtype=np.float64))
+    y_ref = np.abs(np.asarray(y_ref, dtype=np.float64))
+    e = SILU_SLOPE * eg * (u + eu) + np.abs(silu(g)) * eu
+    e = e + 2.0 ** -20 * (y_ref + e)
+    return e + _f16_rounding(y_ref, e) if f16 else e

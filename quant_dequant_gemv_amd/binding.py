@@ -15,13 +15,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqkgemv.so")
 
 Q4_K, Q5_K, Q6_K = 12, 13, 14
-QK_OK, QK_EINVAL_TYPE, QK_EINVAL_SHAPE, QK_EINVAL_PTR, QK_ELAUNCH = 0, -1, -2, -3, -4
+QK_OK, QK_EINVAL_TYPE, QK_EINVAL_SHAPE, QK_EINVAL_PTR, QK_ELAUNCH, QK_EINVAL_FLAGS = 0, -1, -2, -3, -4, -5
 MAX_NCOLS = 8
 MAX_BATCH = 16
 PLANAR = 0x100  # QK_PLANAR: layout flag OR'ed into a type
+Y_F16 = 0x1  # QK_Y_F16: epilogue flag, y stored as fp16
 
-EXPORTS = ("qk_gemv", "qk_gemv_batch", "qk_dequant", "qk_repack", "qk_block_bytes", "qk_row_bytes",
-           "qk_strerror", "qk_version")
+EXPORTS = ("qk_gemv", "qk_gemv_ex", "qk_gemv_swiglu", "qk_gemv_batch", "qk_dequant", "qk_repack",
+           "qk_block_bytes", "qk_row_bytes", "qk_strerror", "qk_version")
 
 
 class qk_gemv_item(ctypes.Structure):
@@ -51,6 +52,10 @@ def load_library(path: str = LIB_PATH):
     P, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.qk_gemv.argtypes = [c_int, P, P, P, i64, i64, c_int, P]
     lib.qk_gemv.restype = c_int
+    lib.qk_gemv_ex.argtypes = [c_int, P, P, P, i64, i64, c_int, P, c_int, P]
+    lib.qk_gemv_ex.restype = c_int
+    lib.qk_gemv_swiglu.argtypes = [c_int, P, P, P, P, i64, i64, c_int, c_int, P]
+    lib.qk_gemv_swiglu.restype = c_int
     lib.qk_gemv_batch.argtypes = [ctypes.POINTER(qk_gemv_item), c_int, P]
     lib.qk_gemv_batch.restype = c_int
     lib.qk_dequant.argtypes = [c_int, P, P, i64, i64, P]
@@ -73,6 +78,16 @@ def load_library(path: str = LIB_PATH):
 
 def qk_gemv(qtype: int, W: int, x: int, y: int, N: int, K: int, ncols: int, stream: int = 0) -> int:
     return load_library().qk_gemv(qtype, W, x, y, N, K, ncols, stream)
+
+
+def qk_gemv_ex(qtype: int, W: int, x: int, y: int, N: int, K: int, ncols: int, residual, flags: int,
+               stream: int = 0) -> int:
+    return load_library().qk_gemv_ex(qtype, W, x, y, N, K, ncols, residual, flags, stream)
+
+
+def qk_gemv_swiglu(qtype: int, Wg: int, Wu: int, x: int, y: int, N: int, K: int, ncols: int, flags: int,
+                   stream: int = 0) -> int:
+    return load_library().qk_gemv_swiglu(qtype, Wg, Wu, x, y, N, K, ncols, flags, stream)
 
 
 def qk_gemv_batch(items, stream: int = 0) -> int:
@@ -129,6 +144,54 @@ def gemv(qtype: int, W, x, N: int, K: int, out=None, stream=None):
     rc = qk_gemv(qtype, W.data_ptr(), x.data_ptr(), out.data_ptr(), N, K, ncols, _stream_handle(stream))
     if rc != QK_OK:
         raise QKError(rc, "qk_gemv")
+    return out
+
+
+def _check_out(x, out, f16, N, ncols):
+    import torch
+    dt = torch.float16 if f16 else torch.float32
+    if out is None:
+        out = torch.empty((N, ncols), dtype=dt, device=x.device)
+    if out.dtype != dt or not out.is_contiguous() or out.numel() != N * ncols:
+        raise ValueError(f"out must be a contiguous {dt} tensor of N*ncols elements")
+    return out
+
+
+def gemv_ex(qtype: int, W, x, N: int, K: int, residual=None, f16: bool = False, out=None, stream=None):
+    """y = residual + dequant(W) @ x, stored as float32 (or float16 with f16).
+    residual: None or a float32 device tensor of N*ncols elements (may be
+    ``out`` itself for an in-place update of a float32 y)."""
+    import torch
+    ncols = 1 if x.dim() == 1 else int(x.shape[1])
+    if x.dtype != torch.float16 or W.dtype != torch.uint8 or not (W.is_contiguous() and x.is_contiguous()):
+        raise TypeError("W must be contiguous uint8, x contiguous float16")
+    out = _check_out(x, out, f16, N, ncols)
+    rp = 0
+    if residual is not None:
+        if residual.dtype != torch.float32 or not residual.is_contiguous() or residual.numel() != N * ncols:
+            raise ValueError("residual must be a contiguous float32 tensor of N*ncols elements")
+        rp = residual.data_ptr()
+    rc = qk_gemv_ex(qtype, W.data_ptr(), x.data_ptr(), out.data_ptr(), N, K, ncols, rp or None,
+                    Y_F16 if f16 else 0, _stream_handle(stream))
+    if rc != QK_OK:
+        raise QKError(rc, "qk_gemv_ex")
+    return out
+
+
+def gemv_swiglu(qtype: int, Wg, Wu, x, N: int, K: int, f16: bool = False, out=None, stream=None):
+    """y = silu(dequant(Wg) @ x) * (dequant(Wu) @ x) in one launch."""
+    import torch
+    ncols = 1 if x.dim() == 1 else int(x.shape[1])
+    for W in (Wg, Wu):
+        if W.dtype != torch.uint8 or not W.is_contiguous():
+            raise TypeError("Wg and Wu must be contiguous uint8")
+    if x.dtype != torch.float16 or not x.is_contiguous():
+        raise TypeError("x must be contiguous float16")
+    out = _check_out(x, out, f16, N, ncols)
+    rc = qk_gemv_swiglu(qtype, Wg.data_ptr(), Wu.data_ptr(), x.data_ptr(), out.data_ptr(), N, K, ncols,
+                        Y_F16 if f16 else 0, _stream_handle(stream))
+    if rc != QK_OK:
+        raise QKError(rc, "qk_gemv_swiglu")
     return out
 
 

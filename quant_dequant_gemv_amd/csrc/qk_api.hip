@@ -49,6 +49,36 @@ int check_shape(int type, int64_t N, int64_t K, int ncols) {
     return QK_OK;
 }
 
+int launched(hipError_t e);
+
+// [a, a + na) and [b, b + nb) share a byte.
+bool overlap(const void *a, int64_t na, const void *b, int64_t nb) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+// Pointer checks of the GEMV entry points (y fp32 or, with QK_Y_F16, fp16;
+// the residual may be y itself only when y is fp32).
+int check_io(const void *x, void *y, const void *res, int64_t N, int ncols, int flags) {
+    if (!x || !y || !aligned(x, 16)) return QK_EINVAL_PTR;
+    const bool f16 = (flags & QK_Y_F16) != 0;
+    if (!aligned(y, f16 ? 2 : 4)) return QK_EINVAL_PTR;
+    if (res) {
+        if (!aligned(res, 4)) return QK_EINVAL_PTR;
+        const int64_t n = N * ncols;
+        if (!(res == y && !f16) && overlap(res, 4 * n, y, (f16 ? 2 : 4) * n)) return QK_EINVAL_PTR;
+    }
+    return QK_OK;
+}
+
+int gemv_launch(int type, const void *W, const void *W2, const void *x, void *y, int64_t N, int64_t K,
+                int ncols, const void *residual, int flags, void *stream) {
+    const qk::Epilogue ep{W2, (const float *)residual, (flags & QK_Y_F16) ? 1 : 0};
+    hipStream_t st = (hipStream_t)stream;
+    if (ncols == 1) return launched(qk::launch_gemv1(type, W, x, y, N, K, ep, st));
+    return launched(qk::launch_gemv_multi(type, W, x, y, N, K, ncols, ep, st));
+}
+
 int launched(hipError_t e) {
     if (e == hipSuccess) return QK_OK;
     snprintf(g_launch_msg, sizeof g_launch_msg, "launch failed: %s", hipGetErrorString(e));
@@ -64,12 +94,27 @@ int qk_block_bytes(int type) { return block_bytes(type); }
 int64_t qk_row_bytes(int type, int64_t K) { return row_bytes_of(type, K); }
 
 int qk_gemv(int type, const void *W, const void *x, void *y, int64_t N, int64_t K, int ncols, void *stream) {
-    const int rc = check_shape(type, N, K, ncols);
+    return qk_gemv_ex(type, W, x, y, N, K, ncols, nullptr, 0, stream);
+}
+
+int qk_gemv_ex(int type, const void *W, const void *x, void *y, int64_t N, int64_t K, int ncols,
+               const void *residual, int flags, void *stream) {
+    int rc = check_shape(type, N, K, ncols);
     if (rc) return rc;
-    if (!W || !x || !y || !aligned(W, 16) || !aligned(x, 16) || !aligned(y, 4)) return QK_EINVAL_PTR;
-    hipStream_t st = (hipStream_t)stream;
-    if (ncols == 1) return launched(qk::launch_gemv1(type, W, x, y, N, K, st));
-    return launched(qk::launch_gemv_multi(type, W, x, y, N, K, ncols, st));
+    if (flags & ~QK_Y_F16) return QK_EINVAL_FLAGS;
+    if (!W || !aligned(W, 16)) return QK_EINVAL_PTR;
+    if ((rc = check_io(x, y, residual, N, ncols, flags))) return rc;
+    return gemv_launch(type, W, nullptr, x, y, N, K, ncols, residual, flags, stream);
+}
+
+int qk_gemv_swiglu(int type, const void *Wg, const void *Wu, const void *x, void *y, int64_t N, int64_t K,
+                   int ncols, int flags, void *stream) {
+    int rc = check_shape(type, N, K, ncols);
+    if (rc) return rc;
+    if (flags & ~QK_Y_F16) return QK_EINVAL_FLAGS;
+    if (!Wg || !Wu || !aligned(Wg, 16) || !aligned(Wu, 16)) return QK_EINVAL_PTR;
+    if ((rc = check_io(x, y, nullptr, N, ncols, flags))) return rc;
+    return gemv_launch(type, Wg, Wu, x, y, N, K, ncols, nullptr, flags, stream);
 }
 
 int qk_gemv_batch(const qk_gemv_item *items, int count, void *stream) {
@@ -111,7 +156,10 @@ const char *qk_strerror(int code) {
         return "invalid type: expected QK_Q4_K (12), QK_Q5_K (13) or QK_Q6_K (14), optionally | QK_PLANAR "
                "(0x100) with ncols = 1 (qk_repack takes the type without the flag)";
     case QK_EINVAL_SHAPE: return "invalid shape: need N >= 1, K a positive multiple of 256, 1 <= ncols <= 8";
-    case QK_EINVAL_PTR: return "invalid pointer: NULL, or W/x not 16-byte aligned, or y/out not 4-byte aligned";
+    case QK_EINVAL_PTR:
+        return "invalid pointer: NULL, or W/x not 16-byte aligned, or y/out/residual not 4-byte aligned (fp16 y: 2), "
+               "or a residual that overlaps y without being y (fp32 y)";
+    case QK_EINVAL_FLAGS: return "invalid flags: the only epilogue flag is QK_Y_F16 (0x1)";
     case QK_ELAUNCH: return g_launch_msg;
     default: return "unknown error code";
     }

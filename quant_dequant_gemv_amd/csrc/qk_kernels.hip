@@ -18,6 +18,7 @@
 // The group sums of x are formed once per lane (x stays in registers), so
 // the per-weight work is the quant unpack and one half of a dot2.
 #include "qk_format.h"
+#include "qk_epilogue.h"
 #include "qk_launch.h"
 
 #include <algorithm>
@@ -220,11 +221,13 @@ __device__ __forceinline__ float unit_dot(const Unit<T> &U, int q, const KScaleS
 // are added in a fixed order.
 // ---------------------------------------------------------------------------
 // Workgroup blk of nblk (nthr threads, a multiple of 64) takes rows
-// [blk*N/nblk, (blk+1)*N/nblk).
-template <int T, int L, int RL, int D, bool NT>
+// [blk*N/nblk, (blk+1)*N/nblk).  PAIR (the SwiGLU epilogue): the workgroup
+// streams those rows of W and then of ep.W2 as 2R rows of one schedule, and
+// row r's output combines the sums of rows r and R + r.
+template <int T, int L, int RL, int D, bool NT, bool PAIR>
 __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const uint16_t *__restrict__ x,
-                                           float *__restrict__ y, int N, int K, int useg, int P, int blk,
-                                           int nblk, int nthr) {
+                                           void *y, int N, int K, int useg, int P, int blk, int nblk,
+                                           int nthr, const Epilogue &ep) {
     extern __shared__ __attribute__((aligned(16))) float part[];  // partial sums, slot rows of useg floats
     constexpr int BB = Fmt<T>::bytes;
     constexpr int DD = D < RL ? D : RL;  // units in flight
@@ -232,12 +235,13 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     const int r0 = (int)((int64_t)blk * N / nblk);
     const int r1 = (int)((int64_t)(blk + 1) * N / nblk);
     const int R = r1 - r0;
+    const int RV = PAIR ? 2 * R : R;  // rows of the schedule
     const int U = K >> 6;
     const size_t row_bytes = (size_t)layout_row_bytes(T, L, K);
     const int ph = tid / useg, uc = tid - ph * useg;
     const bool lane_ok = ph < P;
     const int ph_c = lane_ok ? ph : 0;
-    const int rows_lane = (R + P - 1) / P;  // same schedule for every lane
+    const int rows_lane = (RV + P - 1) / P;  // same schedule for every lane
     // Partial sums: the lane of phase ph (tail lanes ph >= P included) writes
     // its i-th row to slot row i*PT + ph, PT = phases incl. the tail, so every
     // lane owns a distinct slot and no write needs a guard.  Row r of the
@@ -270,8 +274,16 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
             // (64-bit row pointers: loads addressed as a uniform base plus a
             // 32-bit lane offset measured 10-30% slower)
             auto load_row = [&](Unit<T> &dst, int i) {
-                const int row = min(r0 + ph_c + P * (i0 + i), r1 - 1);
-                dst.template load<NT, L>(W + (size_t)row * row_bytes, 0u, ua);
+                if constexpr (PAIR) {
+                    const int v = min(ph_c + P * (i0 + i), RV - 1);
+                    const uint8_t *base = v < R ? W + (size_t)(r0 + v) * row_bytes
+                                                : reinterpret_cast<const uint8_t *>(ep.W2) +
+                                                      (size_t)(r0 + v - R) * row_bytes;
+                    dst.template load<NT, L>(base, 0u, ua);
+                } else {
+                    const int row = min(r0 + ph_c + P * (i0 + i), r1 - 1);
+                    dst.template load<NT, L>(W + (size_t)row * row_bytes, 0u, ua);
+                }
             };
 #pragma unroll
             for (int p = 0; p < DD; ++p) load_row(buf[p], p);
@@ -296,17 +308,20 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     // so the shuffles see whole groups.
     const int c4 = min(useg, U) >> 2;
     const int j = tid & 15;
-    const uint32_t inv_p = 0xffffffffu / (uint32_t)P + 1u;  // rr / P = umulhi(rr, inv_p) for rr < 2^20
-    for (int rr = tid >> 4; rr - (tid >> 4) < R; rr += nthr >> 4) {
-        const bool rok = rr < R;
-        const int ri = (int)__umulhi((uint32_t)rr, inv_p);
-        const int sr = rok ? ri * PT + (rr - ri * P) : 0;
+    // v / P = umulhi(v, inv_p) for v < 2^20 and P >= 2 (for P = 1 the
+    // multiplier would be 2^32)
+    const uint32_t inv_p = 0xffffffffu / (uint32_t)P + 1u;
+    constexpr float oscale = T == Q6_K ? 1.f : 0x1p48f;
+    // the sum of schedule row v (valid or not, every lane of the 16 takes part)
+    auto row_sum = [&](int v, bool ok) {
+        const int vi = P == 1 ? v : (int)__umulhi((uint32_t)v, inv_p);
+        const int sr = ok ? vi * PT + (v - vi * P) : 0;
         const float4 *pr = reinterpret_cast<const float4 *>(part + (size_t)sr * useg);
         float a = 0.f;
 #pragma unroll 4
         for (int c = j; c < c4; c += 16) {
-            const float4 v = pr[c];
-            a += (v.x + v.y) + (v.z + v.w);
+            const float4 w = pr[c];
+            a += (w.x + w.y) + (w.z + w.w);
         }
         // sum over the 16-lane row with DPP (no LDS round trips): pairs, quads,
         // the two quads of each half-row, the two half-rows
@@ -314,15 +329,22 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
         a += dpp_f32<0x4e>(a);   // quad_perm [2,3,0,1]
         a += dpp_f32<0x141>(a);  // row_half_mirror
         a += dpp_f32<0x140>(a);  // row_mirror
-        if (rok && j == 0) y[r0 + rr] = a * (T == Q6_K ? 1.f : 0x1p48f);
+        return a * oscale;
+    };
+    for (int rr = tid >> 4; rr - (tid >> 4) < R; rr += nthr >> 4) {
+        const bool rok = rr < R;
+        float v = row_sum(rr, rok);
+        if constexpr (PAIR) v = silu(v) * row_sum(R + rr, rok);
+        if (rok && j == 0) store_y(y, ep, (size_t)(r0 + rr), v);
     }
 }
 
-template <int T, int L, int RL, int D, bool NT>
+template <int T, int L, int RL, int D, bool NT, bool PAIR>
 __global__ void __launch_bounds__(1024) gemv1_kernel(const uint8_t *__restrict__ W,
-                                                      const uint16_t *__restrict__ x,
-                                                      float *__restrict__ y, int N, int K, int useg, int P) {
-    gemv1_body<T, L, RL, D, NT>(W, x, y, N, K, useg, P, (int)blockIdx.x, (int)gridDim.x, (int)blockDim.x);
+                                                      const uint16_t *__restrict__ x, void *y, int N, int K,
+                                                      int useg, int P, const Epilogue ep) {
+    gemv1_body<T, L, RL, D, NT, PAIR>(W, x, y, N, K, useg, P, (int)blockIdx.x, (int)gridDim.x, (int)blockDim.x,
+                                      ep);
 }
 
 // ---------------------------------------------------------------------------
@@ -354,8 +376,11 @@ __global__ void __launch_bounds__(1024) gemv1_batch_kernel(const BatchArgs a) {
     const BatchItem &e = a.it[i];
     if ((int)threadIdx.x >= e.threads) return;
     const int blk = (int)blockIdx.x - a.first[i], nblk = a.first[i + 1] - a.first[i];
-#define QK_BODY(T, RL, D) gemv1_body<T, GGUF, RL, D, false>(e.W, e.x, e.y, e.N, e.K, e.useg, e.P, blk, nblk, e.threads)
-#define QK_BODYP(T, RL, D) gemv1_body<T, PLANAR, RL, D, false>(e.W, e.x, e.y, e.N, e.K, e.useg, e.P, blk, nblk, e.threads)
+    const Epilogue plain{nullptr, nullptr, 0};
+#define QK_BODY(T, RL, D) \
+    gemv1_body<T, GGUF, RL, D, false, false>(e.W, e.x, e.y, e.N, e.K, e.useg, e.P, blk, nblk, e.threads, plain)
+#define QK_BODYP(T, RL, D) \
+    gemv1_body<T, PLANAR, RL, D, false, false>(e.W, e.x, e.y, e.N, e.K, e.useg, e.P, blk, nblk, e.threads, plain)
     switch (e.code) {
     case B_Q4_1: QK_BODY(Q4_K, 1, 1); break;
     case B_Q4_2: QK_BODY(Q4_K, 2, 2); break;
@@ -535,9 +560,10 @@ template <> struct RowRounds<Q4_K> { static constexpr int n = 6, rl[n] = {1, 2, 
 template <> struct RowRounds<Q5_K> { static constexpr int n = 2, rl[n] = {1, 2}, max_threads = 512; };
 template <> struct RowRounds<Q6_K> { static constexpr int n = 1, rl[n] = {1}, max_threads = 1024; };
 
-// LDS of one workgroup: ceil(R / P) slot rows per phase, tail phase included.
-static size_t part_lds(int64_t N, const Geo &g) {
-    const int64_t R = (N + g.G - 1) / g.G, rows_lane = (R + g.P - 1) / g.P;
+// LDS of one workgroup: ceil(R / P) slot rows per phase, tail phase included
+// (mult = 2: the paired rows of the SwiGLU epilogue).
+static size_t part_lds(int64_t N, const Geo &g, int mult = 1) {
+    const int64_t R = mult * ((N + g.G - 1) / g.G), rows_lane = (R + g.P - 1) / g.P;
     const int64_t PT = (g.threads + g.useg - 1) / g.useg;
     return (size_t)(rows_lane * PT * g.useg) * 4 + (size_t)g.useg * XSTRIDE;  // partial sums + x copy (Q4_K/Q5_K)
 }
@@ -546,9 +572,9 @@ static size_t part_lds(int64_t N, const Geo &g) {
 // sums would not fit in LDS).  Within a workgroup P row phases of useg lanes
 // each take every P-th row, RL rows per straight-line round.  P and RL are
 // chosen to waste the fewest row slots (P * rounds * RL - R), then for the
-// most lanes.
+// most lanes.  mult = 2: each workgroup streams its rows of two tensors.
 template <int T>
-static Geo geometry(int64_t N, int64_t K, int cus) {
+static Geo geometry(int64_t N, int64_t K, int cus, int mult = 1) {
     using RR = RowRounds<T>;
     Geo g;
     const int64_t U = K / 64;
@@ -557,7 +583,7 @@ static Geo geometry(int64_t N, int64_t K, int cus) {
     for (int64_t G = N < cus ? N : cus;; G *= 2) {
         if (G > N) G = N;
         g.G = (int)G;
-        const int64_t R = (N + G - 1) / G;
+        const int64_t R = mult * ((N + G - 1) / G);
         int64_t best = INT64_MAX;
         g.P = 1;
         g.RL = 1;
@@ -570,7 +596,7 @@ static Geo geometry(int64_t N, int64_t K, int cus) {
             if (slots <= best) { best = slots; g.P = p; g.RL = rl; }
         }
         g.threads = (g.P * g.useg + 63) / 64 * 64;
-        if (G == N || part_lds(N, g) <= (size_t)LDS_PART) break;  // the partial sums fit in LDS
+        if (G == N || part_lds(N, g, mult) <= (size_t)LDS_PART) break;  // the partial sums fit in LDS
     }
     return g;
 }
@@ -588,39 +614,49 @@ static void allow_lds() {
     (void)done;
 }
 
-template <int T, int L, int RL, int D, bool NT>
-static hipError_t launch1(const void *W, const void *x, void *y, int64_t N, int64_t K, Geo geo, hipStream_t st) {
-    const size_t lds = part_lds(N, geo);
-    allow_lds<gemv1_kernel<T, L, RL, D, NT>>();
-    hipLaunchKernelGGL((gemv1_kernel<T, L, RL, D, NT>), dim3(geo.G), dim3(geo.threads), lds, st,
-                       (const uint8_t *)W, (const uint16_t *)x, (float *)y, (int)N, (int)K, geo.useg, geo.P);
+template <int T, int L, int RL, int D, bool NT, bool PAIR>
+static hipError_t launch1(const void *W, const void *x, void *y, int64_t N, int64_t K, Geo geo,
+                          const Epilogue &ep, hipStream_t st) {
+    const size_t lds = part_lds(N, geo, PAIR ? 2 : 1);
+    allow_lds<gemv1_kernel<T, L, RL, D, NT, PAIR>>();
+    hipLaunchKernelGGL((gemv1_kernel<T, L, RL, D, NT, PAIR>), dim3(geo.G), dim3(geo.threads), lds, st,
+                       (const uint8_t *)W, (const uint16_t *)x, y, (int)N, (int)K, geo.useg, geo.P, ep);
     return hipGetLastError();
 }
 
 // Two units in flight per lane, one for one-row rounds.
-template <int T, int L>
-static hipError_t gemv1_dispatch(const void *W, const void *x, void *y, int64_t N, int64_t K, hipStream_t st) {
-    const Geo geo = geometry<T>(N, K, cu_count());
+template <int T, int L, bool PAIR>
+static hipError_t gemv1_dispatch(const void *W, const void *x, void *y, int64_t N, int64_t K,
+                                 const Epilogue &ep, hipStream_t st) {
+    const Geo geo = geometry<T>(N, K, cu_count(), PAIR ? 2 : 1);
     switch (geo.RL) {
-    case 1: return launch1<T, L, 1, 1, false>(W, x, y, N, K, geo, st);
-    case 2: if constexpr (T != Q6_K) return launch1<T, L, 2, 2, false>(W, x, y, N, K, geo, st); break;
-    case 4: if constexpr (T == Q4_K) return launch1<T, L, 4, 2, false>(W, x, y, N, K, geo, st); break;
-    case 6: if constexpr (T == Q4_K) return launch1<T, L, 6, 2, false>(W, x, y, N, K, geo, st); break;
-    case 8: if constexpr (T == Q4_K) return launch1<T, L, 8, 2, false>(W, x, y, N, K, geo, st); break;
-    case 12: if constexpr (T == Q4_K) return launch1<T, L, 12, 2, false>(W, x, y, N, K, geo, st); break;
+    case 1: return launch1<T, L, 1, 1, false, PAIR>(W, x, y, N, K, geo, ep, st);
+    case 2: if constexpr (T != Q6_K) return launch1<T, L, 2, 2, false, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 4: if constexpr (T == Q4_K) return launch1<T, L, 4, 2, false, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 6: if constexpr (T == Q4_K) return launch1<T, L, 6, 2, false, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 8: if constexpr (T == Q4_K) return launch1<T, L, 8, 2, false, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 12: if constexpr (T == Q4_K) return launch1<T, L, 12, 2, false, PAIR>(W, x, y, N, K, geo, ep, st); break;
     default: break;
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemv1(int type, const void *W, const void *x, void *y, int64_t N, int64_t K, hipStream_t st) {
+template <int T, int L>
+static hipError_t gemv1_pair(const void *W, const void *x, void *y, int64_t N, int64_t K, const Epilogue &ep,
+                             hipStream_t st) {
+    return ep.W2 ? gemv1_dispatch<T, L, true>(W, x, y, N, K, ep, st)
+                 : gemv1_dispatch<T, L, false>(W, x, y, N, K, ep, st);
+}
+
+hipError_t launch_gemv1(int type, const void *W, const void *x, void *y, int64_t N, int64_t K,
+                        const Epilogue &ep, hipStream_t st) {
     switch (type) {
-    case Q4_K: return gemv1_dispatch<Q4_K, GGUF>(W, x, y, N, K, st);
-    case Q5_K: return gemv1_dispatch<Q5_K, GGUF>(W, x, y, N, K, st);
-    case Q6_K: return gemv1_dispatch<Q6_K, GGUF>(W, x, y, N, K, st);
-    case Q4_K | PLANAR_FLAG: return gemv1_dispatch<Q4_K, PLANAR>(W, x, y, N, K, st);
-    case Q5_K | PLANAR_FLAG: return gemv1_dispatch<Q5_K, PLANAR>(W, x, y, N, K, st);
-    case Q6_K | PLANAR_FLAG: return gemv1_dispatch<Q6_K, PLANAR>(W, x, y, N, K, st);
+    case Q4_K: return gemv1_pair<Q4_K, GGUF>(W, x, y, N, K, ep, st);
+    case Q5_K: return gemv1_pair<Q5_K, GGUF>(W, x, y, N, K, ep, st);
+    case Q6_K: return gemv1_pair<Q6_K, GGUF>(W, x, y, N, K, ep, st);
+    case Q4_K | PLANAR_FLAG: return gemv1_pair<Q4_K, PLANAR>(W, x, y, N, K, ep, st);
+    case Q5_K | PLANAR_FLAG: return gemv1_pair<Q5_K, PLANAR>(W, x, y, N, K, ep, st);
+    case Q6_K | PLANAR_FLAG: return gemv1_pair<Q6_K, PLANAR>(W, x, y, N, K, ep, st);
     default: return hipErrorInvalidValue;
     }
 }

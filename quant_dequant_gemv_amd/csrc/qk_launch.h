@@ -10,9 +10,19 @@ namespace qk {
 // Layout flag carried in the type argument (QK_PLANAR of the C ABI).
 constexpr int PLANAR_FLAG = 0x100;
 
+// What happens at the store of y (a by-value kernel argument; all-zero = the
+// plain GEMV): act = W x, or silu(W x) * (W2 x) when W2 is set (the up tensor,
+// same type, layout and shape as W); then y = act + res when res is set (fp32
+// [N][ncols], may be y itself); y is fp16 (round to nearest even) when f16.
+struct Epilogue {
+    const void *W2;
+    const float *res;
+    int f16;
+};
+
 // ncols == 1: the streaming GEMV.
 hipError_t launch_gemv1(int type, const void *W, const void *x, void *y, int64_t N, int64_t K,
-                        hipStream_t stream);
+                        const Epilogue &ep, hipStream_t stream);
 
 // Independent one-column GEMVs in one launch (at most MAX_BATCH).
 constexpr int MAX_BATCH = 16;
@@ -27,7 +37,7 @@ hipError_t launch_gemv_batch(const BatchEntry *entries, int count, hipStream_t s
 
 // ncols in 2..8: the few-column verify form (matrix cores).
 hipError_t launch_gemv_multi(int type, const void *W, const void *x, void *y, int64_t N, int64_t K,
-                             int ncols, hipStream_t stream);
+                             int ncols, const Epilogue &ep, hipStream_t stream);
 
 // fp32 dequantisation of the whole tensor (either layout).
 hipError_t launch_dequant(int type, const void *W, void *out, int64_t N, int64_t K, hipStream_t stream);

@@ -25,6 +25,7 @@
 // folded with DPP rotations inside each 16-lane row and the 4 results per
 // wave and column go to LDS; at the end each (row, column) adds its slots in
 // a fixed order.
+#include "qk_epilogue.h"
 #include "qk_format.h"
 #include "qk_launch.h"
 
@@ -144,11 +145,14 @@ __device__ __forceinline__ void stage_planes(const uint8_t *xg, uint8_t *planes,
 template <int J>
 __device__ __forceinline__ float quad_bcast(float a) { return vdpp<J | (J << 2) | (J << 4) | (J << 6)>(a); }
 
-template <int T, int NCB, int RL, int D>
+// PAIR (the SwiGLU epilogue): the workgroup's rows of W and then of ep.W2
+// form one schedule of 2R rows; row r's outputs combine the sums of rows r
+// and R + r.
+template <int T, int NCB, int RL, int D, bool PAIR>
 __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint8_t *__restrict__ W,
-                                                               const uint16_t *__restrict__ x,
-                                                               float *__restrict__ y, int N, int K, int nc,
-                                                               int useg, int P) {
+                                                               const uint16_t *__restrict__ x, void *y,
+                                                               int N, int K, int nc, int useg, int P,
+                                                               const Epilogue ep) {
     extern __shared__ __attribute__((aligned(16))) float vsm[];
     constexpr int G = vgroups<T>(), NC = 4 * NCB;
     constexpr int DD = D < RL ? D : RL;
@@ -159,7 +163,7 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
     const int uc = 16 * wip + blk;  // unit column within the segment
     const int r0 = (int)((int64_t)blockIdx.x * N / gridDim.x);
     const int r1 = (int)((int64_t)(blockIdx.x + 1) * N / gridDim.x);
-    const int R = r1 - r0, Q = (R + 3) >> 2;
+    const int R = r1 - r0, RV = PAIR ? 2 * R : R, Q = (RV + 3) >> 2;
     const int quads_lane = (Q + P - 1) / P;
     const int U = K >> 6;
     const size_t row_bytes = (size_t)(K >> 8) * Fmt<T>::bytes;
@@ -227,8 +231,11 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
         for (int i0 = 0; i0 < quads_lane; i0 += RL) {
             Unit<T> buf[DD];
             auto load_quad = [&](Unit<T> &dst, int i) {
-                const int row = min(r0 + 4 * (ph + P * (i0 + i)) + j, r1 - 1);
-                dst.template load<false, GGUF>(W + (size_t)row * row_bytes, 0u, ua);
+                const int v = min(4 * (ph + P * (i0 + i)) + j, RV - 1);  // row of the schedule
+                const uint8_t *base = W + (size_t)(r0 + v) * row_bytes;
+                if constexpr (PAIR)
+                    if (v >= R) base = reinterpret_cast<const uint8_t *>(ep.W2) + (size_t)(r0 + v - R) * row_bytes;
+                dst.template load<false, GGUF>(base, 0u, ua);
             };
 #pragma unroll
             for (int p = 0; p < DD; ++p) load_quad(buf[p], p);
@@ -328,36 +335,46 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
     // y[row][c] = sum over the slots, fixed order: 16 lanes per row, lane s
     // adds slots s, s+16, ..., then a DPP fold of the 16 lanes per column
     const int s16 = tid & 15;
-    const float oscale = T == Q6_K ? 1.f : 0x1p48f;
-    for (int rr = tid >> 4; rr - (tid >> 4) < R; rr += (int)blockDim.x >> 4) {
-        const bool rok = rr < R;
-        const float *pr = part + (size_t)(rok ? rr : 0) * nslot * NC;
-        float a[NC];
+    constexpr float oscale = T == Q6_K ? 1.f : 0x1p48f;
+    // the sums of schedule row v per column (every lane of the 16 takes part)
+    auto row_sums = [&](int v, bool ok, float *a) {
+        const float *pr = part + (size_t)(ok ? v : 0) * nslot * NC;
 #pragma unroll
         for (int c = 0; c < NC; ++c) a[c] = 0.f;
         for (int sl = s16; sl < nslot; sl += 16) {
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
-                const float4 v = reinterpret_cast<const float4 *>(pr + (size_t)sl * NC)[cb];
-                a[4 * cb] += v.x;
-                a[4 * cb + 1] += v.y;
-                a[4 * cb + 2] += v.z;
-                a[4 * cb + 3] += v.w;
+                const float4 w = reinterpret_cast<const float4 *>(pr + (size_t)sl * NC)[cb];
+                a[4 * cb] += w.x;
+                a[4 * cb + 1] += w.y;
+                a[4 * cb + 2] += w.z;
+                a[4 * cb + 3] += w.w;
             }
         }
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            float v = a[c];
-            v += vdpp<0xb1>(v);   // quad_perm [1,0,3,2]
-            v += vdpp<0x4e>(v);   // quad_perm [2,3,0,1]
-            v += vdpp<0x141>(v);  // row_half_mirror
-            v += vdpp<0x140>(v);  // row_mirror
-            a[c] = v;
+            float t = a[c];
+            t += vdpp<0xb1>(t);   // quad_perm [1,0,3,2]
+            t += vdpp<0x4e>(t);   // quad_perm [2,3,0,1]
+            t += vdpp<0x141>(t);  // row_half_mirror
+            t += vdpp<0x140>(t);  // row_mirror
+            a[c] = t * oscale;
+        }
+    };
+    for (int rr = tid >> 4; rr - (tid >> 4) < R; rr += (int)blockDim.x >> 4) {
+        const bool rok = rr < R;
+        float a[NC];
+        row_sums(rr, rok, a);
+        if constexpr (PAIR) {
+            float b[NC];
+            row_sums(R + rr, rok, b);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) a[c] = silu(a[c]) * b[c];
         }
         if (rok && s16 == 0)
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-                if (c < nc) y[(size_t)(r0 + rr) * nc + c] = a[c] * oscale;
+                if (c < nc) store_y(y, ep, (size_t)(r0 + rr) * nc + c, a[c]);
     }
 }
 
@@ -383,7 +400,8 @@ static int cus_v() {
     return cus;
 }
 
-static bool vgeo(int64_t N, int64_t K, int nc, int ncb, VGeo &g) {
+// mult = 2: each workgroup streams its rows of two tensors (SwiGLU).
+static bool vgeo(int64_t N, int64_t K, int nc, int ncb, int mult, VGeo &g) {
     const int64_t U = K / 64;
     const int64_t xs = (int64_t)VXSTRIDE * nc;  // plane bytes per unit column
     const int max_waves = (ncb == 1 ? v_max_threads<1>() : v_max_threads<2>()) / 64;
@@ -396,7 +414,7 @@ static bool vgeo(int64_t N, int64_t K, int nc, int ncb, VGeo &g) {
     for (int64_t G = std::min<int64_t>(N, cus_v());; G *= 2) {
         if (G > N) G = N;
         g.G = (int)G;
-        const int64_t R = (N + G - 1) / G, Q = (R + 3) / 4;
+        const int64_t R = mult * ((N + G - 1) / G), Q = (R + 3) / 4;
         // Each lane's quads run in straight-line rounds of RL <= V_MAX_RL; a
         // round starts with an empty load ring, so the fewest rounds come
         // first, then the fewest quad slots in all (P lanes' worth, the
@@ -431,44 +449,51 @@ static hipError_t v_allow_lds() {
     return e;
 }
 
-template <int T, int NCB, int RL>
+template <int T, int NCB, int RL, bool PAIR>
 static hipError_t launch_v(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, const VGeo &g,
-                           hipStream_t st) {
+                           const Epilogue &ep, hipStream_t st) {
     constexpr int D = 2;
-    const hipError_t e = v_allow_lds<verify_kernel<T, NCB, RL, D>>();
+    const hipError_t e = v_allow_lds<verify_kernel<T, NCB, RL, D, PAIR>>();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((verify_kernel<T, NCB, RL, D>), dim3((unsigned)g.G), dim3(g.threads), g.lds, st,
-                       (const uint8_t *)W, (const uint16_t *)x, (float *)y, (int)N, (int)K, nc, g.useg, g.P);
+    hipLaunchKernelGGL((verify_kernel<T, NCB, RL, D, PAIR>), dim3((unsigned)g.G), dim3(g.threads), g.lds, st,
+                       (const uint8_t *)W, (const uint16_t *)x, y, (int)N, (int)K, nc, g.useg, g.P, ep);
     return hipGetLastError();
 }
 
-template <int T, int NCB>
+template <int T, int NCB, bool PAIR>
 static hipError_t verify_dispatch(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
-                                  hipStream_t st) {
+                                  const Epilogue &ep, hipStream_t st) {
     VGeo g;
-    if (!vgeo(N, K, nc, NCB, g)) return hipErrorInvalidValue;
+    if (!vgeo(N, K, nc, NCB, PAIR ? 2 : 1, g)) return hipErrorInvalidValue;
     switch (g.RL) {
-    case 1: return launch_v<T, NCB, 1>(W, x, y, N, K, nc, g, st);
-    case 2: return launch_v<T, NCB, 2>(W, x, y, N, K, nc, g, st);
-    case 3: return launch_v<T, NCB, 3>(W, x, y, N, K, nc, g, st);
-    case 4: return launch_v<T, NCB, 4>(W, x, y, N, K, nc, g, st);
-    case 5: return launch_v<T, NCB, 5>(W, x, y, N, K, nc, g, st);
-    case 6: return launch_v<T, NCB, 6>(W, x, y, N, K, nc, g, st);
-    case 7: return launch_v<T, NCB, 7>(W, x, y, N, K, nc, g, st);
-    default: return launch_v<T, NCB, 8>(W, x, y, N, K, nc, g, st);
+    case 1: return launch_v<T, NCB, 1, PAIR>(W, x, y, N, K, nc, g, ep, st);
+    case 2: return launch_v<T, NCB, 2, PAIR>(W, x, y, N, K, nc, g, ep, st);
+    case 3: return launch_v<T, NCB, 3, PAIR>(W, x, y, N, K, nc, g, ep, st);
+    case 4: return launch_v<T, NCB, 4, PAIR>(W, x, y, N, K, nc, g, ep, st);
+    case 5: return launch_v<T, NCB, 5, PAIR>(W, x, y, N, K, nc, g, ep, st);
+    case 6: return launch_v<T, NCB, 6, PAIR>(W, x, y, N, K, nc, g, ep, st);
+    case 7: return launch_v<T, NCB, 7, PAIR>(W, x, y, N, K, nc, g, ep, st);
+    default: return launch_v<T, NCB, 8, PAIR>(W, x, y, N, K, nc, g, ep, st);
     }
 }
 
+template <int T>
+static hipError_t verify_type(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
+                              const Epilogue &ep, hipStream_t st) {
+    const bool two = nc > 4;
+    if (ep.W2)
+        return two ? verify_dispatch<T, 2, true>(W, x, y, N, K, nc, ep, st)
+                   : verify_dispatch<T, 1, true>(W, x, y, N, K, nc, ep, st);
+    return two ? verify_dispatch<T, 2, false>(W, x, y, N, K, nc, ep, st)
+               : verify_dispatch<T, 1, false>(W, x, y, N, K, nc, ep, st);
+}
+
 hipError_t launch_gemv_multi(int type, const void *W, const void *x, void *y, int64_t N, int64_t K, int ncols,
-                             hipStream_t stream) {
-    const bool two = ncols > 4;
+                             const Epilogue &ep, hipStream_t stream) {
     switch (type) {
-    case Q4_K: return two ? verify_dispatch<Q4_K, 2>(W, x, y, N, K, ncols, stream)
-                          : verify_dispatch<Q4_K, 1>(W, x, y, N, K, ncols, stream);
-    case Q5_K: return two ? verify_dispatch<Q5_K, 2>(W, x, y, N, K, ncols, stream)
-                          : verify_dispatch<Q5_K, 1>(W, x, y, N, K, ncols, stream);
-    case Q6_K: return two ? verify_dispatch<Q6_K, 2>(W, x, y, N, K, ncols, stream)
-                          : verify_dispatch<Q6_K, 1>(W, x, y, N, K, ncols, stream);
+    case Q4_K: return verify_type<Q4_K>(W, x, y, N, K, ncols, ep, stream);
+    case Q5_K: return verify_type<Q5_K>(W, x, y, N, K, ncols, ep, stream);
+    case Q6_K: return verify_type<Q6_K>(W, x, y, N, K, ncols, ep, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -126,3 +126,36 @@ def test_repack_validation_codes():
     assert binding.qk_repack(binding.Q4_K, FAKE + 8, 4 * FAKE, 4, 256, 0) == binding.QK_EINVAL_PTR
     assert binding.qk_repack(binding.Q4_K, FAKE, 4 * FAKE + 4, 4, 256, 0) == binding.QK_EINVAL_PTR
     assert binding.qk_repack(binding.Q6_K, FAKE, FAKE + 16 * 210, 32, 256, 0) == binding.QK_EINVAL_PTR  # overlap
+
+
+def test_epilogue_validation_codes():
+    """qk_gemv_ex / qk_gemv_swiglu: shape and type checks as qk_gemv, then the
+    flags, then the pointers (the residual may be y only for an fp32 y)."""
+    Q4, Q6 = binding.Q4_K, binding.Q6_K
+    F16 = binding.Y_F16
+    ex = binding.qk_gemv_ex
+    sw = binding.qk_gemv_swiglu
+    assert ex(99, FAKE, FAKE, FAKE, 4, 256, 1, None, 0, 0) == binding.QK_EINVAL_TYPE
+    assert ex(Q4, FAKE, FAKE, FAKE, 4, 300, 1, None, 0, 0) == binding.QK_EINVAL_SHAPE
+    assert ex(Q4, FAKE, FAKE, FAKE, 4, 256, 9, None, 0, 0) == binding.QK_EINVAL_SHAPE
+    assert ex(Q4, FAKE, FAKE, FAKE, 4, 256, 1, None, 2, 0) == binding.QK_EINVAL_FLAGS
+    assert ex(Q4, FAKE, FAKE, FAKE, 4, 256, 1, None, F16 | 4, 0) == binding.QK_EINVAL_FLAGS
+    assert ex(Q4, 0, FAKE, FAKE, 4, 256, 1, None, 0, 0) == binding.QK_EINVAL_PTR
+    assert ex(Q4, FAKE, FAKE + 8, FAKE, 4, 256, 1, None, 0, 0) == binding.QK_EINVAL_PTR
+    assert ex(Q4, FAKE, FAKE, FAKE + 2, 4, 256, 1, None, 0, 0) == binding.QK_EINVAL_PTR  # fp32 y, 2-aligned
+    assert ex(Q4, FAKE, FAKE, FAKE + 1, 4, 256, 1, None, F16, 0) == binding.QK_EINVAL_PTR  # fp16 y, odd
+    assert ex(Q4, FAKE, FAKE, FAKE, 4, 256, 1, FAKE + 2, 0, 0) == binding.QK_EINVAL_PTR  # residual alignment
+    # residual overlapping y: allowed only as y itself with an fp32 y
+    assert ex(Q4, FAKE, FAKE, FAKE, 4, 256, 2, FAKE + 4, 0, 0) == binding.QK_EINVAL_PTR
+    assert ex(Q4, FAKE, FAKE, FAKE, 4, 256, 2, FAKE, F16, 0) == binding.QK_EINVAL_PTR
+    assert ex(Q4, FAKE, FAKE, FAKE + 32, 4, 256, 2, FAKE + 16, F16, 0) == binding.QK_EINVAL_PTR
+    assert binding.qk_gemv_ex(Q4 | binding.PLANAR, FAKE, FAKE, FAKE, 4, 256, 2, None, 0, 0) == \
+        binding.QK_EINVAL_TYPE
+    assert sw(99, FAKE, FAKE, FAKE, FAKE, 4, 256, 1, 0, 0) == binding.QK_EINVAL_TYPE
+    assert sw(Q6, FAKE, FAKE, FAKE, FAKE, 0, 256, 1, 0, 0) == binding.QK_EINVAL_SHAPE
+    assert sw(Q6, FAKE, FAKE, FAKE, FAKE, 4, 256, 1, 8, 0) == binding.QK_EINVAL_FLAGS
+    assert sw(Q6, FAKE, 0, FAKE, FAKE, 4, 256, 1, 0, 0) == binding.QK_EINVAL_PTR
+    assert sw(Q6, FAKE, FAKE + 4, FAKE, FAKE, 4, 256, 1, 0, 0) == binding.QK_EINVAL_PTR
+    assert sw(Q6, FAKE, FAKE, FAKE, FAKE + 1, 4, 256, 1, F16, 0) == binding.QK_EINVAL_PTR
+    for code in (binding.QK_EINVAL_FLAGS,):
+        assert "flag" in binding.qk_strerror(code)

@@ -77,3 +77,8 @@ def test_batch_sixteen_entries_shared_weights():
 def test_large_partial_sum_lds():
     # 34 rows x 512 unit columns per workgroup: 68 KB of partial sums, above the default 64 KB
     _check([(Q4, 8500, 32768, 30, "a"), (Q6, 64, 512, 31, "b")], sample=128)
+
+
+def test_batch_single_phase_entries():
+    # entries whose launch has one row phase and several rows per workgroup
+    _check([(Q4, 1000, 17408, 21, "a"), (Q5, 600, 17408, 22, "a"), (Q6, 300, 5120, 23, "b")])

@@ -1,0 +1,145 @@
+"""GPU parity of the fused epilogues through the C ABI (qk_gemv_ex,
+qk_gemv_swiglu): residual add (separate and in place), fp16 y, and the SwiGLU
+pair (silu(Wg x) * (Wu x) in one launch), for the one-column kernel and the
+verify form, against the oracle's f64 definitions within the tolerances the
+row bound implies (oracle.residual_bound, oracle.swiglu_bound).  fp16 y is
+also the round-to-nearest-even of the same launch's fp32 y, bit for bit."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import dev, needs_gpu, torch
+from quant_dequant_gemv_amd import binding, synth
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+Q4, Q5, Q6 = synth.Q4_K, synth.Q5_K, synth.Q6_K
+TYPES = [Q4, Q5, Q6]
+NAMES = {Q4: "Q4_K", Q5: "Q5_K", Q6: "Q6_K"}
+# ragged rows, a partial 16-unit step, a long K (several x segments)
+SHAPES = [(1, 256), (37, 1280), (130, 5120), (300, 6144), (61, 17408)]
+
+
+def _assert_within(y, y_ref, tol, what, f16=False):
+    y = np.asarray(y, dtype=np.float64).reshape(y_ref.shape)
+    bad = ~oracle.within(y, y_ref, tol, f16)
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(bad, 1.0, 0.0)), y.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside the bound; worst at {i}: "
+                             f"gpu={y[i]!r} ref={y_ref[i]!r} tol={tol[i]!r}")
+
+
+def _residual(N, ncols, seed):
+    return (np.random.default_rng([seed, 7]).standard_normal((N, ncols)) * 4).astype(np.float32)
+
+
+@pytest.mark.parametrize("ncols", [1, 2, 5, 8])
+@pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_residual_and_f16(qt, N, K, ncols):
+    W = synth.superblocks(qt, N, K, 500 + N)
+    x = synth.activations(K, ncols, 500 + N)
+    r = _residual(N, ncols, N)
+    Wd, xd, rd = dev(W.reshape(-1)), dev(x), dev(r)
+    y32 = binding.gemv_ex(qt, Wd, xd, N, K, residual=rd)
+    y16 = binding.gemv_ex(qt, Wd, xd, N, K, residual=rd, f16=True)
+    yin = rd.clone()  # in place: y += W x
+    binding.gemv_ex(qt, Wd, xd, N, K, residual=yin, out=yin)
+    torch.cuda.synchronize()
+    y32, y16, yin = y32.cpu().numpy(), y16.cpu().numpy(), yin.cpu().numpy().reshape(N, ncols)
+    y_ref, S = oracle.gemv_residual(qt, W, x, K, r)
+    what = f"{NAMES[qt]} N={N} K={K} ncols={ncols}"
+    _assert_within(y32, y_ref, oracle.residual_bound(y_ref, S), what + " fp32")
+    _assert_within(y16, y_ref, oracle.residual_bound(y_ref, S, f16=True), what + " fp16", f16=True)
+    assert np.array_equal(y16.view(np.uint16), y32.astype(np.float16).view(np.uint16)), what + " fp16 = RNE(fp32)"
+    assert np.array_equal(yin.view(np.uint32), y32.view(np.uint32)), what + " in place"
+
+
+@pytest.mark.parametrize("ncols", [1, 3, 8])
+@pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
+def test_ex_without_epilogue_is_qk_gemv(qt, ncols):
+    N, K = 257, 5120
+    W = synth.superblocks(qt, N, K, 61)
+    x = synth.activations(K, ncols, 61)
+    Wd, xd = dev(W.reshape(-1)), dev(x)
+    a = binding.gemv(qt, Wd, xd, N, K)
+    b = binding.gemv_ex(qt, Wd, xd, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("ncols", [1, 2, 4, 5, 8])
+@pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_swiglu(qt, N, K, ncols):
+    Wg = synth.superblocks(qt, N, K, 600 + N)
+    Wu = synth.superblocks(qt, N, K, 700 + N)
+    x = synth.activations(K, ncols, 600 + N)
+    Wgd, Wud, xd = dev(Wg.reshape(-1)), dev(Wu.reshape(-1)), dev(x)
+    y32 = binding.gemv_swiglu(qt, Wgd, Wud, xd, N, K)
+    y16 = binding.gemv_swiglu(qt, Wgd, Wud, xd, N, K, f16=True)
+    torch.cuda.synchronize()
+    y32, y16 = y32.cpu().numpy(), y16.cpu().numpy()
+    y_ref, g, Sg, u, Su = oracle.swiglu(qt, Wg, Wu, x, K)
+    what = f"{NAMES[qt]} N={N} K={K} ncols={ncols}"
+    _assert_within(y32, y_ref, oracle.swiglu_bound(y_ref, g, Sg, u, Su), what + " fp32")
+    _assert_within(y16, y_ref, oracle.swiglu_bound(y_ref, g, Sg, u, Su, f16=True), what + " fp16", f16=True)
+    assert np.array_equal(y16.view(np.uint16), y32.astype(np.float16).view(np.uint16)), what + " fp16 = RNE(fp32)"
+    assert np.isfinite(y32).all()  # (fp16 may overflow: its infinities are checked above)
+
+
+@pytest.mark.parametrize("ncols", [1, 4])
+@pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
+def test_swiglu_same_tensor_and_planar(qt, ncols):
+    """Wg == Wu is allowed (y = silu(g) * g); PLANAR rows give the same bits
+    as GGUF rows at ncols = 1."""
+    N, K = 211, 5120
+    W = synth.superblocks(qt, N, K, 81)
+    x = synth.activations(K, ncols, 81)
+    Wd, xd = dev(W.reshape(-1)), dev(x)
+    y = binding.gemv_swiglu(qt, Wd, Wd, xd, N, K)
+    torch.cuda.synchronize()
+    y_ref, g, Sg, u, Su = oracle.swiglu(qt, W, W, x, K)
+    _assert_within(y.cpu().numpy(), y_ref, oracle.swiglu_bound(y_ref, g, Sg, u, Su), f"{NAMES[qt]} same tensor")
+    if ncols == 1:
+        Wp = binding.repack(qt, Wd, N, K)
+        W2 = synth.superblocks(qt, N, K, 82)
+        W2d = dev(W2.reshape(-1))
+        W2p = binding.repack(qt, W2d, N, K)
+        a = binding.gemv_swiglu(qt, Wd, W2d, xd, N, K)
+        b = binding.gemv_swiglu(qt | binding.PLANAR, Wp, W2p, xd, N, K)
+        torch.cuda.synchronize()
+        assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("ncols", [1, 2, 8])
+def test_swiglu_ffn_shape_sampled(ncols):
+    """The FFN gate/up pair at its real shape (Q4_K 17408 x 5120), sampled rows
+    (both ends of many workgroups' row ranges)."""
+    N, K = 17408, 5120
+    Wg = synth.superblocks(Q4, N, K, 2)
+    Wu = synth.superblocks(Q4, N, K, 3)
+    x = synth.activations(K, ncols, 2)
+    y = binding.gemv_swiglu(Q4, dev(Wg.reshape(-1)), dev(Wu.reshape(-1)), dev(x), N, K)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    edges = np.array([b * N // 256 for b in range(0, 256, 5)])
+    rows = np.unique(np.clip(np.concatenate([[0, N - 1], edges, edges - 1, edges + 67]), 0, N - 1))
+    y_ref, g, Sg, u, Su = oracle.swiglu(Q4, Wg[rows], Wu[rows], x, K)
+    _assert_within(y[rows], y_ref, oracle.swiglu_bound(y_ref, g, Sg, u, Su), f"ffn gate/up ncols={ncols}")
+    assert np.isfinite(y).all()
+
+
+def test_residual_down_shape_sampled():
+    """FFN down (Q6_K 5120 x 17408) with its residual, in place, sampled rows."""
+    N, K = 5120, 17408
+    W = synth.superblocks(Q6, N, K, 4)
+    x = synth.activations(K, 1, 4)
+    r = _residual(N, 1, 4)
+    y = dev(r.copy())
+    binding.gemv_ex(Q6, dev(W.reshape(-1)), dev(x), N, K, residual=y, out=y)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy().reshape(N, 1)
+    rows = np.unique(np.concatenate([[0, N - 1], np.arange(0, N, 37)]))
+    y_ref, S = oracle.gemv_residual(Q6, W[rows], x, K, r[rows])
+    _assert_within(y[rows], y_ref, oracle.residual_bound(y_ref, S), "ffn down + residual")

@@ -144,3 +144,19 @@ def test_gemv_row_rounds_all_rows(qt, N):
     y = gpu_gemv(qt, W, x, N, K)
     y_ref, S = oracle.gemv(qt, W, x, K)
     assert_row_bound(y, y_ref, S, f"{NAMES[qt]} {N}x{K}")
+
+
+# K > 16384 leaves room for one row phase of useg = K/64 lanes (Q4_K/Q5_K:
+# 512 threads at most), and useg = 272 is not a multiple of 64, so the last
+# wave holds a second, partial phase: P = 1 with two slot rows per schedule
+# row.  Several rows per workgroup (N > 256) then exercise the slot-row
+# mapping of the reduction at P = 1.  Q6_K (up to 1024 threads) takes P = 1
+# at K = 17408 when five rows per workgroup fit one phase best (N = 1200).
+# Every row is checked.
+@pytest.mark.parametrize("qt,N,K", [(Q4, 1000, 17408), (Q5, 600, 17408), (Q4, 300, 16640), (Q6, 1200, 17408)],
+                         ids=lambda v: NAMES.get(v, str(v)))
+def test_gemv_single_phase_several_rows(qt, N, K):
+    W, x = _case(qt, N, K, 800 + N)
+    y = gpu_gemv(qt, W, x, N, K)
+    y_ref, S = oracle.gemv(qt, W, x, K)
+    assert_row_bound(y, y_ref, S, f"{NAMES[qt]} {N}x{K}")
