@@ -132,6 +132,107 @@ def per_shape(torch, launcher, tensors):
     return out
 
 
+def ab_us(torch, launches, n, reps=3):
+    """Average duration (us) per call of each launch(i, stream), i < n, each
+    captured in its own graph; the graphs are replayed in turn `reps` times
+    (so neither always runs first on freshly allocated memory) and each
+    keeps its fastest replay."""
+    graphs = []
+    for launch in launches:
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(n):
+                launch(i, s.cuda_stream)
+        graphs.append(g)
+    best = [float("inf")] * len(graphs)
+    for _ in range(reps):
+        for k, g in enumerate(graphs):
+            best[k] = min(best[k], graph_span(torch, g, reps=1) / n * 1e6)
+    del graphs
+    return best
+
+
+def fused_epilogues(torch):
+    """The fused epilogues at the FFN shapes, each beside its unfused form on
+    the same weights: gate/up as one SwiGLU launch vs the two-entry merged
+    launch (no SiLU, no product), and FFN down with its residual added in
+    place vs plain.  Rotation over >= 1.2 GB of weight copies."""
+    import ctypes
+
+    from quant_dequant_gemv_amd import binding, synth
+    lib = binding.load_library()
+    out = []
+    N, K = 17408, 5120
+    for nc in (1, 4):
+        Wg = torch.from_numpy(synth.superblocks(synth.Q4_K, N, K, 1005).reshape(-1)).cuda()
+        Wu = torch.from_numpy(synth.superblocks(synth.Q4_K, N, K, 1006).reshape(-1)).cuda()
+        pair = 2 * Wg.numel()
+        copies = max(2, int(-(-MIN_ROTATION_BYTES // pair)))
+        Wgs = [Wg] + [Wg.clone() for _ in range(copies - 1)]
+        Wus = [Wu] + [Wu.clone() for _ in range(copies - 1)]
+        x = torch.from_numpy(synth.activations(K, nc, 1005)).cuda()
+        y = torch.empty((N, nc), dtype=torch.float32, device="cuda")
+        y2 = torch.empty((N, nc), dtype=torch.float32, device="cuda")
+
+        def swiglu(i, st):
+            rc = lib.qk_gemv_swiglu(synth.Q4_K, Wgs[i % copies].data_ptr(), Wus[i % copies].data_ptr(),
+                                    x.data_ptr(), y.data_ptr(), N, K, nc, 0, st)
+            if rc:
+                raise binding.QKError(rc, "qk_gemv_swiglu")
+
+        def separate(i, st):
+            if nc == 1:
+                items = (binding.qk_gemv_item * 2)(
+                    binding.qk_gemv_item(synth.Q4_K, Wgs[i % copies].data_ptr(), x.data_ptr(), y.data_ptr(), N, K),
+                    binding.qk_gemv_item(synth.Q4_K, Wus[i % copies].data_ptr(), x.data_ptr(), y2.data_ptr(), N, K))
+                rc = lib.qk_gemv_batch(items, 2, st)
+            else:
+                rc = lib.qk_gemv(synth.Q4_K, Wgs[i % copies].data_ptr(), x.data_ptr(), y.data_ptr(), N, K, nc, st)
+                rc = rc or lib.qk_gemv(synth.Q4_K, Wus[i % copies].data_ptr(), x.data_ptr(), y2.data_ptr(), N, K,
+                                       nc, st)
+            if rc:
+                raise binding.QKError(rc, "unfused gate/up")
+
+        t_f, t_s = ab_us(torch, [swiglu, separate], 4 * copies)
+        out.append({"name": f"ffn_gate_up_swiglu_ncols{nc}", "type": "Q4_K", "N": N, "K": K, "ncols": nc,
+                    "us": round(t_f, 3), "weight_GBs": round(pair / t_f / 1e3, 1),
+                    "frac_peak": round(pair / t_f / 1e3 / PEAK_HBM_GBS, 4),
+                    "unfused": "one qk_gemv_batch launch of both" if nc == 1 else "two qk_gemv launches",
+                    "unfused_us": round(t_s, 3), "rotation_copies": copies})
+        del Wgs, Wus, Wg, Wu
+        torch.cuda.empty_cache()
+
+    Nd, Kd = 5120, 17408
+    W = torch.from_numpy(synth.superblocks(synth.Q6_K, Nd, Kd, 4).reshape(-1)).cuda()
+    copies = max(2, int(-(-MIN_ROTATION_BYTES // W.numel())))
+    Ws = [W] + [W.clone() for _ in range(copies - 1)]
+    x = torch.from_numpy(synth.activations(Kd, 1, 4)).cuda()
+    h = torch.zeros((Nd, 1), dtype=torch.float32, device="cuda")
+    yp = torch.empty((Nd, 1), dtype=torch.float32, device="cuda")
+
+    def resid(i, st):
+        rc = lib.qk_gemv_ex(synth.Q6_K, Ws[i % copies].data_ptr(), x.data_ptr(), h.data_ptr(), Nd, Kd, 1,
+                            ctypes.c_void_p(h.data_ptr()), 0, st)
+        if rc:
+            raise binding.QKError(rc, "qk_gemv_ex")
+
+    def plain(i, st):
+        rc = lib.qk_gemv(synth.Q6_K, Ws[i % copies].data_ptr(), x.data_ptr(), yp.data_ptr(), Nd, Kd, 1, st)
+        if rc:
+            raise binding.QKError(rc, "qk_gemv")
+
+    t_f, t_p = ab_us(torch, [resid, plain], 4 * copies)
+    out.append({"name": "ffn_down_residual_inplace", "type": "Q6_K", "N": Nd, "K": Kd, "ncols": 1,
+                "us": round(t_f, 3), "weight_GBs": round(W.numel() / t_f / 1e3, 1),
+                "frac_peak": round(W.numel() / t_f / 1e3 / PEAK_HBM_GBS, 4),
+                "unfused": "qk_gemv without the residual", "unfused_us": round(t_p, 3),
+                "rotation_copies": copies})
+    del Ws, W
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(entries, min_seconds=10.0):
     """The CPU oracle on the step's three GEMVs (all rows), repeated until at
     least `min_seconds` of wall time; plus one single-threaded step."""
@@ -187,10 +288,11 @@ def traffic_for(kernel, frac_bytes):
 
 def run_stream(torch, launcher, warm=2):
     """448 GEMVs of one decode token, all weights resident, back to back on
-    one stream: one launch per GEMV, and one qk_gemv_batch launch per group of
-    projections that read the same activations (256 launches).  Each is timed
-    as plain launches enqueued ahead of the GPU (behind a spin kernel) and as
-    one captured graph; HIP-event spans."""
+    one stream: one launch per GEMV; one qk_gemv_batch launch per group of
+    projections that read the same activations (256 launches); and the same
+    256 launches with the epilogues fused (SwiGLU gate/up, residual adds).
+    Each is timed as plain launches enqueued ahead of the GPU (behind a spin
+    kernel) and as one captured graph; HIP-event spans."""
     import ctypes
 
     from quant_dequant_gemv_amd import binding, synth
@@ -209,6 +311,36 @@ def run_stream(torch, launcher, warm=2):
             binding.qk_gemv_item(tensors[i]["qtype"], tensors[i]["W"][0].data_ptr(), tensors[i]["x"].data_ptr(),
                                  tensors[i]["y"].data_ptr(), tensors[i]["N"], tensors[i]["K"]) for i in idx])
         batches.append((arr, len(idx)))
+
+    # fused: gate+up as one SwiGLU launch, the mixer output and FFN down
+    # projections adding into an fp32 residual stream in place, the other
+    # groups merged as above -- the same launch count
+    hres = torch.zeros(synth.HIDDEN, dtype=torch.float32, device="cuda")
+    fused = []
+    for (arr, n), idx in zip(batches, groups):
+        names = [entries[i]["name"] for i in idx]
+        if names == ["ffn_gate", "ffn_up"]:
+            g, u = tensors[idx[0]], tensors[idx[1]]
+            fused.append(("swiglu", (g["qtype"], g["W"][0].data_ptr(), u["W"][0].data_ptr(), g["x"].data_ptr(),
+                                     g["y"].data_ptr(), g["N"], g["K"], 1, 0)))
+        elif len(idx) == 1 and names[0] in ("ssm_out", "attn_output", "ffn_down"):
+            t = tensors[idx[0]]
+            fused.append(("ex", (t["qtype"], t["W"][0].data_ptr(), t["x"].data_ptr(), hres.data_ptr(), t["N"],
+                                 t["K"], 1, ctypes.c_void_p(hres.data_ptr()), 0)))
+        else:
+            fused.append(("batch", (arr, n)))
+
+    def one_token_fused(st=None):
+        h = sh if st is None else st
+        for kind, a in fused:
+            if kind == "swiglu":
+                rc = lib.qk_gemv_swiglu(*a, h)
+            elif kind == "ex":
+                rc = lib.qk_gemv_ex(*a, h)
+            else:
+                rc = lib.qk_gemv_batch(*a, h)
+            if rc != 0:
+                raise binding.QKError(rc, kind)
 
     def one_token():
         for t in tensors:
@@ -253,8 +385,10 @@ def run_stream(torch, launcher, warm=2):
     del g
     bspan = spans_of(one_token_batched)
     bgspan = graph_of(one_token_batched)
+    fspan = spans_of(one_token_fused)
+    fgspan = graph_of(one_token_fused)
     nbytes = synth.weight_bytes(entries)
-    del tensors, batches
+    del tensors, batches, fused
     torch.cuda.empty_cache()
 
     def rec(sp, launches):
@@ -262,7 +396,8 @@ def run_stream(torch, launcher, warm=2):
                 "weight_GBs": round(nbytes / sp / 1e9, 1)}
     return {"gemvs": len(entries), "weight_bytes": nbytes,
             "launches": rec(span, len(entries)), "graph": rec(gspan, len(entries)),
-            "batched": rec(bspan, len(groups)), "batched_graph": rec(bgspan, len(groups))}
+            "batched": rec(bspan, len(groups)), "batched_graph": rec(bgspan, len(groups)),
+            "fused": rec(fspan, len(groups)), "fused_graph": rec(fgspan, len(groups))}
 
 
 def main():
@@ -341,6 +476,8 @@ def main():
         del vt
         torch.cuda.empty_cache()
 
+    fused_out = fused_epilogues(torch)
+
     stream_out = None if args.no_stream else run_stream(torch, launcher)
     cpu = None if args.no_cpu else cpu_baseline(entries)
 
@@ -370,6 +507,7 @@ def main():
         "per_gemv": shapes,
         "mixed_types": mixed_out,
         "verify": verify_out,
+        "fused_epilogues": fused_out,
         "decode_stream": stream_out,
         "event_span_ms_per_step": round(span / args.steps * 1e3, 5),
         "kernel_hash": kernel_hash(),

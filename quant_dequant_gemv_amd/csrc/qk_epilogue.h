@@ -13,14 +13,17 @@ namespace qk {
 // expf; e^-z overflows to +inf for z < -88.7 and the quotient is then -0.
 __device__ __forceinline__ float silu(float z) { return z / (1.f + expf(-z)); }
 
-// y[i] = v (+ res[i]), stored as fp32 or fp16 (RNE).  res may alias y: the
-// same lane reads res[i] before it writes y[i].
-__device__ __forceinline__ void store_y(void *y, const Epilogue &ep, size_t i, float v) {
-    if (ep.res) v += ep.res[i];
-    if (ep.f16)
+// y[i] = v, stored as fp32 or fp16 (RNE).
+__device__ __forceinline__ void store_y(void *y, bool f16, size_t i, float v) {
+    if (f16)
         reinterpret_cast<_Float16 *>(y)[i] = (_Float16)v;
     else
         reinterpret_cast<float *>(y)[i] = v;
 }
+
+// The residual is read early: a load issued at the store would add a full
+// memory latency to every workgroup's tail.  The lane that stores row r
+// reads res[r] before its own store of y[r], and no other workgroup touches
+// row r, so res may be y itself.
 
 }  // namespace qk

@@ -223,8 +223,9 @@ __device__ __forceinline__ float unit_dot(const Unit<T> &U, int q, const KScaleS
 // Workgroup blk of nblk (nthr threads, a multiple of 64) takes rows
 // [blk*N/nblk, (blk+1)*N/nblk).  PAIR (the SwiGLU epilogue): the workgroup
 // streams those rows of W and then of ep.W2 as 2R rows of one schedule, and
-// row r's output combines the sums of rows r and R + r.
-template <int T, int L, int RL, int D, bool NT, bool PAIR>
+// row r's output combines the sums of rows r and R + r.  EPI: the store
+// applies ep's residual / fp16 options (else it is the plain fp32 store).
+template <int T, int L, int RL, int D, bool NT, bool PAIR, bool EPI>
 __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const uint16_t *__restrict__ x,
                                            void *y, int N, int K, int useg, int P, int blk, int nblk,
                                            int nthr, const Epilogue &ep) {
@@ -249,6 +250,15 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     const int PT = (nthr + useg - 1) / useg;
     const int slot0 = ph * useg + uc, slot_step = PT * useg;
     uint8_t *xl = reinterpret_cast<uint8_t *>(part + rows_lane * PT * useg);  // the segment's x
+    // residuals for the store: the final reduction gives row group g = tid/16
+    // rows g, g + NG, g + 2NG, ... (NG = nthr/16); lane j of the group reads
+    // the residual of its j-th row now, and the storing lane fetches it with
+    // a cross-lane read at the end
+    float resp = 0.f;
+    if constexpr (EPI) {
+        const int rj = (tid >> 4) + (tid & 15) * (nthr >> 4);
+        if (ep.res && rj < R) resp = ep.res[r0 + rj];
+    }
 
     for (int s0 = 0; s0 < U; s0 += useg) {
         const int ns = min(useg, U - s0);
@@ -308,13 +318,16 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     // so the shuffles see whole groups.
     const int c4 = min(useg, U) >> 2;
     const int j = tid & 15;
-    // v / P = umulhi(v, inv_p) for v < 2^20 and P >= 2 (for P = 1 the
-    // multiplier would be 2^32)
-    const uint32_t inv_p = 0xffffffffu / (uint32_t)P + 1u;
+    // v / P = umulhi(2v, ceil(2^31 / P)) for v < 2^20 (the partial sums in
+    // LDS bound the rows far lower) and P <= 1024: the multiplier exceeds
+    // 2^31 / P by less than 1, so the product exceeds 2^32 v / P by less than
+    // 2^21, short of the next multiple of 2^32 (at least 2^32 / P >= 2^22
+    // away).  ceil(2^32 / P) itself would not fit 32 bits for P = 1.
+    const uint32_t inv_p2 = (0x80000000u + (uint32_t)P - 1u) / (uint32_t)P;
     constexpr float oscale = T == Q6_K ? 1.f : 0x1p48f;
     // the sum of schedule row v (valid or not, every lane of the 16 takes part)
     auto row_sum = [&](int v, bool ok) {
-        const int vi = P == 1 ? v : (int)__umulhi((uint32_t)v, inv_p);
+        const int vi = (int)__umulhi(2u * (uint32_t)v, inv_p2);
         const int sr = ok ? vi * PT + (v - vi * P) : 0;
         const float4 *pr = reinterpret_cast<const float4 *>(part + (size_t)sr * useg);
         float a = 0.f;
@@ -331,20 +344,31 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
         a += dpp_f32<0x140>(a);  // row_mirror
         return a * oscale;
     };
-    for (int rr = tid >> 4; rr - (tid >> 4) < R; rr += nthr >> 4) {
+    int pass = 0;
+    for (int rr = tid >> 4; rr - (tid >> 4) < R; rr += nthr >> 4, ++pass) {
         const bool rok = rr < R;
         float v = row_sum(rr, rok);
         if constexpr (PAIR) v = silu(v) * row_sum(R + rr, rok);
-        if (rok && j == 0) store_y(y, ep, (size_t)(r0 + rr), v);
+        float rv = 0.f;
+        if constexpr (EPI)  // (all 16 lanes take part in the cross-lane read)
+            if (pass < 16) rv = __shfl(resp, (tid & 63 & ~15) + pass);
+        if (rok && j == 0) {
+            if constexpr (EPI) {
+                if (ep.res) v += pass < 16 ? rv : ep.res[r0 + rr];
+                store_y(y, ep.f16, (size_t)(r0 + rr), v);
+            } else {
+                reinterpret_cast<float *>(y)[r0 + rr] = v;
+            }
+        }
     }
 }
 
-template <int T, int L, int RL, int D, bool NT, bool PAIR>
+template <int T, int L, int RL, int D, bool NT, bool PAIR, bool EPI>
 __global__ void __launch_bounds__(1024) gemv1_kernel(const uint8_t *__restrict__ W,
                                                       const uint16_t *__restrict__ x, void *y, int N, int K,
                                                       int useg, int P, const Epilogue ep) {
-    gemv1_body<T, L, RL, D, NT, PAIR>(W, x, y, N, K, useg, P, (int)blockIdx.x, (int)gridDim.x, (int)blockDim.x,
-                                      ep);
+    gemv1_body<T, L, RL, D, NT, PAIR, EPI>(W, x, y, N, K, useg, P, (int)blockIdx.x, (int)gridDim.x,
+                                           (int)blockDim.x, ep);
 }
 
 // ---------------------------------------------------------------------------
@@ -378,9 +402,11 @@ __global__ void __launch_bounds__(1024) gemv1_batch_kernel(const BatchArgs a) {
     const int blk = (int)blockIdx.x - a.first[i], nblk = a.first[i + 1] - a.first[i];
     const Epilogue plain{nullptr, nullptr, 0};
 #define QK_BODY(T, RL, D) \
-    gemv1_body<T, GGUF, RL, D, false, false>(e.W, e.x, e.y, e.N, e.K, e.useg, e.P, blk, nblk, e.threads, plain)
+    gemv1_body<T, GGUF, RL, D, false, false, false>(e.W, e.x, e.y, e.N, e.K, e.useg, e.P, blk, nblk, e.threads, \
+                                                    plain)
 #define QK_BODYP(T, RL, D) \
-    gemv1_body<T, PLANAR, RL, D, false, false>(e.W, e.x, e.y, e.N, e.K, e.useg, e.P, blk, nblk, e.threads, plain)
+    gemv1_body<T, PLANAR, RL, D, false, false, false>(e.W, e.x, e.y, e.N, e.K, e.useg, e.P, blk, nblk, e.threads, \
+                                                      plain)
     switch (e.code) {
     case B_Q4_1: QK_BODY(Q4_K, 1, 1); break;
     case B_Q4_2: QK_BODY(Q4_K, 2, 2); break;
@@ -580,7 +606,9 @@ static Geo geometry(int64_t N, int64_t K, int cus, int mult = 1) {
     const int64_t U = K / 64;
     g.useg = (int)(U < 512 ? U : 512);
     const int pmax = RR::max_threads / g.useg > 0 ? RR::max_threads / g.useg : 1;
-    for (int64_t G = N < cus ? N : cus;; G *= 2) {
+    // one workgroup per CU and tensor streamed (mult = 2: both halves of the
+    // pair have their own CU's worth of rows, as two launches would)
+    for (int64_t G = std::min<int64_t>(N, (int64_t)cus * mult);; G *= 2) {
         if (G > N) G = N;
         g.G = (int)G;
         const int64_t R = mult * ((N + G - 1) / G);
@@ -618,9 +646,16 @@ template <int T, int L, int RL, int D, bool NT, bool PAIR>
 static hipError_t launch1(const void *W, const void *x, void *y, int64_t N, int64_t K, Geo geo,
                           const Epilogue &ep, hipStream_t st) {
     const size_t lds = part_lds(N, geo, PAIR ? 2 : 1);
-    allow_lds<gemv1_kernel<T, L, RL, D, NT, PAIR>>();
-    hipLaunchKernelGGL((gemv1_kernel<T, L, RL, D, NT, PAIR>), dim3(geo.G), dim3(geo.threads), lds, st,
-                       (const uint8_t *)W, (const uint16_t *)x, y, (int)N, (int)K, geo.useg, geo.P, ep);
+    // plain launches run a body without the epilogue's store options
+    if (!PAIR && !ep.res && !ep.f16) {
+        allow_lds<gemv1_kernel<T, L, RL, D, NT, false, false>>();
+        hipLaunchKernelGGL((gemv1_kernel<T, L, RL, D, NT, false, false>), dim3(geo.G), dim3(geo.threads), lds, st,
+                           (const uint8_t *)W, (const uint16_t *)x, y, (int)N, (int)K, geo.useg, geo.P, ep);
+    } else {
+        allow_lds<gemv1_kernel<T, L, RL, D, NT, PAIR, true>>();
+        hipLaunchKernelGGL((gemv1_kernel<T, L, RL, D, NT, PAIR, true>), dim3(geo.G), dim3(geo.threads), lds, st,
+                           (const uint8_t *)W, (const uint16_t *)x, y, (int)N, (int)K, geo.useg, geo.P, ep);
+    }
     return hipGetLastError();
 }
 

@@ -147,8 +147,9 @@ __device__ __forceinline__ float quad_bcast(float a) { return vdpp<J | (J << 2) 
 
 // PAIR (the SwiGLU epilogue): the workgroup's rows of W and then of ep.W2
 // form one schedule of 2R rows; row r's outputs combine the sums of rows r
-// and R + r.
-template <int T, int NCB, int RL, int D, bool PAIR>
+// and R + r.  EPI: the store applies ep's residual / fp16 options (else it is
+// the plain fp32 store).
+template <int T, int NCB, int RL, int D, bool PAIR, bool EPI>
 __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint8_t *__restrict__ W,
                                                                const uint16_t *__restrict__ x, void *y,
                                                                int N, int K, int nc, int useg, int P,
@@ -174,6 +175,15 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
     uint8_t *planes = reinterpret_cast<uint8_t *>(vsm + (size_t)quads_lane * P * 4 * nslot * NC);
     const int ps = useg * VXSTRIDE;  // bytes per column plane
     const int slot = 4 * wip + (blk >> 2);  // this lane's slot if it writes (blk % 4 == 0)
+    // the residuals of the first row this lane stores (lane 0 of each 16)
+    float res0[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) res0[c] = 0.f;
+    if constexpr (EPI)
+        if (ep.res && (tid & 15) == 0 && (tid >> 4) < R)
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                if (c < nc) res0[c] = ep.res[(size_t)(r0 + (tid >> 4)) * nc + c];
 
     for (int s0 = 0; s0 < U; s0 += useg) {
         const int ns = min(useg, U - s0);
@@ -231,11 +241,16 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
         for (int i0 = 0; i0 < quads_lane; i0 += RL) {
             Unit<T> buf[DD];
             auto load_quad = [&](Unit<T> &dst, int i) {
-                const int v = min(4 * (ph + P * (i0 + i)) + j, RV - 1);  // row of the schedule
-                const uint8_t *base = W + (size_t)(r0 + v) * row_bytes;
-                if constexpr (PAIR)
-                    if (v >= R) base = reinterpret_cast<const uint8_t *>(ep.W2) + (size_t)(r0 + v - R) * row_bytes;
-                dst.template load<false, GGUF>(base, 0u, ua);
+                if constexpr (PAIR) {
+                    const int v = min(4 * (ph + P * (i0 + i)) + j, RV - 1);  // row of the schedule
+                    const uint8_t *base = v < R ? W + (size_t)(r0 + v) * row_bytes
+                                                : reinterpret_cast<const uint8_t *>(ep.W2) +
+                                                      (size_t)(r0 + v - R) * row_bytes;
+                    dst.template load<false, GGUF>(base, 0u, ua);
+                } else {
+                    const int row = min(r0 + 4 * (ph + P * (i0 + i)) + j, r1 - 1);
+                    dst.template load<false, GGUF>(W + (size_t)row * row_bytes, 0u, ua);
+                }
             };
 #pragma unroll
             for (int p = 0; p < DD; ++p) load_quad(buf[p], p);
@@ -371,10 +386,23 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
 #pragma unroll
             for (int c = 0; c < NC; ++c) a[c] = silu(a[c]) * b[c];
         }
-        if (rok && s16 == 0)
+        if (rok && s16 == 0) {
+            const size_t o = (size_t)(r0 + rr) * nc;
+            if constexpr (EPI) {
+                const bool first = rr == (tid >> 4);
 #pragma unroll
-            for (int c = 0; c < NC; ++c)
-                if (c < nc) store_y(y, ep, (size_t)(r0 + rr) * nc + c, a[c]);
+                for (int c = 0; c < NC; ++c)
+                    if (c < nc) {
+                        float v = a[c];
+                        if (ep.res) v += first ? res0[c] : ep.res[o + c];
+                        store_y(y, ep.f16, o + c, v);
+                    }
+            } else {
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    if (c < nc) reinterpret_cast<float *>(y)[o + c] = a[c];
+            }
+        }
     }
 }
 
@@ -411,6 +439,9 @@ static bool vgeo(int64_t N, int64_t K, int nc, int ncb, int mult, VGeo &g) {
     g.useg = (int)(((U + nseg - 1) / nseg + 15) / 16 * 16);
     const int wpp = g.useg / 16;
     const int pmax = std::max(1, ((ncb == 1 ? v_max_threads<1>() : v_max_threads<2>()) / 64) / wpp);
+    // one workgroup per CU, also for a pair of tensors (each workgroup stages
+    // x for its columns once: more workgroups would stage it more often;
+    // measured slower for the pair at ncols = 4)
     for (int64_t G = std::min<int64_t>(N, cus_v());; G *= 2) {
         if (G > N) G = N;
         g.G = (int)G;
@@ -449,15 +480,23 @@ static hipError_t v_allow_lds() {
     return e;
 }
 
+template <int T, int NCB, int RL, bool PAIR, bool EPI>
+static hipError_t launch_ve(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, const VGeo &g,
+                            const Epilogue &ep, hipStream_t st) {
+    constexpr int D = 2;
+    const hipError_t e = v_allow_lds<verify_kernel<T, NCB, RL, D, PAIR, EPI>>();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((verify_kernel<T, NCB, RL, D, PAIR, EPI>), dim3((unsigned)g.G), dim3(g.threads), g.lds, st,
+                       (const uint8_t *)W, (const uint16_t *)x, y, (int)N, (int)K, nc, g.useg, g.P, ep);
+    return hipGetLastError();
+}
+
+// plain launches run a body without the epilogue's store options
 template <int T, int NCB, int RL, bool PAIR>
 static hipError_t launch_v(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, const VGeo &g,
                            const Epilogue &ep, hipStream_t st) {
-    constexpr int D = 2;
-    const hipError_t e = v_allow_lds<verify_kernel<T, NCB, RL, D, PAIR>>();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((verify_kernel<T, NCB, RL, D, PAIR>), dim3((unsigned)g.G), dim3(g.threads), g.lds, st,
-                       (const uint8_t *)W, (const uint16_t *)x, y, (int)N, (int)K, nc, g.useg, g.P, ep);
-    return hipGetLastError();
+    if (!PAIR && !ep.res && !ep.f16) return launch_ve<T, NCB, RL, false, false>(W, x, y, N, K, nc, g, ep, st);
+    return launch_ve<T, NCB, RL, PAIR, true>(W, x, y, N, K, nc, g, ep, st);
 }
 
 template <int T, int NCB, bool PAIR>

@@ -143,3 +143,22 @@ def test_residual_down_shape_sampled():
     rows = np.unique(np.concatenate([[0, N - 1], np.arange(0, N, 37)]))
     y_ref, S = oracle.gemv_residual(Q6, W[rows], x, K, r[rows])
     _assert_within(y[rows], y_ref, oracle.residual_bound(y_ref, S), "ffn down + residual")
+
+
+@pytest.mark.parametrize("qt,N,K", [(Q4, 17408, 5120), (Q4, 200000, 256), (Q5, 120000, 512)],
+                         ids=["rows68_per_wg", "rows782_per_wg", "Q5_rows469_per_wg"])
+def test_residual_many_rows_per_workgroup(qt, N, K):
+    """Each 16-lane row group of the final reduction stores several rows (3,
+    and more than 16, whose residuals are read late): every pass must add its
+    own row's residual.  Sampled rows: both ends of many workgroups' ranges."""
+    W = synth.superblocks(qt, N, K, 90)
+    x = synth.activations(K, 1, 90)
+    r = _residual(N, 1, 90)
+    y = binding.gemv_ex(qt, dev(W.reshape(-1)), dev(x), N, K, residual=dev(r))
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    edges = np.array([b * N // 256 for b in range(256)])
+    rng = np.random.default_rng(N)
+    rows = np.unique(np.clip(np.concatenate([[0, N - 1], edges, edges - 1, rng.integers(0, N, 400)]), 0, N - 1))
+    y_ref, S = oracle.gemv_residual(qt, W[rows], x, K, r[rows])
+    _assert_within(y[rows], y_ref, oracle.residual_bound(y_ref, S), f"{NAMES[qt]} {N}x{K} residual")
