@@ -476,6 +476,17 @@ def main():
         del vt
         torch.cuda.empty_cache()
 
+    # wider verification (column groups of <= 8, one launch): 16 and 17 columns
+    for nc in (16, 17):
+        vt = make_tensors(torch, [dict(name=f"verify_ncols{nc}", qtype=v["qtype"], N=v["N"], K=v["K"],
+                                       seed=v["seed"], ncols=nc)])
+        r = per_shape(torch, launcher, vt)[0]
+        r["ncols"] = nc
+        r["TFLOPs"] = round(2.0 * v["N"] * v["K"] * nc / r["us"] / 1e6, 2)
+        verify_out.append(r)
+        del vt
+        torch.cuda.empty_cache()
+
     fused_out = fused_epilogues(torch)
 
     stream_out = None if args.no_stream else run_stream(torch, launcher)

@@ -57,7 +57,7 @@ enum {
 enum {
     QK_OK = 0,
     QK_EINVAL_TYPE = -1,  /* type is not one of QK_Q4_K / QK_Q5_K / QK_Q6_K        */
-    QK_EINVAL_SHAPE = -2, /* N < 1, K < 256, K % 256 != 0, ncols not in 1..8,
+    QK_EINVAL_SHAPE = -2, /* N < 1, K < 256, K % 256 != 0, ncols not in 1..32,
                              or a size whose byte count overflows int64          */
     QK_EINVAL_PTR = -3,   /* a NULL pointer, W or x not 16-byte aligned, or y /
                              out not 4-byte aligned                               */
@@ -65,7 +65,7 @@ enum {
     QK_EINVAL_FLAGS = -5  /* an epilogue flag other than QK_Y_F16                 */
 };
 
-#define QK_MAX_NCOLS 8
+#define QK_MAX_NCOLS 32
 
 /*
  * Row layout flag, OR'ed into a type argument: QK_Q4_K | QK_PLANAR names a
@@ -83,8 +83,9 @@ enum {
  * qk_row_bytes(type | QK_PLANAR, K) bytes apart.  This is a repack for this
  * GPU, not a format of the pages; the B70 plan ("Qwen3.6 27B Single-B70
  * Maximum-Speed Requirements And Execution Plan", Non-Negotiable Requirements,
- * item 7) allows GPU-native weight packs that are built once and kept resident.  qk_gemv (ncols = 1), qk_gemv_batch and qk_dequant
- * accept it; qk_gemv with ncols > 1 does not (QK_EINVAL_TYPE).
+ * item 7) allows GPU-native weight packs that are built once and kept
+ * resident.  qk_gemv (ncols = 1), qk_gemv_batch and qk_dequant accept it;
+ * qk_gemv with ncols > 1 does not (QK_EINVAL_TYPE).
  */
 #define QK_PLANAR 0x100
 
@@ -98,8 +99,12 @@ enum {
  *   y      device pointer to N*ncols fp32 values, 4-byte aligned (written)
  *   N      rows (output features), >= 1
  *   K      columns of W (input features), a multiple of 256
- *   ncols  columns of x and y, 1..8: 1 is the decode GEMV, 2..8 the
- *          few-column verify form; W is read once per call in both
+ *   ncols  columns of x and y, 1..32: 1 is the decode GEMV, 2..8 the
+ *          few-column verify form with W read once per call; 9..32 take
+ *          the columns in ceil(ncols / 8) groups of (nearly) equal width
+ *          inside one launch, each group streaming W again (from the
+ *          on-chip caches where W fits them) -- the B70 plan's checklist
+ *          asks for verifier widths up to 17
  *   stream hipStream_t to enqueue on
  *
  * Accuracy: |y - y_exact| <= 1e-4 * sum_k |w * x| for every (n, c), where
@@ -148,7 +153,7 @@ int qk_gemv_ex(int type, const void *W, const void *x, void *y,
  *
  * (the B70 plan, "Phase 3: Maximum Useful Fusion", family 3: the combined
  * gate/up projection with SiLU and the multiply fused; family 7 asks for the
- * same at verifier widths, hence ncols 1..8).  Every workgroup streams the
+ * same at verifier widths, hence ncols 1..32).  Every workgroup streams the
  * same rows of both tensors, so g and u never leave the chip.
  *
  *   type   one type (and layout) for both tensors, as for qk_gemv

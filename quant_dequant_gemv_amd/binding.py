@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libqkgemv.so")
 
 Q4_K, Q5_K, Q6_K = 12, 13, 14
 QK_OK, QK_EINVAL_TYPE, QK_EINVAL_SHAPE, QK_EINVAL_PTR, QK_ELAUNCH, QK_EINVAL_FLAGS = 0, -1, -2, -3, -4, -5
-MAX_NCOLS = 8
+MAX_NCOLS = 32
 MAX_BATCH = 16
 PLANAR = 0x100  # QK_PLANAR: layout flag OR'ed into a type
 Y_F16 = 0x1  # QK_Y_F16: epilogue flag, y stored as fp16

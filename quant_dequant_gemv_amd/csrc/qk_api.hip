@@ -155,7 +155,7 @@ const char *qk_strerror(int code) {
     case QK_EINVAL_TYPE:
         return "invalid type: expected QK_Q4_K (12), QK_Q5_K (13) or QK_Q6_K (14), optionally | QK_PLANAR "
                "(0x100) with ncols = 1 (qk_repack takes the type without the flag)";
-    case QK_EINVAL_SHAPE: return "invalid shape: need N >= 1, K a positive multiple of 256, 1 <= ncols <= 8";
+    case QK_EINVAL_SHAPE: return "invalid shape: need N >= 1, K a positive multiple of 256, 1 <= ncols <= 32";
     case QK_EINVAL_PTR:
         return "invalid pointer: NULL, or W/x not 16-byte aligned, or y/out/residual not 4-byte aligned (fp16 y: 2), "
                "or a residual that overlaps y without being y (fp32 y)";

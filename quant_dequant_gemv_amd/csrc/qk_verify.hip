@@ -1,9 +1,12 @@
-// qk_verify.hip -- few-column verify GEMV (ncols 2..8) on gfx950 matrix cores.
+// qk_verify.hip -- few-column verify GEMV (ncols 2..32) on gfx950 matrix cores.
 //
-// y[n][c] = sum_k dequant(W)[n][k] * x[k][c] for c < ncols <= 8: the batched
+// y[n][c] = sum_k dequant(W)[n][k] * x[k][c] for c < ncols: the batched
 // verification of drafted tokens (T4 dossier design-doc prompt, deliverable 3
 // "MTP Verify Plan"; B70 plan, Phase 3 item 7 and Phase 4 "True Xe2 Batched
-// Verification").  W is read from HBM once per call whatever ncols is.
+// Verification"; its checklist names verifier widths up to 17).  Up to 8
+// columns W is streamed once per call; wider calls take the columns in
+// groups of at most 8 inside the one launch, each group streaming the
+// workgroup's rows again (mostly from the caches after the first).
 //
 // Same skeleton as the one-column kernel (x-stationary, rows balanced over
 // the CUs, a ring of units in flight, partial sums in LDS, a fixed-order
@@ -141,6 +144,30 @@ __device__ __forceinline__ void stage_planes(const uint8_t *xg, uint8_t *planes,
     }
 }
 
+// The same planes for a column window of a wider x (row stride ldx halves,
+// the window's first column at xg): one task per 8 rows and column, eight
+// 16-bit loads, one 16-byte write.
+template <int T>
+__device__ __forceinline__ void stage_planes_strided(const uint16_t *xg, int ldx, int nc, uint8_t *planes, int ps,
+                                                     int ns, int tid) {
+    const int ntask = ns * 8 * nc;
+    for (int t = tid; t < ntask; t += (int)blockDim.x) {
+        const int c = t % nc, b = t / nc;  // column, block of 8 rows
+        const uint16_t *src = xg + (size_t)b * 8 * ldx + c;
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = (uint32_t)src[(2 * i) * ldx] | ((uint32_t)src[(2 * i + 1) * ldx] << 16);
+        int off;
+        if constexpr (T == Q6_K) {
+            const int g = (b >> 1) & 15;
+            off = (4 * (b >> 5) + 2 * (g >> 3) + (g & 1)) * VXSTRIDE + 32 * ((g >> 1) & 3) + 16 * (b & 1);
+        } else {
+            off = (b >> 3) * VXSTRIDE + 16 * (b & 7);
+        }
+        *reinterpret_cast<uint4 *>(planes + c * ps + off) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
 // DPP quad_perm broadcast of lane J of each quad (J = 0..3)
 template <int J>
 __device__ __forceinline__ float quad_bcast(float a) { return vdpp<J | (J << 2) | (J << 4) | (J << 6)>(a); }
@@ -148,11 +175,13 @@ __device__ __forceinline__ float quad_bcast(float a) { return vdpp<J | (J << 2) 
 // PAIR (the SwiGLU epilogue): the workgroup's rows of W and then of ep.W2
 // form one schedule of 2R rows; row r's outputs combine the sums of rows r
 // and R + r.  EPI: the store applies ep's residual / fp16 options (else it is
-// the plain fp32 store).
-template <int T, int NCB, int RL, int D, bool PAIR, bool EPI>
+// the plain fp32 store).  x is [K][nct], y (and the residual) [N][nct]; the
+// nct columns are taken in ngrp groups of at most 4 * NCB (WIDE; otherwise
+// ngrp is 1 and the group loop compiles away).
+template <int T, int NCB, int RL, int D, bool PAIR, bool EPI, bool WIDE>
 __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint8_t *__restrict__ W,
                                                                const uint16_t *__restrict__ x, void *y,
-                                                               int N, int K, int nc, int useg, int P,
+                                                               int N, int K, int nct, int ngrp, int useg, int P,
                                                                const Epilogue ep) {
     extern __shared__ __attribute__((aligned(16))) float vsm[];
     constexpr int G = vgroups<T>(), NC = 4 * NCB;
@@ -175,7 +204,10 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
     uint8_t *planes = reinterpret_cast<uint8_t *>(vsm + (size_t)quads_lane * P * 4 * nslot * NC);
     const int ps = useg * VXSTRIDE;  // bytes per column plane
     const int slot = 4 * wip + (blk >> 2);  // this lane's slot if it writes (blk % 4 == 0)
-    // the residuals of the first row this lane stores (lane 0 of each 16)
+    // the residuals of the first row this lane stores (lane 0 of each 16),
+    // first column group
+    if constexpr (!WIDE) ngrp = 1;
+    const int nc0 = nct / ngrp;  // width of group 0
     float res0[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) res0[c] = 0.f;
@@ -183,8 +215,12 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
         if (ep.res && (tid & 15) == 0 && (tid >> 4) < R)
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-                if (c < nc) res0[c] = ep.res[(size_t)(r0 + (tid >> 4)) * nc + c];
+                if (c < nc0) res0[c] = ep.res[(size_t)(r0 + (tid >> 4)) * nct + c];
 
+  for (int grp = 0; grp < ngrp; ++grp) {
+    // columns [c0, c0 + nc) of x, y and the residual
+    const int c0 = grp * nct / ngrp, nc = (grp + 1) * nct / ngrp - c0;
+    if (grp > 0) __syncthreads();  // the previous group's partial sums are read everywhere
     for (int s0 = 0; s0 < U; s0 += useg) {
         const int ns = min(useg, U - s0);
         const bool col_ok = uc < ns;
@@ -194,7 +230,9 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
 
         // x of the segment into the column planes
         if (s0 > 0) __syncthreads();  // the previous segment's x is in registers everywhere
-        {
+        if constexpr (WIDE) {
+            stage_planes_strided<T>(x + (size_t)s0 * 64 * nct + c0, nct, nc, planes, ps, ns, tid);
+        } else {
             const uint8_t *xg = reinterpret_cast<const uint8_t *>(x + (size_t)s0 * 64 * nc);
             switch (nc) {
             case 2: stage_planes<T, 2>(xg, planes, ps, ns, tid); break;
@@ -387,9 +425,9 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
             for (int c = 0; c < NC; ++c) a[c] = silu(a[c]) * b[c];
         }
         if (rok && s16 == 0) {
-            const size_t o = (size_t)(r0 + rr) * nc;
+            const size_t o = (size_t)(r0 + rr) * nct + c0;
             if constexpr (EPI) {
-                const bool first = rr == (tid >> 4);
+                const bool first = rr == (tid >> 4) && grp == 0;
 #pragma unroll
                 for (int c = 0; c < NC; ++c)
                     if (c < nc) {
@@ -404,6 +442,7 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
             }
         }
     }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -480,30 +519,44 @@ static hipError_t v_allow_lds() {
     return e;
 }
 
-template <int T, int NCB, int RL, bool PAIR, bool EPI>
+template <int T, int NCB, int RL, bool PAIR, bool EPI, bool WIDE>
 static hipError_t launch_ve(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, const VGeo &g,
                             const Epilogue &ep, hipStream_t st) {
     constexpr int D = 2;
-    const hipError_t e = v_allow_lds<verify_kernel<T, NCB, RL, D, PAIR, EPI>>();
+    const hipError_t e = v_allow_lds<verify_kernel<T, NCB, RL, D, PAIR, EPI, WIDE>>();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((verify_kernel<T, NCB, RL, D, PAIR, EPI>), dim3((unsigned)g.G), dim3(g.threads), g.lds, st,
-                       (const uint8_t *)W, (const uint16_t *)x, y, (int)N, (int)K, nc, g.useg, g.P, ep);
+    const int ngrp = (nc + 7) / 8;
+    hipLaunchKernelGGL((verify_kernel<T, NCB, RL, D, PAIR, EPI, WIDE>), dim3((unsigned)g.G), dim3(g.threads), g.lds,
+                       st, (const uint8_t *)W, (const uint16_t *)x, y, (int)N, (int)K, nc, ngrp, g.useg, g.P, ep);
     return hipGetLastError();
 }
 
-// plain launches run a body without the epilogue's store options
+// Plain launches run a body without the epilogue's store options.  More
+// than 8 columns run the group loop (always with two column blocks: the
+// groups are then 5 to 8 wide), with the general store.
 template <int T, int NCB, int RL, bool PAIR>
 static hipError_t launch_v(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, const VGeo &g,
                            const Epilogue &ep, hipStream_t st) {
-    if (!PAIR && !ep.res && !ep.f16) return launch_ve<T, NCB, RL, false, false>(W, x, y, N, K, nc, g, ep, st);
-    return launch_ve<T, NCB, RL, PAIR, true>(W, x, y, N, K, nc, g, ep, st);
+    if (nc > 8) {
+        if constexpr (NCB == 2) return launch_ve<T, NCB, RL, PAIR, true, true>(W, x, y, N, K, nc, g, ep, st);
+        return hipErrorInvalidValue;
+    }
+    if (!PAIR && !ep.res && !ep.f16) return launch_ve<T, NCB, RL, false, false, false>(W, x, y, N, K, nc, g, ep, st);
+    return launch_ve<T, NCB, RL, PAIR, true, false>(W, x, y, N, K, nc, g, ep, st);
+}
+
+// nc: all columns; the launch takes them in groups of at most 8, of widths
+// differing by at most one (the widest decides the planes' size and NCB)
+static int widest_group(int nc) {
+    const int ngrp = (nc + 7) / 8;
+    return (nc + ngrp - 1) / ngrp;
 }
 
 template <int T, int NCB, bool PAIR>
 static hipError_t verify_dispatch(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
                                   const Epilogue &ep, hipStream_t st) {
     VGeo g;
-    if (!vgeo(N, K, nc, NCB, PAIR ? 2 : 1, g)) return hipErrorInvalidValue;
+    if (!vgeo(N, K, widest_group(nc), NCB, PAIR ? 2 : 1, g)) return hipErrorInvalidValue;
     switch (g.RL) {
     case 1: return launch_v<T, NCB, 1, PAIR>(W, x, y, N, K, nc, g, ep, st);
     case 2: return launch_v<T, NCB, 2, PAIR>(W, x, y, N, K, nc, g, ep, st);
@@ -519,7 +572,7 @@ static hipError_t verify_dispatch(const void *W, const void *x, void *y, int64_t
 template <int T>
 static hipError_t verify_type(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
                               const Epilogue &ep, hipStream_t st) {
-    const bool two = nc > 4;
+    const bool two = widest_group(nc) > 4;
     if (ep.W2)
         return two ? verify_dispatch<T, 2, true>(W, x, y, N, K, nc, ep, st)
                    : verify_dispatch<T, 1, true>(W, x, y, N, K, nc, ep, st);

@@ -59,7 +59,7 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address: never dereferenced, the ch
     ((binding.Q4_K, FAKE, FAKE, FAKE, 4, 0, 1), binding.QK_EINVAL_SHAPE),
     ((binding.Q5_K, FAKE, FAKE, FAKE, 4, 512 + 128, 1), binding.QK_EINVAL_SHAPE),
     ((binding.Q6_K, FAKE, FAKE, FAKE, 4, 256, 0), binding.QK_EINVAL_SHAPE),
-    ((binding.Q6_K, FAKE, FAKE, FAKE, 4, 256, 9), binding.QK_EINVAL_SHAPE),
+    ((binding.Q6_K, FAKE, FAKE, FAKE, 4, 256, 33), binding.QK_EINVAL_SHAPE),
     ((binding.Q4_K, 0, FAKE, FAKE, 4, 256, 1), binding.QK_EINVAL_PTR),
     ((binding.Q4_K, FAKE, 0, FAKE, 4, 256, 1), binding.QK_EINVAL_PTR),
     ((binding.Q4_K, FAKE, FAKE, 0, 4, 256, 1), binding.QK_EINVAL_PTR),
@@ -137,7 +137,7 @@ def test_epilogue_validation_codes():
     sw = binding.qk_gemv_swiglu
     assert ex(99, FAKE, FAKE, FAKE, 4, 256, 1, None, 0, 0) == binding.QK_EINVAL_TYPE
     assert ex(Q4, FAKE, FAKE, FAKE, 4, 300, 1, None, 0, 0) == binding.QK_EINVAL_SHAPE
-    assert ex(Q4, FAKE, FAKE, FAKE, 4, 256, 9, None, 0, 0) == binding.QK_EINVAL_SHAPE
+    assert ex(Q4, FAKE, FAKE, FAKE, 4, 256, 33, None, 0, 0) == binding.QK_EINVAL_SHAPE
     assert ex(Q4, FAKE, FAKE, FAKE, 4, 256, 1, None, 2, 0) == binding.QK_EINVAL_FLAGS
     assert ex(Q4, FAKE, FAKE, FAKE, 4, 256, 1, None, F16 | 4, 0) == binding.QK_EINVAL_FLAGS
     assert ex(Q4, 0, FAKE, FAKE, 4, 256, 1, None, 0, 0) == binding.QK_EINVAL_PTR

@@ -33,7 +33,7 @@ def _residual(N, ncols, seed):
     return (np.random.default_rng([seed, 7]).standard_normal((N, ncols)) * 4).astype(np.float32)
 
 
-@pytest.mark.parametrize("ncols", [1, 2, 5, 8])
+@pytest.mark.parametrize("ncols", [1, 2, 5, 8, 12, 17])
 @pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_residual_and_f16(qt, N, K, ncols):
@@ -68,7 +68,7 @@ def test_ex_without_epilogue_is_qk_gemv(qt, ncols):
     assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
 
 
-@pytest.mark.parametrize("ncols", [1, 2, 4, 5, 8])
+@pytest.mark.parametrize("ncols", [1, 2, 4, 5, 8, 9, 16])
 @pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_swiglu(qt, N, K, ncols):

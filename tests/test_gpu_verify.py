@@ -109,3 +109,46 @@ def test_verify_round_lengths_sampled(qt, N, K, ncols):
     y_ref, S = oracle.gemv(qt, W[rows], x, K)
     assert_row_bound(y[rows], y_ref, S, f"{NAMES[qt]} N={N} K={K} ncols={ncols}")
     assert np.isfinite(y).all()
+
+
+# Wider verification: the columns go in ceil(ncols / 8) groups of nearly equal
+# width (9 -> 4 + 5, 17 -> 5 + 6 + 6, 32 -> 4 x 8), each staged from the
+# strided rows of x and written to its columns of y.
+@pytest.mark.parametrize("ncols", [9, 12, 16, 17, 24, 32])
+@pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
+@pytest.mark.parametrize("N,K", [(5, 512), (130, 5120), (37, 17408)])
+def test_verify_wide_row_bound(qt, N, K, ncols):
+    W = synth.superblocks(qt, N, K, 1300 + N)
+    x = synth.activations(K, ncols, 1300 + N)
+    y = gpu_gemv(qt, W, x, N, K)
+    y_ref, S = oracle.gemv(qt, W, x, K)
+    assert y.shape == (N, ncols)
+    assert_row_bound(y, y_ref, S, f"{NAMES[qt]} N={N} K={K} ncols={ncols}")
+
+
+@pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
+def test_verify_wide_one_hot_columns_exact(qt):
+    """Column c of x = e_{k_c}: column c of y is column k_c of W, bit-exact,
+    in every column group."""
+    N, K, ncols = 53, 1024, 17
+    W = synth.superblocks(qt, N, K, 19)
+    w = oracle.dequant(qt, W, K)
+    ks = [0, 1, 2, 3, 63, 64, 127, 200, 255, 256, 511, 512, 700, 768, 1000, 1022, 1023]
+    x = np.zeros((K, ncols), dtype=np.float16)
+    for c, k in enumerate(ks):
+        x[k, c] = 1.0
+    y = gpu_gemv(qt, W, x, N, K)
+    for c, k in enumerate(ks):
+        assert same_f32(y[:, c], w[:, k]), f"{NAMES[qt]} column {c} (k={k})"
+
+
+@pytest.mark.parametrize("ncols", [16, 17])
+def test_verify_wide_full_shape_sampled(ncols):
+    c = synth.VERIFY
+    N, K = c["N"], c["K"]
+    W = synth.superblocks(c["qtype"], N, K, c["seed"])
+    x = synth.activations(K, ncols, c["seed"])
+    y = gpu_gemv(c["qtype"], W, x, N, K)
+    rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(ncols).integers(0, N, 160)]))
+    y_ref, S = oracle.gemv(c["qtype"], W[rows], x, K)
+    assert_row_bound(y[rows], y_ref, S, f"verify {N}x{K} ncols={ncols}")
