@@ -18,7 +18,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -31,15 +30,11 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 MIN_ROTATION_BYTES = 1.2e9  # > 4x the 256 MB Infinity Cache
 METRIC = "weight GB/s and % of HBM peak per GEMV; implied tok/s for 64-layer stream"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["quant_dequant_gemv_amd/csrc/qk_kernels.hip", "quant_dequant_gemv_amd/csrc/qk_format.h"]
-
 
 def kernel_hash() -> str:
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    """Hash of the one-column kernel's sources (the one profiles/traffic.json records)."""
+    from quant_dequant_gemv_amd import traffic
+    return traffic.kernel_hash()
 
 
 def algorithmic_bytes(qt, N, K, ncols=1):

@@ -28,7 +28,8 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 COPY_BYTES = 512 * 1024 * 1024
 OUT = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["quant_dequant_gemv_amd/csrc/qk_kernels.hip", "quant_dequant_gemv_amd/csrc/qk_format.h"]
+KERNEL_SOURCES = ["quant_dequant_gemv_amd/csrc/qk_kernels.hip", "quant_dequant_gemv_amd/csrc/qk_format.h",
+                  "quant_dequant_gemv_amd/csrc/qk_epilogue.h"]
 
 
 def kernel_hash() -> str:
