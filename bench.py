@@ -228,6 +228,42 @@ def fused_epilogues(torch):
     return out
 
 
+def read_ceiling(torch, sizes):
+    """The achievable-bandwidth reference: a plain 16-byte read of buffers of
+    the step's sizes (libqkcalib.so: non-temporal loads, grid-stride), one
+    launch per buffer, rotated over >= 1.2 GB of copies like the GEMV step and
+    replayed from one graph; the fastest of three launch shapes."""
+    import ctypes
+
+    from quant_dequant_gemv_amd import build as qb
+    lib = ctypes.CDLL(qb.CALIB_LIB)
+    lib.qk_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.qk_stream_read.restype = ctypes.c_int
+    total = sum(sizes)
+    copies = max(2, int(-(-MIN_ROTATION_BYTES // total)))
+    bufs = [[torch.empty(n, dtype=torch.uint8, device="cuda").fill_(c % 251) for n in sizes] for c in range(copies)]
+    out = torch.empty(1 << 20, dtype=torch.int32, device="cuda")
+    best = None
+    for blocks, threads in ((512, 1024), (1024, 512), (2048, 256)):
+        def launch(i, st, blocks=blocks, threads=threads):
+            c, k = divmod(i, len(sizes))
+            rc = lib.qk_stream_read(bufs[c % copies][k].data_ptr(), sizes[k], out.data_ptr(), blocks, threads, st)
+            if rc != 0:
+                raise RuntimeError(f"qk_stream_read failed: {rc}")
+        n = 4 * copies * len(sizes)
+        us = ab_us(torch, [launch], n)[0]
+        if best is None or us < best[0]:
+            best = (us, blocks, threads)
+    us, blocks, threads = best
+    del bufs
+    torch.cuda.empty_cache()
+    return {"kernel": "plain 16-byte read, non-temporal loads, grid-stride (libqkcalib.so)",
+            "bytes_per_launch": round(total / len(sizes)), "avg_launch_us": round(us, 3),
+            "GBs": round(total / len(sizes) / us / 1e3, 1), "blocks": blocks, "threads": threads,
+            "rotation_copies": copies}
+
+
 def cpu_baseline(entries, min_seconds=10.0):
     """The CPU oracle on the step's three GEMVs (all rows), repeated until at
     least `min_seconds` of wall time; plus one single-threaded step."""
@@ -449,6 +485,7 @@ def main():
     for t in tensors:
         t["W"] = t["W"][:1]
     torch.cuda.empty_cache()
+    ceiling = read_ceiling(torch, [t["bytes"] for t in tensors])
     shapes = per_shape(torch, launcher, tensors)
     del tensors
     torch.cuda.empty_cache()
@@ -508,7 +545,10 @@ def main():
                      "avg_launch_us": round(span / launches * 1e6, 3),
                      "bytes_per_launch": round(step_alg / per_step),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_for("gemv1_kernel<Q4_K>", None)},
+                     "traffic": traffic_for("gemv1_kernel<Q4_K>", None),
+                     "read_ceiling_GBs": ceiling["GBs"],
+                     "frac_of_read_ceiling": round(achieved / ceiling["GBs"], 4)},
+        "read_ceiling": ceiling,
         "cpu_baseline": cpu,
         "per_gemv": shapes,
         "mixed_types": mixed_out,

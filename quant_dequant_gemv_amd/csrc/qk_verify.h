@@ -1,0 +1,587 @@
+// qk_verify.h -- few-column verify GEMV (ncols 2..32) on gfx950 matrix cores.
+// Included by one translation unit per quant type (qk_verify_q4k.hip, ...),
+// which compile in parallel; qk_verify.hip dispatches on the type.
+//
+// y[n][c] = sum_k dequant(W)[n][k] * x[k][c] for c < ncols: the batched
+// verification of drafted tokens (T4 dossier design-doc prompt, deliverable 3
+// "MTP Verify Plan"; B70 plan, Phase 3 item 7 and Phase 4 "True Xe2 Batched
+// Verification"; its checklist names verifier widths up to 17).  Up to 8
+// columns W is streamed once per call; wider calls take the columns in
+// groups of at most 8 inside the one launch, each group streaming the
+// workgroup's rows again (mostly from the caches after the first).
+//
+// Same skeleton as the one-column kernel (x-stationary, rows balanced over
+// the CUs, a ring of units in flight, partial sums in LDS, a fixed-order
+// final sum), with the column products on the matrix cores:
+//   v_mfma_f32_4x4x4_16b_f16 runs 16 independent 4x4x4 blocks; block b is
+//   the 4 lanes 4b..4b+3, lane 4b+j supplies row j of A and column j of B and
+//   receives D[0..3][j].  Here block b is one unit column (64 weights of a
+//   superblock) of four rows, lane j being row j of a row quad:
+//     B column j = the quant patterns of row j for one 32-bit quant word
+//                  (exact fp16 values s*q*2^-24, weights (l, l+2, l+1, l+3)),
+//     A row i    = x column 4*cb + i at the same four weights, held in
+//                  registers by lane i of the block for the whole segment,
+//     D[i][j]    = sum over the word of x_i * q_j.
+//   D is accumulated over a scale group, then each lane scales its own row's
+//   four columns by d*sc (and subtracts the min term) in fp32.
+// A wave covers 16 consecutive unit columns of a row quad; the unit columns
+// of one K segment form a phase of useg/16 waves, and P phases take the row
+// quads of the workgroup in turn.  Per row quad the 16 blocks of a wave are
+// folded with DPP rotations inside each 16-lane row and the 4 results per
+// wave and column go to LDS; at the end each (row, column) adds its slots in
+// a fixed order.
+#pragma once
+
+#include "qk_epilogue.h"
+#include "qk_format.h"
+#include "qk_launch.h"
+
+#include <algorithm>
+
+namespace qk {
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, float4_t c) {
+    const half4_t a = __builtin_bit_cast(half4_t, make_uint2(a0, a1));
+    const half4_t b = __builtin_bit_cast(half4_t, make_uint2(b0, b1));
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 0, 0, 0);
+}
+
+// a from the lane that the DPP control names
+template <int CTRL>
+__device__ __forceinline__ float vdpp(float a) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), CTRL, 0xf, 0xf, false));
+}
+
+// Largest workgroup: 12 waves (3 per SIMD, 168 registers each) for one
+// column block; 8 waves (2 per SIMD, 256 registers) for two, whose x alone
+// takes 64 registers.
+template <int NCB>
+__host__ __device__ constexpr int v_max_threads() { return NCB == 1 ? 768 : 512; }
+constexpr int V_MAX_RL = 8;  // quads per straight-line round, at most
+constexpr int V_RAW_BUDGET = 96 * 1024;  // LDS for the x planes of one segment
+constexpr int V_LDS_MAX = 160 * 1024;
+
+template <int T>
+__host__ __device__ constexpr int vgroups() { return T == Q6_K ? 4 : 2; }  // scale groups per unit
+
+// x of one K segment in LDS, transposed into one plane per column: the 64
+// x values unit ul of the segment multiplies sit in block ul of column c's
+// plane, at c*ps + ul*144 (128 bytes + a 16-byte pad per block, so the 16
+// unit columns of a wave read different banks).  For Q4_K and Q5_K that is
+// k = 64*ul .. 64*ul+63 in order; for Q6_K the unit's four 16-value quarters.
+constexpr int VXSTRIDE = 144;
+
+__device__ __forceinline__ uint4 xplane16(const uint8_t *pl, int kb, int off) {
+    return *reinterpret_cast<const uint4 *>(pl + kb * VXSTRIDE + off);
+}
+
+// Sixteen halves (two 16-byte vectors) -> 8 pair dwords in the pattern order
+// (0, 2), (1, 3) per group of four, + their fp32 sum.
+__device__ __forceinline__ float vx_pairs16(const uint4 &v0, const uint4 &v1, uint32_t *o) {
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        o[2 * g] = (w[2 * g] & 0xffffu) | (w[2 * g + 1] << 16);
+        o[2 * g + 1] = (w[2 * g] >> 16) | (w[2 * g + 1] & 0xffff0000u);
+        s += (f16_lo(w[2 * g]) + f16_hi(w[2 * g])) + (f16_lo(w[2 * g + 1]) + f16_hi(w[2 * g + 1]));
+    }
+    return s;
+}
+
+// Column plane pl at the unit's 64 weights (segment-relative unit ul), in
+// the register order of the quant patterns; plus the fp32 sum of each scale
+// group (16 weights for Q6_K, 32 otherwise).
+template <int T>
+__device__ __forceinline__ void gather_x(const uint8_t *pl, int ul, uint32_t *xr, float *sums) {
+    float s[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) s[m] = vx_pairs16(xplane16(pl, ul, 32 * m), xplane16(pl, ul, 32 * m + 16), xr + 8 * m);
+    if constexpr (T == Q6_K) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) sums[m] = s[m];
+    } else {
+        sums[0] = s[0] + s[1];
+        sums[1] = s[2] + s[3];
+    }
+}
+
+// Copy ns blocks of 64 rows of x (NCV columns, row-major) into the column
+// planes: each task takes 8 rows, contiguous in x (NCV 16-byte loads),
+// transposes them in registers and writes one 16-byte vector per column.
+// For Q6_K the plane block of unit ul holds the unit's four quarters in
+// order instead (the same 16-byte reads then serve every type).
+template <int T, int NCV>
+__device__ __forceinline__ void stage_planes(const uint8_t *xg, uint8_t *planes, int ps, int ns, int tid) {
+    const int ntask = ns * 8;
+    for (int t = tid; t < ntask; t += (int)blockDim.x) {
+        uint32_t h[4 * NCV];
+#pragma unroll
+        for (int i = 0; i < NCV; ++i) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(xg + ((size_t)t * NCV + i) * 16);
+            h[4 * i] = v.x; h[4 * i + 1] = v.y; h[4 * i + 2] = v.z; h[4 * i + 3] = v.w;
+        }
+        // half e of the task is x[8t + e / NCV][e % NCV]
+        auto half = [&](int e) -> uint32_t { return (h[e >> 1] >> (16 * (e & 1))) & 0xffffu; };
+        int off;
+        if constexpr (T == Q6_K) {
+            // rows 8t..8t+7: superblock t/32, 16-row group g = (t/2)%16 of it
+            // (quarter (g/2)%4 of unit 4*(t/32) + 2*(g/8) + g%2), half t%2 of the group
+            const int g = (t >> 1) & 15;
+            off = (4 * (t >> 5) + 2 * (g >> 3) + (g & 1)) * VXSTRIDE + 32 * ((g >> 1) & 3) + 16 * (t & 1);
+        } else {
+            off = (t >> 3) * VXSTRIDE + 16 * (t & 7);
+        }
+        uint8_t *dst = planes + off;
+#pragma unroll
+        for (int c = 0; c < NCV; ++c) {
+            uint4 o;
+            o.x = half(0 * NCV + c) | (half(1 * NCV + c) << 16);
+            o.y = half(2 * NCV + c) | (half(3 * NCV + c) << 16);
+            o.z = half(4 * NCV + c) | (half(5 * NCV + c) << 16);
+            o.w = half(6 * NCV + c) | (half(7 * NCV + c) << 16);
+            *reinterpret_cast<uint4 *>(dst + c * ps) = o;
+        }
+    }
+}
+
+// The same planes for a column window of a wider x (row stride ldx halves,
+// the window's first column at xg): one task per 8 rows and column, eight
+// 16-bit loads, one 16-byte write.
+template <int T>
+__device__ __forceinline__ void stage_planes_strided(const uint16_t *xg, int ldx, int nc, uint8_t *planes, int ps,
+                                                     int ns, int tid) {
+    const int ntask = ns * 8 * nc;
+    for (int t = tid; t < ntask; t += (int)blockDim.x) {
+        const int c = t % nc, b = t / nc;  // column, block of 8 rows
+        const uint16_t *src = xg + (size_t)b * 8 * ldx + c;
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = (uint32_t)src[(2 * i) * ldx] | ((uint32_t)src[(2 * i + 1) * ldx] << 16);
+        int off;
+        if constexpr (T == Q6_K) {
+            const int g = (b >> 1) & 15;
+            off = (4 * (b >> 5) + 2 * (g >> 3) + (g & 1)) * VXSTRIDE + 32 * ((g >> 1) & 3) + 16 * (b & 1);
+        } else {
+            off = (b >> 3) * VXSTRIDE + 16 * (b & 7);
+        }
+        *reinterpret_cast<uint4 *>(planes + c * ps + off) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+// DPP quad_perm broadcast of lane J of each quad (J = 0..3)
+template <int J>
+__device__ __forceinline__ float quad_bcast(float a) { return vdpp<J | (J << 2) | (J << 4) | (J << 6)>(a); }
+
+// PAIR (the SwiGLU epilogue): the workgroup's rows of W and then of ep.W2
+// form one schedule of 2R rows; row r's outputs combine the sums of rows r
+// and R + r.  EPI: the store applies ep's residual / fp16 options (else it is
+// the plain fp32 store).  x is [K][nct], y (and the residual) [N][nct]; the
+// nct columns are taken in ngrp groups of at most 4 * NCB (WIDE; otherwise
+// ngrp is 1 and the group loop compiles away).
+template <int T, int NCB, int RL, int D, bool PAIR, bool EPI, bool WIDE>
+__global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint8_t *__restrict__ W,
+                                                               const uint16_t *__restrict__ x, void *y,
+                                                               int N, int K, int nct, int ngrp, int useg, int P,
+                                                               const Epilogue ep) {
+    extern __shared__ __attribute__((aligned(16))) float vsm[];
+    constexpr int G = vgroups<T>(), NC = 4 * NCB;
+    constexpr int DD = D < RL ? D : RL;
+    const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int blk = lane >> 2, j = lane & 3;
+    const int wpp = useg >> 4;  // waves per phase
+    const int ph = wave / wpp, wip = wave - ph * wpp;
+    const int uc = 16 * wip + blk;  // unit column within the segment
+    const int r0 = (int)((int64_t)blockIdx.x * N / gridDim.x);
+    const int r1 = (int)((int64_t)(blockIdx.x + 1) * N / gridDim.x);
+    const int R = r1 - r0, RV = PAIR ? 2 * R : R, Q = (RV + 3) >> 2;
+    const int quads_lane = (Q + P - 1) / P;
+    const int U = K >> 6;
+    const size_t row_bytes = (size_t)(K >> 8) * Fmt<T>::bytes;
+    const int nslot = 4 * wpp;  // partial slots per (row, column): 4 per wave of a phase
+    // LDS: partial sums [row][slot][NC] (rows of every quad a phase visits),
+    // then the x planes of a segment
+    float *part = vsm;
+    uint8_t *planes = reinterpret_cast<uint8_t *>(vsm + (size_t)quads_lane * P * 4 * nslot * NC);
+    const int ps = useg * VXSTRIDE;  // bytes per column plane
+    const int slot = 4 * wip + (blk >> 2);  // this lane's slot if it writes (blk % 4 == 0)
+    // the residuals of the first row this lane stores (lane 0 of each 16),
+    // first column group
+    if constexpr (!WIDE) ngrp = 1;
+    const int nc0 = nct / ngrp;  // width of group 0
+    float res0[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) res0[c] = 0.f;
+    if constexpr (EPI)
+        if (ep.res && (tid & 15) == 0 && (tid >> 4) < R)
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                if (c < nc0) res0[c] = ep.res[(size_t)(r0 + (tid >> 4)) * nct + c];
+
+  for (int grp = 0; grp < ngrp; ++grp) {
+    // columns [c0, c0 + nc) of x, y and the residual
+    const int c0 = grp * nct / ngrp, nc = (grp + 1) * nct / ngrp - c0;
+    if (grp > 0) __syncthreads();  // the previous group's partial sums are read everywhere
+    for (int s0 = 0; s0 < U; s0 += useg) {
+        const int ns = min(useg, U - s0);
+        const bool col_ok = uc < ns;
+        const int u = s0 + min(uc, ns - 4 + (uc & 3));  // clamped, same q
+        const int q = u & 3;
+        const KScaleSel sel(q);
+
+        // x of the segment into the column planes
+        if (s0 > 0) __syncthreads();  // the previous segment's x is in registers everywhere
+        if constexpr (WIDE) {
+            stage_planes_strided<T>(x + (size_t)s0 * 64 * nct + c0, nct, nc, planes, ps, ns, tid);
+        } else {
+            const uint8_t *xg = reinterpret_cast<const uint8_t *>(x + (size_t)s0 * 64 * nc);
+            switch (nc) {
+            case 2: stage_planes<T, 2>(xg, planes, ps, ns, tid); break;
+            case 3: if constexpr (NC >= 4) stage_planes<T, 3>(xg, planes, ps, ns, tid); break;
+            case 4: if constexpr (NC >= 4) stage_planes<T, 4>(xg, planes, ps, ns, tid); break;
+            case 5: if constexpr (NC >= 8) stage_planes<T, 5>(xg, planes, ps, ns, tid); break;
+            case 6: if constexpr (NC >= 8) stage_planes<T, 6>(xg, planes, ps, ns, tid); break;
+            case 7: if constexpr (NC >= 8) stage_planes<T, 7>(xg, planes, ps, ns, tid); break;
+            default: if constexpr (NC >= 8) stage_planes<T, 8>(xg, planes, ps, ns, tid); break;
+            }
+        }
+        __syncthreads();
+        // this lane's columns j, j+4 in registers; group sums of all columns of the unit
+        uint32_t xr[NCB][32];
+        float xsum[NC][G];
+        {
+            float own[NCB][G];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const int c = 4 * cb + j;
+                if (c < nc) {
+                    gather_x<T>(planes + c * ps, u - s0, xr[cb], own[cb]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) xr[cb][i] = 0u;
+#pragma unroll
+                    for (int g = 0; g < G; ++g) own[cb][g] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    // pre-scaled for the 2^-48 units of the Q4_K/Q5_K partials
+                    const float v = T == Q6_K ? own[cb][g] : own[cb][g] * 0x1p-24f;
+                    xsum[4 * cb + 0][g] = quad_bcast<0>(v);
+                    xsum[4 * cb + 1][g] = quad_bcast<1>(v);
+                    xsum[4 * cb + 2][g] = quad_bcast<2>(v);
+                    xsum[4 * cb + 3][g] = quad_bcast<3>(v);
+                }
+        }
+        const UnitAddr<T, GGUF> ua(K >> 8, u);
+
+        for (int i0 = 0; i0 < quads_lane; i0 += RL) {
+            Unit<T> buf[DD];
+            auto load_quad = [&](Unit<T> &dst, int i) {
+                if constexpr (PAIR) {
+                    const int v = min(4 * (ph + P * (i0 + i)) + j, RV - 1);  // row of the schedule
+                    const uint8_t *base = v < R ? W + (size_t)(r0 + v) * row_bytes
+                                                : reinterpret_cast<const uint8_t *>(ep.W2) +
+                                                      (size_t)(r0 + v - R) * row_bytes;
+                    dst.template load<false, GGUF>(base, 0u, ua);
+                } else {
+                    const int row = min(r0 + 4 * (ph + P * (i0 + i)) + j, r1 - 1);
+                    dst.template load<false, GGUF>(W + (size_t)row * row_bytes, 0u, ua);
+                }
+            };
+#pragma unroll
+            for (int p = 0; p < DD; ++p) load_quad(buf[p], p);
+#pragma unroll
+            for (int p = 0; p < RL; ++p) {
+                const Unit<T> &Un = buf[p % DD];
+                float val[NC];
+                // one column block at a time: its accumulators only (the quant
+                // patterns are recomputed per block, cheaper than the registers)
+                if constexpr (T == Q6_K) {
+                    const float d = f16_lo(Un.d);
+                    float f[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) f[t] = d * (float)Un.scale(t, q);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        float4_t Dq[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) Dq[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            uint32_t pt[8];
+                            Un.patterns(i, q, pt);
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)
+                                Dq[t] = mfma4(xr[cb][8 * t + 2 * i], xr[cb][8 * t + 2 * i + 1], pt[2 * t], pt[2 * t + 1],
+                                              Dq[t]);
+                        }
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            float a = 0.f;
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)  // patterns hold q*2^-24 (t < 2) or 16q*2^-24
+                                a = __builtin_fmaf(f[t],
+                                                   Dq[t][i] * (t < 2 ? 0x1p24f : 0x1p20f) - 32.f * xsum[4 * cb + i][t],
+                                                   a);
+                            val[4 * cb + i] = a;
+                        }
+                    }
+                } else {
+                    // units of 2^-48, as in the one-column kernel: sc and m read as fp16
+                    // patterns are sc*2^-24 and m*2^-24; the x sums are held times 2^-24
+                    const uint4 h = Un.header();
+                    const KScales sk = k_scales(h, sel);
+                    auto pat = [](uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)v); };
+                    const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)h.x);
+                    const float dmin = (float)__builtin_bit_cast(_Float16, (uint16_t)(h.x >> 16));
+                    const float fl = __builtin_fmaf(d, pat(sk.sc_lo), 0.f);
+                    const float fh = __builtin_fmaf(d, pat(sk.sc_hi), 0.f) * 0x1p-4f;
+                    const float ml = __builtin_fmaf(dmin, pat(sk.m_lo), 0.f);
+                    const float mh = __builtin_fmaf(dmin, pat(sk.m_hi), 0.f);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        float4_t Dl = float4_t{0.f, 0.f, 0.f, 0.f}, Dh = Dl;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            uint32_t pt[4];
+                            Un.patterns(i, q, pt);
+                            Dl = mfma4(xr[cb][2 * i], xr[cb][2 * i + 1], pt[0], pt[1], Dl);
+                            Dh = mfma4(xr[cb][16 + 2 * i], xr[cb][17 + 2 * i], pt[2], pt[3], Dh);
+                        }
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float mn = __builtin_fmaf(ml, xsum[4 * cb + i][0], mh * xsum[4 * cb + i][1]);
+                            val[4 * cb + i] = __builtin_fmaf(fl, Dl[i], __builtin_fmaf(fh, Dh[i], -mn));
+                        }
+                    }
+                }
+                if (p + DD < RL) load_quad(buf[p % DD], p + DD);
+                // fold the 4 blocks of each 16-lane row (same row j, consecutive units)
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    float v = col_ok ? val[c] : 0.f;
+                    v += vdpp<0x124>(v);  // row_ror:4
+                    v += vdpp<0x128>(v);  // row_ror:8
+                    val[c] = v;
+                }
+                // quads past quads_lane (RL need not divide it) have no slot rows
+                if ((blk & 3) == 0 && i0 + p < quads_lane) {
+                    const int row = 4 * (ph + P * (i0 + p)) + j;  // slot row (rows >= R are never read)
+                    float4 *d4 = reinterpret_cast<float4 *>(part + ((size_t)row * nslot + slot) * NC);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        const float4 v = make_float4(val[4 * cb], val[4 * cb + 1], val[4 * cb + 2], val[4 * cb + 3]);
+                        if (s0 == 0) {
+                            d4[cb] = v;
+                        } else {
+                            const float4 o = d4[cb];
+                            d4[cb] = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+                        }
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // y[row][c] = sum over the slots, fixed order: 16 lanes per row, lane s
+    // adds slots s, s+16, ..., then a DPP fold of the 16 lanes per column
+    const int s16 = tid & 15;
+    constexpr float oscale = T == Q6_K ? 1.f : 0x1p48f;
+    // the sums of schedule row v per column (every lane of the 16 takes part)
+    auto row_sums = [&](int v, bool ok, float *a) {
+        const float *pr = part + (size_t)(ok ? v : 0) * nslot * NC;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) a[c] = 0.f;
+        for (int sl = s16; sl < nslot; sl += 16) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const float4 w = reinterpret_cast<const float4 *>(pr + (size_t)sl * NC)[cb];
+                a[4 * cb] += w.x;
+                a[4 * cb + 1] += w.y;
+                a[4 * cb + 2] += w.z;
+                a[4 * cb + 3] += w.w;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            float t = a[c];
+            t += vdpp<0xb1>(t);   // quad_perm [1,0,3,2]
+            t += vdpp<0x4e>(t);   // quad_perm [2,3,0,1]
+            t += vdpp<0x141>(t);  // row_half_mirror
+            t += vdpp<0x140>(t);  // row_mirror
+            a[c] = t * oscale;
+        }
+    };
+    for (int rr = tid >> 4; rr - (tid >> 4) < R; rr += (int)blockDim.x >> 4) {
+        const bool rok = rr < R;
+        float a[NC];
+        row_sums(rr, rok, a);
+        if constexpr (PAIR) {
+            float b[NC];
+            row_sums(R + rr, rok, b);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) a[c] = silu(a[c]) * b[c];
+        }
+        if (rok && s16 == 0) {
+            const size_t o = (size_t)(r0 + rr) * nct + c0;
+            if constexpr (EPI) {
+                const bool first = rr == (tid >> 4) && grp == 0;
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    if (c < nc) {
+                        float v = a[c];
+                        if (ep.res) v += first ? res0[c] : ep.res[o + c];
+                        store_y(y, ep.f16, o + c, v);
+                    }
+            } else {
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    if (c < nc) reinterpret_cast<float *>(y)[o + c] = a[c];
+            }
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launch geometry.  useg: unit columns per segment, a multiple of 16 (one
+// wave per 16), at most 192 and with the x planes within their budget; the
+// segments of K are made as even as possible.  G: one workgroup per CU unless
+// the LDS does not fit.  P phases and RL quads per straight-line round as
+// ranked below.
+// ---------------------------------------------------------------------------
+struct VGeo { int G, useg, P, RL, threads; size_t lds; };
+
+static int cus_v() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            cus = v;
+        else
+            cus = 256;
+    }
+    return cus;
+}
+
+// mult = 2: each workgroup streams its rows of two tensors (SwiGLU).
+static bool vgeo(int64_t N, int64_t K, int nc, int ncb, int mult, VGeo &g) {
+    const int64_t U = K / 64;
+    const int64_t xs = (int64_t)VXSTRIDE * nc;  // plane bytes per unit column
+    const int max_waves = (ncb == 1 ? v_max_threads<1>() : v_max_threads<2>()) / 64;
+    const int cap = (int)std::min<int64_t>(16 * max_waves, V_RAW_BUDGET / xs) / 16 * 16;
+    if (cap < 16) return false;
+    const int64_t nseg = (U + cap - 1) / cap;
+    g.useg = (int)(((U + nseg - 1) / nseg + 15) / 16 * 16);
+    const int wpp = g.useg / 16;
+    const int pmax = std::max(1, ((ncb == 1 ? v_max_threads<1>() : v_max_threads<2>()) / 64) / wpp);
+    // one workgroup per CU, also for a pair of tensors (each workgroup stages
+    // x for its columns once: more workgroups would stage it more often;
+    // measured slower for the pair at ncols = 4)
+    for (int64_t G = std::min<int64_t>(N, cus_v());; G *= 2) {
+        if (G > N) G = N;
+        g.G = (int)G;
+        const int64_t R = mult * ((N + G - 1) / G), Q = (R + 3) / 4;
+        // Each lane's quads run in straight-line rounds of RL <= V_MAX_RL; a
+        // round starts with an empty load ring, so the fewest rounds come
+        // first, then the fewest quad slots in all (P lanes' worth, the
+        // wasted ones included), then the fewest per lane.  Fewer than 4
+        // waves leave SIMDs idle: avoided wherever the segment allows.
+        const int min_waves = std::min(4, pmax * wpp);
+        int64_t best[4] = {INT64_MAX, INT64_MAX, INT64_MAX, INT64_MAX};
+        for (int p = 1; p <= pmax; ++p) {
+            const int64_t ql = (Q + p - 1) / p;
+            const int64_t rounds = (ql + V_MAX_RL - 1) / V_MAX_RL;
+            const int rl = (int)((ql + rounds - 1) / rounds);
+            const int64_t lane = rounds * rl;
+            const int64_t key[4] = {p * wpp < min_waves ? 1 : 0, rounds, p * lane, lane};
+            if (std::lexicographical_compare(key, key + 4, best, best + 4)) {
+                std::copy(key, key + 4, best);
+                g.P = p;
+                g.RL = rl;
+            }
+        }
+        const int64_t ql = (Q + g.P - 1) / g.P;
+        g.threads = g.P * wpp * 64;
+        g.lds = (size_t)(ql * g.P * 4 * (4 * wpp) * (4 * ncb)) * 4 + (size_t)g.useg * xs;
+        if (g.lds <= (size_t)V_LDS_MAX) return true;
+        if (G == N) return false;
+    }
+}
+
+template <auto Kernel>
+static hipError_t v_allow_lds() {
+    static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, V_LDS_MAX);
+    return e;
+}
+
+template <int T, int NCB, int RL, bool PAIR, bool EPI, bool WIDE>
+static hipError_t launch_ve(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, const VGeo &g,
+                            const Epilogue &ep, hipStream_t st) {
+    constexpr int D = 2;
+    const hipError_t e = v_allow_lds<verify_kernel<T, NCB, RL, D, PAIR, EPI, WIDE>>();
+    if (e != hipSuccess) return e;
+    const int ngrp = (nc + 7) / 8;
+    hipLaunchKernelGGL((verify_kernel<T, NCB, RL, D, PAIR, EPI, WIDE>), dim3((unsigned)g.G), dim3(g.threads), g.lds,
+                       st, (const uint8_t *)W, (const uint16_t *)x, y, (int)N, (int)K, nc, ngrp, g.useg, g.P, ep);
+    return hipGetLastError();
+}
+
+// Plain launches run a body without the epilogue's store options.  More
+// than 8 columns run the group loop (always with two column blocks: the
+// groups are then 5 to 8 wide), with the general store.
+template <int T, int NCB, int RL, bool PAIR>
+static hipError_t launch_v(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, const VGeo &g,
+                           const Epilogue &ep, hipStream_t st) {
+    if (nc > 8) {
+        if constexpr (NCB == 2) return launch_ve<T, NCB, RL, PAIR, true, true>(W, x, y, N, K, nc, g, ep, st);
+        return hipErrorInvalidValue;
+    }
+    if (!PAIR && !ep.res && !ep.f16) return launch_ve<T, NCB, RL, false, false, false>(W, x, y, N, K, nc, g, ep, st);
+    return launch_ve<T, NCB, RL, PAIR, true, false>(W, x, y, N, K, nc, g, ep, st);
+}
+
+// nc: all columns; the launch takes them in groups of at most 8, of widths
+// differing by at most one (the widest decides the planes' size and NCB)
+static int widest_group(int nc) {
+    const int ngrp = (nc + 7) / 8;
+    return (nc + ngrp - 1) / ngrp;
+}
+
+template <int T, int NCB, bool PAIR>
+static hipError_t verify_dispatch(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
+                                  const Epilogue &ep, hipStream_t st) {
+    VGeo g;
+    if (!vgeo(N, K, widest_group(nc), NCB, PAIR ? 2 : 1, g)) return hipErrorInvalidValue;
+    switch (g.RL) {
+    case 1: return launch_v<T, NCB, 1, PAIR>(W, x, y, N, K, nc, g, ep, st);
+    case 2: return launch_v<T, NCB, 2, PAIR>(W, x, y, N, K, nc, g, ep, st);
+    case 3: return launch_v<T, NCB, 3, PAIR>(W, x, y, N, K, nc, g, ep, st);
+    case 4: return launch_v<T, NCB, 4, PAIR>(W, x, y, N, K, nc, g, ep, st);
+    case 5: return launch_v<T, NCB, 5, PAIR>(W, x, y, N, K, nc, g, ep, st);
+    case 6: return launch_v<T, NCB, 6, PAIR>(W, x, y, N, K, nc, g, ep, st);
+    case 7: return launch_v<T, NCB, 7, PAIR>(W, x, y, N, K, nc, g, ep, st);
+    default: return launch_v<T, NCB, 8, PAIR>(W, x, y, N, K, nc, g, ep, st);
+    }
+}
+
+template <int T>
+static hipError_t verify_type(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
+                              const Epilogue &ep, hipStream_t st) {
+    const bool two = widest_group(nc) > 4;
+    if (ep.W2)
+        return two ? verify_dispatch<T, 2, true>(W, x, y, N, K, nc, ep, st)
+                   : verify_dispatch<T, 1, true>(W, x, y, N, K, nc, ep, st);
+    return two ? verify_dispatch<T, 2, false>(W, x, y, N, K, nc, ep, st)
+               : verify_dispatch<T, 1, false>(W, x, y, N, K, nc, ep, st);
+}
+
+}  // namespace qk

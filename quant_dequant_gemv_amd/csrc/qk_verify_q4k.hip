@@ -1,0 +1,11 @@
+// qk_verify_q4k.hip -- the Q4_K instances of the verify kernels (qk_verify.h).
+#include "qk_verify.h"
+
+namespace qk {
+
+hipError_t launch_verify_q4k(const void *W, const void *x, void *y, int64_t N, int64_t K, int ncols,
+                               const Epilogue &ep, hipStream_t stream) {
+    return verify_type<Q4_K>(W, x, y, N, K, ncols, ep, stream);
+}
+
+}  // namespace qk
