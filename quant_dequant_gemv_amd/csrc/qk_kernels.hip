@@ -405,7 +405,7 @@ __global__ void __launch_bounds__(1024) gemv1_batch_kernel(const BatchArgs a) {
     gemv1_body<T, GGUF, RL, D, false, false, false>(e.W, e.x, e.y, e.N, e.K, e.useg, e.P, blk, nblk, e.threads, \
                                                     plain)
 #define QK_BODYP(T, RL, D) \
-    gemv1_body<T, PLANAR, RL, D, false, false, false>(e.W, e.x, e.y, e.N, e.K, e.useg, e.P, blk, nblk, e.threads, \
+    gemv1_body<T, PLANAR, RL, D, true, false, false>(e.W, e.x, e.y, e.N, e.K, e.useg, e.P, blk, nblk, e.threads, \
                                                       plain)
     switch (e.code) {
     case B_Q4_1: QK_BODY(Q4_K, 1, 1); break;
@@ -599,13 +599,39 @@ static size_t part_lds(int64_t N, const Geo &g, int mult = 1) {
 // each take every P-th row, RL rows per straight-line round.  P and RL are
 // chosen to waste the fewest row slots (P * rounds * RL - R), then for the
 // most lanes.  mult = 2: each workgroup streams its rows of two tensors.
-template <int T>
+// Q4_K: several small workgroups of four waves (P = 256 / useg row phases)
+// per CU hide latency better than one large one, measured on the projection
+// shapes at K = 5120 -- four per CU on GGUF rows when every lane still gets
+// 6..12 rows in one round (fewer rows do not amortise the workgroup's x
+// staging and reduction), two per CU on PLANAR rows when a lane gets 4..12.
+template <int T, int L>
+static bool small_workgroups(int64_t N, int cus, int mult, Geo &g) {
+    if constexpr (T != Q4_K) {
+        return false;
+    } else {
+        using RR = RowRounds<T>;
+        const int p4 = 256 / g.useg;
+        if (p4 < 1) return false;
+        const int64_t G = std::min<int64_t>(N, (int64_t)cus * mult * (L == PLANAR ? 2 : 4));
+        const int64_t R = mult * ((N + G - 1) / G), rows = (R + p4 - 1) / p4;
+        if (rows < (L == PLANAR ? 4 : 6) || rows > RR::rl[RR::n - 1]) return false;
+        g.G = (int)G;
+        g.P = p4;
+        for (int k = 0; k < RR::n; ++k)
+            if (RR::rl[k] >= rows) { g.RL = RR::rl[k]; break; }
+        g.threads = (p4 * g.useg + 63) / 64 * 64;
+        return part_lds(N, g, mult) <= (size_t)LDS_PART;
+    }
+}
+
+template <int T, int L = GGUF>
 static Geo geometry(int64_t N, int64_t K, int cus, int mult = 1) {
     using RR = RowRounds<T>;
     Geo g;
     const int64_t U = K / 64;
     g.useg = (int)(U < 512 ? U : 512);
     const int pmax = RR::max_threads / g.useg > 0 ? RR::max_threads / g.useg : 1;
+    if (small_workgroups<T, L>(N, cus, mult, g)) return g;
     // one workgroup per CU and tensor streamed (mult = 2: both halves of the
     // pair have their own CU's worth of rows, as two launches would)
     for (int64_t G = std::min<int64_t>(N, (int64_t)cus * mult);; G *= 2) {
@@ -663,14 +689,17 @@ static hipError_t launch1(const void *W, const void *x, void *y, int64_t N, int6
 template <int T, int L, bool PAIR>
 static hipError_t gemv1_dispatch(const void *W, const void *x, void *y, int64_t N, int64_t K,
                                  const Epilogue &ep, hipStream_t st) {
-    const Geo geo = geometry<T>(N, K, cu_count(), PAIR ? 2 : 1);
+    const Geo geo = geometry<T, L>(N, K, cu_count(), PAIR ? 2 : 1);
+    // PLANAR rows stream with non-temporal loads (measured faster there; no
+    // change on GGUF rows)
+    constexpr bool NT = L == PLANAR;
     switch (geo.RL) {
-    case 1: return launch1<T, L, 1, 1, false, PAIR>(W, x, y, N, K, geo, ep, st);
-    case 2: if constexpr (T != Q6_K) return launch1<T, L, 2, 2, false, PAIR>(W, x, y, N, K, geo, ep, st); break;
-    case 4: if constexpr (T == Q4_K) return launch1<T, L, 4, 2, false, PAIR>(W, x, y, N, K, geo, ep, st); break;
-    case 6: if constexpr (T == Q4_K) return launch1<T, L, 6, 2, false, PAIR>(W, x, y, N, K, geo, ep, st); break;
-    case 8: if constexpr (T == Q4_K) return launch1<T, L, 8, 2, false, PAIR>(W, x, y, N, K, geo, ep, st); break;
-    case 12: if constexpr (T == Q4_K) return launch1<T, L, 12, 2, false, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 1: return launch1<T, L, 1, 1, NT, PAIR>(W, x, y, N, K, geo, ep, st);
+    case 2: if constexpr (T != Q6_K) return launch1<T, L, 2, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 4: if constexpr (T == Q4_K) return launch1<T, L, 4, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 6: if constexpr (T == Q4_K) return launch1<T, L, 6, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 8: if constexpr (T == Q4_K) return launch1<T, L, 8, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 12: if constexpr (T == Q4_K) return launch1<T, L, 12, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
     default: break;
     }
     return hipErrorInvalidValue;
@@ -697,8 +726,9 @@ hipError_t launch_gemv1(int type, const void *W, const void *x, void *y, int64_t
 }
 
 static Geo geometry_of(int type, int64_t N, int64_t K, int cus) {
+    const bool planar = (type & PLANAR_FLAG) != 0;
     switch (type & ~PLANAR_FLAG) {
-    case Q4_K: return geometry<Q4_K>(N, K, cus);
+    case Q4_K: return planar ? geometry<Q4_K, PLANAR>(N, K, cus) : geometry<Q4_K, GGUF>(N, K, cus);
     case Q5_K: return geometry<Q5_K>(N, K, cus);
     default: return geometry<Q6_K>(N, K, cus);
     }
