@@ -638,16 +638,27 @@ static Geo geometry(int64_t N, int64_t K, int cus, int mult = 1) {
         if (G > N) G = N;
         g.G = (int)G;
         const int64_t R = mult * ((N + G - 1) / G);
+        auto plan = [&](int p, int &rl) {  // row slots of p phases, and the round length
+            const int64_t rows = (R + p - 1) / p;
+            rl = RR::rl[RR::n - 1];
+            for (int k = 0; k < RR::n; ++k)
+                if (RR::rl[k] >= rows) { rl = RR::rl[k]; break; }
+            return (int64_t)p * ((rows + rl - 1) / rl) * rl;
+        };
         int64_t best = INT64_MAX;
+        for (int p = 1; p <= pmax; ++p) {
+            int rl;
+            best = std::min(best, plan(p, rl));
+        }
+        // the most phases among the fewest slots; Q6_K on PLANAR rows takes
+        // up to 5% more slots for more phases (measured: 3 phases beat 2 at
+        // 5120 x 17408, where GGUF rows prefer 2)
+        const int64_t limit = (T == Q6_K && L == PLANAR) ? best + best / 20 : best;
         g.P = 1;
         g.RL = 1;
         for (int p = 1; p <= pmax; ++p) {
-            const int64_t rows = (R + p - 1) / p;
-            int rl = RR::rl[RR::n - 1];
-            for (int k = 0; k < RR::n; ++k)
-                if (RR::rl[k] >= rows) { rl = RR::rl[k]; break; }
-            const int64_t slots = (int64_t)p * ((rows + rl - 1) / rl) * rl;
-            if (slots <= best) { best = slots; g.P = p; g.RL = rl; }
+            int rl;
+            if (plan(p, rl) <= limit) { g.P = p; g.RL = rl; }
         }
         g.threads = (g.P * g.useg + 63) / 64 * 64;
         if (G == N || part_lds(N, g, mult) <= (size_t)LDS_PART) break;  // the partial sums fit in LDS
@@ -730,7 +741,7 @@ static Geo geometry_of(int type, int64_t N, int64_t K, int cus) {
     switch (type & ~PLANAR_FLAG) {
     case Q4_K: return planar ? geometry<Q4_K, PLANAR>(N, K, cus) : geometry<Q4_K, GGUF>(N, K, cus);
     case Q5_K: return geometry<Q5_K>(N, K, cus);
-    default: return geometry<Q6_K>(N, K, cus);
+    default: return planar ? geometry<Q6_K, PLANAR>(N, K, cus) : geometry<Q6_K, GGUF>(N, K, cus);
     }
 }
 
