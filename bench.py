@@ -383,6 +383,52 @@ def run_stream(torch, launcher, warm=2):
         else:
             fused.append(("batch", (arr, n)))
 
+    # the same fused stream on PLANAR rows for the Q4_K / Q5_K tensors (each
+    # repacked once here, outside the timed regions; Q6_K stays on GGUF rows,
+    # where PLANAR measured no faster)
+    planar_w = {}
+    for i, t in enumerate(tensors):
+        if t["qtype"] in (synth.Q4_K, synth.Q5_K):
+            planar_w[i] = binding.repack(t["qtype"], t["W"][0], t["N"], t["K"])
+    torch.cuda.synchronize()
+
+    def wp(i):  # (type, weight address) of entry i on the rows this stream uses
+        t = tensors[i]
+        return (t["qtype"] | binding.PLANAR, planar_w[i].data_ptr()) if i in planar_w else \
+            (t["qtype"], t["W"][0].data_ptr())
+
+    fused_planar = []
+    for (arr, n), idx in zip(batches, groups):
+        names = [entries[i]["name"] for i in idx]
+        if names == ["ffn_gate", "ffn_up"]:
+            (tg, pg), (_, pu) = wp(idx[0]), wp(idx[1])
+            g = tensors[idx[0]]
+            fused_planar.append(("swiglu", (tg, pg, pu, g["x"].data_ptr(), g["y"].data_ptr(), g["N"], g["K"], 1, 0)))
+        elif len(idx) == 1 and names[0] in ("ssm_out", "attn_output", "ffn_down"):
+            t = tensors[idx[0]]
+            tt, pw = wp(idx[0])
+            fused_planar.append(("ex", (tt, pw, t["x"].data_ptr(), hres.data_ptr(), t["N"], t["K"], 1,
+                                        ctypes.c_void_p(hres.data_ptr()), 0)))
+        else:
+            items = (binding.qk_gemv_item * len(idx))(*[
+                binding.qk_gemv_item(*wp(i), tensors[i]["x"].data_ptr(), tensors[i]["y"].data_ptr(),
+                                     tensors[i]["N"], tensors[i]["K"]) for i in idx])
+            fused_planar.append(("batch", (items, len(idx))))
+
+    def run_fused(plan, h):
+        for kind, a in plan:
+            if kind == "swiglu":
+                rc = lib.qk_gemv_swiglu(*a, h)
+            elif kind == "ex":
+                rc = lib.qk_gemv_ex(*a, h)
+            else:
+                rc = lib.qk_gemv_batch(*a, h)
+            if rc != 0:
+                raise binding.QKError(rc, kind)
+
+    def one_token_fused_planar(st=None):
+        run_fused(fused_planar, sh if st is None else st)
+
     def one_token_fused(st=None):
         h = sh if st is None else st
         for kind, a in fused:
@@ -440,8 +486,9 @@ def run_stream(torch, launcher, warm=2):
     bgspan = graph_of(one_token_batched)
     fspan = spans_of(one_token_fused)
     fgspan = graph_of(one_token_fused)
+    fpgspan = graph_of(one_token_fused_planar)
     nbytes = synth.weight_bytes(entries)
-    del tensors, batches, fused
+    del tensors, batches, fused, fused_planar, planar_w
     torch.cuda.empty_cache()
 
     def rec(sp, launches):
@@ -450,7 +497,8 @@ def run_stream(torch, launcher, warm=2):
     return {"gemvs": len(entries), "weight_bytes": nbytes,
             "launches": rec(span, len(entries)), "graph": rec(gspan, len(entries)),
             "batched": rec(bspan, len(groups)), "batched_graph": rec(bgspan, len(groups)),
-            "fused": rec(fspan, len(groups)), "fused_graph": rec(fgspan, len(groups))}
+            "fused": rec(fspan, len(groups)), "fused_graph": rec(fgspan, len(groups)),
+            "fused_planar_graph": rec(fpgspan, len(groups))}
 
 
 def main():
