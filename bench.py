@@ -339,7 +339,24 @@ def traffic_for(kernel, frac_bytes):
     return v
 
 
-def run_stream(torch, launcher, warm=2):
+def device_info(torch):
+    """GPU name, architecture, CUs, memory and HIP version; clocks from
+    rocm-smi when it answers (read-only query)."""
+    import subprocess
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count,
+            "memory_GB": round(p.total_memory / 1e9, 1), "hip": torch.version.hip}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=15)
+        if r.returncode == 0:
+            card = next(iter(json.loads(r.stdout).values()))
+            info["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower()}
+    except (OSError, ValueError, StopIteration, subprocess.SubprocessError):
+        pass
+    return info
+
+
+def run_stream(torch, launcher, warm=2, only=None, tokens=1):
     """448 GEMVs of one decode token, all weights resident, back to back on
     one stream: one launch per GEMV; one qk_gemv_batch launch per group of
     projections that read the same activations (256 launches); and the same
@@ -478,6 +495,41 @@ def run_stream(torch, launcher, warm=2):
         del g
         return sp
 
+    if only is not None:
+        # one variant, `tokens` tokens back to back after a warm-up (for a
+        # kernel trace: the last tokens * launches dispatches are the timed ones)
+        fns = {"launches": one_token, "batched": one_token_batched, "fused": one_token_fused,
+               "fused_planar": one_token_fused_planar}
+        graph = only.endswith("_graph")
+        fn = fns[only[:-6] if graph else only]
+        launches = len(entries) if fn is one_token else len(groups)
+        if graph:
+            s2 = torch.cuda.Stream()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=s2):
+                if fn is one_token:
+                    for t in tensors:
+                        launcher.gemv(t["qtype"], t["W"][0].data_ptr(), t["x"].data_ptr(), t["y"].data_ptr(),
+                                      t["N"], t["K"], 1, s2.cuda_stream)
+                else:
+                    fn(s2.cuda_stream)
+            run = gr.replay
+        else:
+            run = fn
+        for _ in range(warm):
+            run()
+        torch.cuda._sleep(SPIN_CYCLES)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(tokens):
+            run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        sp = a.elapsed_time(b) * 1e-3 / tokens
+        return {"variant": only, "tokens": tokens, "launches_per_token": launches, "warm_tokens": warm,
+                "token_ms": round(sp * 1e3, 4), "tok_s": round(1 / sp, 2)}
+
     span = spans_of(one_token)
     g = capture(torch, launcher, [(t, 0) for t in tensors])
     gspan = graph_span(torch, g)
@@ -508,6 +560,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-stream", action="store_true", help="skip the 448-GEMV decode stream")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--stream-only", metavar="VARIANT",
+                    choices=["launches", "launches_graph", "batched", "batched_graph", "fused", "fused_graph",
+                             "fused_planar", "fused_planar_graph"],
+                    help="only time this decode-stream variant for --tokens tokens (for a kernel trace); "
+                         "prints its own JSON line instead of the benchmark's")
+    ap.add_argument("--tokens", type=int, default=5)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -522,6 +580,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     launcher = Launcher()
+    if args.stream_only:
+        r = run_stream(torch, launcher, only=args.stream_only, tokens=args.tokens)
+        r["device"] = device_info(torch)
+        print(json.dumps(r))
+        return
 
     entries = synth.Q4K_PROJECTIONS
     tensors = make_tensors(torch, entries)
@@ -638,6 +701,7 @@ def main():
         "decode_stream": stream_out,
         "event_span_ms_per_step": round(span / args.steps * 1e3, 5),
         "kernel_hash": kernel_hash(),
+        "device": device_info(torch),
     }
     print(json.dumps(out))
 

@@ -363,8 +363,10 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     }
 }
 
+// Q4_K and Q5_K launches never exceed 512 threads (RowRounds): the bound
+// leaves them 256 VGPRs, which Q5_K rounds of 3 or 4 rows need.
 template <int T, int L, int RL, int D, bool NT, bool PAIR, bool EPI>
-__global__ void __launch_bounds__(1024) gemv1_kernel(const uint8_t *__restrict__ W,
+__global__ void __launch_bounds__(T == Q6_K ? 1024 : 512) gemv1_kernel(const uint8_t *__restrict__ W,
                                                       const uint16_t *__restrict__ x, void *y, int N, int K,
                                                       int useg, int P, const Epilogue ep) {
     gemv1_body<T, L, RL, D, NT, PAIR, EPI>(W, x, y, N, K, useg, P, (int)blockIdx.x, (int)gridDim.x,
@@ -579,11 +581,14 @@ static int cu_count() {
 
 // Rows per straight-line round that each type is compiled for.  Q6_K units
 // are the largest (58 B of loads per lane): one unit in flight per lane
-// streams them fastest.  Q5_K units hold 20 dwords: rounds longer than two
-// rows would spill under 128 VGPRs.  Q4_K rounds go up to 12 rows.
+// streams them fastest.  Q5_K units hold 20 dwords: rounds of 3 or 4 rows
+// need the 256 VGPRs that the single-launch kernel's 512-thread bound leaves
+// (measured: 5120 x 6144 in one round of 4 beats two rounds of 2 by 5%);
+// the merged-launch kernel (1024-thread bound) runs Q5_K in rounds of 2.
+// Q4_K rounds go up to 12 rows.
 template <int T> struct RowRounds;
 template <> struct RowRounds<Q4_K> { static constexpr int n = 6, rl[n] = {1, 2, 4, 6, 8, 12}, max_threads = 512; };
-template <> struct RowRounds<Q5_K> { static constexpr int n = 2, rl[n] = {1, 2}, max_threads = 512; };
+template <> struct RowRounds<Q5_K> { static constexpr int n = 4, rl[n] = {1, 2, 3, 4}, max_threads = 512; };
 template <> struct RowRounds<Q6_K> { static constexpr int n = 1, rl[n] = {1}, max_threads = 1024; };
 
 // LDS of one workgroup: ceil(R / P) slot rows per phase, tail phase included
@@ -707,7 +712,8 @@ static hipError_t gemv1_dispatch(const void *W, const void *x, void *y, int64_t 
     switch (geo.RL) {
     case 1: return launch1<T, L, 1, 1, NT, PAIR>(W, x, y, N, K, geo, ep, st);
     case 2: if constexpr (T != Q6_K) return launch1<T, L, 2, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
-    case 4: if constexpr (T == Q4_K) return launch1<T, L, 4, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 3: if constexpr (T == Q5_K) return launch1<T, L, 3, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 4: if constexpr (T != Q6_K) return launch1<T, L, 4, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
     case 6: if constexpr (T == Q4_K) return launch1<T, L, 6, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
     case 8: if constexpr (T == Q4_K) return launch1<T, L, 8, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
     case 12: if constexpr (T == Q4_K) return launch1<T, L, 12, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
@@ -765,7 +771,10 @@ static int body_code_gguf(int type, int rl) {
         default: return -1;
         }
     }
-    if (type == Q5_K) return rl == 1 ? B_Q5_1 : rl == 2 ? B_Q5_2 : -1;
+    // (rounds of 3 or 4 Q5_K rows need more registers than the merged kernel
+    // has: two-row rounds instead, the same arithmetic in a different order
+    // of loads)
+    if (type == Q5_K) return rl == 1 ? B_Q5_1 : (rl >= 2 && rl <= 4) ? B_Q5_2 : -1;
     if (type == Q6_K) return rl == 1 ? B_Q6_1 : -1;
     return -1;
 }

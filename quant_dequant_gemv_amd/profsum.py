@@ -97,6 +97,39 @@ def summarise(trace: str, bench_json: str, command: str, plain_json: str | None 
     return "\n".join(lines) + "\n"
 
 
+def summarise_stream(trace: str, stream_json: str, command: str, plain_json: str | None = None) -> str:
+    """A trace of `bench.py --stream-only VARIANT --tokens T`: the last
+    T * launches_per_token dispatches of the library's kernels are the timed
+    tokens; their summed durations per token are the gap-free bound of the
+    stream, beside the event span per token."""
+    rows = [r for r in load(trace) if r["name"].startswith("qk::")]
+    st = _bench(stream_json)
+    T, L = st["tokens"], st["launches_per_token"]
+    timed = rows[-T * L:]
+    kern_ms = sum(r["us"] for r in timed) / T * 1e-3
+    groups = {}
+    for r in timed:
+        groups.setdefault(r["name"], []).append(r["us"])
+    lines = [f"Command (run from the repository root on one MI355X):\n\n    {command}\n",
+             f"Decode stream variant `{st['variant']}`: {L} launches per token, {T} timed tokens after "
+             f"{st['warm_tokens']} warm-up tokens.\n",
+             "| kernel | dispatches per token | total us per token | share |", "|---|---|---|---|"]
+    for name, d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{name}` | {len(d) / T:.0f} | {sum(d) / T:.1f} | {sum(d) / T / (kern_ms * 1e3):.1%} |")
+    lines += ["",
+              f"- sum of kernel durations per token (the gap-free bound): {kern_ms:.4f} ms "
+              f"-> {1 / kern_ms * 1e3:.1f} tok/s",
+              f"- event span per token in the same traced run: {st['token_ms']:.4f} ms "
+              f"(kernels busy {kern_ms / st['token_ms']:.1%} of it)"]
+    if plain_json:
+        pl = _bench(plain_json)
+        lines.append(f"- the same variant without the profiler, just before on the same GPU: {pl['token_ms']:.4f} ms "
+                     f"per token ({pl['tok_s']:.1f} tok/s; kernels busy {kern_ms / pl['token_ms']:.1%} of it)")
+    if "device" in st:
+        lines.append(f"- device: {st['device']}")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("trace")
@@ -105,8 +138,10 @@ def main():
     ap.add_argument("--command", required=True)
     ap.add_argument("--plain", help="bench.py JSON of an unprofiled run on the same GPU")
     ap.add_argument("--title", default="gemv1_kernel (one column): Q4_K projection step, rocprofv3 kernel trace")
+    ap.add_argument("--stream", action="store_true", help="the trace is of bench.py --stream-only")
     a = ap.parse_args()
-    text = f"# {a.title}\n\n" + summarise(a.trace, a.bench_json, a.command, a.plain)
+    body = (summarise_stream if a.stream else summarise)(a.trace, a.bench_json, a.command, a.plain)
+    text = f"# {a.title}\n\n" + body
     with open(a.out, "w") as f:
         f.write(text)
     print(text)
