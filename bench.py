@@ -400,13 +400,11 @@ def run_stream(torch, launcher, warm=2, only=None, tokens=1):
         else:
             fused.append(("batch", (arr, n)))
 
-    # the same fused stream on PLANAR rows for the Q4_K / Q5_K tensors (each
-    # repacked once here, outside the timed regions; Q6_K stays on GGUF rows,
-    # where PLANAR measured no faster)
+    # the same fused stream with every tensor on PLANAR rows (each repacked
+    # once here, outside the timed regions)
     planar_w = {}
     for i, t in enumerate(tensors):
-        if t["qtype"] in (synth.Q4_K, synth.Q5_K):
-            planar_w[i] = binding.repack(t["qtype"], t["W"][0], t["N"], t["K"])
+        planar_w[i] = binding.repack(t["qtype"], t["W"][0], t["N"], t["K"])
     torch.cuda.synchronize()
 
     def wp(i):  # (type, weight address) of entry i on the rows this stream uses

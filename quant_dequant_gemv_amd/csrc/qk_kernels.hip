@@ -363,10 +363,19 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     }
 }
 
-// Q4_K and Q5_K launches never exceed 512 threads (RowRounds): the bound
-// leaves them 256 VGPRs, which Q5_K rounds of 3 or 4 rows need.
+// Thread bound of a one-column kernel: 1024 (128 VGPRs), except where a
+// round needs more registers: Q5_K rounds of 3 or 4 rows take at most 512
+// threads (256 VGPRs), Q6_K rounds with a ring of units at most 768.  (More
+// registers than a round needs are not free: given 256 VGPRs the scheduler
+// hoists the x reads of Q4_K one-row rounds, measured 10% slower at
+// 1024 x 5120.)
+template <int T, int RL, int D>
+constexpr int gemv1_bound() {
+    return T == Q5_K && RL > 2 ? 512 : T == Q6_K && D > 1 ? 768 : 1024;
+}
+
 template <int T, int L, int RL, int D, bool NT, bool PAIR, bool EPI>
-__global__ void __launch_bounds__(T == Q6_K ? 1024 : 512) gemv1_kernel(const uint8_t *__restrict__ W,
+__global__ void __launch_bounds__((gemv1_bound<T, RL, D>())) gemv1_kernel(const uint8_t *__restrict__ W,
                                                       const uint16_t *__restrict__ x, void *y, int N, int K,
                                                       int useg, int P, const Epilogue ep) {
     gemv1_body<T, L, RL, D, NT, PAIR, EPI>(W, x, y, N, K, useg, P, (int)blockIdx.x, (int)gridDim.x,
@@ -381,7 +390,7 @@ __global__ void __launch_bounds__(T == Q6_K ? 1024 : 512) gemv1_kernel(const uin
 // A workgroup with more threads than its entry needs retires the surplus
 // waves at once (a retired wave does not hold up the barrier).
 // ---------------------------------------------------------------------------
-enum BodyCode { B_Q4_1, B_Q4_2, B_Q4_4, B_Q4_6, B_Q4_8, B_Q4_12, B_Q5_1, B_Q5_2, B_Q6_1, B_COUNT };
+enum BodyCode { B_Q4_1, B_Q4_2, B_Q4_4, B_Q4_6, B_Q4_8, B_Q4_12, B_Q5_1, B_Q5_2, B_Q6_1, B_Q6_2, B_COUNT };
 // code + B_COUNT: the same body on the PLANAR layout
 
 struct BatchItem {
@@ -419,6 +428,7 @@ __global__ void __launch_bounds__(1024) gemv1_batch_kernel(const BatchArgs a) {
     case B_Q5_1: QK_BODY(Q5_K, 1, 1); break;
     case B_Q5_2: QK_BODY(Q5_K, 2, 2); break;
     case B_Q6_1: QK_BODY(Q6_K, 1, 1); break;
+    case B_Q6_2: QK_BODY(Q6_K, 2, 2); break;
     case B_COUNT + B_Q4_1: QK_BODYP(Q4_K, 1, 1); break;
     case B_COUNT + B_Q4_2: QK_BODYP(Q4_K, 2, 2); break;
     case B_COUNT + B_Q4_4: QK_BODYP(Q4_K, 4, 2); break;
@@ -428,6 +438,7 @@ __global__ void __launch_bounds__(1024) gemv1_batch_kernel(const BatchArgs a) {
     case B_COUNT + B_Q5_1: QK_BODYP(Q5_K, 1, 1); break;
     case B_COUNT + B_Q5_2: QK_BODYP(Q5_K, 2, 2); break;
     case B_COUNT + B_Q6_1: QK_BODYP(Q6_K, 1, 1); break;
+    case B_COUNT + B_Q6_2: QK_BODYP(Q6_K, 2, 2); break;
     default: break;
     }
 #undef QK_BODYP
@@ -580,8 +591,11 @@ static int cu_count() {
 }
 
 // Rows per straight-line round that each type is compiled for.  Q6_K units
-// are the largest (58 B of loads per lane): one unit in flight per lane
-// streams them fastest.  Q5_K units hold 20 dwords: rounds of 3 or 4 rows
+// are the largest (58 B of loads per lane): on GGUF rows one unit in flight
+// per lane streams them fastest (two-row rounds with a ring measured 10-30%
+// slower); PLANAR rows take the same phases in two-row rounds with two units
+// in flight when the launch has at most ring_threads threads (5% faster at
+// 5120 x 17408; see geometry).  Q5_K units hold 20 dwords: rounds of 3 or 4 rows
 // need the 256 VGPRs that the single-launch kernel's 512-thread bound leaves
 // (measured: 5120 x 6144 in one round of 4 beats two rounds of 2 by 5%);
 // the merged-launch kernel (1024-thread bound) runs Q5_K in rounds of 2.
@@ -589,7 +603,9 @@ static int cu_count() {
 template <int T> struct RowRounds;
 template <> struct RowRounds<Q4_K> { static constexpr int n = 6, rl[n] = {1, 2, 4, 6, 8, 12}, max_threads = 512; };
 template <> struct RowRounds<Q5_K> { static constexpr int n = 4, rl[n] = {1, 2, 3, 4}, max_threads = 512; };
-template <> struct RowRounds<Q6_K> { static constexpr int n = 1, rl[n] = {1}, max_threads = 1024; };
+template <> struct RowRounds<Q6_K> { static constexpr int n = 1, rl[n] = {1}, max_threads = 1024, ring_threads = 768; };
+static_assert(RowRounds<Q6_K>::ring_threads == gemv1_bound<Q6_K, 2, 2>(), "gemv1_kernel's bound for Q6_K rings");
+static_assert(RowRounds<Q5_K>::max_threads <= gemv1_bound<Q5_K, 4, 2>(), "gemv1_kernel's bound for Q5_K rounds");
 
 // LDS of one workgroup: ceil(R / P) slot rows per phase, tail phase included
 // (mult = 2: the paired rows of the SwiGLU epilogue).
@@ -655,17 +671,19 @@ static Geo geometry(int64_t N, int64_t K, int cus, int mult = 1) {
             int rl;
             best = std::min(best, plan(p, rl));
         }
-        // the most phases among the fewest slots; Q6_K on PLANAR rows takes
-        // up to 5% more slots for more phases (measured: 3 phases beat 2 at
-        // 5120 x 17408, where GGUF rows prefer 2)
-        const int64_t limit = (T == Q6_K && L == PLANAR) ? best + best / 20 : best;
+        // the most phases among the fewest slots
         g.P = 1;
         g.RL = 1;
         for (int p = 1; p <= pmax; ++p) {
             int rl;
-            if (plan(p, rl) <= limit) { g.P = p; g.RL = rl; }
+            if (plan(p, rl) <= best) { g.P = p; g.RL = rl; }
         }
         g.threads = (g.P * g.useg + 63) / 64 * 64;
+        // Q6_K on PLANAR rows: the same phases in two-row rounds, two units
+        // in flight per lane (the kernel's bound for a ring is ring_threads;
+        // an odd row count re-reads the last row once)
+        if constexpr (T == Q6_K && L == PLANAR)
+            if (g.threads <= RR::ring_threads && (R + g.P - 1) / g.P >= 2) g.RL = 2;
         if (G == N || part_lds(N, g, mult) <= (size_t)LDS_PART) break;  // the partial sums fit in LDS
     }
     return g;
@@ -711,7 +729,7 @@ static hipError_t gemv1_dispatch(const void *W, const void *x, void *y, int64_t 
     constexpr bool NT = L == PLANAR;
     switch (geo.RL) {
     case 1: return launch1<T, L, 1, 1, NT, PAIR>(W, x, y, N, K, geo, ep, st);
-    case 2: if constexpr (T != Q6_K) return launch1<T, L, 2, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 2: if constexpr (T != Q6_K || L == PLANAR) return launch1<T, L, 2, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
     case 3: if constexpr (T == Q5_K) return launch1<T, L, 3, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
     case 4: if constexpr (T != Q6_K) return launch1<T, L, 4, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
     case 6: if constexpr (T == Q4_K) return launch1<T, L, 6, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
@@ -775,7 +793,7 @@ static int body_code_gguf(int type, int rl) {
     // has: two-row rounds instead, the same arithmetic in a different order
     // of loads)
     if (type == Q5_K) return rl == 1 ? B_Q5_1 : (rl >= 2 && rl <= 4) ? B_Q5_2 : -1;
-    if (type == Q6_K) return rl == 1 ? B_Q6_1 : -1;
+    if (type == Q6_K) return rl == 1 ? B_Q6_1 : rl == 2 ? B_Q6_2 : -1;
     return -1;
 }
 

@@ -89,3 +89,56 @@ def test_planar_batch_mixed_layouts():
         assert np.array_equal(yb.view(np.uint32), y1.view(np.uint32))
         y_ref, S = oracle.gemv(qt, W, x, K)
         assert_row_bound(yb, y_ref, S, f"batch type {e[0]:#x}")
+
+
+# Q6_K launches on PLANAR rows with at most 768 threads run two-row rounds
+# with two units in flight.  Odd rows per lane leave the last round half used
+# (3400x17408: 2 phases of 7 rows; 2300x11008: 3 phases of 3; 2600x8192: one
+# phase of 11); 4000x5120 has 8 phases of 2 rows; 5120x17408 is the FFN down
+# projection.  Every row is checked against the oracle and must equal the
+# GGUF launch bit for bit (the summation order depends only on the segment
+# length).
+@pytest.mark.parametrize("N,K", [(3400, 17408), (2300, 11008), (2600, 8192), (4000, 5120), (5120, 17408)])
+def test_planar_q6k_two_row_rounds(N, K):
+    W = synth.superblocks(Q6, N, K, 70 + N)
+    x = synth.activations(K, 1, 70 + N)
+    Wp = _repacked(Q6, W, N, K)
+    yp = binding.gemv(Q6 | P, Wp, dev(x).reshape(-1), N, K).cpu().numpy().reshape(-1)
+    yg = gpu_gemv(Q6, W, x, N, K).reshape(-1)
+    assert np.array_equal(yp.view(np.uint32), yg.view(np.uint32)), "planar != GGUF"
+    y_ref, S = oracle.gemv(Q6, W, x, K)
+    assert_row_bound(yp, y_ref, S, f"Q6_K planar {N}x{K}")
+
+
+def test_planar_q6k_two_row_rounds_merged_and_pair():
+    """The same rounds inside the merged launch (bit-identical to single calls)
+    and in the SwiGLU pair (1700 x 17408: 2 phases of 4 paired rows;
+    bit-identical to GGUF rows and within the oracle's bound)."""
+    ents, host = [], []
+    for qt, N, K, seed in [(Q6, 3400, 17408, 11), (Q6, 48, 5120, 12), (Q4, 1000, 5120, 13)]:
+        W = synth.superblocks(qt, N, K, seed)
+        x = synth.activations(K, 1, seed)
+        ents.append((qt | P, _repacked(qt, W, N, K), dev(x).reshape(-1), N, K))
+        host.append((qt, W, x, N, K))
+    ys = binding.gemv_batch(ents)
+    torch.cuda.synchronize()
+    for (qt, W, x, N, K), e, y in zip(host, ents, ys):
+        y1 = binding.gemv(*e).cpu().numpy().reshape(-1)
+        yb = y.cpu().numpy()
+        assert np.array_equal(yb.view(np.uint32), y1.view(np.uint32)), f"merged != single {N}x{K}"
+        y_ref, S = oracle.gemv(qt, W, x, K)
+        assert_row_bound(yb, y_ref, S, f"merged type {e[0]:#x} {N}x{K}")
+
+    N, K = 1700, 17408
+    Wg, Wu = synth.superblocks(Q6, N, K, 14), synth.superblocks(Q6, N, K, 15)
+    x = synth.activations(K, 1, 14)
+    Wgd, Wud, xd = dev(Wg.reshape(-1)), dev(Wu.reshape(-1)), dev(x).reshape(-1)
+    a = binding.gemv_swiglu(Q6, Wgd, Wud, xd, N, K)
+    b = binding.gemv_swiglu(Q6 | P, binding.repack(Q6, Wgd, N, K), binding.repack(Q6, Wud, N, K), xd, N, K)
+    torch.cuda.synchronize()
+    a, b = a.cpu().numpy().reshape(-1), b.cpu().numpy().reshape(-1)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "planar pair != GGUF pair"
+    y_ref, g, Sg, u, Su = oracle.swiglu(Q6, Wg, Wu, x, K)
+    y_ref = y_ref.reshape(-1)
+    tol = oracle.swiglu_bound(y_ref, g.reshape(-1), Sg.reshape(-1), u.reshape(-1), Su.reshape(-1))
+    assert oracle.within(b, y_ref, tol, False).all(), "Q6_K planar SwiGLU pair outside the oracle's bound"
