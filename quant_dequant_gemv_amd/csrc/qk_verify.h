@@ -61,6 +61,15 @@ __device__ __forceinline__ float vdpp(float a) {
 template <int NCB>
 __host__ __device__ constexpr int v_max_threads() { return NCB == 1 ? 768 : 512; }
 constexpr int V_MAX_RL = 8;  // quads per straight-line round, at most
+// Plain Q4_K launches of two column blocks in rounds of at most V_SHORT_RL
+// quads fit 168 registers without spills, so they may take 12 waves: two
+// row phases at K = 5120 (measured 4-5% faster at 17408 x 5120, 6 and 8
+// columns).  The epilogue and group-loop variants would spill there.
+constexpr int V_SHORT_RL = 3;
+template <int T, int NCB, int RL, bool PAIR, bool EPI, bool WIDE>
+constexpr int v_bound() {
+    return NCB == 2 && T == Q4_K && RL <= V_SHORT_RL && !PAIR && !EPI && !WIDE ? 768 : v_max_threads<NCB>();
+}
 constexpr int V_RAW_BUDGET = 96 * 1024;  // LDS for the x planes of one segment
 constexpr int V_LDS_MAX = 160 * 1024;
 
@@ -183,7 +192,7 @@ __device__ __forceinline__ float quad_bcast(float a) { return vdpp<J | (J << 2) 
 // nct columns are taken in ngrp groups of at most 4 * NCB (WIDE; otherwise
 // ngrp is 1 and the group loop compiles away).
 template <int T, int NCB, int RL, int D, bool PAIR, bool EPI, bool WIDE>
-__global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint8_t *__restrict__ W,
+__global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) verify_kernel(const uint8_t *__restrict__ W,
                                                                const uint16_t *__restrict__ x, void *y,
                                                                int N, int K, int nct, int ngrp, int useg, int P,
                                                                const Epilogue ep) {
@@ -300,38 +309,41 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
             for (int p = 0; p < RL; ++p) {
                 const Unit<T> &Un = buf[p % DD];
                 float val[NC];
-                // one column block at a time: its accumulators only (the quant
-                // patterns are recomputed per block, cheaper than the registers)
+                // each quant word's patterns once, multiplied into every
+                // column block's accumulators
                 if constexpr (T == Q6_K) {
                     const float d = f16_lo(Un.d);
                     float f[4];
 #pragma unroll
                     for (int t = 0; t < 4; ++t) f[t] = d * (float)Un.scale(t, q);
+                    float4_t Dq[NCB][4];
 #pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb) {
-                        float4_t Dq[4];
+                    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) Dq[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+                        for (int t = 0; t < 4; ++t) Dq[cb][t] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            uint32_t pt[8];
-                            Un.patterns(i, q, pt);
+                    for (int i = 0; i < 4; ++i) {
+                        uint32_t pt[8];
+                        Un.patterns(i, q, pt);
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
                             for (int t = 0; t < 4; ++t)
-                                Dq[t] = mfma4(xr[cb][8 * t + 2 * i], xr[cb][8 * t + 2 * i + 1], pt[2 * t], pt[2 * t + 1],
-                                              Dq[t]);
-                        }
+                                Dq[cb][t] = mfma4(xr[cb][8 * t + 2 * i], xr[cb][8 * t + 2 * i + 1], pt[2 * t],
+                                                  pt[2 * t + 1], Dq[cb][t]);
+                    }
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             float a = 0.f;
 #pragma unroll
                             for (int t = 0; t < 4; ++t)  // patterns hold q*2^-24 (t < 2) or 16q*2^-24
                                 a = __builtin_fmaf(f[t],
-                                                   Dq[t][i] * (t < 2 ? 0x1p24f : 0x1p20f) - 32.f * xsum[4 * cb + i][t],
+                                                   Dq[cb][t][i] * (t < 2 ? 0x1p24f : 0x1p20f) - 32.f * xsum[4 * cb + i][t],
                                                    a);
                             val[4 * cb + i] = a;
                         }
-                    }
                 } else {
                     // units of 2^-48, as in the one-column kernel: sc and m read as fp16
                     // patterns are sc*2^-24 and m*2^-24; the x sums are held times 2^-24
@@ -344,22 +356,26 @@ __global__ void __launch_bounds__(v_max_threads<NCB>()) verify_kernel(const uint
                     const float fh = __builtin_fmaf(d, pat(sk.sc_hi), 0.f) * 0x1p-4f;
                     const float ml = __builtin_fmaf(dmin, pat(sk.m_lo), 0.f);
                     const float mh = __builtin_fmaf(dmin, pat(sk.m_hi), 0.f);
+                    float4_t Dl[NCB], Dh[NCB];
 #pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb) {
-                        float4_t Dl = float4_t{0.f, 0.f, 0.f, 0.f}, Dh = Dl;
+                    for (int cb = 0; cb < NCB; ++cb) Dl[cb] = Dh[cb] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            uint32_t pt[4];
-                            Un.patterns(i, q, pt);
-                            Dl = mfma4(xr[cb][2 * i], xr[cb][2 * i + 1], pt[0], pt[1], Dl);
-                            Dh = mfma4(xr[cb][16 + 2 * i], xr[cb][17 + 2 * i], pt[2], pt[3], Dh);
+                    for (int i = 0; i < 8; ++i) {
+                        uint32_t pt[4];
+                        Un.patterns(i, q, pt);
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb) {
+                            Dl[cb] = mfma4(xr[cb][2 * i], xr[cb][2 * i + 1], pt[0], pt[1], Dl[cb]);
+                            Dh[cb] = mfma4(xr[cb][16 + 2 * i], xr[cb][17 + 2 * i], pt[2], pt[3], Dh[cb]);
                         }
+                    }
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const float mn = __builtin_fmaf(ml, xsum[4 * cb + i][0], mh * xsum[4 * cb + i][1]);
-                            val[4 * cb + i] = __builtin_fmaf(fl, Dl[i], __builtin_fmaf(fh, Dh[i], -mn));
+                            val[4 * cb + i] = __builtin_fmaf(fl, Dl[cb][i], __builtin_fmaf(fh, Dh[cb][i], -mn));
                         }
-                    }
                 }
                 if (p + DD < RL) load_quad(buf[p % DD], p + DD);
                 // fold the 4 blocks of each 16-lane row (same row j, consecutive units)
@@ -472,16 +488,20 @@ static int cus_v() {
 }
 
 // mult = 2: each workgroup streams its rows of two tensors (SwiGLU).
-static bool vgeo(int64_t N, int64_t K, int nc, int ncb, int mult, VGeo &g) {
+// short_threads: the largest workgroup for rounds of at most V_SHORT_RL
+// quads (at least the general limit).
+static bool vgeo(int64_t N, int64_t K, int nc, int ncb, int mult, int short_threads, VGeo &g) {
     const int64_t U = K / 64;
     const int64_t xs = (int64_t)VXSTRIDE * nc;  // plane bytes per unit column
-    const int max_waves = (ncb == 1 ? v_max_threads<1>() : v_max_threads<2>()) / 64;
+    const int long_threads = ncb == 1 ? v_max_threads<1>() : v_max_threads<2>();
+    short_threads = std::max(short_threads, long_threads);
+    const int max_waves = long_threads / 64;
     const int cap = (int)std::min<int64_t>(16 * max_waves, V_RAW_BUDGET / xs) / 16 * 16;
     if (cap < 16) return false;
     const int64_t nseg = (U + cap - 1) / cap;
     g.useg = (int)(((U + nseg - 1) / nseg + 15) / 16 * 16);
     const int wpp = g.useg / 16;
-    const int pmax = std::max(1, ((ncb == 1 ? v_max_threads<1>() : v_max_threads<2>()) / 64) / wpp);
+    const int pmax = std::max(1, (short_threads / 64) / wpp);
     // one workgroup per CU, also for a pair of tensors (each workgroup stages
     // x for its columns once: more workgroups would stage it more often;
     // measured slower for the pair at ncols = 4)
@@ -497,8 +517,10 @@ static bool vgeo(int64_t N, int64_t K, int nc, int ncb, int mult, VGeo &g) {
         const int min_waves = std::min(4, pmax * wpp);
         int64_t best[4] = {INT64_MAX, INT64_MAX, INT64_MAX, INT64_MAX};
         for (int p = 1; p <= pmax; ++p) {
+            // above the general limit only short rounds fit the registers
+            const int maxrl = p * wpp * 64 <= long_threads ? V_MAX_RL : V_SHORT_RL;
             const int64_t ql = (Q + p - 1) / p;
-            const int64_t rounds = (ql + V_MAX_RL - 1) / V_MAX_RL;
+            const int64_t rounds = (ql + maxrl - 1) / maxrl;
             const int rl = (int)((ql + rounds - 1) / rounds);
             const int64_t lane = rounds * rl;
             const int64_t key[4] = {p * wpp < min_waves ? 1 : 0, rounds, p * lane, lane};
@@ -527,6 +549,7 @@ template <int T, int NCB, int RL, bool PAIR, bool EPI, bool WIDE>
 static hipError_t launch_ve(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, const VGeo &g,
                             const Epilogue &ep, hipStream_t st) {
     constexpr int D = 2;
+    if (g.threads > v_bound<T, NCB, RL, PAIR, EPI, WIDE>()) return hipErrorInvalidValue;
     const hipError_t e = v_allow_lds<verify_kernel<T, NCB, RL, D, PAIR, EPI, WIDE>>();
     if (e != hipSuccess) return e;
     const int ngrp = (nc + 7) / 8;
@@ -560,7 +583,10 @@ template <int T, int NCB, bool PAIR>
 static hipError_t verify_dispatch(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
                                   const Epilogue &ep, hipStream_t st) {
     VGeo g;
-    if (!vgeo(N, K, widest_group(nc), NCB, PAIR ? 2 : 1, g)) return hipErrorInvalidValue;
+    // plain launches of up to 8 columns may take the larger workgroups of short rounds
+    const bool plain = !PAIR && !ep.res && !ep.f16 && nc <= 8;
+    const int short_threads = plain ? v_bound<T, NCB, 1, false, false, false>() : v_max_threads<NCB>();
+    if (!vgeo(N, K, widest_group(nc), NCB, PAIR ? 2 : 1, short_threads, g)) return hipErrorInvalidValue;
     switch (g.RL) {
     case 1: return launch_v<T, NCB, 1, PAIR>(W, x, y, N, K, nc, g, ep, st);
     case 2: return launch_v<T, NCB, 2, PAIR>(W, x, y, N, K, nc, g, ep, st);

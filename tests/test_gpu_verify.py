@@ -86,11 +86,14 @@ def test_verify_mixed_shapes_sampled(case):
 
 # Row counts at which each workgroup's quads (4 rows) per lane take straight-
 # line rounds of every length 1..8 (the launch picks the length from the rows
-# per workgroup and the phases), for one and two column blocks.
+# per workgroup and the phases), for one and two column blocks.  Plain Q4_K
+# launches of two blocks also take workgroups above 512 threads in rounds of
+# 1..3 quads (8254, 16395, 25608 x 256 and the FFN shape at 6 columns).
 ROUND_CASES = [(1, 256, 2), (12328, 256, 2), (14365, 256, 2), (27654, 256, 2), (24647, 256, 2),
                (10291, 5120, 2), (6217, 5120, 2), (14365, 5120, 2),
                (8254, 256, 8), (14365, 256, 8), (18439, 256, 8), (24647, 256, 8), (35899, 256, 8),
-               (6217, 5120, 8), (7187, 5120, 8)]
+               (6217, 5120, 8), (7187, 5120, 8), (27680, 256, 8), (16395, 256, 8), (25608, 256, 8),
+               (17408, 5120, 6)]
 
 
 @pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
