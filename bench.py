@@ -69,6 +69,11 @@ def make_tensors(torch, entries, seed_offset=0):
     return out
 
 
+def progress(msg):
+    """One line per finished section on stderr (the JSON line stays alone on stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def make_planar(torch, entries):
     """The same tensors repacked once into PLANAR rows (qk_repack, outside any
     timed region); bytes stay the GGUF weight bytes, the algorithmic count."""
@@ -613,6 +618,7 @@ def main():
     # dominant kernel: every launch of the timed region is the Q4_K one-column GEMV
     achieved = (step_alg / per_step) / (span / launches) / 1e9
     del timed, warm
+    progress(f"timed steps: {value:.1f} GB/s")
 
     for t in tensors:
         t["W"] = t["W"][:1]
@@ -621,6 +627,7 @@ def main():
     shapes = per_shape(torch, launcher, tensors)
     del tensors
     torch.cuda.empty_cache()
+    progress("read ceiling and per-shape figures")
 
     mixed = make_tensors(torch, synth.MIXED)
     mixed_out = per_shape(torch, launcher, mixed)
@@ -634,6 +641,7 @@ def main():
         r["layout"] = "PLANAR"
     del planar
     torch.cuda.empty_cache()
+    progress("mixed types and PLANAR rows")
 
     # few-column verify: Q4_K 17408 x 5120, weights read once per call
     v = synth.VERIFY
@@ -659,10 +667,14 @@ def main():
         del vt
         torch.cuda.empty_cache()
 
+    progress("verify")
     fused_out = fused_epilogues(torch)
+    progress("fused epilogues")
 
     stream_out = None if args.no_stream else run_stream(torch, launcher)
+    progress("decode stream")
     cpu = None if args.no_cpu else cpu_baseline(entries)
+    progress("cpu baseline")
 
     out = {
         "metric": METRIC,

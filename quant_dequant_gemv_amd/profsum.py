@@ -137,11 +137,18 @@ def main():
     ap.add_argument("out")
     ap.add_argument("--command", required=True)
     ap.add_argument("--plain", help="bench.py JSON of an unprofiled run on the same GPU")
-    ap.add_argument("--title", default="gemv1_kernel (one column): Q4_K projection step, rocprofv3 kernel trace")
+    ap.add_argument("--title", help="heading (default: by the kind of trace)")
     ap.add_argument("--stream", action="store_true", help="the trace is of bench.py --stream-only")
     a = ap.parse_args()
     body = (summarise_stream if a.stream else summarise)(a.trace, a.bench_json, a.command, a.plain)
-    text = f"# {a.title}\n\n" + body
+    title = a.title
+    if title is None and a.stream:
+        with open(a.bench_json) as f:
+            variant = json.loads(f.read().strip().splitlines()[-1])["variant"]
+        title = f"Decode stream, one token of the 64-layer weight stream ({variant}): rocprofv3 kernel trace"
+    elif title is None:
+        title = "gemv1_kernel (one column): Q4_K projection step, rocprofv3 kernel trace"
+    text = f"# {title}\n\n" + body
     with open(a.out, "w") as f:
         f.write(text)
     print(text)
