@@ -207,6 +207,11 @@ typedef struct qk_gemv_item {
  *   count  1..QK_MAX_BATCH
  *   stream hipStream_t to enqueue on
  *
+ * Adjacent entries of the same type and K that read the same x (the same
+ * pointer) are streamed with the geometry of one launch of all their rows,
+ * each entry taking its share of the workgroups (performance only: results
+ * are as below).
+ *
  * Entries may share W and x.  No entry's y may overlap any entry's W, x or y.
  * Every y_i is bit-identical to what qk_gemv(type_i, W_i, x_i, y_i, N_i, K_i,
  * 1, stream) writes; the accuracy bound is that of qk_gemv.  Every entry is

@@ -82,3 +82,58 @@ def test_large_partial_sum_lds():
 def test_batch_single_phase_entries():
     # entries whose launch has one row phase and several rows per workgroup
     _check([(Q4, 1000, 17408, 21, "a"), (Q5, 600, 17408, 22, "a"), (Q6, 300, 5120, 23, "b")])
+
+
+# Adjacent entries of one type and K that read the same x are stacked into one
+# row range (up to four tensors per stack) with the geometry of a single launch
+# of all their rows; every output must still equal its single call bit for bit.
+def test_batch_stacked_attention_qkv():
+    # an attention layer's q, k and v (Q4_K 12288 / 1024 / 1024 x 5120), one x
+    _check([(Q4, 12288, 5120, 1010, "h"), (Q4, 1024, 5120, 1011, "h"), (Q4, 1024, 5120, 1012, "h")], sample=256)
+
+
+def test_batch_stacked_runs_all_rows():
+    # six Q4_K tensors on one x: a stack of four, then one of two (every row);
+    # then Q5_K and Q6_K runs on another x, a repeated tensor, and a Q4_K entry
+    # after a type change (not stacked with the first run)
+    _check([(Q4, 300, 5120, 40, "a"), (Q4, 7, 5120, 41, "a"), (Q4, 1, 5120, 42, "a"), (Q4, 129, 5120, 43, "a"),
+            (Q4, 64, 5120, 44, "a"), (Q4, 500, 5120, 45, "a"),
+            (Q5, 250, 6144, 46, "b"), (Q5, 33, 6144, 47, "b"), (Q6, 48, 6144, 48, "b"), (Q6, 48, 6144, 48, "b"),
+            (Q4, 90, 5120, 49, "a")])
+
+
+def test_batch_same_x_pointer_other_k_not_stacked():
+    # one x buffer read with K = 5120 and, by the next entry, with K = 2560
+    # (its first half): equal type and x pointer but another K -- no stack
+    W1 = synth.superblocks(Q4, 400, 5120, 50)
+    W2 = synth.superblocks(Q4, 300, 2560, 51)
+    x = synth.activations(5120, 1, 50)
+    xd = dev(x).reshape(-1)
+    entries = [(Q4, dev(W1.reshape(-1)), xd, 400, 5120), (Q4, dev(W2.reshape(-1)), xd, 300, 2560)]
+    ys = binding.gemv_batch(entries)
+    torch.cuda.synchronize()
+    for e, y, W, K in zip(entries, ys, (W1, W2), (5120, 2560)):
+        yb = y.cpu().numpy()
+        assert np.array_equal(yb.view(np.uint32), _single(e).view(np.uint32))
+        y_ref, S = oracle.gemv(Q4, W, np.ascontiguousarray(x[:K]), K)
+        assert_row_bound(yb, y_ref, S, f"K={K}")
+
+
+def test_batch_stacked_planar():
+    # PLANAR rows stack like GGUF rows: q/k/v-like Q4_K and a Q6_K pair, one x
+    P = binding.PLANAR
+    x = synth.activations(5120, 1, 60)
+    xd = dev(x).reshape(-1)
+    host, entries = [], []
+    for qt, N, seed in [(Q4, 2000, 61), (Q4, 130, 62), (Q4, 130, 63), (Q6, 48, 64), (Q6, 48, 65)]:
+        W = synth.superblocks(qt, N, 5120, seed)
+        Wp = binding.repack(qt, dev(W.reshape(-1)), N, 5120)
+        host.append((qt, W, N))
+        entries.append((qt | P, Wp, xd, N, 5120))
+    ys = binding.gemv_batch(entries)
+    torch.cuda.synchronize()
+    for (qt, W, N), e, y in zip(host, entries, ys):
+        yb = y.cpu().numpy()
+        assert np.array_equal(yb.view(np.uint32), _single(e).view(np.uint32)), f"planar type {qt} {N} rows"
+        y_ref, S = oracle.gemv(qt, W, x, 5120)
+        assert_row_bound(yb, y_ref, S, f"planar type {qt} {N} rows")
