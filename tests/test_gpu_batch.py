@@ -79,6 +79,12 @@ def test_large_partial_sum_lds():
     _check([(Q4, 8500, 32768, 30, "a"), (Q6, 64, 512, 31, "b")], sample=128)
 
 
+def test_batch_several_k_segments():
+    # K = 65792: segments of 512, 512 and 4 units; a run sharing x and one entry on its own
+    _check([(Q4, 300, 65792, 32, "a"), (Q4, 45, 65792, 33, "a"), (Q6, 64, 65792, 34, "b"),
+            (Q5, 100, 33024, 35, "c")])
+
+
 def test_batch_single_phase_entries():
     # entries whose launch has one row phase and several rows per workgroup
     _check([(Q4, 1000, 17408, 21, "a"), (Q5, 600, 17408, 22, "a"), (Q6, 300, 5120, 23, "b")])

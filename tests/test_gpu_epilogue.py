@@ -17,7 +17,8 @@ Q4, Q5, Q6 = synth.Q4_K, synth.Q5_K, synth.Q6_K
 TYPES = [Q4, Q5, Q6]
 NAMES = {Q4: "Q4_K", Q5: "Q5_K", Q6: "Q6_K"}
 # ragged rows, a partial 16-unit step, a long K (several x segments)
-SHAPES = [(1, 256), (37, 1280), (130, 5120), (300, 6144), (61, 17408)]
+# (29 x 33024: two K segments of the one-column kernel, the second of 4 units)
+SHAPES = [(1, 256), (37, 1280), (130, 5120), (300, 6144), (61, 17408), (29, 33024)]
 
 
 def _assert_within(y, y_ref, tol, what, f16=False):

@@ -23,8 +23,11 @@ TYPES = [Q4, Q5, Q6]
 NAMES = {Q4: "Q4_K", Q5: "Q5_K", Q6: "Q6_K"}
 
 # (N, K): tiny, ragged row counts, several superblocks, the real K values, and
-# a K beyond one staged x tile (28928 weights) so the tile loop runs twice.
-SMALL_SHAPES = [(1, 256), (47, 512), (48, 5120), (1023, 768), (129, 6144), (96, 17408), (40, 29184)]
+# K beyond one segment of the one-column kernel (512 units = 32768 weights):
+# 33024 runs segments of 512 and 4 units, 65792 of 512, 512 and 4 (the short
+# last segment leaves most lanes without a unit).
+SMALL_SHAPES = [(1, 256), (47, 512), (48, 5120), (1023, 768), (129, 6144), (96, 17408), (40, 29184),
+                (37, 33024), (20, 65792)]
 
 
 def _case(qt, N, K, seed):

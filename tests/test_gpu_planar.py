@@ -18,7 +18,8 @@ TYPES = [Q4, Q5, Q6]
 NAMES = {Q4: "Q4_K", Q5: "Q5_K", Q6: "Q6_K"}
 P = binding.PLANAR
 # K = 2048 (8 superblocks: Q6_K rows need no pad), 1280 and 17408 (Q6_K rows padded)
-SHAPES = [(1, 256), (5, 1280), (47, 2048), (130, 5120), (37, 17408), (3000, 5120)]
+# (37 x 33024: two K segments of the one-column kernel, the second of 4 units)
+SHAPES = [(1, 256), (5, 1280), (47, 2048), (130, 5120), (37, 17408), (3000, 5120), (37, 33024)]
 
 
 def _repacked(qt, W, N, K):
