@@ -1,4 +1,4 @@
-"""HBM traffic of the one-column GEMV from rocprofv3 counters.
+"""HBM traffic of the GEMV kernels from rocprofv3 counters.
 
 Two steps, each a separate rocprofv3 counter pass (FETCH_SIZE, then WRITE_SIZE),
 run from the repository root on the GPU:
@@ -8,13 +8,17 @@ run from the repository root on the GPU:
     python3 -m quant_dequant_gemv_amd.traffic parse gpurun_out/traffic_fetch/run_results.db \\
         gpurun_out/traffic_write/run_results.db
 
-`run` launches each of the three Q4_K projection shapes (N = 10240, 12288,
-17408; K = 5120) a few times on distinct weight copies, directly (one dispatch
-per launch), and a plain device-to-device copy of 512 MiB as the calibration:
-its counters are scaled to the known 512 MiB read and 512 MiB written, and the
-same factors are applied to the GEMV's counters.  `parse` writes
-profiles/traffic.json (per-launch HBM bytes of the kernel, with the hash of
-the kernel sources it was measured on) that bench.py reports as
+`run` launches, a few times each on distinct weight copies and directly (one
+dispatch per launch), the groups of plan(): the three Q4_K projection shapes
+(N = 10240, 12288, 17408; K = 5120) -- the benchmark's step --, the Q4_K
+17408 x 5120 verify form at 2, 4 and 8 columns, and the one-column Q6_K and
+Q5_K shapes; then a plain device-to-device copy of 512 MiB as the
+calibration: its counters are scaled to the known 512 MiB read and 512 MiB
+written, and the same factors are applied to the GEMV's counters.  `parse`
+maps the dispatches back to plan() by their order and writes
+profiles/traffic.json (per-launch HBM bytes of each group against its
+algorithmic bytes, with the hash of the kernel sources it was measured on)
+and the markdown summary beside it; bench.py reports the step's figure as
 roofline.traffic while the sources are unchanged.
 """
 from __future__ import annotations
@@ -28,7 +32,12 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 COPY_BYTES = 512 * 1024 * 1024
 OUT = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["quant_dequant_gemv_amd/csrc/qk_kernels.hip", "quant_dequant_gemv_amd/csrc/qk_format.h",
+MD = os.path.join(ROOT, "profiles", "traffic_gemv1_verify_workload_shapes.md")
+COMMANDS = """    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/traffic_fetch -o run -- python3 -m quant_dequant_gemv_amd.traffic run
+    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/traffic_write -o run -- python3 -m quant_dequant_gemv_amd.traffic run
+    python3 -m quant_dequant_gemv_amd.traffic parse gpurun_out/traffic_fetch/run_results.db gpurun_out/traffic_write/run_results.db"""
+KERNEL_SOURCES = ["quant_dequant_gemv_amd/csrc/qk_kernels.hip", "quant_dequant_gemv_amd/csrc/qk_verify.h",
+                  "quant_dequant_gemv_amd/csrc/qk_format.h",
                   "quant_dequant_gemv_amd/csrc/qk_epilogue.h"]
 
 
@@ -40,23 +49,41 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def run(reps: int = 4) -> None:
+REPS = 4
+STEP = "gemv1_kernel<Q4_K>"  # the key bench.py reads
+
+
+def plan():
+    """[(label, [(qtype, N, K, seed, ncols), ...])]: the launch groups, in order."""
+    from quant_dequant_gemv_amd import synth
+    v = synth.VERIFY
+    groups = [(STEP, [(e["qtype"], e["N"], e["K"], e["seed"], 1) for e in synth.Q4K_PROJECTIONS])]
+    for nc in (2, 4, 8):
+        groups.append((f"verify_kernel<Q4_K> {v['N']}x{v['K']} ncols {nc}", [(v["qtype"], v["N"], v["K"], v["seed"], nc)]))
+    for e in synth.MIXED:
+        groups.append((f"gemv1_kernel<{synth.TYPE_NAMES[e['qtype']]}> {e['N']}x{e['K']}",
+                       [(e["qtype"], e["N"], e["K"], e["seed"], 1)]))
+    return groups
+
+
+def run(reps: int = REPS) -> None:
     import torch
 
     from quant_dequant_gemv_amd import binding, synth
     lib = binding.load_library()
     stream = torch.cuda.current_stream().cuda_stream
-    for e in synth.Q4K_PROJECTIONS:
-        W = synth.superblocks(e["qtype"], e["N"], e["K"], e["seed"])
-        Ws = [torch.from_numpy(W.reshape(-1)).cuda() for _ in range(reps)]
-        x = torch.from_numpy(synth.activations(e["K"], 1, e["seed"])).cuda()
-        y = torch.empty(e["N"], dtype=torch.float32, device="cuda")
-        for Wd in Ws:
-            rc = lib.qk_gemv(e["qtype"], Wd.data_ptr(), x.data_ptr(), y.data_ptr(), e["N"], e["K"], 1, stream)
-            if rc:
-                raise binding.QKError(rc, "qk_gemv")
-            torch.cuda.synchronize()
-        del Ws
+    for _, launches in plan():
+        for qt, N, K, seed, nc in launches:
+            W = synth.superblocks(qt, N, K, seed)
+            Ws = [torch.from_numpy(W.reshape(-1)).cuda() for _ in range(reps)]
+            x = torch.from_numpy(synth.activations(K, nc, seed)).cuda()
+            y = torch.empty(N * nc, dtype=torch.float32, device="cuda")
+            for Wd in Ws:
+                rc = lib.qk_gemv(qt, Wd.data_ptr(), x.data_ptr(), y.data_ptr(), N, K, nc, stream)
+                if rc:
+                    raise binding.QKError(rc, "qk_gemv")
+                torch.cuda.synchronize()
+            del Ws
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     for _ in range(reps):
@@ -66,43 +93,83 @@ def run(reps: int = 4) -> None:
 
 
 def _per_dispatch(db: str, counter: str):
+    """[(dispatch_id, name, value)] of one counter, in dispatch order."""
     con = sqlite3.connect(db)
     rows = con.execute("select name, dispatch_id, counter_name, counter_value from pmc_events").fetchall()
     agg = {}
     for name, did, cn, v in rows:
         if cn != counter:
             continue
-        agg.setdefault((name, did), 0.0)
-        agg[(name, did)] += v
-    return agg
+        agg.setdefault((did, name), 0.0)
+        agg[(did, name)] += v
+    return [(did, name, v) for (did, name), v in sorted(agg.items())]
 
 
-def parse(fetch_db: str, write_db: str) -> dict:
+def _alg_bytes(qt, N, K, nc):
     from quant_dequant_gemv_amd import synth
+    return N * synth.row_bytes(qt, K) + 2 * K * nc + 4 * N * nc
+
+
+def parse(fetch_db: str, write_db: str, reps: int = REPS, out_path: str = OUT) -> dict:
+    groups = plan()
     res = {}
     for label, db, counter in (("fetch", fetch_db, "FETCH_SIZE"), ("write", write_db, "WRITE_SIZE")):
         d = _per_dispatch(db, counter)
-        gemv = [v for (n, _), v in d.items() if "gemv1_kernel<12" in n]
-        copy = [v for (n, _), v in d.items() if "copy" in n.lower() and v > 0]
-        if not gemv or not copy:
-            raise RuntimeError(f"{counter}: missing dispatches (gemv {len(gemv)}, copy {len(copy)})")
-        gemv_kib = sum(gemv) / len(gemv)  # mean over the three shapes, like achieved
-        copy_kib = max(copy)  # the 512 MiB copy is the largest copy dispatch
-        factor = COPY_BYTES / (copy_kib * 1024.0)
-        res[label] = {"counter": counter, "gemv_kib_mean": gemv_kib, "copy_kib": copy_kib,
-                      "scale": factor, "gemv_bytes": gemv_kib * 1024.0 * factor}
-    step = synth.Q4K_PROJECTIONS
-    alg = sum(e["N"] * synth.row_bytes(e["qtype"], e["K"]) + 2 * e["K"] + 4 * e["N"] for e in step) / len(step)
-    per_launch = res["fetch"]["gemv_bytes"] + res["write"]["gemv_bytes"]
-    out = {"kernel_hash": kernel_hash(), "kernel": "gemv1_kernel<Q4_K>",
-           "per_launch_bytes": {"gemv1_kernel<Q4_K>": round(per_launch)},
-           "algorithmic_bytes_per_launch": round(alg),
-           "ratio_to_algorithmic": round(per_launch / alg, 4),
+        ours = [v for _, n, v in d if "qk::" in n]
+        copy = [v for _, n, v in d if "copy" in n.lower() and v > 0]
+        want = reps * sum(len(launches) for _, launches in groups)
+        if len(ours) != want or not copy:
+            raise RuntimeError(f"{counter}: {len(ours)} GEMV dispatches (expected {want}), {len(copy)} copies")
+        factor = COPY_BYTES / (max(copy) * 1024.0)  # the 512 MiB copy is the largest copy dispatch
+        per_group, i = {}, 0
+        for name, launches in groups:
+            n = reps * len(launches)
+            kib = sum(ours[i:i + n]) / n  # mean over the group's launches
+            per_group[name] = {"kib_mean": kib, "bytes": kib * 1024.0 * factor}
+            i += n
+        res[label] = {"counter": counter, "copy_kib": max(copy), "scale": factor, "groups": per_group}
+    per_launch, alg, ratio = {}, {}, {}
+    for name, launches in groups:
+        per_launch[name] = round(res["fetch"]["groups"][name]["bytes"] + res["write"]["groups"][name]["bytes"])
+        alg[name] = round(sum(_alg_bytes(*l[:3], l[4]) for l in launches) / len(launches))
+        ratio[name] = round(per_launch[name] / alg[name], 4)
+    out = {"kernel_hash": kernel_hash(), "kernel": STEP,
+           "per_launch_bytes": per_launch,
+           "algorithmic_bytes_per_launch": alg[STEP],
+           "ratio_to_algorithmic": ratio[STEP],
+           "algorithmic_bytes": alg,
+           "ratios": ratio,
            "counters": res,
-           "note": "mean over the step's three shapes' launches; scaled by a 512 MiB device copy"}
-    with open(OUT, "w") as f:
+           "note": "means over each group's launches (the step: its three shapes); counters scaled by a "
+                   "512 MiB device copy"}
+    with open(out_path, "w") as f:
         json.dump(out, f, indent=1)
     return out
+
+
+def markdown(out: dict, reps: int = REPS) -> str:
+    """The summary kept with the profiles."""
+    f, w = out["counters"]["fetch"], out["counters"]["write"]
+    lines = ["# HBM traffic of the GEMV kernels at the workload shapes: rocprofv3 counters", "",
+             "Commands (run from the repository root on one MI355X; one counter per pass):", "", COMMANDS, "",
+             f"`traffic run` launches each group below {reps} times on distinct weight copies (one dispatch per "
+             "launch), then a 512 MiB device-to-device copy.", "",
+             "Calibration by the copy (known 512 MiB read, 512 MiB written):", "",
+             "| counter | copy reads as | scale |", "|---|---|---|",
+             f"| FETCH_SIZE | {f['copy_kib']:.1f} KiB | {f['scale']:.4f} |",
+             f"| WRITE_SIZE | {w['copy_kib']:.1f} KiB | {w['scale']:.4f} |", "",
+             "Per launch (mean over the group's dispatches; the step: its three Q4_K shapes 10240 / 12288 / "
+             "17408 x 5120):", "",
+             "| group | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes | algorithmic bytes (W + x + y) | ratio |",
+             "|---|---|---|---|---|---|"]
+    for name in out["per_launch_bytes"]:
+        lines.append(f"| `{name}` | {f['groups'][name]['kib_mean']:.1f} | {w['groups'][name]['kib_mean']:.1f} | "
+                     f"{out['per_launch_bytes'][name]} | {out['algorithmic_bytes'][name]} | {out['ratios'][name]:.4f} |")
+    lines += ["", "A ratio near 1 means every weight byte is fetched from HBM once per launch (the verify form "
+              "included: W is read once for all its columns).  Kernel source hash " + out["kernel_hash"] +
+              " (bench.py reports `roofline.traffic` from profiles/traffic.json only while the sources hash the "
+              "same).", ""]
+    return "\n".join(lines)
 
 
 if __name__ == "__main__":
@@ -111,7 +178,10 @@ if __name__ == "__main__":
         run()
     elif len(sys.argv) == 4 and sys.argv[1] == "parse":
         sys.path.insert(0, ROOT)
-        print(json.dumps(parse(sys.argv[2], sys.argv[3]), indent=1))
+        res = parse(sys.argv[2], sys.argv[3])
+        with open(MD, "w") as fh:
+            fh.write(markdown(res))
+        print(json.dumps(res, indent=1))
     else:
         print(__doc__)
         sys.exit(2)
