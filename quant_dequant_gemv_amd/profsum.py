@@ -124,7 +124,7 @@ def summarise_stream(trace: str, stream_json: str, command: str, plain_json: str
     if plain_json:
         pl = _bench(plain_json)
         lines.append(f"- the same variant without the profiler, just before on the same GPU: {pl['token_ms']:.4f} ms "
-                     f"per token ({pl['tok_s']:.1f} tok/s; kernels busy {kern_ms / pl['token_ms']:.1%} of it)")
+                     f"per token ({pl['tok_s']:.1f} tok/s; the traced kernel durations sum to {kern_ms / pl['token_ms']:.1%} of it)")
     if "device" in st:
         lines.append(f"- device: {st['device']}")
     return "\n".join(lines) + "\n"
