@@ -230,7 +230,6 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
                                            void *y, int N, int K, int useg, int P, int blk, int nblk,
                                            int nthr, const Epilogue &ep) {
     extern __shared__ __attribute__((aligned(16))) float part[];  // partial sums, slot rows of useg floats
-    constexpr int BB = Fmt<T>::bytes;
     constexpr int DD = D < RL ? D : RL;  // units in flight
     const int tid = (int)threadIdx.x;
     const int r0 = (int)((int64_t)blk * N / nblk);
