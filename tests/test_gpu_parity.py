@@ -163,3 +163,21 @@ def test_gemv_single_phase_several_rows(qt, N, K):
     y = gpu_gemv(qt, W, x, N, K)
     y_ref, S = oracle.gemv(qt, W, x, K)
     assert_row_bound(y, y_ref, S, f"{NAMES[qt]} {N}x{K}")
+
+
+# Large extents, sampled rows (both ends and every workgroup boundary region):
+# a million rows of K = 256 (the launch grows its workgroup count until the
+# partial sums fit LDS), 2^18 rows of K = 512, and K = 2^20 (32 segments of
+# the one-column kernel; some 200 of the verify kernel at 8 columns).
+@pytest.mark.parametrize("qt,N,K,ncols", [(Q4, 1 << 20, 256, 1), (Q6, 1 << 18, 512, 1), (Q5, 16, 1 << 20, 1),
+                                          (Q4, 16, 1 << 20, 8), (Q6, 24, 1 << 20, 3)],
+                         ids=lambda v: NAMES.get(v, str(v)))
+def test_gemv_large_extents_sampled(qt, N, K, ncols):
+    W = synth.superblocks(qt, N, K, 1200 + ncols)
+    x = synth.activations(K, ncols, 1200 + ncols)
+    y = gpu_gemv(qt, W, x, N, K)
+    rng = np.random.default_rng(N + K)
+    rows = np.unique(np.concatenate([[0, 1, N - 2, N - 1], rng.integers(0, N, 256)]))
+    y_ref, S = oracle.gemv(qt, W[rows], x, K)
+    assert_row_bound(y.reshape(N, ncols)[rows], y_ref, S, f"{NAMES[qt]} {N}x{K} ncols={ncols}")
+    assert np.isfinite(y).all()
