@@ -27,9 +27,11 @@
  *   y  fp32, row-major [N][ncols]
  *
  * Ownership.  Every pointer is owned by the caller; the library keeps no
- * state, allocates nothing and never synchronises.  `stream` is a hipStream_t
- * (NULL = the null stream); every call only enqueues work on it and returns.
- * Calls are thread-safe.  Results are deterministic: the same inputs give the
+ * device state, allocates nothing and never synchronises.  `stream` is a
+ * hipStream_t (NULL = the null stream); every call only enqueues work on it
+ * and returns.  The host side caches, per device, the compute-unit count and
+ * each kernel's opt-in to large LDS, filled on first use of that device.
+ * Calls are thread-safe, from any number of threads and devices.  Results are deterministic: the same inputs give the
  * same bits on every call (no atomics, fixed summation order).
  *
  * Errors.  Arguments are checked before anything is enqueued; a bad argument

@@ -583,18 +583,7 @@ constexpr int LDS_MAX = 160 * 1024;   // gfx950: the most one workgroup may take
 // Launch geometry of the ncols = 1 kernel.
 struct Geo { int G, threads, useg, P, RL; };
 
-static int cu_count() {
-    static int cus = 0;
-    if (!cus) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            cus = v;
-        else
-            cus = 256;
-    }
-    return cus;
-}
+static int cu_count() { return device_cus(); }
 
 // Rows per straight-line round that each type is compiled for.  Q6_K units
 // are the largest (58 B of loads per lane): on GGUF rows one unit in flight
@@ -696,16 +685,11 @@ static Geo geometry(int64_t N, int64_t K, int cus, int mult = 1) {
 }
 
 
-// Dynamic LDS above the default 64 KB needs the kernel's opt-in (once per
-// kernel: the static is per template instance, i.e. per kernel).
+// Dynamic LDS above the default 64 KB needs the kernel's opt-in (a failed
+// opt-in shows as the launch's error).
 template <auto Kernel>
 static void allow_lds() {
-    static const bool done = [] {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, LDS_MAX);
-        return true;
-    }();
-    (void)done;
+    (void)lds_opt_in<Kernel>(LDS_MAX);
 }
 
 template <int T, int L, int RL, int D, bool NT, bool PAIR>

@@ -5,7 +5,44 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace qk {
+
+// Host state kept per device and safe under concurrent calls from several
+// threads (the C ABI's calls are thread-safe).  Devices are numbered below
+// MAX_DEVICES.
+constexpr int MAX_DEVICES = 64;
+
+inline int current_device() {
+    int d = 0;
+    return hipGetDevice(&d) == hipSuccess && d >= 0 && d < MAX_DEVICES ? d : 0;
+}
+
+// Compute units of the current device, read once per device.
+inline int device_cus() {
+    static std::atomic<int> cache[MAX_DEVICES];
+    const int dev = current_device();
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+// Kernel F's opt-in to `bytes` of dynamic LDS (above the default 64 KB) on
+// the current device, made once per device and kernel (a racing thread may
+// repeat it: harmless).
+template <auto F>
+inline hipError_t lds_opt_in(int bytes) {
+    static std::atomic<uint64_t> done{0};
+    const uint64_t bit = uint64_t(1) << current_device();
+    if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(F),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 // Layout flag carried in the type argument (QK_PLANAR of the C ABI).
 constexpr int PLANAR_FLAG = 0x100;

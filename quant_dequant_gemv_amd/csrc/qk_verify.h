@@ -474,18 +474,7 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
 // ---------------------------------------------------------------------------
 struct VGeo { int G, useg, P, RL, threads; size_t lds; };
 
-static int cus_v() {
-    static int cus = 0;
-    if (!cus) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            cus = v;
-        else
-            cus = 256;
-    }
-    return cus;
-}
+static int cus_v() { return device_cus(); }
 
 // mult = 2: each workgroup streams its rows of two tensors (SwiGLU).
 // short_threads: the largest workgroup for rounds of at most V_SHORT_RL
@@ -540,9 +529,7 @@ static bool vgeo(int64_t N, int64_t K, int nc, int ncb, int mult, int short_thre
 
 template <auto Kernel>
 static hipError_t v_allow_lds() {
-    static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
-                                                    hipFuncAttributeMaxDynamicSharedMemorySize, V_LDS_MAX);
-    return e;
+    return lds_opt_in<Kernel>(V_LDS_MAX);
 }
 
 template <int T, int NCB, int RL, bool PAIR, bool EPI, bool WIDE>
