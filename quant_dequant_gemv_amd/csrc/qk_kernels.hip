@@ -44,23 +44,37 @@ struct XReg {
     float xsum[4];
 };
 
-// Sixteen consecutive halves (two 16-byte vectors) -> 8 pair dwords + fp32 sum.
-__device__ __forceinline__ float x_pairs16(const uint4 &v0, const uint4 &v1, uint32_t *o) {
-    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {  // group j = halves 4j .. 4j+3 = words w[2j], w[2j+1]
-        o[2 * j] = (w[2 * j] & 0xffffu) | (w[2 * j + 1] << 16);            // (0, 2)
-        o[2 * j + 1] = (w[2 * j] >> 16) | (w[2 * j + 1] & 0xffff0000u);    // (1, 3)
-        s += (f16_lo(w[2 * j]) + f16_hi(w[2 * j])) + (f16_lo(w[2 * j + 1]) + f16_hi(w[2 * j + 1]));
-    }
-    return s;
+// a from the lane that the DPP control names (a full-rate VALU move)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float a) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), CTRL, 0xf, 0xf, false));
 }
 
-// x of one segment is staged in LDS with every 64-weight unit's 128 bytes at
-// a 144-byte stride: 16-byte chunk c of the segment sits at 144*(c/8) +
-// 16*(c%8).  The pad puts the eight 16-byte reads of the lanes of a wave
-// (each of its own unit) on distinct banks.
+constexpr uint32_t ONES_F16X2 = 0x3c003c00u;  // the fp16 pair (1, 1)
+
+// Eight consecutive halves (one 16-byte vector, two groups of four) -> the
+// four pair dwords of pattern order (per group: (0, 2), then (1, 3)); returns
+// their sum (fp32, fixed order: one pair after the other).
+__device__ __forceinline__ float x_pairs8(const uint4 &v, uint32_t *o) {
+    o[0] = (v.x & 0xffffu) | (v.y << 16);
+    o[1] = (v.x >> 16) | (v.y & 0xffff0000u);
+    o[2] = (v.z & 0xffffu) | (v.w << 16);
+    o[3] = (v.z >> 16) | (v.w & 0xffff0000u);
+    return dot2(v.w, ONES_F16X2, dot2(v.z, ONES_F16X2, dot2(v.y, ONES_F16X2, dot2(v.x, ONES_F16X2, 0.f))));
+}
+
+// Sixteen consecutive halves (two 16-byte vectors) -> 8 pair dwords + fp32 sum.
+__device__ __forceinline__ float x_pairs16(const uint4 &v0, const uint4 &v1, uint32_t *o) {
+    return x_pairs8(v0, o) + x_pairs8(v1, o + 4);
+}
+
+// x of one segment is staged in LDS ready for the dot: every 64-weight unit
+// takes 144 bytes, its 32 pair dwords (16-byte chunk c of the segment, i.e.
+// halves 8c .. 8c+7, as the four pair dwords of x_pairs8 at 144*(c/8) +
+// 16*(c%8)) and then the fp32 sums of its two 32-weight sub-blocks (times
+// 2^-24, the unit of the partial sums) at 144*(c/8) + 128.  The 16-byte pad
+// also puts the eight 16-byte reads of the lanes of a wave (each of its own
+// unit) on distinct banks.
 constexpr int XSTRIDE = 144;
 
 __device__ __forceinline__ uint4 x_chunk(const uint8_t *xl, int c) {
@@ -68,23 +82,34 @@ __device__ __forceinline__ uint4 x_chunk(const uint8_t *xl, int c) {
 }
 
 // Stage x[64*s0 .. 64*(s0+ns)) into LDS: coalesced 16-byte global reads, four
-// per thread per round, issued together (indices clamped: repeats rewrite the
-// same bytes), then written to the padded layout.
+// per thread per round, issued together, each chunk turned into its pair
+// dwords and sum by the thread that read it.  The four chunks of a
+// sub-block are consecutive, and chunk b + tid + k*nthr (b, nthr multiples
+// of 4) has the residue of tid mod 4: they sit in one quad of lanes, whose
+// DPP sum (pairs, then the two pairs) every lane of the quad holds.
+// Indices past the segment are clamped for the reads (every lane takes part
+// in the DPP sums) and write nothing.
 __device__ __forceinline__ void stage_x(uint8_t *xl, const uint16_t *__restrict__ x, int s0, int ns, int tid,
                                         int nthr) {
     const uint4 *xg = reinterpret_cast<const uint4 *>(x) + (size_t)s0 * 8;
     const int nch = ns * 8;
     for (int b = 0; b < nch; b += 4 * nthr) {
         uint4 v[4];
-        int c[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = xg[min(b + tid + k * nthr, nch - 1)];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            c[k] = min(b + tid + k * nthr, nch - 1);
-            v[k] = xg[c[k]];
+            const int c = b + tid + k * nthr;
+            uint32_t o[4];
+            float sum = x_pairs8(v[k], o);
+            sum += dpp_f32<0xb1>(sum);  // quad_perm [1,0,3,2]
+            sum += dpp_f32<0x4e>(sum);  // quad_perm [2,3,0,1]
+            if (c < nch) {
+                uint8_t *unit = xl + XSTRIDE * (c >> 3);
+                *reinterpret_cast<uint4 *>(unit + 16 * (c & 7)) = make_uint4(o[0], o[1], o[2], o[3]);
+                if ((c & 3) == 0) reinterpret_cast<float *>(unit + 128)[(c >> 2) & 1] = sum * 0x1p-24f;
+            }
         }
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            *reinterpret_cast<uint4 *>(xl + XSTRIDE * (c[k] >> 3) + 16 * (c[k] & 7)) = v[k];
     }
 }
 
@@ -106,37 +131,21 @@ __device__ __forceinline__ void load_x_q6(XReg<Q6_K> &X, const uint16_t *__restr
     for (int t = 0; t < 4; ++t) X.xsum[t] = x_pairs16(v[2 * t], v[2 * t + 1], X.xr + 8 * t);
 }
 
-// The lane's x from the staged copy; ul is the unit index within the segment
-// (segments start on superblock boundaries, so ul % 4 == u % 4).
+// The lane's x (Q4_K/Q5_K) from the staged copy; ul is the unit index within
+// the segment.
 template <int T>
 __device__ __forceinline__ void load_x(XReg<T> &X, const uint8_t *xl, int ul) {
-    uint4 v[8];
-    if constexpr (T == Q6_K) {
-        const int s = ul >> 2, n = (ul >> 1) & 1, b = ul & 1;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int c = 32 * s + 16 * n + 4 * t + 2 * b;  // first chunk of quarter t
-            v[2 * t] = x_chunk(xl, c);
-            v[2 * t + 1] = x_chunk(xl, c + 1);
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) X.xsum[t] = x_pairs16(v[2 * t], v[2 * t + 1], X.xr + 8 * t);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = x_chunk(xl, 8 * ul + j);
-        const float s0 = x_pairs16(v[0], v[1], X.xr + 0);
-        const float s1 = x_pairs16(v[2], v[3], X.xr + 8);
-        const float s2 = x_pairs16(v[4], v[5], X.xr + 16);
-        const float s3 = x_pairs16(v[6], v[7], X.xr + 24);
-        X.xsum[0] = (s0 + s1) * 0x1p-24f;  // Q4_K/Q5_K partials are kept in units of 2^-48
-        X.xsum[1] = (s2 + s3) * 0x1p-24f;
+    for (int j = 0; j < 8; ++j) {
+        const uint4 v = x_chunk(xl, 8 * ul + j);
+        X.xr[4 * j] = v.x;
+        X.xr[4 * j + 1] = v.y;
+        X.xr[4 * j + 2] = v.z;
+        X.xr[4 * j + 3] = v.w;
     }
-}
-
-// a from the lane that the DPP control names (a full-rate VALU move)
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float a) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), CTRL, 0xf, 0xf, false));
+    const float2 sums = *reinterpret_cast<const float2 *>(xl + XSTRIDE * ul + 128);
+    X.xsum[0] = sums.x;
+    X.xsum[1] = sums.y;
 }
 
 template <int L>
