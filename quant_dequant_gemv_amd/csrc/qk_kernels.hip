@@ -654,9 +654,10 @@ static size_t part_lds(int64_t N, const Geo &g, int mult = 1) {
 // most lanes.  mult = 2: each workgroup streams its rows of two tensors.
 // Q4_K: several small workgroups of four waves (P = 256 / useg row phases)
 // per CU hide latency better than one large one, measured on the projection
-// shapes at K = 5120 -- four per CU on GGUF rows when every lane still gets
-// 6..12 rows in one round (fewer rows do not amortise the workgroup's x
-// staging and reduction), two per CU on PLANAR rows when a lane gets 4..12.
+// shapes at K = 5120: the fewest per CU (two to four) that keep a lane's
+// rows within one round of at most 8 (whose ring the kernel issues before
+// staging x), when a lane still gets 4..12 rows (fewer do not amortise the
+// workgroup's x staging and reduction).
 template <int T, int L>
 static bool small_workgroups(int64_t N, int cus, int mult, Geo &g) {
     if constexpr (T != Q4_K) {
@@ -665,9 +666,16 @@ static bool small_workgroups(int64_t N, int cus, int mult, Geo &g) {
         using RR = RowRounds<T>;
         const int p4 = 256 / g.useg;
         if (p4 < 1) return false;
-        const int64_t G = std::min<int64_t>(N, (int64_t)cus * mult * (L == PLANAR ? 2 : 4));
-        const int64_t R = mult * ((N + G - 1) / G), rows = (R + p4 - 1) / p4;
-        if (rows < (L == PLANAR ? 4 : 6) || rows > RR::rl[RR::n - 1]) return false;
+        // the fewest workgroups per CU (two to four) that leave a lane at most
+        // eight rows: one round of RL <= 8
+        int64_t G = 0, R = 0, rows = 0;
+        for (int k = 2; k <= 4; ++k) {
+            G = std::min<int64_t>(N, (int64_t)cus * mult * k);
+            R = mult * ((N + G - 1) / G);
+            rows = (R + p4 - 1) / p4;
+            if (rows <= 8) break;
+        }
+        if (rows < 4 || rows > RR::rl[RR::n - 1]) return false;
         g.G = (int)G;
         g.P = p4;
         for (int k = 0; k < RR::n; ++k)
@@ -698,15 +706,18 @@ static Geo geometry(int64_t N, int64_t K, int cus, int mult = 1) {
                 if (RR::rl[k] >= rows) { rl = RR::rl[k]; break; }
             return (int64_t)p * ((rows + rl - 1) / rl) * rl;
         };
+        // with at least pmax rows, at least half the phases (the fewest
+        // slots alone could pick one phase of a handful of lanes per CU)
+        const int plo = R >= pmax ? (pmax + 1) / 2 : 1;
         int64_t best = INT64_MAX;
-        for (int p = 1; p <= pmax; ++p) {
+        for (int p = plo; p <= pmax; ++p) {
             int rl;
             best = std::min(best, plan(p, rl));
         }
         // the most phases among the fewest slots
-        g.P = 1;
+        g.P = plo;
         g.RL = 1;
-        for (int p = 1; p <= pmax; ++p) {
+        for (int p = plo; p <= pmax; ++p) {
             int rl;
             if (plan(p, rl) <= best) { g.P = p; g.RL = rl; }
         }

@@ -134,11 +134,15 @@ def test_gemv_stream_small_shapes(name, qt, N, K):
     assert_row_bound(y, y_ref, S, name)
 
 
-# With 256 workgroups at K = 5120 these row counts give every lane 2, 4, 6, 12
-# and 12+12+12 rows (Q4_K), two-row rounds (Q5_K) and one-row rounds over two
-# and three row phases (Q6_K); N is not a multiple of 256, so workgroups differ
-# by one row.  Every row is checked.
-@pytest.mark.parametrize("qt,N", [(Q4, 3000), (Q4, 6000), (Q4, 9000), (Q4, 17000), (Q4, 25600),
+# At K = 5120 these row counts give every lane (Q4_K) 2 rows (one workgroup
+# per CU), 4, 6, 8 and 9 rows in rounds of 4, 6, 8 and 12 (two to four small
+# workgroups per CU; the 4-, 8- and 12-row rounds issue their first weights
+# before x is staged, the 6-row rounds after), and three rounds of 12 (one
+# workgroup per CU, the later rounds' rings issued in the loop); two-row
+# rounds (Q5_K) and one-row rounds over two and three row phases (Q6_K).  N is
+# not a multiple of the workgroup count, so workgroups differ by one row.
+# Every row is checked.
+@pytest.mark.parametrize("qt,N", [(Q4, 3000), (Q4, 6000), (Q4, 9000), (Q4, 17000), (Q4, 25600), (Q4, 38000),
                                   (Q5, 3000), (Q5, 9000), (Q6, 3000), (Q6, 9000)],
                          ids=lambda v: NAMES.get(v, str(v)))
 def test_gemv_row_rounds_all_rows(qt, N):
