@@ -298,7 +298,7 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
         };
         // the round of RL rows from row i0 of the lane: a straight line with
         // a ring of DD units in flight, the first DD already issued
-        auto round = [&](Unit<T> *buf, const XReg<T> &X, int i0) {
+        auto run_round = [&](Unit<T> *buf, const XReg<T> &X, int i0) {
 #pragma unroll
             for (int p = 0; p < RL; ++p) {
                 const float v = unit_dot<T, L>(buf[p % DD], q, sel, X);
@@ -328,7 +328,7 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
                 if (i0 > 0)
 #pragma unroll
                     for (int p = 0; p < DD; ++p) load_row(buf[p], i0 + p);
-                round(buf, X, i0);
+                run_round(buf, X, i0);
             }
         } else {
             if constexpr (T == Q6_K) {
@@ -343,7 +343,7 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
                 Unit<T> buf[DD];
 #pragma unroll
                 for (int p = 0; p < DD; ++p) load_row(buf[p], i0 + p);
-                round(buf, X, i0);
+                run_round(buf, X, i0);
             }
         }
     }
