@@ -1,10 +1,11 @@
 """Summarise a rocprofv3 kernel trace of bench.py as the markdown kept with
 the profiles.
 
-    rocprofv3 --kernel-trace --output-format csv -d gpurun_out/prof_bench -o bench -- \\
+    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_bench -o bench -- \\
         python3 -u bench.py --no-stream --no-cpu > gpurun_out/prof_bench.json
     python3 -m quant_dequant_gemv_amd.profsum gpurun_out/prof_bench/bench_kernel_trace.csv \\
-        gpurun_out/prof_bench.json profiles/<name>.md --command "<the rocprofv3 command>"
+        gpurun_out/prof_bench.json profiles/<name>.md --command "<the rocprofv3 command>" \\
+        --stats gpurun_out/prof_bench/bench_kernel_stats.csv
 
 Dispatches are grouped by kernel, workgroup size and grid size (one group per
 tensor shape, since shapes sharing a kernel instance differ in launch
@@ -46,7 +47,23 @@ def _bench(path: str) -> dict:
         return json.loads(f.read().strip().splitlines()[-1])
 
 
-def summarise(trace: str, bench_json: str, command: str, plain_json: str | None = None) -> str:
+def stats_rows(stats_csv: str) -> list:
+    """The library's rows of a rocprofv3 --stats kernel table (all dispatches
+    of each kernel name in the run)."""
+    out = ["| kernel (rocprofv3 --stats) | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    with open(stats_csv, newline="") as f:
+        for r in csv.DictReader(f):
+            name = short(r["Name"])
+            if not name.startswith("qk::"):
+                continue
+            out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) * 1e-3:.3f} | "
+                       f"{float(r['MinNs']) * 1e-3:.3f} | {float(r['MaxNs']) * 1e-3:.3f} | "
+                       f"{float(r['Percentage']):.1f}% |")
+    return out
+
+
+def summarise(trace: str, bench_json: str, command: str, plain_json: str | None = None,
+              stats_csv: str | None = None) -> str:
     rows = load(trace)
     bench = _bench(bench_json)
     total = sum(r["us"] for r in rows)
@@ -86,6 +103,10 @@ def summarise(trace: str, bench_json: str, command: str, plain_json: str | None 
                       f"to the traced kernel mean), achieved {prl['achieved']:.1f} GB/s = {prl['frac']:.3f}, "
                       f"`value` {pb['value']} {pb['unit']}.  Tracing adds time between dispatches, which "
                       f"the event span counts and the kernel durations do not."]
+    if stats_csv:
+        lines += ["", "The same run's rocprofv3 --stats table (averages over every dispatch of a kernel "
+                  "instance in the run: warm-up, timed region and the per-shape sections below):", ""]
+        lines += stats_rows(stats_csv)
     lines += ["", "Per-shape times reported by bench.py in the same run (graph of back-to-back launches of one "
               "tensor over >= 1.2 GB of copies):", ""]
     for sec in ("per_gemv", "mixed_types", "verify"):
@@ -139,8 +160,10 @@ def main():
     ap.add_argument("--plain", help="bench.py JSON of an unprofiled run on the same GPU")
     ap.add_argument("--title", help="heading (default: by the kind of trace)")
     ap.add_argument("--stream", action="store_true", help="the trace is of bench.py --stream-only")
+    ap.add_argument("--stats", help="the run's rocprofv3 --stats kernel table (CSV)")
     a = ap.parse_args()
-    body = (summarise_stream if a.stream else summarise)(a.trace, a.bench_json, a.command, a.plain)
+    body = (summarise_stream(a.trace, a.bench_json, a.command, a.plain) if a.stream
+            else summarise(a.trace, a.bench_json, a.command, a.plain, a.stats))
     title = a.title
     if title is None and a.stream:
         with open(a.bench_json) as f:
