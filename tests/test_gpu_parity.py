@@ -138,10 +138,10 @@ def test_gemv_stream_small_shapes(name, qt, N, K):
 # per CU), 4, 6, 8 and 9 rows in rounds of 4, 6, 8 and 12 (two to four small
 # workgroups per CU; the 4-, 8- and 12-row rounds issue their first weights
 # before x is staged, the 6-row rounds after), and three rounds of 12 (one
-# workgroup per CU, the later rounds' rings issued in the loop); two-row
-# rounds (Q5_K) and one-row rounds over two and three row phases (Q6_K).  N is
-# not a multiple of the workgroup count, so workgroups differ by one row.
-# Every row is checked.
+# workgroup per CU, the later rounds' rings issued in the loop); Q5_K one
+# round of two rows and three rounds of four; Q6_K one-row rounds over twelve
+# row phases, one and three rows per lane.  N is not a multiple of the
+# workgroup count, so workgroups differ by one row.  Every row is checked.
 @pytest.mark.parametrize("qt,N", [(Q4, 3000), (Q4, 6000), (Q4, 9000), (Q4, 17000), (Q4, 25600), (Q4, 38000),
                                   (Q5, 3000), (Q5, 9000), (Q6, 3000), (Q6, 9000)],
                          ids=lambda v: NAMES.get(v, str(v)))
