@@ -8,12 +8,14 @@ The arithmetic lives in ``qk_oracle.c`` (plain scalar C, built with
 ``-ffp-contract=off``); this module only builds and marshals.  What it computes,
 and from which passage of the pages, is written at the top of that file:
 
-* ``dequant``  -- fp32 weights, ``w = d*(sc*q) - dmin*m`` (Q4_K/Q5_K) or
-  ``w = d*sc*(q-32)`` (Q6_K), one rounding at most;
+* ``dequant``  -- fp32 weights, ``w = d*(sc*q) - dmin*m`` (Q4_K/Q5_K),
+  ``w = d*sc*(q-32)`` (Q6_K) or ``w = d*(ls-32)*kv[idx]`` (IQ4_XS), one
+  rounding at most;
 * ``gemv``     -- the f64 reference ``y = sum_k w*x`` in ascending k, plus
   ``S = sum_k |w*x|`` for the per-row tolerance;
-* ``half_to_float``, ``k_scale_min``, ``quant``, ``q6k_scale`` -- the field
-  readers, exposed so the tests can pin each one on its own;
+* ``half_to_float``, ``k_scale_min``, ``quant``, ``q6k_scale``,
+  ``iq4xs_scale``, ``iq4nl_value`` -- the field readers, exposed so the tests
+  can pin each one on its own;
 * ``silu``, ``gemv_residual``, ``swiglu`` -- the fused epilogues, in f64 numpy
   on top of ``gemv``; ``residual_bound`` / ``swiglu_bound``, the tolerances
   that the row bound 1e-4 * sum|w*x| implies for them, and ``within``, the
@@ -30,7 +32,7 @@ import subprocess
 
 import numpy as np
 
-Q4_K, Q5_K, Q6_K = 12, 13, 14
+Q4_K, Q5_K, Q6_K, IQ4_XS = 12, 13, 14, 23
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "qk_oracle.c")
@@ -75,6 +77,8 @@ class Oracle:
             "oracle_k_scale_min": ([P, c_int, P, P], None),
             "oracle_quant": ([c_int, P, c_int], c_int),
             "oracle_q6k_scale": ([P, c_int], c_int),
+            "oracle_iq4xs_scale": ([P, c_int], c_int),
+            "oracle_iq4nl_value": ([c_int], c_int),
             "oracle_dequant": ([c_int, P, i64, i64, P, c_int], c_int),
             "oracle_gemv": ([c_int, P, P, i64, i64, c_int, P, P, c_int], c_int),
         }
@@ -111,6 +115,16 @@ class Oracle:
     def q6k_scale(self, block, i: int) -> int:
         b = np.ascontiguousarray(np.asarray(block, dtype=np.uint8))
         return self.lib.oracle_q6k_scale(_ptr(b), int(i))
+
+    def iq4xs_scale(self, block, ib: int) -> int:
+        """6-bit scale ls of sub-block ib of an IQ4_XS superblock (the weight
+        factor is ls - 32)."""
+        b = np.ascontiguousarray(np.asarray(block, dtype=np.uint8))
+        return self.lib.oracle_iq4xs_scale(_ptr(b), int(ib))
+
+    def iq4nl_value(self, idx: int) -> int:
+        """Codebook value of a 4-bit IQ4_XS index."""
+        return self.lib.oracle_iq4nl_value(int(idx))
 
     def _rows(self, W, qtype: int, K: int) -> np.ndarray:
         bb = self.block_bytes(qtype)
@@ -181,6 +195,14 @@ def quant(qtype, block, i):
 
 def q6k_scale(block, i):
     return load().q6k_scale(block, i)
+
+
+def iq4xs_scale(block, ib):
+    return load().iq4xs_scale(block, ib)
+
+
+def iq4nl_value(idx):
+    return load().iq4nl_value(idx)
 
 
 def dequant(qtype, W, K, nthreads=None):

@@ -23,6 +23,10 @@
  *               dequantisation logic.
  *  [T4-design]  section "PHYSICS & CONTRACT": fp32 accumulation for all
  *               reductions.
+ *  [T4-design]  section "QUANTIZATION MIX" also lists IQ4_XS among the mixed
+ *               quants ("4-bit with specific superblock packing"), and
+ *               [T4-gemv] "SPEC" asks for it beside Q4_K and Q5_K under the
+ *               same type flag, with GGML's dequantisation as the reference.
  *  [DP4A-issue] "DP4A Q4K/Q6K GEMV profile is catastrophic through the Gated
  *               DeltaNet recurrence", issue description: GEMV error is
  *               measured against an exact f64 dot of the dequantised weights.
@@ -38,6 +42,12 @@
  *    (at most 11+6+5 significant bits), so the only rounding is the one
  *    fp32 subtraction, round-to-nearest-even.  For Q6_K, d*(sc*(q-32)) is
  *    exact (at most 11+7+5 bits): no rounding at all.
+ *  - IQ4_XS follows GGML's block_iq4_xs (136 bytes: fp16 d, a 16-bit word
+ *    and 4 bytes of 6-bit sub-block scales, 128 bytes of 4-bit indices into
+ *    GGML's 16-entry non-linear int8 codebook shared with IQ4_NL); offsets
+ *    and bit positions are written out below.  w = d * (ls - 32) * kv[idx]:
+ *    |ls - 32| <= 32 and |kv| <= 127 make the integer factor at most 12
+ *    significant bits, so with d's 11 the product is exact in fp32.
  *  - fp16 widening is exact, subnormals included (no flush to zero).
  *  - The GEMV reference is the f64 sum over k in ascending order of
  *    f64(w[n,k]) * f64(x[k,c]); alongside it the oracle returns
@@ -49,10 +59,11 @@
 #include <stdlib.h>
 #include <string.h>
 
-/* GGUF tensor-type ids of the three k-quant formats. */
+/* GGUF tensor-type ids of the formats. */
 #define ORACLE_Q4_K 12
 #define ORACLE_Q5_K 13
 #define ORACLE_Q6_K 14
+#define ORACLE_IQ4_XS 23
 
 #define ORACLE_QK 256 /* weights per superblock */
 
@@ -62,6 +73,7 @@ int oracle_block_bytes(int type)
     case ORACLE_Q4_K: return 144; /* 2 + 2 + 12 + 128 */
     case ORACLE_Q5_K: return 176; /* 2 + 2 + 12 + 32 + 128 */
     case ORACLE_Q6_K: return 210; /* 128 + 64 + 16 + 2 */
+    case ORACLE_IQ4_XS: return 136; /* 2 + 2 + 4 + 128 */
     default: return -1;
     }
 }
@@ -117,7 +129,11 @@ void oracle_k_scale_min(const uint8_t *scales, int j, int *sc, int *m)
  *        in 4 quarters t of 32; quarter t of half n takes its low 4 bits from
  *        ql[64n + 32(t mod 2) + l] (low nibble for t < 2, high for t >= 2)
  *        and its high 2 bits from bits 2t, 2t+1 of qh[32n + l].  q in 0..63,
- *        returned before the -32 offset. */
+ *        returned before the -32 offset.
+ *  IQ4_XS: qs[128] at byte 8, 16 bytes per sub-block ib = i/32: weight
+ *        32ib + l takes the low nibble of qs[16ib + l] for l < 16 and the
+ *        high nibble of qs[16ib + l - 16] for l >= 16.  The 4-bit index into
+ *        the codebook (oracle_iq4nl_value), 0..15. */
 int oracle_quant(int type, const uint8_t *sb, int i)
 {
     int l = i % 32;
@@ -139,12 +155,35 @@ int oracle_quant(int type, const uint8_t *sb, int i)
         int hi = (qh[32 * n + l] >> (2 * t)) & 3;
         return lo | (hi << 4);
     }
+    if (type == ORACLE_IQ4_XS) {
+        const uint8_t *qs = sb + 8;
+        int ib = i / 32;
+        return (qs[16 * ib + (l % 16)] >> (4 * (l / 16))) & 0x0f;
+    }
     return -1;
 }
 
 /* Q6_K signed 8-bit scale of weight i: scales[16] at byte 192, one per 16
  * consecutive weights. */
 int oracle_q6k_scale(const uint8_t *sb, int i) { return (int8_t)sb[192 + i / 16]; }
+
+/* IQ4_XS: d fp16 @0, scales_h (16 bits, little-endian) @2, scales_l[4] @4,
+ * qs[128] @8.  Sub-block ib (0..7) holds weights 32ib .. 32ib+31 and the
+ * 6-bit scale ls: its low 4 bits are nibble (ib mod 2) of scales_l[ib/2]
+ * (low nibble for even ib), its high 2 bits are bits 2ib, 2ib+1 of
+ * scales_h. */
+int oracle_iq4xs_scale(const uint8_t *sb, int ib)
+{
+    int lo = (sb[4 + ib / 2] >> (4 * (ib % 2))) & 0x0f;
+    int hi = (rd16(sb + 2) >> (2 * ib)) & 3;
+    return lo | (hi << 4);
+}
+
+/* The non-linear codebook of the 4-bit indices (IQ4_NL / IQ4_XS). */
+static const int iq4nl_codebook[16] = {-127, -104, -83, -65, -49, -35, -22, -10,
+                                       1,    13,   25,  38,  53,  69,  89,  113};
+
+int oracle_iq4nl_value(int idx) { return (idx >= 0 && idx < 16) ? iq4nl_codebook[idx] : 0; }
 
 /* Dequantise one superblock into out[256]. */
 static void dequant_block(int type, const uint8_t *sb, float *out)
@@ -161,12 +200,19 @@ static void dequant_block(int type, const uint8_t *sb, float *out)
             float b = dmin * (float)m;
             out[i] = a - b;
         }
-    } else { /* ORACLE_Q6_K */
+    } else if (type == ORACLE_Q6_K) {
         float d = oracle_half_to_float(rd16(sb + 208));
         for (int i = 0; i < ORACLE_QK; i++) {
             int sc = oracle_q6k_scale(sb, i);
             int q = oracle_quant(type, sb, i);
             out[i] = d * (float)(sc * (q - 32)); /* exact */
+        }
+    } else { /* ORACLE_IQ4_XS: d is the first field */
+        float d = oracle_half_to_float(rd16(sb));
+        for (int i = 0; i < ORACLE_QK; i++) {
+            int ls = oracle_iq4xs_scale(sb, i / 32);
+            int kv = oracle_iq4nl_value(oracle_quant(type, sb, i));
+            out[i] = d * (float)((ls - 32) * kv); /* exact */
         }
     }
 }

@@ -15,6 +15,8 @@ for them at the same shapes):
 * ``d`` and ``dmin`` are then overwritten with ``fp16(2**u)``, ``u ~ U[-12, -6)``
   (log-uniform in [2^-12, 2^-6]); Q6_K has ``d`` only;
 * Q6_K ``scales[16]`` are overwritten with int8 values uniform over -32..31;
+* IQ4_XS keeps its random 6-bit sub-block scales and 4-bit codebook indices
+  (uniform over their ranges) and gets ``d`` as above;
 * x is ``fp16(N(0, 1))`` of shape ``[K, ncols]`` (row-major).
 
 Streams: weights of a tensor come from ``default_rng([seed, 0])`` and x from
@@ -25,13 +27,13 @@ from __future__ import annotations
 
 import numpy as np
 
-Q4_K, Q5_K, Q6_K = 12, 13, 14
-TYPE_NAMES = {Q4_K: "Q4_K", Q5_K: "Q5_K", Q6_K: "Q6_K"}
-BLOCK_BYTES = {Q4_K: 144, Q5_K: 176, Q6_K: 210}
+Q4_K, Q5_K, Q6_K, IQ4_XS = 12, 13, 14, 23
+TYPE_NAMES = {Q4_K: "Q4_K", Q5_K: "Q5_K", Q6_K: "Q6_K", IQ4_XS: "IQ4_XS"}
+BLOCK_BYTES = {Q4_K: 144, Q5_K: 176, Q6_K: 210, IQ4_XS: 136}
 QK = 256
 
 # Byte offsets of the fp16 scale headers and of the Q6_K int8 scales.
-_D_OFFSET = {Q4_K: 0, Q5_K: 0, Q6_K: 208}
+_D_OFFSET = {Q4_K: 0, Q5_K: 0, Q6_K: 208, IQ4_XS: 0}
 _DMIN_OFFSET = {Q4_K: 2, Q5_K: 2}
 _Q6_SCALES = (192, 208)
 
@@ -62,7 +64,7 @@ def superblocks(qtype: int, N: int, K: int, seed: int) -> np.ndarray:
         dmin = log_uniform_fp16(rng, nsb)
         o = _DMIN_OFFSET[qtype]
         raw[:, o:o + 2] = dmin.view(np.uint8).reshape(nsb, 2)
-    else:
+    elif qtype == Q6_K:
         a, b = _Q6_SCALES
         raw[:, a:b] = rng.integers(-32, 32, size=(nsb, b - a), dtype=np.int8).view(np.uint8)
     return raw.reshape(N, (K // QK) * bb)

@@ -11,13 +11,16 @@ prompt, section QUANTIZATION MIX):
 * Q4_K 144 B: d fp16 @0, dmin fp16 @2, scales[12] @4, qs[128] @16
 * Q5_K 176 B: d @0, dmin @2, scales[12] @4, qh[32] @16, qs[128] @48
 * Q6_K 210 B: ql[128] @0, qh[64] @128, scales[16] int8 @192, d fp16 @208
+* IQ4_XS 136 B: d fp16 @0, scales_h u16 @2, scales_l[4] @4, qs[128] @8 (GGML's
+  block_iq4_xs: the kernel prompt's SPEC asks for IQ4_XS beside Q4_K/Q5_K and
+  names GGML's dequantisation as the reference)
 """
 from __future__ import annotations
 
 import numpy as np
 
-Q4_K, Q5_K, Q6_K = 12, 13, 14
-BLOCK_BYTES = {Q4_K: 144, Q5_K: 176, Q6_K: 210}
+Q4_K, Q5_K, Q6_K, IQ4_XS = 12, 13, 14, 23
+BLOCK_BYTES = {Q4_K: 144, Q5_K: 176, Q6_K: 210, IQ4_XS: 136}
 QS_OFFSET = {Q4_K: 16, Q5_K: 48}
 
 
@@ -53,6 +56,11 @@ def put_quant(qtype: int, block: np.ndarray, i: int, v: int) -> None:
         n, t = i // 128, (i % 128) // 32
         block[64 * n + 32 * (t % 2) + l] |= (v & 0xF) << (4 * (t // 2))
         block[128 + 32 * n + l] |= (v >> 4) << (2 * t)
+    elif qtype == IQ4_XS:
+        # sub-block ib = i // 32: its first 16 weights in the low nibbles of
+        # qs[16 ib ..], the next 16 in the high nibbles of the same bytes
+        assert 0 <= v < 16
+        block[8 + 16 * (i // 32) + l % 16] |= v << (4 * (l // 16))
     else:
         raise ValueError(qtype)
 
@@ -82,9 +90,28 @@ def make_q6_block(d_bits: int, scales, q) -> np.ndarray:
     return b
 
 
+def make_iq4xs_block(d_bits: int, ls, idx) -> np.ndarray:
+    """IQ4_XS superblock from d (fp16 bits), eight 6-bit sub-block scales ls
+    (the weight factor is ls - 32) and 256 4-bit codebook indices.  Low nibble
+    of ls_ib into scales_l[ib // 2] (low half for even ib), its top 2 bits into
+    bits 2 ib, 2 ib + 1 of the little-endian scales_h."""
+    ls = [int(v) for v in ls]
+    assert len(ls) == 8 and all(0 <= v < 64 for v in ls)
+    b = np.zeros(136, dtype=np.uint8)
+    b[0], b[1] = d_bits & 0xFF, d_bits >> 8
+    h = 0
+    for ib, v in enumerate(ls):
+        b[4 + ib // 2] |= (v & 0xF) << (4 * (ib % 2))
+        h |= (v >> 4) << (2 * ib)
+    b[2], b[3] = h & 0xFF, h >> 8
+    for i in range(256):
+        put_quant(IQ4_XS, b, i, int(idx[i]))
+    return b
+
+
 def quant_region(qtype: int):
     """(start, end) byte range of all quant bits of a superblock."""
-    return {Q4_K: (16, 144), Q5_K: (16, 176), Q6_K: (0, 192)}[qtype]
+    return {Q4_K: (16, 144), Q5_K: (16, 176), Q6_K: (0, 192), IQ4_XS: (8, 136)}[qtype]
 
 
 def load_golden(path: str):
@@ -98,7 +125,7 @@ def load_golden(path: str):
             continue
         key, _, rest = line.partition(" ")
         if key == "type":
-            qt = {"Q4_K": Q4_K, "Q5_K": Q5_K, "Q6_K": Q6_K}[rest.strip()]
+            qt = {"Q4_K": Q4_K, "Q5_K": Q5_K, "Q6_K": Q6_K, "IQ4_XS": IQ4_XS}[rest.strip()]
         elif key == "form":
             form = rest.strip()
         elif key == "hex":

@@ -12,7 +12,8 @@ What each check pins against:
                               test-side packer (``kquant_pack``);
 * quant planes             -- every value at every position, via the packer;
 * bit structure            -- each quant bit moves exactly one weight by 2^b;
-* worked examples          -- hand-packed bytes and closed forms in tests/golden;
+* worked examples          -- hand-packed bytes and closed forms in tests/golden
+                              (E4 also fixes the IQ4_XS codebook the oracle uses);
 * rounding                 -- exact integer arithmetic, rounded once to fp32 (RNE);
 * Q5_K / Q4_K invariant    -- Q5_K with qh = 0 equals Q4_K of the same fields;
 * GEMV                     -- integer-weight special case against numpy matmul,
@@ -29,7 +30,7 @@ import numpy as np
 
 import kquant_pack as kp
 
-Q4_K, Q5_K, Q6_K = kp.Q4_K, kp.Q5_K, kp.Q6_K
+Q4_K, Q5_K, Q6_K, IQ4_XS = kp.Q4_K, kp.Q5_K, kp.Q6_K, kp.IQ4_XS
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 ONE, ZERO = kp.half_bits(1.0), 0
 
@@ -73,25 +74,32 @@ def check_scale_min_random(o, n=500, seed=11):
 
 
 def _unit_block(qtype):
-    """A block whose dequantised weights equal the raw quant (Q6_K: quant - 32)."""
+    """A block whose dequantised weights equal the raw quant (Q6_K: quant - 32;
+    IQ4_XS: the codebook value of the index)."""
     if qtype == Q6_K:
         return kp.make_q6_block(ONE, [1] * 16, [0] * 256)
+    if qtype == IQ4_XS:
+        return kp.make_iq4xs_block(ONE, [33] * 8, [0] * 256)
     return kp.make_k_block(qtype, ONE, ZERO, [1] * 8, [0] * 8, [0] * 256)
 
 
 def check_quant_planes(o, qtype):
-    """Every quant value at every position, in one batched dequant call."""
-    levels = {Q4_K: 16, Q5_K: 32, Q6_K: 64}[qtype]
+    """Every quant value at every position, in one batched dequant call.
+    IQ4_XS (d = 1, factor ls - 32 = 1): the weight is the codebook value of
+    the index, here taken from the oracle's codebook reader (the positions are
+    what this pins; the codebook itself is pinned by the worked example)."""
+    levels = {Q4_K: 16, Q5_K: 32, Q6_K: 64, IQ4_XS: 16}[qtype]
     base = _unit_block(qtype)
     rows, exp = [], []
     off = -32.0 if qtype == Q6_K else 0.0
+    val = (lambda v: float(o.iq4nl_value(v))) if qtype == IQ4_XS else (lambda v: v + off)
     for i in range(256):
         for v in range(1, levels):
             b = base.copy()
             kp.put_quant(qtype, b, i, v)
             rows.append(b)
-            e = np.full(256, off, dtype=np.float32)
-            e[i] = v + off
+            e = np.full(256, val(0), dtype=np.float32)
+            e[i] = val(v)
             exp.append(e)
     got = o.dequant(qtype, np.stack(rows), 256)
     assert _same_f32(got, np.stack(exp)), f"quant plane mismatch for type {qtype}"
@@ -127,6 +135,68 @@ def check_bit_structure(o, qtype):
     assert len(seen) == 256 * nbits
 
 
+def check_iq4xs_bit_structure(o):
+    """Each bit of the index plane changes exactly one weight, to the codebook
+    value of the index with that bit flipped; bit -> (weight, index bit) is
+    one-to-one onto weights x 4 bits."""
+    rng = np.random.default_rng(13)
+    idx = rng.integers(0, 16, 256)
+    base = kp.make_iq4xs_block(ONE, [33] * 8, idx)
+    lo, hi = kp.quant_region(IQ4_XS)
+    rows, flips = [], []
+    for byte in range(lo, hi):
+        for bit in range(8):
+            b = base.copy()
+            b[byte] ^= np.uint8(1 << bit)
+            rows.append(b)
+    w0 = o.dequant(IQ4_XS, base[None, :], 256)[0]
+    got = o.dequant(IQ4_XS, np.stack(rows), 256)
+    seen = set()
+    for r in range(got.shape[0]):
+        diff = np.nonzero(got[r] != w0)[0]
+        assert diff.size == 1, f"bit {r} changes {diff.size} weights"
+        i = int(diff[0])
+        matches = [p for p in range(4) if got[r][i] == np.float32(o.iq4nl_value(int(idx[i]) ^ (1 << p)))]
+        assert len(matches) == 1, (r, i)
+        seen.add((i, matches[0]))
+    assert len(seen) == 256 * 4
+
+
+def check_iq4xs_scale_single_field(o):
+    """Every 6-bit scale value alone at every sub-block, through the packer:
+    the reader returns it there and 0 elsewhere, and the weights of that
+    sub-block (d = 1, index 8 whose codebook value the worked example fixes at
+    1) come out as ls - 32."""
+    idx = [8] * 256
+    for ib in range(8):
+        for v in range(64):
+            ls = [0] * 8
+            ls[ib] = v
+            b = kp.make_iq4xs_block(ONE, ls, idx)
+            for jj in range(8):
+                assert o.iq4xs_scale(b, jj) == ls[jj], (ib, v, jj)
+            w = o.dequant(IQ4_XS, b[None, :], 256)[0]
+            exp = np.repeat(np.array(ls, dtype=np.float32) - 32, 32) * np.float32(o.iq4nl_value(8))
+            assert _same_f32(w, exp), (ib, v)
+
+
+def check_iq4xs_exact(o, nblocks=32, seed=14):
+    """w = d * (ls - 32) * kv evaluated in exact integers (d over every fp16
+    class, both signs; every scale; every index) equals the fp32 result: the
+    product never rounds."""
+    rng = np.random.default_rng(seed)
+    kv = [o.iq4nl_value(v) for v in range(16)]
+    blocks, exp = [], []
+    for _ in range(nblocks):
+        d_bits = int(rng.integers(0, 0x7C00)) | (int(rng.integers(0, 2)) << 15)
+        ls, idx = rng.integers(0, 64, 8), rng.integers(0, 16, 256)
+        blocks.append(kp.make_iq4xs_block(d_bits, ls, idx))
+        Md, Ed = _f16_parts(d_bits)
+        exp.append([float(Md * (int(ls[i // 32]) - 32) * kv[int(idx[i])]) * 2.0 ** Ed for i in range(256)])
+    got = o.dequant(IQ4_XS, np.stack(blocks), 256)
+    assert _same_f32(got, np.array(exp, dtype=np.float32))
+
+
 def check_q6k_scale_index(o):
     q = [32 + 1] * 256          # q - 32 == 1 everywhere
     sc = list(range(-8, 8))     # distinct per 16-weight group
@@ -147,7 +217,16 @@ def _closed_form(form, i):
         return (8 * j + 7) * (i % 32) - (63 - 8 * j) / 4.0
     if form == "e3":
         return 2.0 ** -4 * (i // 16 - 8) * (i % 64 - 32)
+    if form == "e4":
+        f = (-4, -3, -2, -1, 1, 2, 3, 4)[i // 32]
+        return 2.0 ** -3 * f * E4_CODEBOOK[i % 16]
     raise ValueError(form)
+
+
+# The codebook as the worked example E4 states it (tests/golden/iq4xs_e4.txt,
+# restated from GGML's IQ4_NL / IQ4_XS format; no GGML build is available
+# here to compare with, so the values are a reading, not a pin against GGML).
+E4_CODEBOOK = (-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113)
 
 
 def _example_fields(form):
@@ -162,12 +241,15 @@ def _example_fields(form):
     if form == "e3":
         return kp.make_q6_block(kp.half_bits(2.0 ** -4), [s - 8 for s in range(16)],
                                 [i % 64 for i in range(256)])
+    if form == "e4":
+        return kp.make_iq4xs_block(kp.half_bits(2.0 ** -3), [28, 29, 30, 31, 33, 34, 35, 36],
+                                   [i % 16 for i in range(256)])
     raise ValueError(form)
 
 
 def check_worked_examples(o):
-    files = sorted(glob.glob(os.path.join(GOLDEN, "q*_e*.txt")))
-    assert len(files) >= 3
+    files = sorted(glob.glob(os.path.join(GOLDEN, "*_e*.txt")))
+    assert len(files) >= 4
     for path in files:
         qt, form, block, values = kp.load_golden(path)
         assert block.size == kp.BLOCK_BYTES[qt]
@@ -263,8 +345,8 @@ def check_gemv_integer_textbook(o, seed=8):
     """d = 1, dmin = 0, sc = 1: W is an integer matrix; y must match numpy's matmul."""
     rng = np.random.default_rng(seed)
     N, K, nc = 37, 768, 3
-    for qt in (Q4_K, Q5_K, Q6_K):
-        levels = {Q4_K: 16, Q5_K: 32, Q6_K: 64}[qt]
+    for qt in (Q4_K, Q5_K, Q6_K, IQ4_XS):
+        levels = {Q4_K: 16, Q5_K: 32, Q6_K: 64, IQ4_XS: 16}[qt]
         q = rng.integers(0, levels, (N, K))
         rows = []
         for n in range(N):
@@ -273,12 +355,17 @@ def check_gemv_integer_textbook(o, seed=8):
                 qq = q[n, 256 * s:256 * s + 256]
                 if qt == Q6_K:
                     blocks.append(kp.make_q6_block(ONE, [1] * 16, qq))
+                elif qt == IQ4_XS:
+                    blocks.append(kp.make_iq4xs_block(ONE, [33] * 8, qq))
                 else:
                     blocks.append(kp.make_k_block(qt, ONE, ZERO, [1] * 8, [0] * 8, qq))
             rows.append(np.concatenate(blocks))
         W = np.stack(rows)
         x = rng.standard_normal((K, nc)).astype(np.float16)
-        Wi = q.astype(np.float64) - (32.0 if qt == Q6_K else 0.0)
+        if qt == IQ4_XS:
+            Wi = np.array(E4_CODEBOOK, dtype=np.float64)[q]
+        else:
+            Wi = q.astype(np.float64) - (32.0 if qt == Q6_K else 0.0)
         yref = Wi @ x.astype(np.float64)
         Sref = np.abs(Wi) @ np.abs(x.astype(np.float64))
         y, S = o.gemv(qt, W, x, K)
@@ -312,7 +399,7 @@ def check_gemv_min_term(o, seed=9):
 
 def check_gemv_dot_of_dequant(o, synth, seed=10):
     """y equals numpy's f64 matmul of the dequantised matrix, for ncols 1 and 5."""
-    for qt in (Q4_K, Q5_K, Q6_K):
+    for qt in (Q4_K, Q5_K, Q6_K, IQ4_XS):
         N, K = 29, 1024
         W = synth.superblocks(qt, N, K, seed)
         w = o.dequant(qt, W, K).astype(np.float64)
@@ -343,6 +430,10 @@ ALL_CHECKS = [
     lambda o: check_quant_planes(o, Q4_K),
     lambda o: check_quant_planes(o, Q5_K),
     lambda o: check_quant_planes(o, Q6_K),
+    lambda o: check_quant_planes(o, IQ4_XS),
+    check_iq4xs_bit_structure,
+    check_iq4xs_scale_single_field,
+    check_iq4xs_exact,
     lambda o: check_bit_structure(o, Q4_K),
     lambda o: check_bit_structure(o, Q5_K),
     lambda o: check_bit_structure(o, Q6_K),

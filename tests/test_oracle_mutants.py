@@ -34,6 +34,14 @@ MUTANTS = {
     "x_transposed": ("j->xd[k * j->ncols + c]", "j->xd[c * j->K + k]"),
     "abs_dropped": ("mag += fabs(p);", "mag += p;"),
     "subnormal_scale": ("ldexpf((float)m, -24)", "ldexpf((float)m, -25)"),
+    "iq4_nibble_order": ("(qs[16 * ib + (l % 16)] >> (4 * (l / 16)))", "(qs[16 * ib + (l % 16)] >> (4 * (1 - l / 16)))"),
+    "iq4_qs_offset": ("const uint8_t *qs = sb + 8;", "const uint8_t *qs = sb + 4;"),
+    "iq4_scale_low_nibble": ("(sb[4 + ib / 2] >> (4 * (ib % 2)))", "(sb[4 + ib / 2] >> (4 * (1 - ib % 2)))"),
+    "iq4_scale_high_bits": ("(rd16(sb + 2) >> (2 * ib)) & 3", "(rd16(sb + 2) >> (2 * ib + 1)) & 3"),
+    "iq4_offset": ("((ls - 32) * kv)", "((ls - 31) * kv)"),
+    "iq4_codebook_index": ("iq4nl_codebook[idx]", "iq4nl_codebook[idx ^ 1]"),
+    "iq4_codebook_entry": ("53,  69", "53,  68"),
+    "iq4_d_position": ("oracle_half_to_float(rd16(sb));", "oracle_half_to_float(rd16(sb + 2));"),
 }
 
 CHECKS = oc.ALL_CHECKS + [lambda o: oc.check_gemv_dot_of_dequant(o, synth)]
