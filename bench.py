@@ -260,13 +260,7 @@ def read_ceiling(torch, sizes):
     the step's sizes (libqkcalib.so: non-temporal loads, grid-stride), one
     launch per buffer, rotated over >= 1.2 GB of copies like the GEMV step and
     replayed from one graph; the fastest of three launch shapes."""
-    import ctypes
-
-    from quant_dequant_gemv_amd import build as qb
-    lib = ctypes.CDLL(qb.CALIB_LIB)
-    lib.qk_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
-                                   ctypes.c_void_p]
-    lib.qk_stream_read.restype = ctypes.c_int
+    lib = _calib_lib()
     total = sum(sizes)
     copies = max(2, int(-(-MIN_ROTATION_BYTES // total)))
     bufs = [[torch.empty(n, dtype=torch.uint8, device="cuda").fill_(c % 251) for n in sizes] for c in range(copies)]
@@ -289,6 +283,57 @@ def read_ceiling(torch, sizes):
             "bytes_per_launch": round(total / len(sizes)), "avg_launch_us": round(us, 3),
             "GBs": round(total / len(sizes) / us / 1e3, 1), "blocks": blocks, "threads": threads,
             "rotation_copies": copies}
+
+
+def _calib_lib():
+    import ctypes
+
+    from quant_dequant_gemv_amd import build as qb
+    lib = ctypes.CDLL(qb.CALIB_LIB)
+    lib.qk_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.qk_stream_read.restype = ctypes.c_int
+    return lib
+
+
+SUSTAINED_BYTES = 4 << 30
+
+
+def sustained_read(torch, shapes=((512, 1024), (1024, 512), (2048, 256), (4096, 256))):
+    """HBM's sustained streaming rate: one launch of the plain 16-byte read
+    (non-temporal loads, XOR-folded) over a 4 GiB buffer -- 16x the Infinity
+    Cache, so nothing is served twice, and ~0.5 ms long, so a launch's fixed
+    dispatch / fill / drain cost is well under 1% of it.  Median of three
+    launches per shape, each after a GPU busy-wait; the fastest shape."""
+    lib = _calib_lib()
+    buf = torch.empty(SUSTAINED_BYTES, dtype=torch.uint8, device="cuda").fill_(7)
+    out = torch.empty(1 << 20, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = None
+    for blocks, threads in shapes:
+        spans = []
+        for _ in range(3):
+            torch.cuda._sleep(SPIN_CYCLES)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            rc = lib.qk_stream_read(buf.data_ptr(), SUSTAINED_BYTES, out.data_ptr(), blocks, threads,
+                                    stream.cuda_stream)
+            b.record(stream)
+            if rc != 0:
+                raise RuntimeError(f"qk_stream_read failed: {rc}")
+            torch.cuda.synchronize()
+            spans.append(a.elapsed_time(b) * 1e-3)
+        us = sorted(spans)[1] * 1e6
+        if best is None or us < best[0]:
+            best = (us, blocks, threads)
+    us, blocks, threads = best
+    del buf
+    torch.cuda.empty_cache()
+    gbs = SUSTAINED_BYTES / us / 1e3
+    return {"kernel": "plain 16-byte read, non-temporal loads, grid-stride (libqkcalib.so)",
+            "bytes": SUSTAINED_BYTES, "us": round(us, 1), "GBs": round(gbs, 1),
+            "frac_peak": round(gbs / PEAK_HBM_GBS, 4), "blocks": blocks, "threads": threads}
 
 
 def cpu_baseline(entries, min_seconds=10.0):
@@ -624,6 +669,12 @@ def main():
         t["W"] = t["W"][:1]
     torch.cuda.empty_cache()
     ceiling = read_ceiling(torch, [t["bytes"] for t in tensors])
+    sustained = sustained_read(torch)
+    # plain reads at the two graded tensor sizes (Q4_K 17408 x 5120, Q6_K 5120 x 17408)
+    size_reads = {}
+    for e in (entries[2], synth.MIXED[0]):
+        nb = e["N"] * synth.row_bytes(e["qtype"], e["K"])
+        size_reads[e["name"]] = read_ceiling(torch, [nb])
     shapes = per_shape(torch, launcher, tensors)
     del tensors
     torch.cuda.empty_cache()
@@ -702,6 +753,8 @@ def main():
                      "read_ceiling_GBs": ceiling["GBs"],
                      "frac_of_read_ceiling": round(achieved / ceiling["GBs"], 4)},
         "read_ceiling": ceiling,
+        "sustained_read": sustained,
+        "read_at_size": size_reads,
         "cpu_baseline": cpu,
         "per_gemv": shapes,
         "mixed_types": mixed_out,

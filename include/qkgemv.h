@@ -61,8 +61,9 @@ enum {
     QK_EINVAL_TYPE = -1,  /* type is not one of QK_Q4_K / QK_Q5_K / QK_Q6_K        */
     QK_EINVAL_SHAPE = -2, /* N < 1, K < 256, K % 256 != 0, ncols not in 1..32,
                              or a size whose byte count overflows int64          */
-    QK_EINVAL_PTR = -3,   /* a NULL pointer, W or x not 16-byte aligned, or y /
-                             out not 4-byte aligned                               */
+    QK_EINVAL_PTR = -3,   /* a NULL pointer, W or x not 16-byte aligned, y /
+                             out not 4-byte aligned, or an output that overlaps
+                             an input                                             */
     QK_ELAUNCH = -4,      /* the HIP launch failed (message via qk_strerror)      */
     QK_EINVAL_FLAGS = -5  /* an epilogue flag other than QK_Y_F16                 */
 };
@@ -109,8 +110,18 @@ enum {
  *          asks for verifier widths up to 17
  *   stream hipStream_t to enqueue on
  *
- * Accuracy: |y - y_exact| <= 1e-4 * sum_k |w * x| for every (n, c), where
- * y_exact is the f64 dot of the dequantised weights; x is never quantised.
+ * y must not overlap W or x (QK_EINVAL_PTR): other workgroups are still
+ * reading them while y is written.
+ *
+ * Accuracy: |y - y_exact| <= 1e-4 * sum_k |w * x| for every (n, c) and every
+ * input (all finite fp16 d / dmin, subnormals and signs included; any int8
+ * Q6_K scale), where y_exact is the f64 dot of the dequantised weights; x is
+ * never quantised.  Each 32-weight (Q6_K: 16) scale group is summed as
+ * a * sum (q - c) x + (a*c - b) * sum x with a = d*sc, b = dmin*m (Q6_K:
+ * b = 32 a) and an integer c nearest b/a, q - c formed exactly per weight:
+ * no term exceeds three times its weight's |w x|, so the fp32 error stays
+ * below about 3 * 40 * 2^-24 * sum |w x| (< 1e-5 of it), and a row whose
+ * weights are all zero (d*sc*q = dmin*m) gives exactly 0.
  */
 int qk_gemv(int type, const void *W, const void *x, void *y,
             int64_t N, int64_t K, int ncols, void *stream);
@@ -178,7 +189,8 @@ int qk_gemv_swiglu(int type, const void *Wg, const void *Wu, const void *x, void
  * nearest-even; Q6_K values are exact.  The check path for the unpacking the
  * GEMV kernels use; not on the timed path.
  *
- *   out    device pointer to N*K fp32 values, 4-byte aligned (written)
+ *   out    device pointer to N*K fp32 values, 4-byte aligned (written),
+ *          not overlapping W (QK_EINVAL_PTR)
  *   other arguments as for qk_gemv
  */
 int qk_dequant(int type, const void *W, void *out, int64_t N, int64_t K, void *stream);
@@ -214,7 +226,8 @@ typedef struct qk_gemv_item {
  * each entry taking its share of the workgroups (performance only: results
  * are as below).
  *
- * Entries may share W and x.  No entry's y may overlap any entry's W, x or y.
+ * Entries may share W and x.  No entry's y may overlap any entry's W, x or y
+ * (checked: QK_EINVAL_PTR).
  * Every y_i is bit-identical to what qk_gemv(type_i, W_i, x_i, y_i, N_i, K_i,
  * 1, stream) writes; the accuracy bound is that of qk_gemv.  Every entry is
  * checked before anything is enqueued, with qk_gemv's codes; a count outside

@@ -121,6 +121,12 @@ def qk_version() -> str:
 
 
 # ---------------------------------------------------------------- torch helpers
+# The C ABI cannot see buffer lengths, so these helpers check every tensor
+# before anything is enqueued: dtype, contiguity, size against N, K and ncols,
+# and that all of them sit on one CUDA device.  (A wrong size or a host tensor
+# passed on would make a kernel read or write out of bounds.)  Type and shape
+# arguments themselves are checked by the library, which returns its error
+# code before launching anything.
 
 def _stream_handle(stream):
     import torch
@@ -129,18 +135,63 @@ def _stream_handle(stream):
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _need(t, name, dtype, numel=None, min_numel=None):
+    """Check one tensor argument (sizes before the device, so the checks run
+    without a GPU too)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, has {t.numel()}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} must have at least {min_numel} elements, has {t.numel()}")
+
+
+def _same_cuda_device(**tensors):
+    devs = {t.device for t in tensors.values() if t is not None}
+    for name, t in tensors.items():
+        if t is not None and t.device.type != "cuda":
+            raise ValueError(f"{name} must be a CUDA (HIP) device tensor, is on {t.device}")
+    if len(devs) > 1:
+        raise ValueError(f"all tensors must be on one device, got {sorted(str(d) for d in devs)}")
+
+
+def _weights(qtype, W, N, K, name="W"):
+    """W: uint8, at least N rows of qk_row_bytes(qtype, K) bytes (skipped when
+    the library would reject the type or shape itself)."""
+    import torch
+    rb = qk_row_bytes(qtype, K) if isinstance(qtype, int) else -1
+    _need(W, name, torch.uint8, min_numel=N * rb if (rb > 0 and N >= 1) else None)
+
+
+def _activations(x, K):
+    """x: float16 [K'] or [K', ncols] with K' >= K (the kernels read the first
+    K rows: a longer buffer is a valid input); returns ncols."""
+    import torch
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("x must be a torch tensor")
+    if x.dim() not in (1, 2) or x.shape[0] < K:
+        raise ValueError(f"x must have shape [K] or [K, ncols] with at least K = {K} rows, got {tuple(x.shape)}")
+    ncols = 1 if x.dim() == 1 else int(x.shape[1])
+    _need(x, "x", torch.float16, min_numel=K * ncols)
+    return ncols
+
+
 def gemv(qtype: int, W, x, N: int, K: int, out=None, stream=None):
     """y = dequant(W) @ x on the GPU.  W: uint8 device tensor of N rows of
     superblocks; x: float16 device tensor [K] or [K, ncols]; returns float32
-    [N, ncols] (or writes ``out``)."""
+    [N, ncols] (or writes ``out``, N*ncols float32 elements)."""
     import torch
-    ncols = 1 if x.dim() == 1 else int(x.shape[1])
+    _weights(qtype, W, N, K)
+    ncols = _activations(x, K)
     if out is None:
-        out = torch.empty((N, ncols), dtype=torch.float32, device=x.device)
-    if x.dtype != torch.float16 or out.dtype != torch.float32 or W.dtype != torch.uint8:
-        raise TypeError("W must be uint8, x float16, out float32")
-    if not (W.is_contiguous() and x.is_contiguous() and out.is_contiguous()):
-        raise ValueError("tensors must be contiguous")
+        out = torch.empty((max(N, 0), ncols), dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.float32, numel=N * ncols)
+    _same_cuda_device(W=W, x=x, out=out)
     rc = qk_gemv(qtype, W.data_ptr(), x.data_ptr(), out.data_ptr(), N, K, ncols, _stream_handle(stream))
     if rc != QK_OK:
         raise QKError(rc, "qk_gemv")
@@ -151,9 +202,8 @@ def _check_out(x, out, f16, N, ncols):
     import torch
     dt = torch.float16 if f16 else torch.float32
     if out is None:
-        out = torch.empty((N, ncols), dtype=dt, device=x.device)
-    if out.dtype != dt or not out.is_contiguous() or out.numel() != N * ncols:
-        raise ValueError(f"out must be a contiguous {dt} tensor of N*ncols elements")
+        out = torch.empty((max(N, 0), ncols), dtype=dt, device=x.device)
+    _need(out, "out", dt, numel=N * ncols)
     return out
 
 
@@ -162,16 +212,14 @@ def gemv_ex(qtype: int, W, x, N: int, K: int, residual=None, f16: bool = False, 
     residual: None or a float32 device tensor of N*ncols elements (may be
     ``out`` itself for an in-place update of a float32 y)."""
     import torch
-    ncols = 1 if x.dim() == 1 else int(x.shape[1])
-    if x.dtype != torch.float16 or W.dtype != torch.uint8 or not (W.is_contiguous() and x.is_contiguous()):
-        raise TypeError("W must be contiguous uint8, x contiguous float16")
+    _weights(qtype, W, N, K)
+    ncols = _activations(x, K)
     out = _check_out(x, out, f16, N, ncols)
-    rp = 0
     if residual is not None:
-        if residual.dtype != torch.float32 or not residual.is_contiguous() or residual.numel() != N * ncols:
-            raise ValueError("residual must be a contiguous float32 tensor of N*ncols elements")
-        rp = residual.data_ptr()
-    rc = qk_gemv_ex(qtype, W.data_ptr(), x.data_ptr(), out.data_ptr(), N, K, ncols, rp or None,
+        _need(residual, "residual", torch.float32, numel=N * ncols)
+    _same_cuda_device(W=W, x=x, out=out, residual=residual)
+    rp = residual.data_ptr() if residual is not None else None
+    rc = qk_gemv_ex(qtype, W.data_ptr(), x.data_ptr(), out.data_ptr(), N, K, ncols, rp,
                     Y_F16 if f16 else 0, _stream_handle(stream))
     if rc != QK_OK:
         raise QKError(rc, "qk_gemv_ex")
@@ -180,14 +228,11 @@ def gemv_ex(qtype: int, W, x, N: int, K: int, residual=None, f16: bool = False, 
 
 def gemv_swiglu(qtype: int, Wg, Wu, x, N: int, K: int, f16: bool = False, out=None, stream=None):
     """y = silu(dequant(Wg) @ x) * (dequant(Wu) @ x) in one launch."""
-    import torch
-    ncols = 1 if x.dim() == 1 else int(x.shape[1])
-    for W in (Wg, Wu):
-        if W.dtype != torch.uint8 or not W.is_contiguous():
-            raise TypeError("Wg and Wu must be contiguous uint8")
-    if x.dtype != torch.float16 or not x.is_contiguous():
-        raise TypeError("x must be contiguous float16")
+    _weights(qtype, Wg, N, K, "Wg")
+    _weights(qtype, Wu, N, K, "Wu")
+    ncols = _activations(x, K)
     out = _check_out(x, out, f16, N, ncols)
+    _same_cuda_device(Wg=Wg, Wu=Wu, x=x, out=out)
     rc = qk_gemv_swiglu(qtype, Wg.data_ptr(), Wu.data_ptr(), x.data_ptr(), out.data_ptr(), N, K, ncols,
                         Y_F16 if f16 else 0, _stream_handle(stream))
     if rc != QK_OK:
@@ -201,15 +246,21 @@ def gemv_batch(entries, stream=None):
     (W uint8, x float16 [K], out float32 [N]); returns the list of outputs."""
     import torch
     items, outs = [], []
-    for e in entries:
+    for i, e in enumerate(entries):
         qtype, W, x, N, K = e[:5]
-        out = e[5] if len(e) > 5 else torch.empty(N, dtype=torch.float32, device=x.device)
-        if x.dtype != torch.float16 or out.dtype != torch.float32 or W.dtype != torch.uint8:
-            raise TypeError("W must be uint8, x float16, out float32")
-        if not (W.is_contiguous() and x.is_contiguous() and out.is_contiguous()):
-            raise ValueError("tensors must be contiguous")
-        items.append((qtype, W.data_ptr(), x.data_ptr(), out.data_ptr(), N, K))
+        _weights(qtype, W, N, K, f"entries[{i}].W")
+        if _activations(x, K) != 1:
+            raise ValueError(f"entries[{i}].x must be one column")
+        out = e[5] if len(e) > 5 else torch.empty(max(N, 0), dtype=torch.float32, device=x.device)
+        _need(out, f"entries[{i}].out", torch.float32, numel=N)
+        items.append((qtype, W, x, out, N, K))
         outs.append(out)
+    tensors = {}
+    for i, (_, W, x, out, _, _) in enumerate(items):
+        tensors.update({f"entries[{i}].W": W, f"entries[{i}].x": x, f"entries[{i}].out": out})
+    if tensors:
+        _same_cuda_device(**tensors)
+    items = [(qt, W.data_ptr(), x.data_ptr(), out.data_ptr(), N, K) for qt, W, x, out, N, K in items]
     rc = qk_gemv_batch(items, _stream_handle(stream))
     if rc != QK_OK:
         raise QKError(rc, "qk_gemv_batch")
@@ -217,10 +268,13 @@ def gemv_batch(entries, stream=None):
 
 
 def dequant(qtype: int, W, N: int, K: int, out=None, stream=None):
-    """fp32 [N, K] dequantised weights on the GPU."""
+    """fp32 [N, K] dequantised weights on the GPU (``out``: N*K float32)."""
     import torch
+    _weights(qtype, W, N, K)
     if out is None:
-        out = torch.empty((N, K), dtype=torch.float32, device=W.device)
+        out = torch.empty((max(N, 0), max(K, 0)), dtype=torch.float32, device=W.device)
+    _need(out, "out", torch.float32, numel=N * K)
+    _same_cuda_device(W=W, out=out)
     rc = qk_dequant(qtype, W.data_ptr(), out.data_ptr(), N, K, _stream_handle(stream))
     if rc != QK_OK:
         raise QKError(rc, "qk_dequant")
@@ -229,11 +283,16 @@ def dequant(qtype: int, W, N: int, K: int, out=None, stream=None):
 
 def repack(qtype: int, W, N: int, K: int, out=None, stream=None):
     """GGUF rows -> PLANAR rows on the GPU; returns the uint8 device tensor to
-    pass with type ``qtype | PLANAR``."""
+    pass with type ``qtype | PLANAR`` (``out``: at least
+    N * qk_row_bytes(qtype | PLANAR, K) bytes)."""
     import torch
-    nbytes = N * qk_row_bytes(qtype | PLANAR, K)
+    _weights(qtype, W, N, K)
+    prb = qk_row_bytes(qtype | PLANAR, K) if isinstance(qtype, int) and not (qtype & PLANAR) else -1
+    nbytes = N * prb if (prb > 0 and N >= 1) else 0
     if out is None:
-        out = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+        out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=W.device)
+    _need(out, "out", torch.uint8, min_numel=nbytes or None)
+    _same_cuda_device(W=W, out=out)
     rc = qk_repack(qtype, W.data_ptr(), out.data_ptr(), N, K, _stream_handle(stream))
     if rc != QK_OK:
         raise QKError(rc, "qk_repack")

@@ -58,15 +58,19 @@ bool overlap(const void *a, int64_t na, const void *b, int64_t nb) {
 }
 
 // Pointer checks of the GEMV entry points (y fp32 or, with QK_Y_F16, fp16;
-// the residual may be y itself only when y is fp32).
-int check_io(const void *x, void *y, const void *res, int64_t N, int ncols, int flags) {
+// the residual may be y itself only when y is fp32).  y is written while W
+// and x are still being read by other workgroups, so y may overlap neither.
+int check_io(int type, const void *W, const void *x, void *y, const void *res, int64_t N, int64_t K, int ncols,
+             int flags) {
     if (!x || !y || !aligned(x, 16)) return QK_EINVAL_PTR;
     const bool f16 = (flags & QK_Y_F16) != 0;
     if (!aligned(y, f16 ? 2 : 4)) return QK_EINVAL_PTR;
+    const int64_t n = N * ncols, ybytes = (f16 ? 2 : 4) * n;
+    if (overlap(y, ybytes, W, N * row_bytes_of(type, K)) || overlap(y, ybytes, x, 2 * K * ncols))
+        return QK_EINVAL_PTR;
     if (res) {
         if (!aligned(res, 4)) return QK_EINVAL_PTR;
-        const int64_t n = N * ncols;
-        if (!(res == y && !f16) && overlap(res, 4 * n, y, (f16 ? 2 : 4) * n)) return QK_EINVAL_PTR;
+        if (!(res == y && !f16) && overlap(res, 4 * n, y, ybytes)) return QK_EINVAL_PTR;
     }
     return QK_OK;
 }
@@ -103,7 +107,7 @@ int qk_gemv_ex(int type, const void *W, const void *x, void *y, int64_t N, int64
     if (rc) return rc;
     if (flags & ~QK_Y_F16) return QK_EINVAL_FLAGS;
     if (!W || !aligned(W, 16)) return QK_EINVAL_PTR;
-    if ((rc = check_io(x, y, residual, N, ncols, flags))) return rc;
+    if ((rc = check_io(type, W, x, y, residual, N, K, ncols, flags))) return rc;
     return gemv_launch(type, W, nullptr, x, y, N, K, ncols, residual, flags, stream);
 }
 
@@ -113,7 +117,8 @@ int qk_gemv_swiglu(int type, const void *Wg, const void *Wu, const void *x, void
     if (rc) return rc;
     if (flags & ~QK_Y_F16) return QK_EINVAL_FLAGS;
     if (!Wg || !Wu || !aligned(Wg, 16) || !aligned(Wu, 16)) return QK_EINVAL_PTR;
-    if ((rc = check_io(x, y, nullptr, N, ncols, flags))) return rc;
+    if ((rc = check_io(type, Wg, x, y, nullptr, N, K, ncols, flags))) return rc;
+    if (overlap(y, ((flags & QK_Y_F16) ? 2 : 4) * N * ncols, Wu, N * row_bytes_of(type, K))) return QK_EINVAL_PTR;
     return gemv_launch(type, Wg, Wu, x, y, N, K, ncols, nullptr, flags, stream);
 }
 
@@ -128,6 +133,14 @@ int qk_gemv_batch(const qk_gemv_item *items, int count, void *stream) {
             return QK_EINVAL_PTR;
         e[i] = qk::BatchEntry{it.type, it.W, it.x, it.y, it.N, it.K};
     }
+    // the entries run concurrently: no y may overlap any entry's W, x or y
+    for (int i = 0; i < count; ++i)
+        for (int j = 0; j < count; ++j) {
+            const qk_gemv_item &a = items[i], &b = items[j];
+            if (overlap(a.y, 4 * a.N, b.W, b.N * row_bytes_of(b.type, b.K)) || overlap(a.y, 4 * a.N, b.x, 2 * b.K) ||
+                (i != j && overlap(a.y, 4 * a.N, b.y, 4 * b.N)))
+                return QK_EINVAL_PTR;
+        }
     return launched(qk::launch_gemv_batch(e, count, (hipStream_t)stream));
 }
 
@@ -135,6 +148,7 @@ int qk_dequant(int type, const void *W, void *out, int64_t N, int64_t K, void *s
     const int rc = check_shape(type, N, K, 1);
     if (rc) return rc;
     if (!W || !out || !aligned(W, 16) || !aligned(out, 4)) return QK_EINVAL_PTR;
+    if (overlap(out, 4 * N * K, W, N * row_bytes_of(type, K))) return QK_EINVAL_PTR;
     return launched(qk::launch_dequant(type, W, out, N, K, (hipStream_t)stream));
 }
 
@@ -158,7 +172,8 @@ const char *qk_strerror(int code) {
     case QK_EINVAL_SHAPE: return "invalid shape: need N >= 1, K a positive multiple of 256, 1 <= ncols <= 32";
     case QK_EINVAL_PTR:
         return "invalid pointer: NULL, or W/x not 16-byte aligned, or y/out/residual not 4-byte aligned (fp16 y: 2), "
-               "or a residual that overlaps y without being y (fp32 y)";
+               "or an output that overlaps an input (y with W or x, out with W, a batch entry's y with any entry's "
+               "W, x or y, Wp with W), or a residual that overlaps y without being y (fp32 y)";
     case QK_EINVAL_FLAGS: return "invalid flags: the only epilogue flag is QK_Y_F16 (0x1)";
     case QK_ELAUNCH: return g_launch_msg;
     default: return "unknown error code";

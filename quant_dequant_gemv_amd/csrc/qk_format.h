@@ -105,6 +105,50 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
 }
 
+// Packed fp16 add (v_pk_add_f16).  On quant patterns (multiples of 2^-24
+// below 2^-14) every sum is exact: the fp16 denormals are kept.
+__device__ __forceinline__ uint32_t padd(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) + __builtin_bit_cast(half2_t, b));
+}
+
+// ---------------------------------------------------------------------------
+// Shifted form of a Q4_K/Q5_K sub-block.  With a = d*sc and b = dmin*m,
+//     sum_i w_i x_i = a * sum_i (q_i - c) x_i + e * sum_i x_i,   e = a*c - b,
+// for any integer c.  Taking c = clamp(rint(b / a), 0, QMAX) gives, for every
+// quant value q of the sub-block, |a|*|q - c| + |e| <= 3 |a*q - b|: no term of
+// the sum is larger than three times its weight's share of sum_i |w_i x_i|,
+// so the fp32 rounding of the sums stays a small multiple of 2^-24 times that
+// (the plain factored form a*sum q x - b*sum x can cancel: a sub-block whose
+// weights are all zero, d*sc*q = dmin*m, leaves rounding noise where the
+// exact answer is 0).  q - c is formed per weight on the fp16 patterns, so
+// every product stays exact; e is one fp32 fma (one rounding, the same value
+// the dequantised weight of quant c takes).  Units: a = d*sc*2^-24, e times
+// 2^-24, as the patterns; c is an exact small integer in fp32.
+// ---------------------------------------------------------------------------
+struct KShift {
+    float a, e;      // d*sc*2^-24, (a*c - dmin*m*2^-24) rounded once
+    uint32_t neg;    // the fp16 pair (-s*c*2^-24, -s*c*2^-24) to add to patterns holding s*q
+};
+
+template <int QMAX, int S>
+__device__ __forceinline__ KShift k_shift(float d, float dmin, float sc_p, float m_p) {
+    KShift k;
+    k.a = d * sc_p;                 // exact: 11 x 6 significant bits
+    const float b = dmin * m_p;     // exact
+    // a = 0 gives b * inf (inf or NaN): fmaxf takes 0 for NaN, the clamp
+    // handles inf; with a = 0 the quant sum is multiplied by 0 anyway
+    const float c = fminf(fmaxf(rintf(b * __builtin_amdgcn_rcpf(k.a)), 0.f), (float)QMAX);
+    k.e = __builtin_fmaf(k.a, c, -b);
+    const float nc = c * (-(float)S * 0x1p-24f);  // exact, a fp16 denormal
+    k.neg = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(nc, nc));
+    return k;
+}
+
+// Q6_K: w = d*sc*(q - 32); the patterns of quarters 0-1 hold q*2^-24, those
+// of quarters 2-3 16q*2^-24, so q - 32 is one packed add of these constants.
+constexpr uint32_t Q6_OFF_LO = 0x80208020u;  // fp16 pair (-32*2^-24, -32*2^-24)
+constexpr uint32_t Q6_OFF_HI = 0x82008200u;  // fp16 pair (-512*2^-24, -512*2^-24)
+
 __device__ __forceinline__ float f16_lo(uint32_t v) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
 }
@@ -145,6 +189,12 @@ __device__ __forceinline__ uint32_t ld2(const uint8_t *p) {
     if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
     else return *reinterpret_cast<const uint16_t *>(p);
 }
+
+// The loads of a unit leave together: the scheduler may not sink any of them
+// into the arithmetic that follows (under register pressure it otherwise
+// spreads them out and serialises their memory latencies: Q6_K 5120 x 17408
+// measured 25.4 us without this barrier, 18.7 us with it).
+__device__ __forceinline__ void issue_together() { __builtin_amdgcn_sched_barrier(0); }
 
 __device__ __forceinline__ uint32_t word(const uint4 &v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -207,6 +257,7 @@ template <> struct Unit<Q4_K> {
         h = ld16<NT>(base + (off + o.h));
         a = ld16<NT>(base + (off + o.a));
         b = ld16<NT>(base + (off + o.b));
+        issue_together();
     }
     __device__ __forceinline__ uint4 header() const { return h; }
     __device__ __forceinline__ uint32_t qword(int i) const { return i < 4 ? word(a, i) : word(b, i - 4); }
@@ -231,6 +282,7 @@ template <> struct Unit<Q5_K> {
         qh1 = ld16<NT>(base + (off + o.qh1));
         a = ld16<NT>(base + (off + o.a));
         b = ld16<NT>(base + (off + o.b));
+        issue_together();
     }
     __device__ __forceinline__ uint4 header() const { return h; }
     __device__ __forceinline__ uint32_t qword(int i) const { return i < 4 ? word(a, i) : word(b, i - 4); }
@@ -263,6 +315,7 @@ template <> struct Unit<Q6_K> {
         if constexpr (L == PLANAR) sc = make_uint2(ld4<NT>(base + (off + o.sc)), 0u);
         else sc = ld8<NT>(base + (off + o.sc));
         d = ld2<NT>(base + (off + o.d));
+        issue_together();
     }
     __device__ __forceinline__ void patterns(int i, int /*q*/, uint32_t p[8]) const {
         const uint32_t A = word(a, i), B = word(b, i), C = word(c, i);

@@ -11,12 +11,16 @@
 // dequant_kernel: the same unit loads and unpacking, writing fp32 weights --
 //                the bit-exact check path.
 //
-// Factored form.  For a Q4_K/Q5_K sub-block j of 32 weights,
-//     sum_i w_i x_i = d*sc_j * sum_i q_i x_i  -  dmin*m_j * sum_i x_i ,
-// and for a Q6_K group g of 16 weights,
-//     sum_i w_i x_i = d*sc_g * (sum_i q_i x_i - 32 * sum_i x_i).
-// The group sums of x are formed once per lane (x stays in registers), so
-// the per-weight work is the quant unpack and one half of a dot2.
+// Shifted form.  For a Q4_K/Q5_K sub-block j of 32 weights (KShift in
+// qk_format.h), with a = d*sc_j, b = dmin*m_j and an integer c_j near b/a,
+//     sum_i w_i x_i = a * sum_i (q_i - c_j) x_i  +  (a*c_j - b) * sum_i x_i ,
+// and for a Q6_K group g of 16 weights
+//     sum_i w_i x_i = d*sc_g * sum_i (q_i - 32) x_i ;
+// q - c is one packed fp16 add per pair of weights, every product is exact,
+// and no term exceeds a few times its weight's share of sum |w x|, so the
+// fp32 sums cannot cancel.  The sub-block sums of x are formed once per lane
+// (x stays in registers), so the per-weight work is the quant unpack, half a
+// packed add and half a dot2.
 #include "qk_format.h"
 #include "qk_epilogue.h"
 #include "qk_launch.h"
@@ -35,13 +39,13 @@ constexpr int WG = 256;  // threads per workgroup
 //              xr[16+2i], xr[17+2i]  = the same for the high sub-block
 //              (pair A = weights (4i, 4i+2), pair B = (4i+1, 4i+3))
 //   Q6_K:      xr[8t+2i], xr[8t+2i+1] = pairs A, B of word i of quarter t
-// plus the fp32 sums of x per scale group (fixed summation order):
-//   Q4_K/Q5_K: xsum[0..1] per sub-block;  Q6_K: xsum[0..3] per quarter.
+// plus, for Q4_K/Q5_K, the fp32 sums of x per sub-block, xsum[0..1] (fixed
+// summation order; Q6_K needs none: its -32 is taken on the patterns).
 // ---------------------------------------------------------------------------
 template <int T>
 struct XReg {
     uint32_t xr[32];
-    float xsum[4];
+    float xsum[2];
 };
 
 // a from the lane that the DPP control names (a full-rate VALU move)
@@ -128,7 +132,7 @@ __device__ __forceinline__ void load_x_q6(XReg<Q6_K> &X, const uint16_t *__restr
         v[2 * t + 1] = xv[(k >> 3) + 1];
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) X.xsum[t] = x_pairs16(v[2 * t], v[2 * t + 1], X.xr + 8 * t);
+    for (int t = 0; t < 4; ++t) (void)x_pairs16(v[2 * t], v[2 * t + 1], X.xr + 8 * t);
 }
 
 // The lane's x (Q4_K/Q5_K) from the staged copy; ul is the unit index within
@@ -148,6 +152,8 @@ __device__ __forceinline__ void load_x(XReg<T> &X, const uint8_t *xl, int ul) {
     X.xsum[1] = sums.y;
 }
 
+// Q6_K: sum over quarter t of sc_t * sum (q - 32) x, the -32 taken on the
+// patterns (every product exact, no cancellation between two sums).
 template <int L>
 __device__ __forceinline__ float unit_dot_q6(const Unit<Q6_K> &U, int q, const XReg<Q6_K> &X) {
     float R[4] = {0.f, 0.f, 0.f, 0.f};
@@ -157,15 +163,16 @@ __device__ __forceinline__ float unit_dot_q6(const Unit<Q6_K> &U, int q, const X
         U.patterns(i, q, p);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            R[t] = dot2(p[2 * t], X.xr[8 * t + 2 * i], R[t]);
-            R[t] = dot2(p[2 * t + 1], X.xr[8 * t + 2 * i + 1], R[t]);
+            const uint32_t off = t < 2 ? Q6_OFF_LO : Q6_OFF_HI;
+            R[t] = dot2(padd(p[2 * t], off), X.xr[8 * t + 2 * i], R[t]);
+            R[t] = dot2(padd(p[2 * t + 1], off), X.xr[8 * t + 2 * i + 1], R[t]);
         }
     }
     float acc = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        const float k = t < 2 ? 0x1p24f : 0x1p20f;  // patterns hold s*q*2^-24, s = 1 or 16
-        acc += (float)U.template scale<L>(t, q) * (R[t] * k - 32.f * X.xsum[t]);
+        const float k = t < 2 ? 0x1p24f : 0x1p20f;  // patterns hold s*(q-32)*2^-24, s = 1 or 16
+        acc = __builtin_fmaf((float)U.template scale<L>(t, q), R[t] * k, acc);
     }
     return f16_lo(U.d) * acc;
 }
@@ -176,35 +183,35 @@ __device__ __forceinline__ float unit_dot(const Unit<T> &U, int q, const KScaleS
     if constexpr (T == Q6_K) {
         return unit_dot_q6<L>(U, q, X);
     } else {
+        // The shifted form of each sub-block (KShift).  Units of 2^-48: the
+        // 6-bit sc / m read as fp16 bit patterns are sc*2^-24 / m*2^-24, the
+        // patterns hold s*(q - c)*2^-24 (s = 1 low, 16 high sub-block) and the
+        // x sums are held times 2^-24.
+        constexpr int QMAX = T == Q4_K ? 15 : 31;
+        const uint4 h = U.header();
+        const KScales s = k_scales(h, sel);
+        const float d = f16_lo(h.x), dmin = f16_hi(h.x);
+        auto pat = [](uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)v); };
+        const KShift kL = k_shift<QMAX, 1>(d, dmin, pat(s.sc_lo), pat(s.m_lo));
+        const KShift kH = k_shift<QMAX, 16>(d, dmin, pat(s.sc_hi), pat(s.m_hi));
         uint32_t p[4];
         U.patterns(0, q, p);
-        float aL = dot2(p[0], X.xr[0], 0.f), aH = dot2(p[2], X.xr[16], 0.f);
-        aL = dot2(p[1], X.xr[1], aL);
-        aH = dot2(p[3], X.xr[17], aH);
+        float aL = dot2(padd(p[0], kL.neg), X.xr[0], 0.f), aH = dot2(padd(p[2], kH.neg), X.xr[16], 0.f);
+        aL = dot2(padd(p[1], kL.neg), X.xr[1], aL);
+        aH = dot2(padd(p[3], kH.neg), X.xr[17], aH);
 #pragma unroll
         for (int i = 1; i < 8; ++i) {
             U.patterns(i, q, p);
-            aL = dot2(p[0], X.xr[2 * i], aL);
-            aL = dot2(p[1], X.xr[2 * i + 1], aL);
-            aH = dot2(p[2], X.xr[16 + 2 * i], aH);
-            aH = dot2(p[3], X.xr[17 + 2 * i], aH);
+            aL = dot2(padd(p[0], kL.neg), X.xr[2 * i], aL);
+            aL = dot2(padd(p[1], kL.neg), X.xr[2 * i + 1], aL);
+            aH = dot2(padd(p[2], kH.neg), X.xr[16 + 2 * i], aH);
+            aH = dot2(padd(p[3], kH.neg), X.xr[17 + 2 * i], aH);
         }
-        // In units of 2^-48.  aL = 2^-24 * sum q*x (low sub-block), aH = 2^-20 * sum q*x
-        // (high: patterns hold 16q); the 6-bit sc / m read as fp16 bit patterns
-        // are sc*2^-24 / m*2^-24, and the x sums are held times 2^-24.  Every
-        // half x float product below is one mixed-precision instruction.
-        const uint4 h = U.header();
-        const KScales s = k_scales(h, sel);
-        const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)h.x);
-        const _Float16 dmin = __builtin_bit_cast(_Float16, (uint16_t)(h.x >> 16));
-        // (fma with a +0 addend is not a multiply for the compiler: it stays one
-        // mixed-precision fma, with the half operand converted for free)
-        auto pat = [](uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)v); };
-        float acc = __builtin_fmaf(pat(s.sc_lo), aL, 0.f);
-        acc = __builtin_fmaf(pat(s.sc_hi), aH * 0x1p-4f, acc);
-        float mn = __builtin_fmaf(pat(s.m_lo), X.xsum[0], 0.f);
-        mn = __builtin_fmaf(pat(s.m_hi), X.xsum[1], mn);
-        return __builtin_fmaf((float)d, acc, -__builtin_fmaf((float)dmin, mn, 0.f));
+        // aL = 2^-24 sum (q-c) x, aH = 2^-20 sum (q-c) x
+        float acc = kL.e * X.xsum[0];
+        acc = __builtin_fmaf(kH.e, X.xsum[1], acc);
+        acc = __builtin_fmaf(kL.a, aL, acc);
+        return __builtin_fmaf(kH.a * 0x1p-4f, aH, acc);
     }
 }
 
@@ -757,7 +764,10 @@ static hipError_t launch1(const void *W, const void *x, void *y, int64_t N, int6
     return hipGetLastError();
 }
 
-// Two units in flight per lane, one for one-row rounds.
+// Units in flight per lane (the ring of a straight-line round): one for
+// one-row rounds, otherwise two (three spill under the 128-register bound and
+// measured 20-40% slower).
+constexpr int RING = 2;
 template <int T, int L, bool PAIR>
 static hipError_t gemv1_dispatch(const void *W, const void *x, void *y, int64_t N, int64_t K,
                                  const Epilogue &ep, hipStream_t st) {
@@ -767,12 +777,12 @@ static hipError_t gemv1_dispatch(const void *W, const void *x, void *y, int64_t 
     constexpr bool NT = L == PLANAR;
     switch (geo.RL) {
     case 1: return launch1<T, L, 1, 1, NT, PAIR>(W, x, y, N, K, geo, ep, st);
-    case 2: if constexpr (T != Q6_K || L == PLANAR) return launch1<T, L, 2, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
-    case 3: if constexpr (T == Q5_K) return launch1<T, L, 3, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
-    case 4: if constexpr (T != Q6_K) return launch1<T, L, 4, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
-    case 6: if constexpr (T == Q4_K) return launch1<T, L, 6, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
-    case 8: if constexpr (T == Q4_K) return launch1<T, L, 8, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
-    case 12: if constexpr (T == Q4_K) return launch1<T, L, 12, 2, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 2: if constexpr (T != Q6_K || L == PLANAR) return launch1<T, L, 2, RING, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 3: if constexpr (T == Q5_K) return launch1<T, L, 3, RING, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 4: if constexpr (T != Q6_K) return launch1<T, L, 4, RING, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 6: if constexpr (T == Q4_K) return launch1<T, L, 6, RING, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 8: if constexpr (T == Q4_K) return launch1<T, L, 8, RING, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 12: if constexpr (T == Q4_K) return launch1<T, L, 12, RING, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
     default: break;
     }
     return hipErrorInvalidValue;

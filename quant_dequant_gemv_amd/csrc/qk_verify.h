@@ -17,13 +17,15 @@
 //   the 4 lanes 4b..4b+3, lane 4b+j supplies row j of A and column j of B and
 //   receives D[0..3][j].  Here block b is one unit column (64 weights of a
 //   superblock) of four rows, lane j being row j of a row quad:
-//     B column j = the quant patterns of row j for one 32-bit quant word
-//                  (exact fp16 values s*q*2^-24, weights (l, l+2, l+1, l+3)),
+//     B column j = the quant patterns of row j for one 32-bit quant word,
+//                  shifted by the row's integer c of the scale group (exact
+//                  fp16 values s*(q-c)*2^-24, weights (l, l+2, l+1, l+3);
+//                  c = 32 for Q6_K, see KShift in qk_format.h),
 //     A row i    = x column 4*cb + i at the same four weights, held in
 //                  registers by lane i of the block for the whole segment,
 //     D[i][j]    = sum over the word of x_i * q_j.
 //   D is accumulated over a scale group, then each lane scales its own row's
-//   four columns by d*sc (and subtracts the min term) in fp32.
+//   four columns by d*sc (and adds (d*sc*c - dmin*m) times the x sums) in fp32.
 // A wave covers 16 consecutive unit columns of a row quad; the unit columns
 // of one K segment form a phase of useg/16 waves, and P phases take the row
 // quads of the workgroup in turn.  Per row quad the 16 blocks of a wave are
@@ -325,6 +327,9 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
                     for (int i = 0; i < 4; ++i) {
                         uint32_t pt[8];
                         Un.patterns(i, q, pt);
+                        // q - 32 on the patterns (exact): no sum of x to subtract
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) pt[t] = padd(pt[t], t < 4 ? Q6_OFF_LO : Q6_OFF_HI);
 #pragma unroll
                         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -338,24 +343,22 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
                         for (int i = 0; i < 4; ++i) {
                             float a = 0.f;
 #pragma unroll
-                            for (int t = 0; t < 4; ++t)  // patterns hold q*2^-24 (t < 2) or 16q*2^-24
-                                a = __builtin_fmaf(f[t],
-                                                   Dq[cb][t][i] * (t < 2 ? 0x1p24f : 0x1p20f) - 32.f * xsum[4 * cb + i][t],
-                                                   a);
+                            for (int t = 0; t < 4; ++t)  // patterns hold (q-32)*2^-24 (t < 2) or 16(q-32)*2^-24
+                                a = __builtin_fmaf(f[t], Dq[cb][t][i] * (t < 2 ? 0x1p24f : 0x1p20f), a);
                             val[4 * cb + i] = a;
                         }
                 } else {
-                    // units of 2^-48, as in the one-column kernel: sc and m read as fp16
-                    // patterns are sc*2^-24 and m*2^-24; the x sums are held times 2^-24
+                    // the shifted form of the one-column kernel (KShift), units of
+                    // 2^-48: sc and m read as fp16 patterns are sc*2^-24 and m*2^-24,
+                    // the patterns hold s*(q - c)*2^-24, the x sums are held times 2^-24
+                    constexpr int QMAX = T == Q4_K ? 15 : 31;
                     const uint4 h = Un.header();
                     const KScales sk = k_scales(h, sel);
                     auto pat = [](uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)v); };
-                    const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)h.x);
-                    const float dmin = (float)__builtin_bit_cast(_Float16, (uint16_t)(h.x >> 16));
-                    const float fl = __builtin_fmaf(d, pat(sk.sc_lo), 0.f);
-                    const float fh = __builtin_fmaf(d, pat(sk.sc_hi), 0.f) * 0x1p-4f;
-                    const float ml = __builtin_fmaf(dmin, pat(sk.m_lo), 0.f);
-                    const float mh = __builtin_fmaf(dmin, pat(sk.m_hi), 0.f);
+                    const float d = f16_lo(h.x), dmin = f16_hi(h.x);
+                    const KShift kL = k_shift<QMAX, 1>(d, dmin, pat(sk.sc_lo), pat(sk.m_lo));
+                    const KShift kH = k_shift<QMAX, 16>(d, dmin, pat(sk.sc_hi), pat(sk.m_hi));
+                    const float fh = kH.a * 0x1p-4f;
                     float4_t Dl[NCB], Dh[NCB];
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb) Dl[cb] = Dh[cb] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -363,6 +366,10 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
                     for (int i = 0; i < 8; ++i) {
                         uint32_t pt[4];
                         Un.patterns(i, q, pt);
+                        pt[0] = padd(pt[0], kL.neg);
+                        pt[1] = padd(pt[1], kL.neg);
+                        pt[2] = padd(pt[2], kH.neg);
+                        pt[3] = padd(pt[3], kH.neg);
 #pragma unroll
                         for (int cb = 0; cb < NCB; ++cb) {
                             Dl[cb] = mfma4(xr[cb][2 * i], xr[cb][2 * i + 1], pt[0], pt[1], Dl[cb]);
@@ -373,8 +380,8 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
                     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const float mn = __builtin_fmaf(ml, xsum[4 * cb + i][0], mh * xsum[4 * cb + i][1]);
-                            val[4 * cb + i] = __builtin_fmaf(fl, Dl[cb][i], __builtin_fmaf(fh, Dh[cb][i], -mn));
+                            const float ex = __builtin_fmaf(kL.e, xsum[4 * cb + i][0], kH.e * xsum[4 * cb + i][1]);
+                            val[4 * cb + i] = __builtin_fmaf(kL.a, Dl[cb][i], __builtin_fmaf(fh, Dh[cb][i], ex));
                         }
                 }
                 if (p + DD < RL) load_quad(buf[p % DD], p + DD);

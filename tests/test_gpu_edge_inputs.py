@@ -1,0 +1,220 @@
+"""GPU parity on inputs the seeded generator never produces, through the C ABI.
+
+* Scales.  The format's fp16 d / dmin (design-doc prompt of the T4 dossier,
+  QUANTIZATION MIX: "half d; half dmin") admit every finite fp16 value: here
+  every finite bit pattern -- +-0, subnormals, negatives, 65504 -- is the d
+  (and, permuted, the dmin) of some superblock; Q6_K scales take every int8
+  value -128..127.  Dequantisation must be bit-exact and every GEMV row within
+  the 1e-4 * sum|w x| bound, with rows grouped by the magnitude of their
+  scales so that the subnormal rows are measured on their own.
+* Cancellation.  A valid superblock can have weights that are exactly zero
+  with nonzero fields: constant q with d*sc*q = dmin*m (Q4_K, Q5_K) or q = 32
+  (Q6_K).  Then sum|w x| = 0 and the result must be exactly 0; rows where a
+  few quants are moved off the cancelling value must meet the bound.  x is
+  N(0, 1), or spread over the whole fp16 range.  Every entry point that
+  computes a dot: one column (GGUF and PLANAR rows), the verify form at
+  2 / 4 / 8 columns, the column groups at 17, the merged launch, the residual
+  and SwiGLU epilogues.
+
+Expected values come from the CPU oracle only.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import assert_row_bound, dev, gpu_dequant, gpu_gemv, needs_gpu, same_f32
+from kquant_pack import half_bits, make_k_block, make_q6_block
+from quant_dequant_gemv_amd import binding, synth
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+Q4, Q5, Q6 = synth.Q4_K, synth.Q5_K, synth.Q6_K
+NAMES = {Q4: "Q4_K", Q5: "Q5_K", Q6: "Q6_K"}
+BB = synth.BLOCK_BYTES
+
+
+def finite_f16_patterns_by_magnitude() -> np.ndarray:
+    """Every finite fp16 bit pattern (63488 of them, +-0 included), ordered by
+    magnitude (a pattern and its negation adjacent)."""
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    b = b[(b & 0x7C00) != 0x7C00]
+    mag = b & 0x7FFF
+    return b[np.lexsort((b >> 15, mag))]
+
+
+def scale_sweep_tensor(qt, rng):
+    """Superblocks whose d (and dmin) run over every finite fp16 pattern.
+
+    Row r holds 128 superblocks with patterns of neighbouring magnitude; dmin
+    is a different permutation of the same row's patterns.  Quants and 6-bit
+    scales are uniform random bytes; Q6_K int8 scales uniform over -128..127."""
+    pats = finite_f16_patterns_by_magnitude()
+    per_row = 128
+    N = len(pats) // per_row
+    pats = pats[:N * per_row].reshape(N, per_row)
+    K = 256 * per_row
+    nsb = N * per_row
+    raw = np.frombuffer(rng.bytes(nsb * BB[qt]), dtype=np.uint8).copy().reshape(N, per_row, BB[qt])
+    d = pats
+    if qt == Q6:
+        raw[:, :, 208:210] = d.view(np.uint8).reshape(N, per_row, 2)
+        raw[:, :, 192:208] = rng.integers(-128, 128, size=(N, per_row, 16), dtype=np.int16).astype(np.int8).view(np.uint8)
+    else:
+        dmin = np.stack([row[rng.permutation(per_row)] for row in pats])
+        raw[:, :, 0:2] = d.view(np.uint8).reshape(N, per_row, 2)
+        raw[:, :, 2:4] = dmin.view(np.uint8).reshape(N, per_row, 2)
+    return raw.reshape(N, per_row * BB[qt]), N, K
+
+
+@pytest.fixture(scope="module", params=[Q4, Q5, Q6], ids=lambda t: NAMES[t])
+def sweep(request):
+    qt = request.param
+    W, N, K = scale_sweep_tensor(qt, np.random.default_rng(4000 + qt))
+    return qt, W, N, K
+
+
+def test_scale_sweep_covers_every_class(sweep):
+    qt, W, N, K = sweep
+    off = 208 if qt == Q6 else 0
+    d = W.reshape(-1, BB[qt])[:, off:off + 2].copy().view(np.uint16).ravel()
+    assert len(np.unique(d)) == 63488  # every finite fp16 pattern once
+    v = d.view(np.float16).astype(np.float32)
+    assert (v == 0).sum() == 2 and (np.signbit(v) & (v == 0)).sum() == 1  # +0 and -0
+    assert ((np.abs(v) > 0) & (np.abs(v) < 2.0 ** -14)).sum() == 2 * 1023  # subnormals of both signs
+    assert np.abs(v).max() == 65504.0 and (v < 0).sum() > 31000
+    if qt == Q6:
+        sc = W.reshape(-1, 210)[:, 192:208].view(np.int8)
+        assert sc.min() == -128 and sc.max() == 127
+
+
+def test_scale_sweep_dequant_bit_exact(sweep):
+    qt, W, N, K = sweep
+    assert same_f32(gpu_dequant(qt, W, N, K), oracle.dequant(qt, W, K))
+
+
+@pytest.mark.parametrize("ncols", [1, 4, 8])
+def test_scale_sweep_gemv_rows(sweep, ncols):
+    qt, W, N, K = sweep
+    x = synth.activations(K, ncols, 4100 + ncols)
+    y = gpu_gemv(qt, W, x, N, K)
+    y_ref, S = oracle.gemv(qt, W, x, K)
+    assert_row_bound(y, y_ref, S, f"{NAMES[qt]} scale sweep ncols={ncols}")
+
+
+def test_scale_sweep_planar_rows(sweep):
+    qt, W, N, K = sweep
+    x = synth.activations(K, 1, 4200)
+    Wd = dev(W.reshape(-1))
+    Wp = binding.repack(qt, Wd, N, K)
+    yp = binding.gemv(qt | binding.PLANAR, Wp, dev(x), N, K)
+    torch.cuda.synchronize()
+    y_ref, S = oracle.gemv(qt, W, x, K)
+    assert_row_bound(yp.cpu().numpy(), y_ref, S, f"{NAMES[qt]} scale sweep PLANAR")
+
+
+# ---------------------------------------------------------------- cancellation
+
+def cancelling_rows(qt, N, K, rng, moved=0.0):
+    """N rows whose weights are exactly zero (moved = 0) or have a fraction
+    `moved` of their quants one step off the cancelling value."""
+    rows = []
+    for _ in range(N):
+        blocks = []
+        for _ in range(K // 256):
+            if qt == Q6:
+                q = np.full(256, 32)
+                d = float(2.0 ** rng.integers(-20, 8)) * float(rng.choice([-1, 1]))
+                sc = rng.integers(-128, 128, 16)
+                flip = rng.random(256) < moved
+                q = np.where(flip, q + rng.choice([-1, 1], 256), q)
+                blocks.append(make_q6_block(half_bits(d), sc, q))
+                continue
+            qmax = 15 if qt == Q4 else 31
+            k = int(rng.integers(1, 5))  # dmin = k * d
+            d = float(2.0 ** rng.integers(-22, 6)) * float(rng.choice([-1, 1]))
+            sc, m, qc = [], [], []
+            while len(sc) < 8:
+                a, c = int(rng.integers(1, 64)), int(rng.integers(0, qmax + 1))
+                if (a * c) % k == 0 and a * c // k <= 63:
+                    sc.append(a)
+                    qc.append(c)
+                    m.append(a * c // k)
+            q = np.repeat(qc, 32)
+            flip = rng.random(256) < moved
+            q = np.where(flip, np.clip(q + rng.choice([-1, 1], 256), 0, qmax), q)
+            blocks.append(make_k_block(qt, half_bits(d), half_bits(d * k), sc, m, q))
+        rows.append(np.concatenate(blocks))
+    return np.stack(rows)
+
+
+def wide_x(K, ncols, rng):
+    """fp16 x spread over the whole range (subnormal to ~3e4), random signs."""
+    v = rng.standard_normal((K, ncols)) * np.exp2(rng.uniform(-24, 15, (K, ncols)))
+    return np.clip(v, -6e4, 6e4).astype(np.float16)
+
+
+CANCEL = [(qt, moved) for qt in (Q4, Q5, Q6) for moved in (0.0, 0.05)]
+
+
+@pytest.fixture(scope="module", params=CANCEL, ids=lambda p: f"{NAMES[p[0]]}-{'exact' if p[1] == 0 else 'near'}")
+def cancel(request):
+    qt, moved = request.param
+    rng = np.random.default_rng(4300 + qt + int(100 * moved))
+    N, K = 70, 1280
+    W = cancelling_rows(qt, N, K, rng, moved)
+    if moved == 0:
+        assert not oracle.dequant(qt, W, K).any()  # every weight is zero
+    return qt, W, N, K, moved
+
+
+def _xs(K, ncols, seed):
+    rng = np.random.default_rng(seed)
+    return {"normal": synth.activations(K, ncols, seed), "wide": wide_x(K, ncols, rng)}
+
+
+@pytest.mark.parametrize("ncols", [1, 2, 4, 8, 17])
+def test_cancelling_rows_gemv(cancel, ncols):
+    qt, W, N, K, moved = cancel
+    for name, x in _xs(K, ncols, 4400 + ncols).items():
+        y = gpu_gemv(qt, W, x, N, K)
+        y_ref, S = oracle.gemv(qt, W, x, K)
+        if moved == 0:
+            assert (S == 0).all() and (y == 0).all(), f"{NAMES[qt]} zero rows, x {name}: y != 0"
+        assert_row_bound(y, y_ref, S, f"{NAMES[qt]} cancelling moved={moved} ncols={ncols} x {name}")
+
+
+def test_cancelling_rows_planar_and_batch(cancel):
+    qt, W, N, K, moved = cancel
+    x = _xs(K, 1, 4500)["wide"]
+    y_ref, S = oracle.gemv(qt, W, x, K)
+    Wd, xd = dev(W.reshape(-1)), dev(x)
+    Wp = binding.repack(qt, Wd, N, K)
+    yp = binding.gemv(qt | binding.PLANAR, Wp, xd, N, K)
+    half = N // 2
+    yb = binding.gemv_batch([(qt, Wd[:half * W.shape[1]], xd, half, K),
+                             (qt | binding.PLANAR, Wp[half * binding.qk_row_bytes(qt | binding.PLANAR, K):], xd,
+                              N - half, K)])
+    torch.cuda.synchronize()
+    assert_row_bound(yp.cpu().numpy(), y_ref, S, f"{NAMES[qt]} cancelling PLANAR")
+    yb = np.concatenate([t.cpu().numpy() for t in yb])
+    assert_row_bound(yb, y_ref, S, f"{NAMES[qt]} cancelling batch")
+
+
+@pytest.mark.parametrize("ncols", [1, 8])
+def test_cancelling_rows_epilogues(cancel, ncols):
+    qt, W, N, K, moved = cancel
+    x = _xs(K, ncols, 4600 + ncols)["wide"]
+    y_ref, S = oracle.gemv(qt, W, x, K)
+    res = np.random.default_rng(4700).standard_normal((N, ncols)).astype(np.float32)
+    Wd, xd = dev(W.reshape(-1)), dev(x)
+    y = binding.gemv_ex(qt, Wd, xd, N, K, residual=dev(res)).cpu().numpy()
+    tol = oracle.residual_bound(y_ref + res, S)
+    assert oracle.within(y, y_ref + res, tol).all(), f"{NAMES[qt]} residual on cancelling rows"
+    if moved == 0:
+        assert np.array_equal(y, res), "residual + exact zero must be the residual"
+    ys = binding.gemv_swiglu(qt, Wd, Wd, xd, N, K).cpu().numpy()
+    yr, g, Sg, u, Su = oracle.swiglu(qt, W, W, x, K)
+    assert oracle.within(ys, yr, oracle.swiglu_bound(yr, g, Sg, u, Su)).all(), f"{NAMES[qt]} SwiGLU cancelling"
+    if moved == 0:
+        assert not ys.any()

@@ -118,9 +118,8 @@ def test_swiglu_same_tensor_and_planar(qt, ncols):
 
 
 @pytest.mark.parametrize("ncols", [1, 2, 8])
-def test_swiglu_ffn_shape_sampled(ncols):
-    """The FFN gate/up pair at its real shape (Q4_K 17408 x 5120), sampled rows
-    (both ends of many workgroups' row ranges)."""
+def test_swiglu_ffn_shape_all_rows(ncols):
+    """The FFN gate/up pair at its real shape (Q4_K 17408 x 5120), every row."""
     N, K = 17408, 5120
     Wg = synth.superblocks(Q4, N, K, 2)
     Wu = synth.superblocks(Q4, N, K, 3)
@@ -128,15 +127,12 @@ def test_swiglu_ffn_shape_sampled(ncols):
     y = binding.gemv_swiglu(Q4, dev(Wg.reshape(-1)), dev(Wu.reshape(-1)), dev(x), N, K)
     torch.cuda.synchronize()
     y = y.cpu().numpy()
-    edges = np.array([b * N // 256 for b in range(0, 256, 5)])
-    rows = np.unique(np.clip(np.concatenate([[0, N - 1], edges, edges - 1, edges + 67]), 0, N - 1))
-    y_ref, g, Sg, u, Su = oracle.swiglu(Q4, Wg[rows], Wu[rows], x, K)
-    _assert_within(y[rows], y_ref, oracle.swiglu_bound(y_ref, g, Sg, u, Su), f"ffn gate/up ncols={ncols}")
-    assert np.isfinite(y).all()
+    y_ref, g, Sg, u, Su = oracle.swiglu(Q4, Wg, Wu, x, K)
+    _assert_within(y, y_ref, oracle.swiglu_bound(y_ref, g, Sg, u, Su), f"ffn gate/up ncols={ncols}")
 
 
-def test_residual_down_shape_sampled():
-    """FFN down (Q6_K 5120 x 17408) with its residual, in place, sampled rows."""
+def test_residual_down_shape_all_rows():
+    """FFN down (Q6_K 5120 x 17408) with its residual, in place, every row."""
     N, K = 5120, 17408
     W = synth.superblocks(Q6, N, K, 4)
     x = synth.activations(K, 1, 4)
@@ -145,9 +141,8 @@ def test_residual_down_shape_sampled():
     binding.gemv_ex(Q6, dev(W.reshape(-1)), dev(x), N, K, residual=y, out=y)
     torch.cuda.synchronize()
     y = y.cpu().numpy().reshape(N, 1)
-    rows = np.unique(np.concatenate([[0, N - 1], np.arange(0, N, 37)]))
-    y_ref, S = oracle.gemv_residual(Q6, W[rows], x, K, r[rows])
-    _assert_within(y[rows], y_ref, oracle.residual_bound(y_ref, S), "ffn down + residual")
+    y_ref, S = oracle.gemv_residual(Q6, W, x, K, r)
+    _assert_within(y, y_ref, oracle.residual_bound(y_ref, S), "ffn down + residual")
 
 
 @pytest.mark.parametrize("qt,N,K", [(Q4, 17408, 5120), (Q4, 200000, 256), (Q5, 120000, 512)],

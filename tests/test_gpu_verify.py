@@ -61,27 +61,24 @@ def test_verify_deterministic_and_matches_single_column(qt):
 
 
 @pytest.mark.parametrize("ncols", [2, 4, 8])
-def test_verify_full_shape_sampled(ncols):
+def test_verify_full_shape_all_rows(ncols):
     c = synth.VERIFY
     N, K = c["N"], c["K"]
     W = synth.superblocks(c["qtype"], N, K, c["seed"])
     x = synth.activations(K, ncols, c["seed"])
     y = gpu_gemv(c["qtype"], W, x, N, K)
-    rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(ncols).integers(0, N, 160)]))
-    y_ref, S = oracle.gemv(c["qtype"], W[rows], x, K)
-    assert_row_bound(y[rows], y_ref, S, f"verify {N}x{K} ncols={ncols}")
-    assert np.isfinite(y).all()
+    y_ref, S = oracle.gemv(c["qtype"], W, x, K)
+    assert_row_bound(y, y_ref, S, f"verify {N}x{K} ncols={ncols}")
 
 
 @pytest.mark.parametrize("case", synth.MIXED, ids=lambda c: c["name"])
-def test_verify_mixed_shapes_sampled(case):
+def test_verify_mixed_shapes_all_rows(case):
     N, K, qt = case["N"], case["K"], case["qtype"]
     W = synth.superblocks(qt, N, K, case["seed"])
     x = synth.activations(K, 4, case["seed"])
     y = gpu_gemv(qt, W, x, N, K)
-    rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(1).integers(0, N, 96)]))
-    y_ref, S = oracle.gemv(qt, W[rows], x, K)
-    assert_row_bound(y[rows], y_ref, S, f"{case['name']} ncols=4")
+    y_ref, S = oracle.gemv(qt, W, x, K)
+    assert_row_bound(y, y_ref, S, f"{case['name']} ncols=4")
 
 
 # Row counts at which each workgroup's quads (4 rows) per lane take straight-
