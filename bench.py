@@ -494,6 +494,37 @@ def run_stream(torch, launcher, warm=2, only=None, tokens=1):
     def one_token_fused_planar(st=None):
         run_fused(fused_planar, sh if st is None else st)
 
+    # the same fused steps as one chain launch (qk_gemv_chain): one step per
+    # group, a barrier between steps, each step's first weights issued before
+    # its wait
+    def chain_of(use_planar):
+        steps = []
+        for idx in groups:
+            names = [entries[i]["name"] for i in idx]
+            ws = [wp(i) if use_planar else (tensors[i]["qtype"], tensors[i]["W"][0]) for i in idx]
+            wt = [(q, planar_w[i] if use_planar else tensors[i]["W"][0]) for (q, _), i in zip(ws, idx)]
+            if names == ["ffn_gate", "ffn_up"]:
+                g = tensors[idx[0]]
+                steps.append([dict(qtype=wt[0][0], W=wt[0][1], W2=wt[1][1], x=g["x"], y=g["y"], N=g["N"],
+                                   K=g["K"])])
+            elif len(idx) == 1 and names[0] in ("ssm_out", "attn_output", "ffn_down"):
+                t = tensors[idx[0]]
+                steps.append([dict(qtype=wt[0][0], W=wt[0][1], x=t["x"], y=hres, residual=hres, N=t["N"],
+                                   K=t["K"])])
+            else:
+                steps.append([dict(qtype=q, W=w, x=tensors[i]["x"], y=tensors[i]["y"], N=tensors[i]["N"],
+                                   K=tensors[i]["K"]) for (q, w), i in zip(wt, idx)])
+        return binding.Chain(steps)
+
+    chains = {"chain": chain_of(False), "chain_planar": chain_of(True)}
+
+    def chain_token(name):
+        ch = chains[name]
+
+        def run(st=None):
+            ch.run(stream=sh if st is None else st)
+        return run
+
     def one_token_fused(st=None):
         h = sh if st is None else st
         for kind, a in fused:
@@ -547,10 +578,11 @@ def run_stream(torch, launcher, warm=2, only=None, tokens=1):
         # one variant, `tokens` tokens back to back after a warm-up (for a
         # kernel trace: the last tokens * launches dispatches are the timed ones)
         fns = {"launches": one_token, "batched": one_token_batched, "fused": one_token_fused,
-               "fused_planar": one_token_fused_planar}
+               "fused_planar": one_token_fused_planar, "chain": chain_token("chain"),
+               "chain_planar": chain_token("chain_planar")}
         graph = only.endswith("_graph")
         fn = fns[only[:-6] if graph else only]
-        launches = len(entries) if fn is one_token else len(groups)
+        launches = len(entries) if fn is one_token else 2 if only.startswith("chain") else len(groups)
         if graph:
             s2 = torch.cuda.Stream()
             gr = torch.cuda.CUDAGraph()
@@ -587,8 +619,13 @@ def run_stream(torch, launcher, warm=2, only=None, tokens=1):
     fspan = spans_of(one_token_fused)
     fgspan = graph_of(one_token_fused)
     fpgspan = graph_of(one_token_fused_planar)
+    cspan = spans_of(chain_token("chain"))
+    cpspan = spans_of(chain_token("chain_planar"))
+    for ch in chains.values():
+        if ch.status() != 0:
+            raise RuntimeError("chain run gave up at a barrier")
     nbytes = synth.weight_bytes(entries)
-    del tensors, batches, fused, fused_planar, planar_w
+    del tensors, batches, fused, fused_planar, planar_w, chains
     torch.cuda.empty_cache()
 
     def rec(sp, launches):
@@ -598,7 +635,8 @@ def run_stream(torch, launcher, warm=2, only=None, tokens=1):
             "launches": rec(span, len(entries)), "graph": rec(gspan, len(entries)),
             "batched": rec(bspan, len(groups)), "batched_graph": rec(bgspan, len(groups)),
             "fused": rec(fspan, len(groups)), "fused_graph": rec(fgspan, len(groups)),
-            "fused_planar_graph": rec(fpgspan, len(groups))}
+            "fused_planar_graph": rec(fpgspan, len(groups)),
+            "chain": rec(cspan, 2), "chain_planar": rec(cpspan, 2)}
 
 
 def main():
@@ -610,7 +648,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--stream-only", metavar="VARIANT",
                     choices=["launches", "launches_graph", "batched", "batched_graph", "fused", "fused_graph",
-                             "fused_planar", "fused_planar_graph"],
+                             "fused_planar", "fused_planar_graph", "chain", "chain_planar"],
                     help="only time this decode-stream variant for --tokens tokens (for a kernel trace); "
                          "prints its own JSON line instead of the benchmark's")
     ap.add_argument("--tokens", type=int, default=5)

@@ -236,6 +236,92 @@ typedef struct qk_gemv_item {
  */
 int qk_gemv_batch(const qk_gemv_item *items, int count, void *stream);
 
+/* One GEMV of a chain step (one column): as qk_gemv_ex, or as
+ * qk_gemv_swiglu when W2 is set. */
+typedef struct qk_chain_entry {
+    int type;             /* QK_Q4_K / QK_Q5_K / QK_Q6_K, optionally | QK_PLANAR    */
+    int flags;            /* 0 or QK_Y_F16                                          */
+    const void *W;        /* N rows of superblocks, 16-byte aligned                 */
+    const void *W2;       /* NULL, or the up tensor of a SwiGLU pair (Q4_K only):
+                             y = silu(W x) * (W2 x)                                 */
+    const void *x;        /* K fp16 values, 16-byte aligned                         */
+    void *y;              /* N fp32 values (fp16 with QK_Y_F16)                     */
+    const void *residual; /* NULL or N fp32 values added at the store; may be y     */
+    int64_t N;
+    int64_t K;
+} qk_chain_entry;
+
+/*
+ * The decode token as one launch: a chain of steps, each a set of up to
+ * QK_MAX_BATCH independent one-column GEMVs (qk_chain_entry), run in order.
+ * A step may read (as x or residual) what an earlier step wrote: between
+ * consecutive steps every workgroup of the launch waits until all of them
+ * have stored their results (a device-wide barrier), exactly as back-to-back
+ * launches on one stream would order them.  The weights of a step do not
+ * depend on earlier steps, so each workgroup issues the first of them before
+ * it waits: the fill of one GEMV overlaps the end of the previous one instead
+ * of following it (the B70 plan, "Performance Model And North Star" and
+ * "Phase 2: Full Device Replay", puts the gap between its observed pass and
+ * the Q4 read floor on per-submission overhead; Non-Negotiable Requirements
+ * item 4 asks for the fewest practical device submissions).
+ *
+ * Every y is bit-identical to what qk_gemv_ex / qk_gemv_swiglu write for the
+ * same entry, with the same accuracy bound.
+ *
+ * Speed: on MI355X a step runs about twice as long as the same GEMV as a
+ * launch of its own (one 1024-thread workgroup per CU, bodies sharing one
+ * register budget), so a 448-GEMV decode token (14.6 GB of weights) takes
+ * 8.0 ms as a chain against 4.2 ms as a captured graph of qk_gemv_batch /
+ * qk_gemv_swiglu launches.  The chain is for callers that want one
+ * submission per token and cannot capture graphs.
+ *
+ * Use: qk_chain_plan (host only) writes a plan of qk_chain_plan_bytes into
+ * caller host memory; the caller copies it, unchanged, to device memory
+ * (plan_dev, 16-byte aligned) and passes both to qk_gemv_chain, as often as
+ * it likes while the tensors it names stay where they are.  The plan is made
+ * for the current device (its compute-unit count) and refuses another.
+ */
+
+/* Bytes of a plan of nsteps steps and nentries entries, or -1. */
+int64_t qk_chain_plan_bytes(int nsteps, int nentries);
+
+/*
+ *   entries     host array of nentries entries, step after step
+ *   step_sizes  host array of nsteps counts, each 1..QK_MAX_BATCH, summing to
+ *               nentries: step s runs the next step_sizes[s] entries
+ *   plan        host memory of plan_bytes >= qk_chain_plan_bytes (written)
+ * Every entry is checked as qk_gemv_ex / qk_gemv_swiglu check theirs, and no
+ * y may overlap what another entry of the same step reads or writes
+ * (QK_EINVAL_PTR).  A bad count or size, or a step the launch geometry cannot
+ * place, gives QK_EINVAL_SHAPE.  Nothing touches the GPU.
+ */
+int qk_chain_plan(const qk_chain_entry *entries, int nentries, const int *step_sizes, int nsteps,
+                  void *plan, int64_t plan_bytes);
+
+/* Bytes of the synchronisation workspace of a chain of nsteps steps, or -1. */
+int64_t qk_chain_workspace_bytes(int nsteps);
+
+/*
+ * qk_gemv_chain -- run a planned chain on `stream`: one small kernel clears
+ * the workspace, then one cooperative launch with a workgroup per compute
+ * unit runs every step.
+ *
+ *   plan        the host plan qk_chain_plan wrote (read during the call)
+ *   plan_dev    the same bytes in device memory, 16-byte aligned
+ *   workspace   device memory of workspace_bytes >= qk_chain_workspace_bytes
+ *               (nsteps), 4-byte aligned, used by this call only: concurrent
+ *               chains need workspaces of their own
+ *   timeout_us  bound on each wait at a barrier (<= 0: 2 s)
+ * Every wait is bounded: if one expires, the workgroup sets bit 0 of the
+ * first 32-bit word of the workspace (QK_CHAIN_TIMEOUT) and every workgroup
+ * abandons the chain at its next wait -- the outputs are then incomplete.
+ * Read that word after synchronising to check a run.  Returns QK_OK, an
+ * argument error, or QK_ELAUNCH (including a grid the device cannot hold).
+ */
+#define QK_CHAIN_TIMEOUT 0x1
+int qk_gemv_chain(const void *plan, const void *plan_dev, void *workspace, int64_t workspace_bytes,
+                  int64_t timeout_us, void *stream);
+
 /*
  * qk_repack -- rewrite N GGUF rows of `type` (no flag) as PLANAR rows: Wp is
  * then a valid QK_PLANAR tensor with the same weights.  One-time, outside the

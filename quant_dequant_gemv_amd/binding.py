@@ -22,12 +22,21 @@ PLANAR = 0x100  # QK_PLANAR: layout flag OR'ed into a type
 Y_F16 = 0x1  # QK_Y_F16: epilogue flag, y stored as fp16
 
 EXPORTS = ("qk_gemv", "qk_gemv_ex", "qk_gemv_swiglu", "qk_gemv_batch", "qk_dequant", "qk_repack",
-           "qk_block_bytes", "qk_row_bytes", "qk_strerror", "qk_version")
+           "qk_block_bytes", "qk_row_bytes", "qk_strerror", "qk_version",
+           "qk_chain_plan_bytes", "qk_chain_plan", "qk_chain_workspace_bytes", "qk_gemv_chain")
+CHAIN_TIMEOUT = 0x1  # QK_CHAIN_TIMEOUT: bit of the chain workspace's first word
 
 
 class qk_gemv_item(ctypes.Structure):
     """struct qk_gemv_item of include/qkgemv.h."""
     _fields_ = [("type", ctypes.c_int), ("W", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class qk_chain_entry(ctypes.Structure):
+    """struct qk_chain_entry of include/qkgemv.h."""
+    _fields_ = [("type", ctypes.c_int), ("flags", ctypes.c_int), ("W", ctypes.c_void_p), ("W2", ctypes.c_void_p),
+                ("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("residual", ctypes.c_void_p),
                 ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
 
 
@@ -70,6 +79,14 @@ def load_library(path: str = LIB_PATH):
     lib.qk_strerror.restype = ctypes.c_char_p
     lib.qk_version.argtypes = []
     lib.qk_version.restype = ctypes.c_char_p
+    lib.qk_chain_plan_bytes.argtypes = [c_int, c_int]
+    lib.qk_chain_plan_bytes.restype = i64
+    lib.qk_chain_plan.argtypes = [ctypes.POINTER(qk_chain_entry), c_int, ctypes.POINTER(c_int), c_int, P, i64]
+    lib.qk_chain_plan.restype = c_int
+    lib.qk_chain_workspace_bytes.argtypes = [c_int]
+    lib.qk_chain_workspace_bytes.restype = i64
+    lib.qk_gemv_chain.argtypes = [P, P, P, i64, i64, P]
+    lib.qk_gemv_chain.restype = c_int
     _lib = lib
     return lib
 
@@ -94,6 +111,31 @@ def qk_gemv_batch(items, stream: int = 0) -> int:
     """items: sequence of (type, W, x, y, N, K) with integer device addresses."""
     arr = (qk_gemv_item * max(1, len(items)))(*[qk_gemv_item(*it) for it in items])
     return load_library().qk_gemv_batch(arr, len(items), stream)
+
+
+def qk_chain_plan_bytes(nsteps: int, nentries: int) -> int:
+    return load_library().qk_chain_plan_bytes(nsteps, nentries)
+
+
+def qk_chain_plan(entries, step_sizes, plan) -> int:
+    """entries: sequence of qk_chain_entry (or tuples of its fields);
+    step_sizes: ints; plan: a writable host buffer (numpy uint8 array)."""
+    arr = (qk_chain_entry * max(1, len(entries)))(*[e if isinstance(e, qk_chain_entry) else qk_chain_entry(*e)
+                                                     for e in entries])
+    sizes = (ctypes.c_int * max(1, len(step_sizes)))(*step_sizes)
+    return load_library().qk_chain_plan(arr, len(entries), sizes, len(step_sizes),
+                                        ctypes.c_void_p(plan.ctypes.data), int(plan.nbytes))
+
+
+def qk_chain_workspace_bytes(nsteps: int) -> int:
+    return load_library().qk_chain_workspace_bytes(nsteps)
+
+
+def qk_gemv_chain(plan, plan_dev: int, workspace: int, workspace_bytes: int, timeout_us: int = 0,
+                  stream: int = 0) -> int:
+    """plan: the host plan (numpy uint8 array)."""
+    return load_library().qk_gemv_chain(ctypes.c_void_p(plan.ctypes.data), plan_dev, workspace, workspace_bytes,
+                                        timeout_us, stream)
 
 
 def qk_dequant(qtype: int, W: int, out: int, N: int, K: int, stream: int = 0) -> int:
@@ -297,3 +339,64 @@ def repack(qtype: int, W, N: int, K: int, out=None, stream=None):
     if rc != QK_OK:
         raise QKError(rc, "qk_repack")
     return out
+
+
+class Chain:
+    """A planned chain of one-column GEMV steps (qk_chain_plan / qk_gemv_chain).
+
+    steps: list of steps; each step a list of dicts with keys qtype, W, x, y,
+    N, K and optionally W2 (SwiGLU up tensor), residual (fp32, may be y) and
+    f16 (y stored as fp16).  Every tensor is checked like the other helpers
+    check theirs; the plan is uploaded once and the workspace allocated here,
+    so run() enqueues the chain and nothing else."""
+
+    def __init__(self, steps):
+        import numpy as np
+        import torch
+        entries, sizes, keep = [], [], []
+        for s, step in enumerate(steps):
+            if not step:
+                raise ValueError(f"step {s} is empty")
+            sizes.append(len(step))
+            for i, e in enumerate(step):
+                qt, W, x, y, N, K = e["qtype"], e["W"], e["x"], e["y"], e["N"], e["K"]
+                f16 = bool(e.get("f16", False))
+                where = f"steps[{s}][{i}]"
+                _weights(qt, W, N, K, where + ".W")
+                if e.get("W2") is not None:
+                    _weights(qt, e["W2"], N, K, where + ".W2")
+                if _activations(x, K) != 1:
+                    raise ValueError(f"{where}.x must be one column")
+                _need(y, where + ".y", torch.float16 if f16 else torch.float32, numel=N)
+                res = e.get("residual")
+                if res is not None:
+                    _need(res, where + ".residual", torch.float32, numel=N)
+                _same_cuda_device(W=W, W2=e.get("W2"), x=x, y=y, residual=res)
+                entries.append(qk_chain_entry(qt, Y_F16 if f16 else 0, W.data_ptr(),
+                                              e["W2"].data_ptr() if e.get("W2") is not None else None,
+                                              x.data_ptr(), y.data_ptr(), res.data_ptr() if res is not None else None,
+                                              N, K))
+                keep.append(e)
+        nbytes = qk_chain_plan_bytes(len(sizes), len(entries))
+        if nbytes < 0:
+            raise ValueError("bad chain size")
+        self.plan = np.zeros(nbytes, dtype=np.uint8)
+        rc = qk_chain_plan(entries, sizes, self.plan)
+        if rc != QK_OK:
+            raise QKError(rc, "qk_chain_plan")
+        dev = entries and steps[0][0]["W"].device
+        self.plan_dev = torch.from_numpy(self.plan).to(dev)
+        self.ws_bytes = qk_chain_workspace_bytes(len(sizes))
+        self.workspace = torch.zeros(self.ws_bytes // 4, dtype=torch.int32, device=dev)
+        self.nsteps = len(sizes)
+        self._keep = keep
+
+    def run(self, stream=None, timeout_us: int = 0):
+        rc = qk_gemv_chain(self.plan, self.plan_dev.data_ptr(), self.workspace.data_ptr(), self.ws_bytes,
+                           timeout_us, _stream_handle(stream))
+        if rc != QK_OK:
+            raise QKError(rc, "qk_gemv_chain")
+
+    def status(self) -> int:
+        """The workspace's flag word (synchronises): 0, or CHAIN_TIMEOUT."""
+        return int(self.workspace[0].item())

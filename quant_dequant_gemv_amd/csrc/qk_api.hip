@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <new>
+
 #include "../../include/qkgemv.h"
 #include "qk_launch.h"
 
@@ -142,6 +144,79 @@ int qk_gemv_batch(const qk_gemv_item *items, int count, void *stream) {
                 return QK_EINVAL_PTR;
         }
     return launched(qk::launch_gemv_batch(e, count, (hipStream_t)stream));
+}
+
+int64_t qk_chain_plan_bytes(int nsteps, int nentries) {
+    if (nsteps < 1 || nentries < nsteps) return -1;
+    return qk::chain_plan_bytes(nsteps, nentries);
+}
+
+int qk_chain_plan(const qk_chain_entry *entries, int nentries, const int *step_sizes, int nsteps, void *plan,
+                  int64_t plan_bytes) {
+    if (!entries || !step_sizes || nsteps < 1 || nentries < nsteps) return QK_EINVAL_SHAPE;
+    if (!plan || plan_bytes < qk::chain_plan_bytes(nsteps, nentries)) return QK_EINVAL_SHAPE;
+    static_assert(sizeof(qk_chain_entry) == 64, "qk_chain_entry layout");
+    int sum = 0;
+    for (int s = 0; s < nsteps; ++s) {
+        if (step_sizes[s] < 1 || step_sizes[s] > QK_MAX_BATCH) return QK_EINVAL_SHAPE;
+        sum += step_sizes[s];
+    }
+    if (sum != nentries) return QK_EINVAL_SHAPE;
+    // each entry as qk_gemv_ex / qk_gemv_swiglu with one column
+    for (int i = 0; i < nentries; ++i) {
+        const qk_chain_entry &e = entries[i];
+        int rc = check_shape(e.type, e.N, e.K, 1);
+        if (rc) return rc;
+        if (e.flags & ~QK_Y_F16) return QK_EINVAL_FLAGS;
+        if (e.W2 && (e.type & ~QK_PLANAR) != QK_Q4_K) return QK_EINVAL_TYPE;  // SwiGLU pairs: Q4_K
+        if (!e.W || !aligned(e.W, 16) || (e.W2 && !aligned(e.W2, 16))) return QK_EINVAL_PTR;
+        if ((rc = check_io(e.type, e.W, e.x, e.y, e.residual, e.N, e.K, 1, e.flags))) return rc;
+        if (e.W2 && overlap(e.y, ((e.flags & QK_Y_F16) ? 2 : 4) * e.N, e.W2, e.N * row_bytes_of(e.type, e.K)))
+            return QK_EINVAL_PTR;
+    }
+    // the entries of a step run concurrently: no y may overlap anything
+    // another entry of the step reads or writes
+    for (int s = 0, e0 = 0; s < nsteps; e0 += step_sizes[s], ++s)
+        for (int i = e0; i < e0 + step_sizes[s]; ++i)
+            for (int j = e0; j < e0 + step_sizes[s]; ++j) {
+                if (i == j) continue;
+                const qk_chain_entry &a = entries[i], &b = entries[j];
+                const int64_t ya = ((a.flags & QK_Y_F16) ? 2 : 4) * a.N, yb = ((b.flags & QK_Y_F16) ? 2 : 4) * b.N;
+                const int64_t wb = b.N * row_bytes_of(b.type, b.K);
+                if (overlap(a.y, ya, b.W, wb) || (b.W2 && overlap(a.y, ya, b.W2, wb)) ||
+                    overlap(a.y, ya, b.x, 2 * b.K) || overlap(a.y, ya, b.y, yb) ||
+                    (b.residual && overlap(a.y, ya, b.residual, 4 * b.N)))
+                    return QK_EINVAL_PTR;
+            }
+    qk::ChainEntryIn in_stack[64];
+    qk::ChainEntryIn *in = nentries <= 64 ? in_stack : new (std::nothrow) qk::ChainEntryIn[nentries];
+    if (!in) return QK_ELAUNCH;
+    for (int i = 0; i < nentries; ++i) {
+        const qk_chain_entry &e = entries[i];
+        in[i] = qk::ChainEntryIn{e.type, (e.flags & QK_Y_F16) ? 1 : 0, e.W, e.W2, e.x, e.y, e.residual, e.N, e.K,
+                                 row_bytes_of(e.type, e.K)};
+    }
+    const hipError_t err = qk::chain_plan(in, nentries, step_sizes, nsteps, plan, plan_bytes);
+    if (in != in_stack) delete[] in;
+    return err == hipSuccess ? QK_OK : QK_EINVAL_SHAPE;
+}
+
+int64_t qk_chain_workspace_bytes(int nsteps) {
+    if (nsteps < 1) return -1;
+    return ((int64_t)(nsteps + 2) * 4 + 255) / 256 * 256;
+}
+
+int qk_gemv_chain(const void *plan, const void *plan_dev, void *workspace, int64_t workspace_bytes,
+                  int64_t timeout_us, void *stream) {
+    if (!plan || !plan_dev || !workspace || !aligned(plan_dev, 16) || !aligned(workspace, 4)) return QK_EINVAL_PTR;
+    const int nsteps = qk::chain_steps(plan);
+    if (nsteps < 1) return QK_EINVAL_SHAPE;
+    if (workspace_bytes < qk_chain_workspace_bytes(nsteps)) return QK_EINVAL_SHAPE;
+    const hipError_t e = qk::launch_chain(plan, plan_dev, static_cast<uint32_t *>(workspace), workspace_bytes / 4,
+                                          timeout_us, (hipStream_t)stream);
+    if (e == hipSuccess) return QK_OK;
+    snprintf(g_launch_msg, sizeof g_launch_msg, "launch failed (%s): %s", qk::chain_stage(), hipGetErrorString(e));
+    return QK_ELAUNCH;
 }
 
 int qk_dequant(int type, const void *W, void *out, int64_t N, int64_t K, void *stream) {

@@ -105,6 +105,18 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
 }
 
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_4x4x4_16b_f16: 16 independent 4x4x4 blocks per wave; block b is
+// lanes 4b..4b+3, lane 4b+j supplies row j of A (a0, a1) and column j of B
+// (b0, b1) and receives D[0..3][j] += sum_k A[i][k] B[k][j].
+__device__ __forceinline__ f32x4 mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c) {
+    const half4_t a = __builtin_bit_cast(half4_t, make_uint2(a0, a1));
+    const half4_t b = __builtin_bit_cast(half4_t, make_uint2(b0, b1));
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 0, 0, 0);
+}
+
 // Packed fp16 add (v_pk_add_f16).  On quant patterns (multiples of 2^-24
 // below 2^-14) every sum is exact: the fp16 denormals are kept.
 __device__ __forceinline__ uint32_t padd(uint32_t a, uint32_t b) {

@@ -241,10 +241,24 @@ __device__ __forceinline__ float unit_dot(const Unit<T> &U, int q, const KScaleS
 // streams those rows of W and then of ep.W2 as 2R rows of one schedule, and
 // row r's output combines the sums of rows r and R + r.  EPI: the store
 // applies ep's residual / fp16 options (else it is the plain fp32 store).
-template <int T, int L, int RL, int D, bool NT, bool PAIR, bool EPI>
+// Hook: called once by every thread after the first round's weight loads are
+// issued and before x or the residual is read (the chain kernel waits there
+// for the previous step; a no-op elsewhere).  With a real hook every type
+// issues its first round before reading x.
+struct NoHook {
+    __device__ void operator()() const {}
+};
+
+// __syncthreads() calls of one body, the hook's own excepted (waves of the
+// workgroup that sit out a body execute as many to keep the barriers in step).
+__host__ __device__ constexpr int body_syncs(int T, int U, int useg) {
+    return T == Q6_K ? 1 : 2 * ((U + useg - 1) / useg);
+}
+
+template <int T, int L, int RL, int D, bool NT, bool PAIR, bool EPI, class Hook = NoHook>
 __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const uint16_t *__restrict__ x,
                                            void *y, int N, int K, int useg, int P, int blk, int nblk,
-                                           int nthr, const Epilogue &ep) {
+                                           int nthr, const Epilogue &ep, const Hook &hook = Hook()) {
     extern __shared__ __attribute__((aligned(16))) float part[];  // partial sums, slot rows of useg floats
     constexpr int DD = D < RL ? D : RL;  // units in flight
     const int tid = (int)threadIdx.x;
@@ -263,7 +277,8 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     // 128-register bound (six-row rounds; four-row rounds with an epilogue).
     // Measured: PLANAR rows 2-3% faster, 1024 x 5120 3-12%; Q5_K (no gain)
     // and Q6_K (x read per lane) keep the plain order.
-    constexpr bool PRE = T == Q4_K && RL != 6 && !(RL == 4 && (EPI || PAIR));
+    constexpr bool CHAIN = !__is_same(Hook, NoHook);
+    constexpr bool PRE = CHAIN || (T == Q4_K && RL != 6 && !(RL == 4 && (EPI || PAIR)));
     // Partial sums: the lane of phase ph (tail lanes ph >= P included) writes
     // its i-th row to slot row i*PT + ph, PT = phases incl. the tail, so every
     // lane owns a distinct slot and no write needs a guard.  Row r of the
@@ -276,9 +291,15 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     // the residual of its j-th row now, and the storing lane fetches it with
     // a cross-lane read at the end
     float resp = 0.f;
-    if constexpr (EPI) {
-        const int rj = (tid >> 4) + (tid & 15) * (nthr >> 4);
-        if (ep.res && rj < R) resp = ep.res[r0 + rj];
+    auto read_res = [&]() {
+        if constexpr (EPI) {
+            const int rj = (tid >> 4) + (tid & 15) * (nthr >> 4);
+            if (ep.res && rj < R) resp = ep.res[r0 + rj];
+        }
+    };
+    if constexpr (!PRE) {
+        hook();
+        read_res();
     }
 
     for (int s0 = 0; s0 < U; s0 += useg) {
@@ -325,12 +346,20 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
             // copy's global reads come after it but are waited for alone:
             // loads retire in order, and the ring is older)
             Unit<T> buf[DD];
-            if (s0 > 0) __syncthreads();  // every lane holds the previous segment's x in registers
+            if (T != Q6_K && s0 > 0) __syncthreads();  // every lane holds the previous segment's x in registers
 #pragma unroll
             for (int p = 0; p < DD; ++p) load_row(buf[p], p);
-            stage_x(xl, x, s0, ns, tid, nthr);
-            __syncthreads();
-            load_x<T>(X, xl, u - s0);
+            if (s0 == 0) {
+                hook();
+                read_res();
+            }
+            if constexpr (T == Q6_K) {
+                load_x_q6(X, x, u);
+            } else {
+                stage_x(xl, x, s0, ns, tid, nthr);
+                __syncthreads();
+                load_x<T>(X, xl, u - s0);
+            }
             for (int i0 = 0; i0 < rows_lane; i0 += RL) {
                 if (i0 > 0)
 #pragma unroll
@@ -905,6 +934,376 @@ hipError_t launch_gemv_batch(const BatchEntry *in, int count, hipStream_t st) {
     allow_lds<gemv1_batch_kernel>();
     hipLaunchKernelGGL(gemv1_batch_kernel, dim3((unsigned)total), dim3(threads), lds, st, a);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Chain: steps of one-column GEMVs in one persistent launch.  Step s+1 may
+// read what step s wrote (its x or residual may be an earlier y), so every
+// workgroup arrives at a barrier after its stores of step s and waits for
+// all arrivals before it reads x of step s+1 -- but it issues the first
+// round of step s+1's weight loads before waiting (weights never depend on
+// earlier steps), so the previous step's tail and this step's first memory
+// latency overlap instead of adding up launch after launch.
+//
+// One workgroup per CU (a cooperative launch: the runtime checks that the
+// whole grid is resident, so the barriers cannot wait on an unscheduled
+// workgroup).  Each step's entries share the grid in proportion to their
+// weight bytes and run the one-column body with the geometry that share
+// gives; a row's arithmetic depends only on K, so every y is bit-identical to
+// what qk_gemv / qk_gemv_ex / qk_gemv_swiglu write.
+//
+// Synchronisation words (caller memory, or the library's own array): [0]
+// error flags, [1] unused, [2 + k] arrivals at the barrier after step k.  A
+// small kernel zeroes them before each launch.  Waits are bounded by a
+// wall-clock limit: a workgroup that times out sets CHAIN_TIMEOUT and every
+// workgroup stops at its next wait (the outputs are then incomplete, and the
+// flag tells the caller so).
+// ---------------------------------------------------------------------------
+constexpr uint32_t CHAIN_MAGIC = 0x31484351u;  // "QCH1"
+constexpr uint32_t CHAIN_TIMEOUT = 1u;
+
+struct ChainHdr {
+    uint32_t magic, nsteps, nentries, G;
+    int32_t threads, cus;
+    uint32_t lds, entries_off;
+};
+struct ChainStepD { int32_t e0, e1; };
+struct ChainEntryD {
+    const uint8_t *W;
+    const void *W2;
+    const uint16_t *x;
+    void *y;
+    const float *res;
+    int32_t N, K, useg, P, threads, code, first, last, f16, pad;
+};
+constexpr int CHAIN_PAIR = 32;  // code + CHAIN_PAIR: the SwiGLU pair body
+// dynamic LDS of the chain kernel: the most a workgroup may take, less the
+// kernel's static word
+constexpr int CHAIN_LDS_MAX = LDS_MAX - 64;
+
+__global__ void __launch_bounds__(256) chain_reset_kernel(uint32_t *sync, int words) {
+    for (int i = (int)threadIdx.x; i < words; i += (int)blockDim.x) sync[i] = 0u;
+}
+
+// Every wave's stores of the step are complete before the workgroup
+// barrier; one thread then makes them visible device-wide (one L2 write-back
+// per workgroup, not one per wave) and counts the arrival.
+__device__ __forceinline__ void chain_arrive(uint32_t *sync, int k) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(&sync[2 + k], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Wait until all G workgroups arrived after step k (every thread calls it
+// once).  Returns false when the chain is abandoned (this workgroup timed
+// out, or another one did).
+__device__ __forceinline__ bool chain_wait(uint32_t *sync, int k, uint32_t G, uint64_t limit, uint32_t *s_ok) {
+    if (threadIdx.x == 0) {
+        uint32_t ok = 1;
+        const uint64_t t0 = wall_clock64();
+        while (__hip_atomic_load(&sync[2 + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < G) {
+            if (__hip_atomic_load(&sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+                ok = 0;
+                break;
+            }
+            if (wall_clock64() - t0 > limit) {
+                __hip_atomic_fetch_or(&sync[0], CHAIN_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+        }
+        // the earlier steps' stores, before any read of the workgroup (one
+        // invalidation of this CU's caches serves every wave)
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        *s_ok = ok;
+    }
+    __syncthreads();
+    return *s_ok != 0u;
+}
+
+// A pointer read from memory is generic to the compiler (flat loads, which
+// also count against the LDS counter); these all point to device memory.
+template <class P>
+__device__ __forceinline__ P *global_ptr(P *p) {
+    return (P *)(__attribute__((address_space(1))) P *)(uintptr_t)p;
+}
+
+// The wait of a chain step (every thread of the workgroup calls it once);
+// its verdict goes to the workgroup's shared word.
+struct ChainHook {
+    uint32_t *sync, *s_ok;
+    uint64_t limit;
+    int k;  // the barrier after step k, or -1: nothing to wait for
+    uint32_t G;
+    __device__ void operator()() const {
+        if (k >= 0) (void)chain_wait(sync, k, G, limit, s_ok);
+    }
+};
+
+// One body of the chain (inlined: compiled as functions of their own, the
+// bodies get the 64-register budget of a device function and spill).
+template <int T, int L, int RL, int D, bool PAIR>
+__device__ __forceinline__ void chain_run(const ChainEntryD &e, int blk, int nblk, ChainHook hook) {
+    const Epilogue ep{global_ptr(e.W2), global_ptr(e.res), e.f16};
+    gemv1_body<T, L, RL, D, L == PLANAR, PAIR, true, ChainHook>(global_ptr(e.W), global_ptr(e.x), global_ptr(e.y),
+                                                                 e.N, e.K, e.useg, e.P, blk, nblk, e.threads, ep,
+                                                                 hook);
+}
+
+__device__ __forceinline__ void chain_body(const ChainEntryD &e, int blk, int nblk, const ChainHook &hook) {
+#define QK_CB(CODE, T, L, RL, D, PAIR) \
+    case CODE: chain_run<T, L, RL, D, PAIR>(e, blk, nblk, hook); break;
+    switch (e.code) {
+        QK_CB(B_Q4_1, Q4_K, GGUF, 1, 1, false)
+        QK_CB(B_Q4_2, Q4_K, GGUF, 2, 2, false)
+        QK_CB(B_Q4_4, Q4_K, GGUF, 4, 2, false)
+        QK_CB(B_Q4_6, Q4_K, GGUF, 6, 2, false)
+        QK_CB(B_Q4_8, Q4_K, GGUF, 8, 2, false)
+        QK_CB(B_Q4_12, Q4_K, GGUF, 12, 2, false)
+        QK_CB(B_Q5_1, Q5_K, GGUF, 1, 1, false)
+        QK_CB(B_Q5_2, Q5_K, GGUF, 2, 2, false)
+        QK_CB(B_Q6_1, Q6_K, GGUF, 1, 1, false)
+        QK_CB(B_COUNT + B_Q4_1, Q4_K, PLANAR, 1, 1, false)
+        QK_CB(B_COUNT + B_Q4_2, Q4_K, PLANAR, 2, 2, false)
+        QK_CB(B_COUNT + B_Q4_4, Q4_K, PLANAR, 4, 2, false)
+        QK_CB(B_COUNT + B_Q4_6, Q4_K, PLANAR, 6, 2, false)
+        QK_CB(B_COUNT + B_Q4_8, Q4_K, PLANAR, 8, 2, false)
+        QK_CB(B_COUNT + B_Q4_12, Q4_K, PLANAR, 12, 2, false)
+        QK_CB(B_COUNT + B_Q5_1, Q5_K, PLANAR, 1, 1, false)
+        QK_CB(B_COUNT + B_Q5_2, Q5_K, PLANAR, 2, 2, false)
+        QK_CB(B_COUNT + B_Q6_1, Q6_K, PLANAR, 1, 1, false)
+        QK_CB(B_COUNT + B_Q6_2, Q6_K, PLANAR, 2, 2, false)
+        QK_CB(CHAIN_PAIR + B_Q4_1, Q4_K, GGUF, 1, 1, true)
+        QK_CB(CHAIN_PAIR + B_Q4_2, Q4_K, GGUF, 2, 2, true)
+        QK_CB(CHAIN_PAIR + B_Q4_4, Q4_K, GGUF, 4, 2, true)
+        QK_CB(CHAIN_PAIR + B_Q4_6, Q4_K, GGUF, 6, 2, true)
+        QK_CB(CHAIN_PAIR + B_Q4_8, Q4_K, GGUF, 8, 2, true)
+        QK_CB(CHAIN_PAIR + B_Q4_12, Q4_K, GGUF, 12, 2, true)
+        QK_CB(CHAIN_PAIR + B_COUNT + B_Q4_1, Q4_K, PLANAR, 1, 1, true)
+        QK_CB(CHAIN_PAIR + B_COUNT + B_Q4_2, Q4_K, PLANAR, 2, 2, true)
+        QK_CB(CHAIN_PAIR + B_COUNT + B_Q4_4, Q4_K, PLANAR, 4, 2, true)
+        QK_CB(CHAIN_PAIR + B_COUNT + B_Q4_6, Q4_K, PLANAR, 6, 2, true)
+        QK_CB(CHAIN_PAIR + B_COUNT + B_Q4_8, Q4_K, PLANAR, 8, 2, true)
+        QK_CB(CHAIN_PAIR + B_COUNT + B_Q4_12, Q4_K, PLANAR, 12, 2, true)
+    default: break;
+    }
+#undef QK_CB
+}
+
+__device__ __forceinline__ int chain_code_type(int code) {
+    const int c = (code & (CHAIN_PAIR - 1)) % B_COUNT;
+    return c <= B_Q4_12 ? Q4_K : c <= B_Q5_2 ? Q5_K : Q6_K;
+}
+
+__global__ void __launch_bounds__(1024) gemv1_chain_kernel(const uint8_t *__restrict__ plan, uint32_t *sync,
+                                                           uint64_t limit) {
+    __shared__ uint32_t s_ok;
+    const ChainHdr h = *reinterpret_cast<const ChainHdr *>(plan);
+    const ChainStepD *steps = reinterpret_cast<const ChainStepD *>(plan + sizeof(ChainHdr));
+    const ChainEntryD *ents = reinterpret_cast<const ChainEntryD *>(plan + h.entries_off);
+    const int blk = (int)blockIdx.x;
+    if (threadIdx.x == 0) s_ok = 1u;
+    for (int s = 0; s < (int)h.nsteps; ++s) {
+        if (s > 0) chain_arrive(sync, s - 1);
+        const ChainHook hook{sync, &s_ok, limit, s - 1, h.G};
+        const ChainStepD st = steps[s];
+        int i = st.e0;
+        while (i < st.e1 && !(blk >= ents[i].first && blk < ents[i].last)) ++i;
+        if (i < st.e1) {
+            const ChainEntryD e = ents[i];
+            if ((int)threadIdx.x < e.threads) {
+                chain_body(e, blk - e.first, e.last - e.first, hook);
+            } else {  // waves this body does not use keep the barriers in step
+                hook();
+                const int n = body_syncs(chain_code_type(e.code), e.K >> 6, e.useg);
+                for (int k = 0; k < n; ++k) __syncthreads();
+            }
+        } else {
+            hook();
+        }
+        if (s > 0 && s_ok == 0u) return;  // the same word for every wave, read after the wait's barrier
+    }
+}
+
+// Chain geometry: one workgroup per CU in the whole launch, so an entry's
+// share g.G of the grid is given; P phases and RL rows per round are chosen
+// as in geometry() for the round lengths the chain's bodies are compiled for
+// and at most 1024 threads.
+// One workgroup per CU of at most 1024 threads (measured: two of 512 or
+// three of 320 per CU were no faster, and three did not all fit at once).
+constexpr int CHAIN_PER_CU = 1;
+constexpr int CHAIN_THREADS = 1024;
+
+template <int T, int L>
+static Geo chain_geo(int64_t N, int64_t K, int G, int mult) {
+    static constexpr int q4[] = {1, 2, 4, 6, 8, 12}, q5[] = {1, 2}, q6[] = {1}, q6p[] = {1, 2};
+    const int *rl = T == Q4_K ? q4 : T == Q5_K ? q5 : (L == PLANAR ? q6p : q6);
+    const int nrl = T == Q4_K ? 6 : T == Q5_K ? 2 : (L == PLANAR ? 2 : 1);
+    Geo g;
+    const int64_t U = K / 64;
+    g.useg = (int)(U < 512 ? U : 512);
+    g.G = G;
+    const int pmax = std::max(1, CHAIN_THREADS / g.useg);
+    const int64_t R = mult * ((N + G - 1) / G);
+    auto plan = [&](int p, int &r) {
+        const int64_t rows = (R + p - 1) / p;
+        r = rl[nrl - 1];
+        for (int k = 0; k < nrl; ++k)
+            if (rl[k] >= rows) { r = rl[k]; break; }
+        return (int64_t)p * ((rows + r - 1) / r) * r;
+    };
+    const int plo = R >= pmax ? (pmax + 1) / 2 : 1;
+    int64_t best = INT64_MAX;
+    for (int p = plo; p <= pmax; ++p) {
+        int r;
+        best = std::min(best, plan(p, r));
+    }
+    g.P = plo;
+    g.RL = 1;
+    for (int p = plo; p <= pmax; ++p) {
+        int r;
+        if (plan(p, r) <= best) { g.P = p; g.RL = r; }
+    }
+    g.threads = (g.P * g.useg + 63) / 64 * 64;
+    return g;
+}
+
+static Geo chain_geo_of(int type, int64_t N, int64_t K, int G, int mult) {
+    const bool planar = (type & PLANAR_FLAG) != 0;
+    switch (type & ~PLANAR_FLAG) {
+    case Q4_K: return planar ? chain_geo<Q4_K, PLANAR>(N, K, G, mult) : chain_geo<Q4_K, GGUF>(N, K, G, mult);
+    case Q5_K: return planar ? chain_geo<Q5_K, PLANAR>(N, K, G, mult) : chain_geo<Q5_K, GGUF>(N, K, G, mult);
+    default: return planar ? chain_geo<Q6_K, PLANAR>(N, K, G, mult) : chain_geo<Q6_K, GGUF>(N, K, G, mult);
+    }
+}
+
+static size_t align16(size_t v) { return (v + 15) / 16 * 16; }
+
+int64_t chain_plan_bytes(int nsteps, int nentries) {
+    if (nsteps < 1 || nentries < nsteps) return -1;
+    return (int64_t)(align16(sizeof(ChainHdr) + sizeof(ChainStepD) * (size_t)nsteps) +
+                     sizeof(ChainEntryD) * (size_t)nentries);
+}
+
+hipError_t chain_plan(const ChainEntryIn *in, int nentries, const int *step_sizes, int nsteps, void *plan,
+                      int64_t bytes) {
+    const int64_t need = chain_plan_bytes(nsteps, nentries);
+    if (need < 0 || bytes < need) return hipErrorInvalidValue;
+    uint8_t *out = static_cast<uint8_t *>(plan);
+    ChainHdr h{};
+    h.magic = CHAIN_MAGIC;
+    h.nsteps = (uint32_t)nsteps;
+    h.nentries = (uint32_t)nentries;
+    h.cus = device_cus();
+    h.G = (uint32_t)(h.cus * CHAIN_PER_CU);
+    h.entries_off = (uint32_t)align16(sizeof(ChainHdr) + sizeof(ChainStepD) * (size_t)nsteps);
+    ChainStepD *steps = reinterpret_cast<ChainStepD *>(out + sizeof(ChainHdr));
+    ChainEntryD *ents = reinterpret_cast<ChainEntryD *>(out + h.entries_off);
+    int threads = 64;
+    size_t lds = 16;
+    int e0 = 0;
+    for (int s = 0; s < nsteps; ++s) {
+        const int n = step_sizes[s];
+        if (n < 1 || n > MAX_BATCH || e0 + n > nentries) return hipErrorInvalidValue;
+        steps[s] = ChainStepD{e0, e0 + n};
+        // the grid shared in proportion to weight bytes (cumulative
+        // rounding), at least one workgroup and at most one per schedule row
+        double total = 0.0;
+        for (int i = e0; i < e0 + n; ++i) total += (in[i].W2 ? 2.0 : 1.0) * (double)in[i].N * (double)in[i].row_bytes;
+        double done = 0.0;
+        int given = 0;
+        for (int i = e0; i < e0 + n; ++i) {
+            const ChainEntryIn &e = in[i];
+            const int mult = e.W2 ? 2 : 1;
+            done += mult * (double)e.N * (double)e.row_bytes;
+            int upto = (int)(h.G * (done / total) + 0.5);
+            if (i == e0 + n - 1) upto = (int)h.G;
+            int share = std::max(1, upto - given);
+            share = (int)std::min<int64_t>(share, e.N);
+            if (given + share > (int)h.G) return hipErrorInvalidValue;  // more entries than workgroups
+            Geo g = chain_geo_of(e.type, e.N, e.K, share, mult);
+            const int base = body_code(e.type, g.RL);
+            if (base < 0 || (e.W2 && (e.type & ~PLANAR_FLAG) != Q4_K)) return hipErrorInvalidValue;
+            const size_t l = part_lds(e.N, g, mult);
+            if (l > (size_t)CHAIN_LDS_MAX) return hipErrorInvalidValue;
+            lds = std::max(lds, l);
+            threads = std::max(threads, g.threads);
+            ChainEntryD d{};
+            d.W = static_cast<const uint8_t *>(e.W);
+            d.W2 = e.W2;
+            d.x = static_cast<const uint16_t *>(e.x);
+            d.y = e.y;
+            d.res = static_cast<const float *>(e.res);
+            d.N = (int32_t)e.N;
+            d.K = (int32_t)e.K;
+            d.useg = g.useg;
+            d.P = g.P;
+            d.threads = g.threads;
+            d.code = base + (e.W2 ? CHAIN_PAIR : 0);
+            d.first = given;
+            d.last = given + share;
+            d.f16 = e.f16;
+            ents[i] = d;
+            given += share;
+        }
+        e0 += n;
+    }
+    if (e0 != nentries) return hipErrorInvalidValue;
+    h.threads = threads;
+    h.lds = (uint32_t)lds;
+    *reinterpret_cast<ChainHdr *>(out) = h;
+    return hipSuccess;
+}
+
+int chain_steps(const void *plan_host) {
+    const ChainHdr *h = static_cast<const ChainHdr *>(plan_host);
+    return h->magic == CHAIN_MAGIC ? (int)h->nsteps : -1;
+}
+
+static uint64_t wall_ticks_per_us() {
+    static std::atomic<uint64_t> cache[MAX_DEVICES];
+    const int dev = current_device();
+    uint64_t v = cache[dev].load(std::memory_order_relaxed);
+    if (v) return v;
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0) khz = 100000;
+    v = std::max<uint64_t>(1, (uint64_t)khz / 1000);
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+static thread_local const char *g_chain_stage = "";
+const char *chain_stage() { return g_chain_stage; }
+
+hipError_t launch_chain(const void *plan_host, const void *plan_dev, uint32_t *sync, int64_t sync_words,
+                        int64_t timeout_us, hipStream_t st) {
+    const ChainHdr &h = *static_cast<const ChainHdr *>(plan_host);
+    g_chain_stage = "plan";
+    if (h.magic != CHAIN_MAGIC || h.cus != device_cus() || sync_words < (int64_t)h.nsteps + 2)
+        return hipErrorInvalidValue;
+    g_chain_stage = "LDS opt-in";
+    hipError_t e = lds_opt_in<gemv1_chain_kernel>(CHAIN_LDS_MAX);
+    if (e != hipSuccess) return e;
+    g_chain_stage = "occupancy";
+    int per_cu = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv1_chain_kernel, h.threads, h.lds);
+    if (e != hipSuccess) return e;
+    if ((int64_t)per_cu * h.cus < (int64_t)h.G) return hipErrorCooperativeLaunchTooLarge;
+    g_chain_stage = "workspace clear";
+    hipLaunchKernelGGL(chain_reset_kernel, dim3(1), dim3(256), 0, st, sync, (int)(h.nsteps + 2));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    g_chain_stage = "cooperative launch";
+    const uint8_t *p = static_cast<const uint8_t *>(plan_dev);
+    uint64_t limit = (uint64_t)(timeout_us > 0 ? timeout_us : 2000000) * wall_ticks_per_us();
+    void *args[] = {&p, &sync, &limit};
+    e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(gemv1_chain_kernel), dim3(h.G), dim3(h.threads),
+                                   args, h.lds, st);
+    if (e == hipSuccess) g_chain_stage = "";
+    return e;
 }
 
 template <int T, int L>

@@ -76,6 +76,22 @@ hipError_t launch_gemv_batch(const BatchEntry *entries, int count, hipStream_t s
 hipError_t launch_gemv_multi(int type, const void *W, const void *x, void *y, int64_t N, int64_t K,
                              int ncols, const Epilogue &ep, hipStream_t stream);
 
+// Chain of one-column steps in one persistent launch (see qk_kernels.hip).
+struct ChainEntryIn {
+    int type, f16;
+    const void *W, *W2, *x;
+    void *y;
+    const void *res;
+    int64_t N, K, row_bytes;
+};
+int64_t chain_plan_bytes(int nsteps, int nentries);
+hipError_t chain_plan(const ChainEntryIn *entries, int nentries, const int *step_sizes, int nsteps, void *plan,
+                      int64_t bytes);
+int chain_steps(const void *plan_host);  // steps of a plan, or -1 if it is not one
+hipError_t launch_chain(const void *plan_host, const void *plan_dev, uint32_t *sync, int64_t sync_words,
+                        int64_t timeout_us, hipStream_t stream);
+const char *chain_stage();  // the step of the calling thread's last failed launch_chain
+
 // fp32 dequantisation of the whole tensor (either layout).
 hipError_t launch_dequant(int type, const void *W, void *out, int64_t N, int64_t K, hipStream_t stream);
 

@@ -42,14 +42,7 @@
 
 namespace qk {
 
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, float4_t c) {
-    const half4_t a = __builtin_bit_cast(half4_t, make_uint2(a0, a1));
-    const half4_t b = __builtin_bit_cast(half4_t, make_uint2(b0, b1));
-    return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 0, 0, 0);
-}
+typedef f32x4 float4_t;
 
 // a from the lane that the DPP control names
 template <int CTRL>
