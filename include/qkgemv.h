@@ -323,6 +323,24 @@ int qk_gemv_chain(const void *plan, const void *plan_dev, void *workspace, int64
                   int64_t timeout_us, void *stream);
 
 /*
+ * qk_gemv_chain_noalloc -- qk_gemv_chain for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same kernels and results, with the barrier
+ * counters in a 16 KiB array the library holds on each GPU until the process
+ * ends instead of a caller workspace.  Nothing is allocated per call.
+ *
+ *   plan, plan_dev, timeout_us, stream   as for qk_gemv_chain
+ *   status      NULL, or a 4-byte aligned device word that receives the
+ *               run's flag word (QK_CHAIN_TIMEOUT) once the chain has run
+ * A plan of more than QK_CHAIN_NOALLOC_MAX_STEPS steps gives QK_EINVAL_SHAPE
+ * before anything is launched.  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * and must not be made; each call clears the words it uses before its chain.
+ */
+#define QK_CHAIN_NOALLOC_MAX_STEPS 4094
+int qk_gemv_chain_noalloc(const void *plan, const void *plan_dev, void *status, int64_t timeout_us, void *stream);
+
+/*
  * qk_repack -- rewrite N GGUF rows of `type` (no flag) as PLANAR rows: Wp is
  * then a valid QK_PLANAR tensor with the same weights.  One-time, outside the
  * decode loop; every y and every dequantised weight computed from Wp is

@@ -23,8 +23,10 @@ Y_F16 = 0x1  # QK_Y_F16: epilogue flag, y stored as fp16
 
 EXPORTS = ("qk_gemv", "qk_gemv_ex", "qk_gemv_swiglu", "qk_gemv_batch", "qk_dequant", "qk_repack",
            "qk_block_bytes", "qk_row_bytes", "qk_strerror", "qk_version",
-           "qk_chain_plan_bytes", "qk_chain_plan", "qk_chain_workspace_bytes", "qk_gemv_chain")
+           "qk_chain_plan_bytes", "qk_chain_plan", "qk_chain_workspace_bytes", "qk_gemv_chain",
+           "qk_gemv_chain_noalloc")
 CHAIN_TIMEOUT = 0x1  # QK_CHAIN_TIMEOUT: bit of the chain workspace's first word
+CHAIN_NOALLOC_MAX_STEPS = 4094  # QK_CHAIN_NOALLOC_MAX_STEPS
 
 
 class qk_gemv_item(ctypes.Structure):
@@ -87,6 +89,8 @@ def load_library(path: str = LIB_PATH):
     lib.qk_chain_workspace_bytes.restype = i64
     lib.qk_gemv_chain.argtypes = [P, P, P, i64, i64, P]
     lib.qk_gemv_chain.restype = c_int
+    lib.qk_gemv_chain_noalloc.argtypes = [P, P, P, i64, P]
+    lib.qk_gemv_chain_noalloc.restype = c_int
     _lib = lib
     return lib
 
@@ -136,6 +140,12 @@ def qk_gemv_chain(plan, plan_dev: int, workspace: int, workspace_bytes: int, tim
     """plan: the host plan (numpy uint8 array)."""
     return load_library().qk_gemv_chain(ctypes.c_void_p(plan.ctypes.data), plan_dev, workspace, workspace_bytes,
                                         timeout_us, stream)
+
+
+def qk_gemv_chain_noalloc(plan, plan_dev: int, status: int = 0, timeout_us: int = 0, stream: int = 0) -> int:
+    """plan: the host plan (numpy uint8 array); status: 0 or a device word."""
+    return load_library().qk_gemv_chain_noalloc(ctypes.c_void_p(plan.ctypes.data), plan_dev, status, timeout_us,
+                                                stream)
 
 
 def qk_dequant(qtype: int, W: int, out: int, N: int, K: int, stream: int = 0) -> int:

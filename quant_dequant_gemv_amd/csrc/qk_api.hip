@@ -219,6 +219,17 @@ int qk_gemv_chain(const void *plan, const void *plan_dev, void *workspace, int64
     return QK_ELAUNCH;
 }
 
+int qk_gemv_chain_noalloc(const void *plan, const void *plan_dev, void *status, int64_t timeout_us, void *stream) {
+    static_assert(QK_CHAIN_NOALLOC_MAX_STEPS + 2 <= qk::CHAIN_SCRATCH_WORDS, "chain scratch size");
+    if (!plan || !plan_dev || !aligned(plan_dev, 16) || !aligned(status, 4)) return QK_EINVAL_PTR;
+    const int nsteps = qk::chain_steps(plan);
+    if (nsteps < 1 || nsteps > QK_CHAIN_NOALLOC_MAX_STEPS) return QK_EINVAL_SHAPE;
+    const hipError_t e = qk::launch_chain_noalloc(plan, plan_dev, status, timeout_us, (hipStream_t)stream);
+    if (e == hipSuccess) return QK_OK;
+    snprintf(g_launch_msg, sizeof g_launch_msg, "launch failed (%s): %s", qk::chain_stage(), hipGetErrorString(e));
+    return QK_ELAUNCH;
+}
+
 int qk_dequant(int type, const void *W, void *out, int64_t N, int64_t K, void *stream) {
     const int rc = check_shape(type, N, K, 1);
     if (rc) return rc;
@@ -244,7 +255,10 @@ const char *qk_strerror(int code) {
     case QK_EINVAL_TYPE:
         return "invalid type: expected QK_Q4_K (12), QK_Q5_K (13) or QK_Q6_K (14), optionally | QK_PLANAR "
                "(0x100) with ncols = 1 (qk_repack takes the type without the flag)";
-    case QK_EINVAL_SHAPE: return "invalid shape: need N >= 1, K a positive multiple of 256, 1 <= ncols <= 32";
+    case QK_EINVAL_SHAPE:
+        return "invalid shape: need N >= 1, K a positive multiple of 256, 1 <= ncols <= 32; a chain needs 1.."
+               "QK_MAX_BATCH entries per step, a workspace of qk_chain_workspace_bytes, and for "
+               "qk_gemv_chain_noalloc at most QK_CHAIN_NOALLOC_MAX_STEPS (4094) steps";
     case QK_EINVAL_PTR:
         return "invalid pointer: NULL, or W/x not 16-byte aligned, or y/out/residual not 4-byte aligned (fp16 y: 2), "
                "or an output that overlaps an input (y with W or x, out with W, a batch entry's y with any entry's "

@@ -26,6 +26,7 @@
 #include "qk_launch.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace qk {
 
@@ -1302,6 +1303,57 @@ hipError_t launch_chain(const void *plan_host, const void *plan_dev, uint32_t *s
     void *args[] = {&p, &sync, &limit};
     e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(gemv1_chain_kernel), dim3(h.G), dim3(h.threads),
                                    args, h.lds, st);
+    if (e == hipSuccess) g_chain_stage = "";
+    return e;
+}
+
+// ---------------------------------------------------------------------------
+// The chain without a caller workspace: its barrier counters live in a
+// file-scope device array, one copy per GPU, kept until the process ends.
+// Host code never passes the array's name to a kernel (in host code it is a
+// stand-in, not a device address): it takes the device address once per
+// device with hipGetSymbolAddress and uses that.  Every call on one GPU
+// shares the array, so calls that overlap on one GPU race; each run clears
+// the words it uses (a kernel, not a memset) before its chain starts.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint32_t scratch[CHAIN_SCRATCH_WORDS];
+
+__global__ void __launch_bounds__(64) chain_status_kernel(const uint32_t *sync, uint32_t *status) {
+    if (threadIdx.x == 0) *status = sync[0];
+}
+
+static hipError_t chain_scratch(uint32_t **out) {
+    static std::atomic<uint32_t *> addr[MAX_DEVICES];
+    static std::mutex mu;
+    const int dev = current_device();
+    uint32_t *p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(mu);
+        p = addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            void *a = nullptr;
+            const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!a) return hipErrorInvalidSymbol;
+            p = static_cast<uint32_t *>(a);
+            addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+hipError_t launch_chain_noalloc(const void *plan_host, const void *plan_dev, void *status, int64_t timeout_us,
+                                hipStream_t st) {
+    uint32_t *sync = nullptr;
+    g_chain_stage = "scratch address";
+    hipError_t e = chain_scratch(&sync);
+    if (e != hipSuccess) return e;
+    e = launch_chain(plan_host, plan_dev, sync, CHAIN_SCRATCH_WORDS, timeout_us, st);
+    if (e != hipSuccess || !status) return e;
+    g_chain_stage = "status copy";
+    hipLaunchKernelGGL(chain_status_kernel, dim3(1), dim3(64), 0, st, (const uint32_t *)sync, (uint32_t *)status);
+    e = hipGetLastError();
     if (e == hipSuccess) g_chain_stage = "";
     return e;
 }

@@ -91,6 +91,12 @@ int chain_steps(const void *plan_host);  // steps of a plan, or -1 if it is not 
 hipError_t launch_chain(const void *plan_host, const void *plan_dev, uint32_t *sync, int64_t sync_words,
                         int64_t timeout_us, hipStream_t stream);
 const char *chain_stage();  // the step of the calling thread's last failed launch_chain
+// launch_chain with the counters in the library's own per-device array of
+// CHAIN_SCRATCH_WORDS words (nsteps + 2 must fit); status: NULL or a device
+// word that receives the run's flag word after the chain.
+constexpr int CHAIN_SCRATCH_WORDS = 4096;
+hipError_t launch_chain_noalloc(const void *plan_host, const void *plan_dev, void *status, int64_t timeout_us,
+                                hipStream_t stream);
 
 // fp32 dequantisation of the whole tensor (either layout).
 hipError_t launch_dequant(int type, const void *W, void *out, int64_t N, int64_t K, hipStream_t stream);
