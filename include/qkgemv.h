@@ -17,6 +17,9 @@
  *   Q4_K (144 B / 256 w):  w = d * (sc * q) - dmin * m,  q 4-bit, sc/m 6-bit
  *   Q5_K (176 B / 256 w):  the same with 5-bit q
  *   Q6_K (210 B / 256 w):  w = d * sc * (q - 32),  q 6-bit, sc int8 per 16 w
+ *   IQ4_XS (136 B / 256 w): w = d * (ls - 32) * kv[q],  q 4-bit, ls 6-bit per
+ *          32 w, kv GGML's 16-entry non-linear int8 codebook (kernel prompt,
+ *          SPEC: IQ4_XS beside Q4_K under the same type flag)
  * Accumulation is fp32 throughout (design-doc prompt, "PHYSICS & CONTRACT").
  *
  * Memory layout (all little-endian, all buffers on the device):
@@ -48,17 +51,19 @@
 extern "C" {
 #endif
 
-/* Tensor-type flag: the GGUF / GGML type ids of the three formats. */
+/* Tensor-type flag: the GGUF / GGML type ids of the four formats. */
 enum {
     QK_Q4_K = 12,
     QK_Q5_K = 13,
-    QK_Q6_K = 14
+    QK_Q6_K = 14,
+    QK_IQ4_XS = 23
 };
 
 /* Return codes. */
 enum {
     QK_OK = 0,
-    QK_EINVAL_TYPE = -1,  /* type is not one of QK_Q4_K / QK_Q5_K / QK_Q6_K        */
+    QK_EINVAL_TYPE = -1,  /* type is not one of QK_Q4_K / QK_Q5_K / QK_Q6_K /
+                             QK_IQ4_XS, or a flag the call does not take       */
     QK_EINVAL_SHAPE = -2, /* N < 1, K < 256, K % 256 != 0, ncols not in 1..32,
                              or a size whose byte count overflows int64          */
     QK_EINVAL_PTR = -3,   /* a NULL pointer, W or x not 16-byte aligned, y /
@@ -88,15 +93,16 @@ enum {
  * Maximum-Speed Requirements And Execution Plan", Non-Negotiable Requirements,
  * item 7) allows GPU-native weight packs that are built once and kept
  * resident.  qk_gemv (ncols = 1), qk_gemv_batch and qk_dequant accept it;
- * qk_gemv with ncols > 1 does not (QK_EINVAL_TYPE).
+ * qk_gemv with ncols > 1 does not (QK_EINVAL_TYPE).  IQ4_XS has no PLANAR
+ * layout (QK_IQ4_XS | QK_PLANAR gives QK_EINVAL_TYPE everywhere).
  */
 #define QK_PLANAR 0x100
 
 /*
  * qk_gemv -- y[n][c] = sum_k dequant(W)[n][k] * x[k][c], fp32 accumulation.
  *
- *   type   QK_Q4_K, QK_Q5_K or QK_Q6_K (one flag for the whole tensor),
- *          optionally | QK_PLANAR (then ncols must be 1)
+ *   type   QK_Q4_K, QK_Q5_K, QK_Q6_K or QK_IQ4_XS (one flag for the whole
+ *          tensor); the k-quants optionally | QK_PLANAR (then ncols must be 1)
  *   W      device pointer to N rows of K/256 superblocks, 16-byte aligned
  *   x      device pointer to K*ncols fp16 values, 16-byte aligned
  *   y      device pointer to N*ncols fp32 values, 4-byte aligned (written)
@@ -121,7 +127,9 @@ enum {
  * b = 32 a) and an integer c nearest b/a, q - c formed exactly per weight:
  * no term exceeds three times its weight's |w x|, so the fp32 error stays
  * below about 3 * 40 * 2^-24 * sum |w x| (< 1e-5 of it), and a row whose
- * weights are all zero (d*sc*q = dmin*m) gives exactly 0.
+ * weights are all zero (d*sc*q = dmin*m) gives exactly 0.  IQ4_XS needs no
+ * shift: each 32-weight group is d*(ls - 32) * sum kv[q] x with the signed
+ * codebook values exact per weight, so every term is its own |w x|.
  */
 int qk_gemv(int type, const void *W, const void *x, void *y,
             int64_t N, int64_t K, int ncols, void *stream);
@@ -239,7 +247,8 @@ int qk_gemv_batch(const qk_gemv_item *items, int count, void *stream);
 /* One GEMV of a chain step (one column): as qk_gemv_ex, or as
  * qk_gemv_swiglu when W2 is set. */
 typedef struct qk_chain_entry {
-    int type;             /* QK_Q4_K / QK_Q5_K / QK_Q6_K, optionally | QK_PLANAR    */
+    int type;             /* QK_Q4_K / QK_Q5_K / QK_Q6_K, optionally | QK_PLANAR
+                             (QK_IQ4_XS: QK_EINVAL_TYPE)                          */
     int flags;            /* 0 or QK_Y_F16                                          */
     const void *W;        /* N rows of superblocks, 16-byte aligned                 */
     const void *W2;       /* NULL, or the up tensor of a SwiGLU pair (Q4_K only):
@@ -349,7 +358,8 @@ int qk_gemv_chain_noalloc(const void *plan, const void *plan_dev, void *status, 
  *   W      device pointer to N GGUF rows, 16-byte aligned (read)
  *   Wp     device pointer to N * qk_row_bytes(type | QK_PLANAR, K) bytes,
  *          16-byte aligned, not overlapping W (written)
- * Errors as for qk_dequant; overlapping W and Wp give QK_EINVAL_PTR.
+ * Errors as for qk_dequant; overlapping W and Wp give QK_EINVAL_PTR; type
+ * QK_IQ4_XS gives QK_EINVAL_TYPE (it has no PLANAR layout).
  */
 int qk_repack(int type, const void *W, void *Wp, int64_t N, int64_t K, void *stream);
 

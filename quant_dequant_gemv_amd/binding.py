@@ -14,7 +14,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqkgemv.so")
 
-Q4_K, Q5_K, Q6_K = 12, 13, 14
+Q4_K, Q5_K, Q6_K, IQ4_XS = 12, 13, 14, 23
 QK_OK, QK_EINVAL_TYPE, QK_EINVAL_SHAPE, QK_EINVAL_PTR, QK_ELAUNCH, QK_EINVAL_FLAGS = 0, -1, -2, -3, -4, -5
 MAX_NCOLS = 32
 MAX_BATCH = 16

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqkgemv.so")
 SOURCES = ["qk_api.hip", "qk_kernels.hip", "qk_verify.hip", "qk_verify_q4k.hip", "qk_verify_q5k.hip",
-           "qk_verify_q6k.hip"]
+           "qk_verify_q6k.hip", "qk_verify_iq4xs.hip"]
 CALIB_LIB = os.path.join(HERE, "libqkcalib.so")
 CALIB_SOURCES = ["qk_stream_read.hip"]
 ARCH = "gfx950"

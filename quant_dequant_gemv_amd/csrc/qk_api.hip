@@ -23,6 +23,7 @@ int block_bytes(int type) {
     case QK_Q4_K: return 144;
     case QK_Q5_K: return 176;
     case QK_Q6_K: return 210;
+    case QK_IQ4_XS: return 136;
     default: return -1;
     }
 }
@@ -33,6 +34,7 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 int64_t row_bytes_of(int type, int64_t K) {
     const int bb = block_bytes(type & ~QK_PLANAR);
     if (bb < 0 || (type & ~(QK_PLANAR | 0xff)) != 0 || K < 256 || (K % 256) != 0) return -1;
+    if (type == (QK_IQ4_XS | QK_PLANAR)) return -1;  // the k-quants only
     const int64_t b = (K / 256) * bb;
     return (type & QK_PLANAR) ? (b + 15) / 16 * 16 : b;
 }
@@ -43,7 +45,7 @@ int check_shape(int type, int64_t N, int64_t K, int ncols) {
     if (block_bytes(type & ~QK_PLANAR) < 0 || (type & ~(QK_PLANAR | 0xff)) != 0) return QK_EINVAL_TYPE;
     if (N < 1 || K < 256 || (K % 256) != 0) return QK_EINVAL_SHAPE;
     if (ncols < 1 || ncols > QK_MAX_NCOLS) return QK_EINVAL_SHAPE;
-    if ((type & QK_PLANAR) && ncols != 1) return QK_EINVAL_TYPE;
+    if ((type & QK_PLANAR) && (ncols != 1 || (type & ~QK_PLANAR) == QK_IQ4_XS)) return QK_EINVAL_TYPE;
     if (K > (int64_t)1 << 30 || N > ((int64_t)1 << 31) - 1) return QK_EINVAL_SHAPE;
     const int64_t row_bytes = row_bytes_of(type, K);
     if (N > INT64_MAX / row_bytes) return QK_EINVAL_SHAPE;
@@ -169,6 +171,7 @@ int qk_chain_plan(const qk_chain_entry *entries, int nentries, const int *step_s
         if (rc) return rc;
         if (e.flags & ~QK_Y_F16) return QK_EINVAL_FLAGS;
         if (e.W2 && (e.type & ~QK_PLANAR) != QK_Q4_K) return QK_EINVAL_TYPE;  // SwiGLU pairs: Q4_K
+        if (e.type == QK_IQ4_XS) return QK_EINVAL_TYPE;                       // k-quants only
         if (!e.W || !aligned(e.W, 16) || (e.W2 && !aligned(e.W2, 16))) return QK_EINVAL_PTR;
         if ((rc = check_io(e.type, e.W, e.x, e.y, e.residual, e.N, e.K, 1, e.flags))) return rc;
         if (e.W2 && overlap(e.y, ((e.flags & QK_Y_F16) ? 2 : 4) * e.N, e.W2, e.N * row_bytes_of(e.type, e.K)))
@@ -239,7 +242,7 @@ int qk_dequant(int type, const void *W, void *out, int64_t N, int64_t K, void *s
 }
 
 int qk_repack(int type, const void *W, void *Wp, int64_t N, int64_t K, void *stream) {
-    if (type & QK_PLANAR) return QK_EINVAL_TYPE;
+    if ((type & QK_PLANAR) || type == QK_IQ4_XS) return QK_EINVAL_TYPE;
     const int rc = check_shape(type, N, K, 1);
     if (rc) return rc;
     if (!W || !Wp || !aligned(W, 16) || !aligned(Wp, 16)) return QK_EINVAL_PTR;
@@ -253,8 +256,9 @@ const char *qk_strerror(int code) {
     switch (code) {
     case QK_OK: return "ok";
     case QK_EINVAL_TYPE:
-        return "invalid type: expected QK_Q4_K (12), QK_Q5_K (13) or QK_Q6_K (14), optionally | QK_PLANAR "
-               "(0x100) with ncols = 1 (qk_repack takes the type without the flag)";
+        return "invalid type: expected QK_Q4_K (12), QK_Q5_K (13), QK_Q6_K (14) or QK_IQ4_XS (23); the k-quants "
+               "optionally | QK_PLANAR (0x100) with ncols = 1 (qk_repack takes the type without the flag); "
+               "qk_repack and chains take the k-quants only, chain SwiGLU pairs Q4_K only";
     case QK_EINVAL_SHAPE:
         return "invalid shape: need N >= 1, K a positive multiple of 256, 1 <= ncols <= 32; a chain needs 1.."
                "QK_MAX_BATCH entries per step, a workspace of qk_chain_workspace_bytes, and for "

@@ -6,6 +6,9 @@
 //   Q4_K 144 B: d f16 @0, dmin f16 @2, scales[12] @4, qs[128] @16
 //   Q5_K 176 B: d @0, dmin @2, scales[12] @4, qh[32] @16, qs[128] @48
 //   Q6_K 210 B: ql[128] @0, qh[64] @128, scales[16] int8 @192, d f16 @208
+//   IQ4_XS 136 B: d f16 @0, scales_h u16 @2, scales_l[4] @4, qs[128] @8
+//            (GGML's block_iq4_xs; the same prompt's SPEC names IQ4_XS beside
+//            Q4_K under the type flag, GGML's dequantisation as the reference)
 //
 // Work unit.  A superblock is split into 4 "units" of 64 weights, one per
 // lane; the unit index q = 0..3 is a per-lane constant in every kernel.
@@ -13,6 +16,9 @@
 //                      2q+1 (high nibbles), i.e. weights 64q .. 64q+63.
 //   Q6_K unit q=2n+b : half n, rows l = 16b..16b+15 of all four quarters t,
 //                      i.e. weights 128n + 32t + 16b + (0..15), t = 0..3.
+//   IQ4_XS unit q    : sub-blocks 2q (qs[32q..32q+15]) and 2q+1 (the next 16
+//                      bytes); byte l of a sub-block holds its weights l (low
+//                      nibble) and l+16 (high nibble): weights 64q .. 64q+63.
 //
 // Quant "patterns".  Quants are turned into packed fp16 pairs without any
 // conversion instruction: a 16-bit pattern p < 2048 read as an fp16 is
@@ -31,7 +37,7 @@
 
 namespace qk {
 
-enum : int { Q4_K = 12, Q5_K = 13, Q6_K = 14 };
+enum : int { Q4_K = 12, Q5_K = 13, Q6_K = 14, IQ4_XS = 23 };
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -39,6 +45,7 @@ template <int T> struct Fmt;
 template <> struct Fmt<Q4_K> { static constexpr int bytes = 144; static constexpr int group = 32; };
 template <> struct Fmt<Q5_K> { static constexpr int bytes = 176; static constexpr int group = 32; };
 template <> struct Fmt<Q6_K> { static constexpr int bytes = 210; static constexpr int group = 16; };
+template <> struct Fmt<IQ4_XS> { static constexpr int bytes = 136; static constexpr int group = 32; };
 
 // ---------------------------------------------------------------------------
 // Row layouts.  GGUF: a row is K/256 superblocks back to back, as in the file.
@@ -59,7 +66,7 @@ enum : int { GGUF = 0, PLANAR = 1 };
 
 __host__ __device__ constexpr int64_t layout_row_bytes(int T, int L, int64_t K) {
     const int64_t S = K / 256;
-    const int64_t b = S * (T == Q4_K ? 144 : T == Q5_K ? 176 : 210);
+    const int64_t b = S * (T == Q4_K ? 144 : T == Q5_K ? 176 : T == IQ4_XS ? 136 : 210);
     return (L == PLANAR && T == Q6_K) ? (b + 15) / 16 * 16 : b;
 }
 
@@ -93,6 +100,10 @@ template <> struct UnitAddr<Q6_K, GGUF> {
         sc = sb + 192u + 8u * n;
         d = sb + 208u;
     }
+};
+template <> struct UnitAddr<IQ4_XS, GGUF> {
+    uint32_t h, a, b;
+    __host__ __device__ UnitAddr(int /*S*/, int u) : h(136u * (u >> 2)), a(h + 8u + 32u * (u & 3)), b(a + 16u) {}
 };
 template <> struct UnitAddr<Q6_K, PLANAR> {
     uint32_t a, b, c, sc, d;
@@ -350,6 +361,70 @@ template <> struct Unit<Q6_K> {
         const uint32_t wv = idx < 4 ? sc.x : sc.y;
         return (int)(int8_t)(uint8_t)(wv >> (8 * (idx & 3)));
     }
+};
+
+// ---------------------------------------------------------------------------
+// IQ4_XS.  A 4-bit index selects one of 16 signed integers kv (GGML's
+// non-linear IQ4_NL codebook, below); sub-block ib's weights are
+// d * (ls_ib - 32) * kv with the 6-bit scale ls_ib = nibble (ib & 1) of
+// scales_l[ib / 2] | bits 2ib..2ib+1 of scales_h << 4.  The codebook is
+// increasing: indices 0..7 are its negative entries, 8..15 its positive ones,
+// so bit 3 of an index is the sign and its low 3 bits pick a magnitude from
+// one of two 8-entry tables.  Patterns are the fp16 values kv * 2^-24 (a
+// sign bit over |kv| <= 127: exact subnormals, so every product with an
+// fp16 x is exact), built with byte permutes (v_perm_b32 picks each result
+// byte from 8 source bytes by a selector byte 0..7), four indices at a time.
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr uint32_t bytes4(int b0, int b1, int b2, int b3) {
+    return (uint32_t)b0 | (uint32_t)b1 << 8 | (uint32_t)b2 << 16 | (uint32_t)b3 << 24;
+}
+// |kv| of indices 0..3, 4..7 (kv < 0) and 8..11, 12..15 (kv > 0)
+constexpr uint32_t IQ4_MAG0 = bytes4(127, 104, 83, 65), IQ4_MAG1 = bytes4(49, 35, 22, 10);
+constexpr uint32_t IQ4_MAG2 = bytes4(1, 13, 25, 38), IQ4_MAG3 = bytes4(53, 69, 89, 113);
+
+// v: four indices in bits 0..3 of its bytes (higher bits ignored), those of
+// weights (l, l+1, l+2, l+3).  pa = the pattern pair of weights (l, l+2),
+// pb = (l+1, l+3), as the other types' pairs A and B.
+__device__ __forceinline__ void iq4_pairs(uint32_t v, uint32_t &pa, uint32_t &pb) {
+    const uint32_t s7 = v & 0x07070707u;
+    const uint32_t neg = __builtin_amdgcn_perm(IQ4_MAG1, IQ4_MAG0, s7);
+    const uint32_t pos = __builtin_amdgcn_perm(IQ4_MAG3, IQ4_MAG2, s7);
+    const uint32_t sel = ((v >> 1) & 0x04040404u) | 0x03020100u;  // byte k: k, or 4 + k if index >= 8
+    const uint32_t mag = __builtin_amdgcn_perm(pos, neg, sel);
+    const uint32_t sgn = __builtin_amdgcn_perm(0u, 0x80808080u, sel);  // 0x80 where index < 8
+    pa = __builtin_amdgcn_perm(sgn, mag, 0x06020400u);  // |kv0|, sign0, |kv2|, sign2
+    pb = __builtin_amdgcn_perm(sgn, mag, 0x07030501u);
+}
+
+// The 8-byte header and the unit's 32 bytes of qs (superblocks are 8-byte
+// aligned only: unaligned 16-byte loads, as for Q6_K).  Patterns of qs word
+// i (bytes l = 4(i & 3) .. of sub-block 2q + (i >> 2)):
+//   p[0], p[1] = pairs A, B of the low nibbles (weights l ..)
+//   p[2], p[3] = pairs A, B of the high nibbles (weights l + 16 ..)
+template <> struct Unit<IQ4_XS> {
+    uint2 h;  // .x = d | scales_h << 16, .y = scales_l[0..3]
+    uint4 a, b;
+    template <bool NT, int L>
+    __device__ __forceinline__ void load(const uint8_t *base, uint32_t off, const UnitAddr<IQ4_XS, L> &o) {
+        h = ld8<NT>(base + (off + o.h));
+        a = ld16<NT>(base + (off + o.a));
+        b = ld16<NT>(base + (off + o.b));
+        issue_together();
+    }
+    __device__ __forceinline__ uint32_t qword(int i) const { return i < 4 ? word(a, i) : word(b, i - 4); }
+    __device__ __forceinline__ void patterns(int i, int /*q*/, uint32_t p[4]) const {
+        const uint32_t w = qword(i);
+        iq4_pairs(w, p[0], p[1]);
+        iq4_pairs(w >> 4, p[2], p[3]);
+    }
+    // ls - 32 of sub-block 2q + hi (hi = 0, 1)
+    __device__ __forceinline__ int scale(int q, int hi) const {
+        const uint32_t lo4 = __builtin_amdgcn_ubfe(h.y, 8u * q + 4u * hi, 4u);
+        const uint32_t hi2 = __builtin_amdgcn_ubfe(h.x, 16u + 4u * q + 2u * hi, 2u);
+        return (int)(lo4 | hi2 << 4) - 32;
+    }
+    // d * 2^24 (exact: the patterns carry 2^-24)
+    __device__ __forceinline__ float d24() const { return f16_lo(h.x) * 0x1p24f; }
 };
 
 }  // namespace qk

@@ -179,9 +179,35 @@ __device__ __forceinline__ float unit_dot_q6(const Unit<Q6_K> &U, int q, const X
 }
 
 // Dot of one unit with the register-held x of the same unit column.
+// IQ4_XS: d*(ls - 32) * sum kv x per sub-block, kv*2^-24 on the patterns
+// (signed, exact) and d*2^24 from the unit: no min term, nothing to cancel.
+// Word i of the low sub-block holds x pairs i (low nibbles) and 4 + i (high);
+// word 4 + i of the high sub-block pairs 8 + i and 12 + i.
+__device__ __forceinline__ float unit_dot_iq4(const Unit<IQ4_XS> &U, int q, const XReg<IQ4_XS> &X) {
+    float aL = 0.f, aH = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t pl[4], ph[4];
+        U.patterns(i, q, pl);
+        U.patterns(i + 4, q, ph);
+        aL = dot2(pl[0], X.xr[2 * i], aL);
+        aH = dot2(ph[0], X.xr[2 * (i + 8)], aH);
+        aL = dot2(pl[1], X.xr[2 * i + 1], aL);
+        aH = dot2(ph[1], X.xr[2 * (i + 8) + 1], aH);
+        aL = dot2(pl[2], X.xr[2 * (i + 4)], aL);
+        aH = dot2(ph[2], X.xr[2 * (i + 12)], aH);
+        aL = dot2(pl[3], X.xr[2 * (i + 4) + 1], aL);
+        aH = dot2(ph[3], X.xr[2 * (i + 12) + 1], aH);
+    }
+    const float d = U.d24();
+    return __builtin_fmaf(d * (float)U.scale(q, 0), aL, d * (float)U.scale(q, 1) * aH);
+}
+
 template <int T, int L>
 __device__ __forceinline__ float unit_dot(const Unit<T> &U, int q, const KScaleSel &sel, const XReg<T> &X) {
-    if constexpr (T == Q6_K) {
+    if constexpr (T == IQ4_XS) {
+        return unit_dot_iq4(U, q, X);
+    } else if constexpr (T == Q6_K) {
         return unit_dot_q6<L>(U, q, X);
     } else {
         // The shifted form of each sub-block (KShift).  Units of 2^-48: the
@@ -397,7 +423,7 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     // 2^21, short of the next multiple of 2^32 (at least 2^32 / P >= 2^22
     // away).  ceil(2^32 / P) itself would not fit 32 bits for P = 1.
     const uint32_t inv_p2 = (0x80000000u + (uint32_t)P - 1u) / (uint32_t)P;
-    constexpr float oscale = T == Q6_K ? 1.f : 0x1p48f;
+    constexpr float oscale = T == Q6_K || T == IQ4_XS ? 1.f : 0x1p48f;
     // the sum of schedule row v (valid or not, every lane of the 16 takes part)
     auto row_sum = [&](int v, bool ok) {
         const int vi = (int)__umulhi(2u * (uint32_t)v, inv_p2);
@@ -470,7 +496,10 @@ __global__ void __launch_bounds__((gemv1_bound<T, RL, D>())) gemv1_kernel(const 
 // with more threads than its entry needs retires the surplus waves at once
 // (a retired wave does not hold up the barrier).
 // ---------------------------------------------------------------------------
-enum BodyCode { B_Q4_1, B_Q4_2, B_Q4_4, B_Q4_6, B_Q4_8, B_Q4_12, B_Q5_1, B_Q5_2, B_Q6_1, B_Q6_2, B_COUNT };
+enum BodyCode {
+    B_Q4_1, B_Q4_2, B_Q4_4, B_Q4_6, B_Q4_8, B_Q4_12, B_Q5_1, B_Q5_2, B_Q6_1, B_Q6_2,
+    B_IQ4_1, B_IQ4_2, B_IQ4_4, B_IQ4_6, B_IQ4_8, B_IQ4_12, B_COUNT
+};
 // code + B_COUNT: the same body on the PLANAR layout
 
 struct BatchItem {
@@ -509,6 +538,12 @@ __global__ void __launch_bounds__(1024) gemv1_batch_kernel(const BatchArgs a) {
     case B_Q5_2: QK_BODY(Q5_K, 2, 2); break;
     case B_Q6_1: QK_BODY(Q6_K, 1, 1); break;
     case B_Q6_2: QK_BODY(Q6_K, 2, 2); break;
+    case B_IQ4_1: QK_BODY(IQ4_XS, 1, 1); break;
+    case B_IQ4_2: QK_BODY(IQ4_XS, 2, 2); break;
+    case B_IQ4_4: QK_BODY(IQ4_XS, 4, 2); break;
+    case B_IQ4_6: QK_BODY(IQ4_XS, 6, 2); break;
+    case B_IQ4_8: QK_BODY(IQ4_XS, 8, 2); break;
+    case B_IQ4_12: QK_BODY(IQ4_XS, 12, 2); break;
     case B_COUNT + B_Q4_1: QK_BODYP(Q4_K, 1, 1); break;
     case B_COUNT + B_Q4_2: QK_BODYP(Q4_K, 2, 2); break;
     case B_COUNT + B_Q4_4: QK_BODYP(Q4_K, 4, 2); break;
@@ -528,7 +563,8 @@ __global__ void __launch_bounds__(1024) gemv1_batch_kernel(const BatchArgs a) {
 // ---------------------------------------------------------------------------
 // Dequantisation, one 64-weight unit per thread, through the same unit loads
 // and pattern decoders as the GEMV.  Q4_K/Q5_K: w = (d*sc)*q - dmin*m (both
-// products exact in fp32, one rounding); Q6_K: w = d * (sc*(q-32)) (exact).
+// products exact in fp32, one rounding); Q6_K: w = d * (sc*(q-32)) (exact);
+// IQ4_XS: w = d*(ls-32)*kv (exact).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t pat_lo(uint32_t p, int shift) { return (p & 0xffffu) >> shift; }
 __device__ __forceinline__ uint32_t pat_hi(uint32_t p, int shift) { return (p >> 16) >> shift; }
@@ -545,7 +581,25 @@ __global__ void __launch_bounds__(WG) dequant_kernel(const uint8_t *__restrict__
     float *o = out + (size_t)row * (size_t)K + 256 * s;
     Unit<T> U;
     U.template load<false, L>(W + (size_t)row * (size_t)layout_row_bytes(T, L, K), 0u, UnitAddr<T, L>(K >> 8, u));
-    if constexpr (T == Q6_K) {
+    if constexpr (T == IQ4_XS) {
+        // d*2^24*(ls - 32) exact (17 significant bits), times kv*2^-24 from
+        // the pattern: at most 24 significant bits, exact
+        const float d = U.d24();
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi) {
+            const float f = d * (float)U.scale(q, hi);
+            float *ob = o + 64 * q + 32 * hi;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t p[4];
+                U.patterns(4 * hi + i, q, p);
+                *reinterpret_cast<float4 *>(ob + 4 * i) =
+                    make_float4(f * f16_lo(p[0]), f * f16_lo(p[1]), f * f16_hi(p[0]), f * f16_hi(p[1]));
+                *reinterpret_cast<float4 *>(ob + 16 + 4 * i) =
+                    make_float4(f * f16_lo(p[2]), f * f16_lo(p[3]), f * f16_hi(p[2]), f * f16_hi(p[3]));
+            }
+        }
+    } else if constexpr (T == Q6_K) {
         const float d = f16_lo(U.d);
         const int kb = 128 * (q >> 1) + 16 * (q & 1);
 #pragma unroll
@@ -671,6 +725,8 @@ static int cu_count() { return device_cus(); }
 // Q4_K rounds go up to 12 rows.
 template <int T> struct RowRounds;
 template <> struct RowRounds<Q4_K> { static constexpr int n = 6, rl[n] = {1, 2, 4, 6, 8, 12}, max_threads = 512; };
+// IQ4_XS: 4-bit quants in units of 10 dwords, rounds as for Q4_K
+template <> struct RowRounds<IQ4_XS> { static constexpr int n = 6, rl[n] = {1, 2, 4, 6, 8, 12}, max_threads = 512; };
 template <> struct RowRounds<Q5_K> { static constexpr int n = 4, rl[n] = {1, 2, 3, 4}, max_threads = 512; };
 template <> struct RowRounds<Q6_K> { static constexpr int n = 1, rl[n] = {1}, max_threads = 1024, ring_threads = 768; };
 static_assert(RowRounds<Q6_K>::ring_threads == gemv1_bound<Q6_K, 2, 2>(), "gemv1_kernel's bound for Q6_K rings");
@@ -697,7 +753,7 @@ static size_t part_lds(int64_t N, const Geo &g, int mult = 1) {
 // workgroup's x staging and reduction).
 template <int T, int L>
 static bool small_workgroups(int64_t N, int cus, int mult, Geo &g) {
-    if constexpr (T != Q4_K) {
+    if constexpr (T != Q4_K && T != IQ4_XS) {
         return false;
     } else {
         using RR = RowRounds<T>;
@@ -810,9 +866,9 @@ static hipError_t gemv1_dispatch(const void *W, const void *x, void *y, int64_t 
     case 2: if constexpr (T != Q6_K || L == PLANAR) return launch1<T, L, 2, RING, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
     case 3: if constexpr (T == Q5_K) return launch1<T, L, 3, RING, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
     case 4: if constexpr (T != Q6_K) return launch1<T, L, 4, RING, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
-    case 6: if constexpr (T == Q4_K) return launch1<T, L, 6, RING, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
-    case 8: if constexpr (T == Q4_K) return launch1<T, L, 8, RING, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
-    case 12: if constexpr (T == Q4_K) return launch1<T, L, 12, RING, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 6: if constexpr (T == Q4_K || T == IQ4_XS) return launch1<T, L, 6, RING, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 8: if constexpr (T == Q4_K || T == IQ4_XS) return launch1<T, L, 8, RING, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
+    case 12: if constexpr (T == Q4_K || T == IQ4_XS) return launch1<T, L, 12, RING, NT, PAIR>(W, x, y, N, K, geo, ep, st); break;
     default: break;
     }
     return hipErrorInvalidValue;
@@ -831,6 +887,7 @@ hipError_t launch_gemv1(int type, const void *W, const void *x, void *y, int64_t
     case Q4_K: return gemv1_pair<Q4_K, GGUF>(W, x, y, N, K, ep, st);
     case Q5_K: return gemv1_pair<Q5_K, GGUF>(W, x, y, N, K, ep, st);
     case Q6_K: return gemv1_pair<Q6_K, GGUF>(W, x, y, N, K, ep, st);
+    case IQ4_XS: return gemv1_pair<IQ4_XS, GGUF>(W, x, y, N, K, ep, st);
     case Q4_K | PLANAR_FLAG: return gemv1_pair<Q4_K, PLANAR>(W, x, y, N, K, ep, st);
     case Q5_K | PLANAR_FLAG: return gemv1_pair<Q5_K, PLANAR>(W, x, y, N, K, ep, st);
     case Q6_K | PLANAR_FLAG: return gemv1_pair<Q6_K, PLANAR>(W, x, y, N, K, ep, st);
@@ -843,6 +900,7 @@ static Geo geometry_of(int type, int64_t N, int64_t K, int cus) {
     switch (type & ~PLANAR_FLAG) {
     case Q4_K: return planar ? geometry<Q4_K, PLANAR>(N, K, cus) : geometry<Q4_K, GGUF>(N, K, cus);
     case Q5_K: return geometry<Q5_K>(N, K, cus);
+    case IQ4_XS: return geometry<IQ4_XS>(N, K, cus);
     default: return planar ? geometry<Q6_K, PLANAR>(N, K, cus) : geometry<Q6_K, GGUF>(N, K, cus);
     }
 }
@@ -851,6 +909,7 @@ static int body_code_gguf(int type, int rl);
 
 static int body_code(int type_flags, int rl) {
     const int type = type_flags & ~PLANAR_FLAG, plane = (type_flags & PLANAR_FLAG) ? B_COUNT : 0;
+    if (plane && type == IQ4_XS) return -1;  // GGUF rows only
     const int c = body_code_gguf(type, rl);
     return c < 0 ? -1 : c + plane;
 }
@@ -872,6 +931,17 @@ static int body_code_gguf(int type, int rl) {
     // of loads)
     if (type == Q5_K) return rl == 1 ? B_Q5_1 : (rl >= 2 && rl <= 4) ? B_Q5_2 : -1;
     if (type == Q6_K) return rl == 1 ? B_Q6_1 : rl == 2 ? B_Q6_2 : -1;
+    if (type == IQ4_XS) {
+        switch (rl) {
+        case 1: return B_IQ4_1;
+        case 2: return B_IQ4_2;
+        case 4: return B_IQ4_4;
+        case 6: return B_IQ4_6;
+        case 8: return B_IQ4_8;
+        case 12: return B_IQ4_12;
+        default: return -1;
+        }
+    }
     return -1;
 }
 
@@ -978,6 +1048,7 @@ struct ChainEntryD {
     int32_t N, K, useg, P, threads, code, first, last, f16, pad;
 };
 constexpr int CHAIN_PAIR = 32;  // code + CHAIN_PAIR: the SwiGLU pair body
+static_assert(2 * B_COUNT <= CHAIN_PAIR, "chain body codes");
 // dynamic LDS of the chain kernel: the most a workgroup may take, less the
 // kernel's static word
 constexpr int CHAIN_LDS_MAX = LDS_MAX - 64;
@@ -1097,7 +1168,7 @@ __device__ __forceinline__ void chain_body(const ChainEntryD &e, int blk, int nb
 
 __device__ __forceinline__ int chain_code_type(int code) {
     const int c = (code & (CHAIN_PAIR - 1)) % B_COUNT;
-    return c <= B_Q4_12 ? Q4_K : c <= B_Q5_2 ? Q5_K : Q6_K;
+    return c <= B_Q4_12 ? Q4_K : c <= B_Q5_2 ? Q5_K : c <= B_Q6_2 ? Q6_K : IQ4_XS;
 }
 
 __global__ void __launch_bounds__(1024) gemv1_chain_kernel(const uint8_t *__restrict__ plan, uint32_t *sync,
@@ -1372,6 +1443,7 @@ hipError_t launch_dequant(int type, const void *W, void *out, int64_t N, int64_t
     case Q4_K: return launch_deq<Q4_K, GGUF>(W, out, N, K, st);
     case Q5_K: return launch_deq<Q5_K, GGUF>(W, out, N, K, st);
     case Q6_K: return launch_deq<Q6_K, GGUF>(W, out, N, K, st);
+    case IQ4_XS: return launch_deq<IQ4_XS, GGUF>(W, out, N, K, st);
     case Q4_K | PLANAR_FLAG: return launch_deq<Q4_K, PLANAR>(W, out, N, K, st);
     case Q5_K | PLANAR_FLAG: return launch_deq<Q5_K, PLANAR>(W, out, N, K, st);
     case Q6_K | PLANAR_FLAG: return launch_deq<Q6_K, PLANAR>(W, out, N, K, st);

@@ -20,7 +20,8 @@
 //     B column j = the quant patterns of row j for one 32-bit quant word,
 //                  shifted by the row's integer c of the scale group (exact
 //                  fp16 values s*(q-c)*2^-24, weights (l, l+2, l+1, l+3);
-//                  c = 32 for Q6_K, see KShift in qk_format.h),
+//                  c = 32 for Q6_K, see KShift in qk_format.h; IQ4_XS: the
+//                  signed codebook values kv*2^-24, nothing to shift),
 //     A row i    = x column 4*cb + i at the same four weights, held in
 //                  registers by lane i of the block for the whole segment,
 //     D[i][j]    = sum over the word of x_i * q_j.
@@ -306,7 +307,32 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
                 float val[NC];
                 // each quant word's patterns once, multiplied into every
                 // column block's accumulators
-                if constexpr (T == Q6_K) {
+                if constexpr (T == IQ4_XS) {
+                    // signed codebook patterns kv*2^-24 (exact), d*2^24*(ls-32)
+                    // per sub-block; x pairs as in the one-column kernel
+                    const float d = Un.d24();
+                    const float fl = d * (float)Un.scale(q, 0), fh = d * (float)Un.scale(q, 1);
+                    float4_t Dl[NCB], Dh[NCB];
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) Dl[cb] = Dh[cb] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        uint32_t pl[4], ph[4];
+                        Un.patterns(i, q, pl);
+                        Un.patterns(i + 4, q, ph);
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb) {
+                            Dl[cb] = mfma4(xr[cb][2 * i], xr[cb][2 * i + 1], pl[0], pl[1], Dl[cb]);
+                            Dh[cb] = mfma4(xr[cb][2 * (i + 8)], xr[cb][2 * (i + 8) + 1], ph[0], ph[1], Dh[cb]);
+                            Dl[cb] = mfma4(xr[cb][2 * (i + 4)], xr[cb][2 * (i + 4) + 1], pl[2], pl[3], Dl[cb]);
+                            Dh[cb] = mfma4(xr[cb][2 * (i + 12)], xr[cb][2 * (i + 12) + 1], ph[2], ph[3], Dh[cb]);
+                        }
+                    }
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) val[4 * cb + i] = __builtin_fmaf(fl, Dl[cb][i], fh * Dh[cb][i]);
+                } else if constexpr (T == Q6_K) {
                     const float d = f16_lo(Un.d);
                     float f[4];
 #pragma unroll
@@ -408,7 +434,7 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
     // y[row][c] = sum over the slots, fixed order: 16 lanes per row, lane s
     // adds slots s, s+16, ..., then a DPP fold of the 16 lanes per column
     const int s16 = tid & 15;
-    constexpr float oscale = T == Q6_K ? 1.f : 0x1p48f;
+    constexpr float oscale = T == Q6_K || T == IQ4_XS ? 1.f : 0x1p48f;
     // the sums of schedule row v per column (every lane of the 16 takes part)
     auto row_sums = [&](int v, bool ok, float *a) {
         const float *pr = part + (size_t)(ok ? v : 0) * nslot * NC;

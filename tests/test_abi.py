@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from quant_dequant_gemv_amd import binding
@@ -116,6 +117,26 @@ def test_planar_row_bytes_and_flag_validation():
     assert binding.qk_gemv(binding.Q4_K | 0x200, FAKE, FAKE, FAKE, 4, 256, 1, 0) == binding.QK_EINVAL_TYPE
     assert binding.qk_dequant(binding.Q5_K | P, FAKE, FAKE, 4, 300, 0) == binding.QK_EINVAL_SHAPE
     assert binding.qk_gemv_batch([(binding.Q6_K | P, FAKE, FAKE, FAKE + 2, 4, 256)], 0) == binding.QK_EINVAL_PTR
+
+
+def test_iq4xs_type_codes():
+    """IQ4_XS (GGUF id 23, 136-byte superblocks) is a type of its own for the
+    GEMV, verify, epilogue, batch and dequant calls; it has no PLANAR layout,
+    no repack and no chain entries."""
+    IQ, P = binding.IQ4_XS, binding.PLANAR
+    assert binding.qk_block_bytes(IQ) == 136
+    assert binding.qk_row_bytes(IQ, 5120) == 20 * 136
+    assert binding.qk_row_bytes(IQ | P, 5120) == -1
+    assert binding.qk_gemv(IQ | P, FAKE, FAKE, FAKE, 4, 256, 1, 0) == binding.QK_EINVAL_TYPE
+    assert binding.qk_dequant(IQ | P, FAKE, 4 * FAKE, 4, 256, 0) == binding.QK_EINVAL_TYPE
+    assert binding.qk_gemv_batch([(IQ | P, FAKE, FAKE, 4 * FAKE, 4, 256)], 0) == binding.QK_EINVAL_TYPE
+    assert binding.qk_repack(IQ, FAKE, 4 * FAKE, 4, 256, 0) == binding.QK_EINVAL_TYPE
+    # the argument checks before any launch apply as for the k-quants
+    assert binding.qk_gemv(IQ, FAKE, FAKE, FAKE, 4, 300, 1, 0) == binding.QK_EINVAL_SHAPE
+    assert binding.qk_gemv(IQ, FAKE + 8, FAKE, 4 * FAKE, 4, 256, 1, 0) == binding.QK_EINVAL_PTR
+    e = binding.qk_chain_entry(IQ, 0, FAKE, None, FAKE, 4 * FAKE, None, 4, 256)
+    plan = np.zeros(binding.qk_chain_plan_bytes(1, 1), dtype=np.uint8)
+    assert binding.qk_chain_plan([e], [1], plan) == binding.QK_EINVAL_TYPE
 
 
 def test_repack_validation_codes():

@@ -10,7 +10,7 @@ from quant_dequant_gemv_amd import binding, synth
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
-Q4, Q5, Q6 = synth.Q4_K, synth.Q5_K, synth.Q6_K
+Q4, Q5, Q6, IQ4 = synth.Q4_K, synth.Q5_K, synth.Q6_K, synth.IQ4_XS
 
 
 def _make(entries):
@@ -58,6 +58,14 @@ def test_batch_gate_up():
 def test_batch_distinct_shapes_all_rows():
     _check([(Q5, 300, 6144, 7, "a"), (Q6, 200, 17408, 8, "b"), (Q4, 1000, 5120, 9, "c"), (Q4, 1, 256, 10, "d"),
             (Q6, 5, 512, 11, "e"), (Q5, 777, 1280, 12, "f")])
+
+
+def test_batch_iq4xs_entries():
+    # IQ4_XS beside the k-quants: a stacked run of two IQ4_XS entries sharing
+    # x (one joint geometry), an IQ4_XS entry at rounds of 12 rows, and
+    # k-quant entries around them
+    _check([(IQ4, 4096, 5120, 30, "h"), (IQ4, 1024, 5120, 31, "h"), (Q4, 512, 5120, 32, "h"),
+            (IQ4, 38000, 5120, 33, "g"), (Q6, 96, 1024, 34, "k"), (IQ4, 7, 256, 35, "m")], sample=256)
 
 
 def test_batch_sixteen_entries_shared_weights():

@@ -24,13 +24,13 @@ import torch
 
 import oracle
 from gpu_util import assert_row_bound, dev, gpu_dequant, gpu_gemv, needs_gpu, same_f32
-from kquant_pack import half_bits, make_k_block, make_q6_block
+from kquant_pack import half_bits, make_iq4xs_block, make_k_block, make_q6_block
 from quant_dequant_gemv_amd import binding, synth
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
-Q4, Q5, Q6 = synth.Q4_K, synth.Q5_K, synth.Q6_K
-NAMES = {Q4: "Q4_K", Q5: "Q5_K", Q6: "Q6_K"}
+Q4, Q5, Q6, IQ4 = synth.Q4_K, synth.Q5_K, synth.Q6_K, synth.IQ4_XS
+NAMES = {Q4: "Q4_K", Q5: "Q5_K", Q6: "Q6_K", IQ4: "IQ4_XS"}
 BB = synth.BLOCK_BYTES
 
 
@@ -60,6 +60,8 @@ def scale_sweep_tensor(qt, rng):
     if qt == Q6:
         raw[:, :, 208:210] = d.view(np.uint8).reshape(N, per_row, 2)
         raw[:, :, 192:208] = rng.integers(-128, 128, size=(N, per_row, 16), dtype=np.int16).astype(np.int8).view(np.uint8)
+    elif qt == IQ4:  # d only; the random scale bytes give every 6-bit ls, 32 (zero sub-blocks) included
+        raw[:, :, 0:2] = d.view(np.uint8).reshape(N, per_row, 2)
     else:
         dmin = np.stack([row[rng.permutation(per_row)] for row in pats])
         raw[:, :, 0:2] = d.view(np.uint8).reshape(N, per_row, 2)
@@ -67,7 +69,7 @@ def scale_sweep_tensor(qt, rng):
     return raw.reshape(N, per_row * BB[qt]), N, K
 
 
-@pytest.fixture(scope="module", params=[Q4, Q5, Q6], ids=lambda t: NAMES[t])
+@pytest.fixture(scope="module", params=[Q4, Q5, Q6, IQ4], ids=lambda t: NAMES[t])
 def sweep(request):
     qt = request.param
     W, N, K = scale_sweep_tensor(qt, np.random.default_rng(4000 + qt))
@@ -86,6 +88,11 @@ def test_scale_sweep_covers_every_class(sweep):
     if qt == Q6:
         sc = W.reshape(-1, 210)[:, 192:208].view(np.int8)
         assert sc.min() == -128 and sc.max() == 127
+    if qt == IQ4:
+        b = W.reshape(-1, 136)
+        sh = b[:, 2:4].copy().view(np.uint16)[:, 0].astype(np.int64)
+        ls = [((b[:, 4 + ib // 2] >> (4 * (ib % 2))) & 15) | (((sh >> (2 * ib)) & 3) << 4) for ib in range(8)]
+        assert len(np.unique(np.concatenate(ls))) == 64  # every 6-bit scale, 32 (zero sub-block) included
 
 
 def test_scale_sweep_dequant_bit_exact(sweep):
@@ -106,6 +113,9 @@ def test_scale_sweep_planar_rows(sweep):
     qt, W, N, K = sweep
     x = synth.activations(K, 1, 4200)
     Wd = dev(W.reshape(-1))
+    if qt == IQ4:  # no PLANAR layout: refused before any launch
+        assert binding.qk_repack(qt, Wd.data_ptr(), Wd.data_ptr(), N, K, 0) == binding.QK_EINVAL_TYPE
+        return
     Wp = binding.repack(qt, Wd, N, K)
     yp = binding.gemv(qt | binding.PLANAR, Wp, dev(x), N, K)
     torch.cuda.synchronize()
@@ -155,6 +165,31 @@ def wide_x(K, ncols, rng):
 
 
 CANCEL = [(qt, moved) for qt in (Q4, Q5, Q6) for moved in (0.0, 0.05)]
+
+
+def test_iq4xs_zero_and_extreme_scales():
+    """IQ4_XS has no min term, so nothing cancels between terms; a sub-block is
+    zero only through ls = 32 (or d = 0).  Rows of zero sub-blocks give
+    exactly 0 at every width; rows mixing zero sub-blocks with ls = 0 / 63
+    and every codebook index meet the bound, x over the whole fp16 range."""
+    rng = np.random.default_rng(4800)
+    N, K = 40, 1280
+    rows = []
+    for r in range(N):
+        blocks = []
+        for _ in range(K // 256):
+            d = float(2.0 ** rng.integers(-24, 10)) * float(rng.choice([-1, 1]))
+            ls = np.full(8, 32) if r < N // 2 else rng.choice([0, 1, 31, 32, 33, 62, 63], 8)
+            blocks.append(make_iq4xs_block(half_bits(d), ls, rng.integers(0, 16, 256)))
+        rows.append(np.concatenate(blocks))
+    W = np.stack(rows)
+    assert not oracle.dequant(IQ4, W[:N // 2], K).any()
+    for ncols in (1, 2, 8, 17):
+        for name, x in _xs(K, ncols, 4810 + ncols).items():
+            y = gpu_gemv(IQ4, W, x, N, K)
+            y_ref, S = oracle.gemv(IQ4, W, x, K)
+            assert (y[:N // 2] == 0).all(), f"IQ4_XS zero rows ncols={ncols} x {name}"
+            assert_row_bound(y, y_ref, S, f"IQ4_XS extreme scales ncols={ncols} x {name}")
 
 
 @pytest.fixture(scope="module", params=CANCEL, ids=lambda p: f"{NAMES[p[0]]}-{'exact' if p[1] == 0 else 'near'}")

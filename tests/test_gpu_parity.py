@@ -18,9 +18,9 @@ from quant_dequant_gemv_amd import synth
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
-Q4, Q5, Q6 = synth.Q4_K, synth.Q5_K, synth.Q6_K
-TYPES = [Q4, Q5, Q6]
-NAMES = {Q4: "Q4_K", Q5: "Q5_K", Q6: "Q6_K"}
+Q4, Q5, Q6, IQ4 = synth.Q4_K, synth.Q5_K, synth.Q6_K, synth.IQ4_XS
+TYPES = [Q4, Q5, Q6, IQ4]
+NAMES = {Q4: "Q4_K", Q5: "Q5_K", Q6: "Q6_K", IQ4: "IQ4_XS"}
 
 # (N, K): tiny, ragged row counts, several superblocks, the real K values, and
 # K beyond one segment of the one-column kernel (512 units = 32768 weights):
@@ -43,7 +43,10 @@ def test_dequant_bit_exact(qt, N, K):
 
 def test_dequant_worked_examples():
     import glob, os
-    for path in sorted(glob.glob(os.path.join(os.path.dirname(__file__), "golden", "q*_e*.txt"))):
+    here = os.path.join(os.path.dirname(__file__), "golden")
+    paths = sorted(glob.glob(os.path.join(here, "q*_e*.txt")) + glob.glob(os.path.join(here, "iq*_e*.txt")))
+    assert any("iq4xs" in p for p in paths)
+    for path in paths:
         qt, form, block, values = load_golden(path)
         w = gpu_dequant(qt, block[None, :], 1, 256)[0]
         assert same_f32(w, oracle.dequant(qt, block[None, :], 256)[0]), path
@@ -116,7 +119,9 @@ def test_gemv_subnormal_x(qt):
 # its own seed.  Checked on every row (the oracle takes tens of ms per tensor).
 FULL_SHAPES = [dict(synth.SMALL, name="small")] + synth.Q4K_PROJECTIONS + synth.MIXED + [
     dict(name="attn_k", qtype=Q4, N=1024, K=5120, seed=1001),
-    dict(name="ssm_alpha", qtype=Q6, N=48, K=5120, seed=1002)]
+    dict(name="ssm_alpha", qtype=Q6, N=48, K=5120, seed=1002),
+    dict(name="iq4xs_ffn_up", qtype=IQ4, N=17408, K=5120, seed=1003),
+    dict(name="iq4xs_ffn_down", qtype=IQ4, N=5120, K=17408, seed=1004)]
 
 
 @pytest.mark.parametrize("case", FULL_SHAPES, ids=lambda c: c["name"])
@@ -153,7 +158,8 @@ def test_gemv_stream_small_shapes(name, qt, N, K):
 # row phases, one and three rows per lane.  N is not a multiple of the
 # workgroup count, so workgroups differ by one row.  Every row is checked.
 @pytest.mark.parametrize("qt,N", [(Q4, 3000), (Q4, 6000), (Q4, 9000), (Q4, 17000), (Q4, 25600), (Q4, 38000),
-                                  (Q5, 3000), (Q5, 9000), (Q6, 3000), (Q6, 9000)],
+                                  (Q5, 3000), (Q5, 9000), (Q6, 3000), (Q6, 9000),
+                                  (IQ4, 3000), (IQ4, 6000), (IQ4, 9000), (IQ4, 17000), (IQ4, 38000)],
                          ids=lambda v: NAMES.get(v, str(v)))
 def test_gemv_row_rounds_all_rows(qt, N):
     K = 5120
@@ -170,7 +176,8 @@ def test_gemv_row_rounds_all_rows(qt, N):
 # mapping of the reduction at P = 1.  Q6_K (up to 1024 threads) takes P = 1
 # at K = 17408 when five rows per workgroup fit one phase best (N = 1200).
 # Every row is checked.
-@pytest.mark.parametrize("qt,N,K", [(Q4, 1000, 17408), (Q5, 600, 17408), (Q4, 300, 16640), (Q6, 1200, 17408)],
+@pytest.mark.parametrize("qt,N,K", [(Q4, 1000, 17408), (Q5, 600, 17408), (Q4, 300, 16640), (Q6, 1200, 17408),
+                                    (IQ4, 1000, 17408)],
                          ids=lambda v: NAMES.get(v, str(v)))
 def test_gemv_single_phase_several_rows(qt, N, K):
     W, x = _case(qt, N, K, 800 + N)
@@ -184,7 +191,8 @@ def test_gemv_single_phase_several_rows(qt, N, K):
 # partial sums fit LDS), 2^18 rows of K = 512, and K = 2^20 (32 segments of
 # the one-column kernel; some 200 of the verify kernel at 8 columns).
 @pytest.mark.parametrize("qt,N,K,ncols", [(Q4, 1 << 20, 256, 1), (Q6, 1 << 18, 512, 1), (Q5, 16, 1 << 20, 1),
-                                          (Q4, 16, 1 << 20, 8), (Q6, 24, 1 << 20, 3)],
+                                          (Q4, 16, 1 << 20, 8), (Q6, 24, 1 << 20, 3), (IQ4, 1 << 19, 256, 1),
+                                          (IQ4, 16, 1 << 20, 5)],
                          ids=lambda v: NAMES.get(v, str(v)))
 def test_gemv_large_extents_sampled(qt, N, K, ncols):
     W = synth.superblocks(qt, N, K, 1200 + ncols)

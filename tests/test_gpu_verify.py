@@ -10,9 +10,9 @@ from quant_dequant_gemv_amd import synth
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
-Q4, Q5, Q6 = synth.Q4_K, synth.Q5_K, synth.Q6_K
-TYPES = [Q4, Q5, Q6]
-NAMES = {Q4: "Q4_K", Q5: "Q5_K", Q6: "Q6_K"}
+Q4, Q5, Q6, IQ4 = synth.Q4_K, synth.Q5_K, synth.Q6_K, synth.IQ4_XS
+TYPES = [Q4, Q5, Q6, IQ4]
+NAMES = {Q4: "Q4_K", Q5: "Q5_K", Q6: "Q6_K", IQ4: "IQ4_XS"}
 
 # ragged rows (not a multiple of 4), K with a partial 16-unit step, the real K
 # values, and K = 29184 so that the x planes need several tiles at ncols = 8
@@ -69,6 +69,16 @@ def test_verify_full_shape_all_rows(ncols):
     y = gpu_gemv(c["qtype"], W, x, N, K)
     y_ref, S = oracle.gemv(c["qtype"], W, x, K)
     assert_row_bound(y, y_ref, S, f"verify {N}x{K} ncols={ncols}")
+
+
+@pytest.mark.parametrize("ncols", [2, 4, 8])
+def test_verify_iq4xs_ffn_shape_all_rows(ncols):
+    N, K = 17408, 5120
+    W = synth.superblocks(IQ4, N, K, 1003)
+    x = synth.activations(K, ncols, 1003)
+    y = gpu_gemv(IQ4, W, x, N, K)
+    y_ref, S = oracle.gemv(IQ4, W, x, K)
+    assert_row_bound(y, y_ref, S, f"IQ4_XS {N}x{K} ncols={ncols}")
 
 
 @pytest.mark.parametrize("case", synth.MIXED, ids=lambda c: c["name"])
