@@ -286,14 +286,8 @@ def read_ceiling(torch, sizes):
 
 
 def _calib_lib():
-    import ctypes
-
-    from quant_dequant_gemv_amd import build as qb
-    lib = ctypes.CDLL(qb.CALIB_LIB)
-    lib.qk_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
-                                   ctypes.c_void_p]
-    lib.qk_stream_read.restype = ctypes.c_int
-    return lib
+    from quant_dequant_gemv_amd import calib
+    return calib.load()
 
 
 SUSTAINED_BYTES = 4 << 30
@@ -362,7 +356,66 @@ def cpu_baseline(entries, min_seconds=10.0):
     return {"value": round(steps * nbytes / t / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{steps} full steps (3 GEMVs, {nbytes} weight bytes each) in {t:.1f} s wall",
             "one_thread_GBs": round(nbytes / one / 1e9, 4),
-            "cpu": _cpu_model()}
+            "cpu": _cpu_model(), "workloads": cpu_workloads(threads)}
+
+
+def _oracle_rate(calls, min_seconds):
+    """Wall seconds per pass of `calls` (oracle GEMVs), repeated until
+    min_seconds (at least one pass)."""
+    import oracle
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for qt, W, x, K, threads in calls:
+            oracle.gemv(qt, W, x, K, nthreads=threads)
+        n += 1
+        t = time.perf_counter() - t0
+        if t >= min_seconds:
+            return t / n, n
+
+
+def cpu_workloads(threads):
+    """The CPU oracle on the other workloads, each a bounded sample: the small
+    Q4_K 1024 x 5120 GEMV; the Q6_K / Q5_K pair; the verify shape at 1-8
+    columns; and the decode token, sampled as layers 0-3 (three DeltaNet
+    layers and one attention layer: 28 of the 448 GEMVs, the same mix as the
+    whole 64 layers) and scaled by 16."""
+    from quant_dequant_gemv_amd import synth
+
+    def data(e, ncols=1):
+        return (e["qtype"], synth.superblocks(e["qtype"], e["N"], e["K"], e["seed"]),
+                synth.activations(e["K"], ncols, e["seed"]), e["K"], threads)
+
+    out = {}
+    d = data(synth.SMALL)
+    sec, n = _oracle_rate([d], 1.0)
+    out["small_q4k_1024x5120"] = {"ms_per_gemv": round(sec * 1e3, 3), "weight_GBs": round(d[1].size / sec / 1e9, 3),
+                                  "passes": n}
+    ds = [data(e) for e in synth.MIXED]
+    out["mixed_types"] = []
+    for e, d in zip(synth.MIXED, ds):
+        sec, n = _oracle_rate([d], 1.0)
+        out["mixed_types"].append({"name": e["name"], "type": synth.TYPE_NAMES[e["qtype"]], "N": e["N"], "K": e["K"],
+                                   "ms_per_gemv": round(sec * 1e3, 2),
+                                   "weight_GBs": round(d[1].size / sec / 1e9, 3), "passes": n})
+    v = synth.VERIFY
+    out["verify_q4k_17408x5120"] = []
+    W = synth.superblocks(v["qtype"], v["N"], v["K"], v["seed"])
+    for nc in v["ncols"]:
+        d = (v["qtype"], W, synth.activations(v["K"], nc, v["seed"]), v["K"], threads)
+        sec, n = _oracle_rate([d], 0.5)
+        out["verify_q4k_17408x5120"].append({"ncols": nc, "ms_per_call": round(sec * 1e3, 2),
+                                             "weight_GBs": round(W.size / sec / 1e9, 3), "passes": n})
+    del W
+    sample = [e for e in synth.decode_stream() if e["layer"] < 4]
+    calls = [data(e) for e in sample]
+    nbytes = sum(c[1].size for c in calls)
+    sec, n = _oracle_rate(calls, 1.0)
+    scale = synth.N_LAYERS / 4
+    out["decode_token"] = {"s_per_token": round(sec * scale, 3), "tok_s": round(1.0 / (sec * scale), 4),
+                           "weight_GBs": round(nbytes / sec / 1e9, 3),
+                           "sample": f"layers 0-3 ({len(sample)} GEMVs, {nbytes} weight bytes) x {n} passes "
+                                     f"in {sec * n:.2f} s, scaled by {scale:g} to the 64-layer token"}
+    return out
 
 
 def _cpu_model():
@@ -390,20 +443,12 @@ def traffic_for(kernel, frac_bytes):
 
 
 def device_info(torch):
-    """GPU name, architecture, CUs, memory and HIP version; clocks from
-    rocm-smi when it answers (read-only query)."""
-    import subprocess
+    """GPU name, architecture, CUs, memory and HIP version.  (No clock
+    reading: a query after the run sees the idle clock, not the one the timed
+    region ran at.)"""
     p = torch.cuda.get_device_properties(0)
-    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count,
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count,
             "memory_GB": round(p.total_memory / 1e9, 1), "hip": torch.version.hip}
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=15)
-        if r.returncode == 0:
-            card = next(iter(json.loads(r.stdout).values()))
-            info["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower()}
-    except (OSError, ValueError, StopIteration, subprocess.SubprocessError):
-        pass
-    return info
 
 
 def run_stream(torch, launcher, warm=2, only=None, tokens=1):
@@ -716,6 +761,19 @@ def main():
     shapes = per_shape(torch, launcher, tensors)
     del tensors
     torch.cuda.empty_cache()
+    # the small Q4_K case (1024 x 5120), and IQ4_XS at the FFN shape, one and eight columns
+    small = make_tensors(torch, [dict(synth.SMALL, name="small_q4k_1024x5120")])
+    small_out = per_shape(torch, launcher, small)[0]
+    del small
+    iq4_out = []
+    for nc in (1, 8):
+        t = make_tensors(torch, [dict(name=f"iq4xs_ffn_up_ncols{nc}", qtype=synth.IQ4_XS, N=17408, K=5120, seed=1003,
+                                      ncols=nc)])
+        r = per_shape(torch, launcher, t)[0]
+        r["ncols"] = nc
+        iq4_out.append(r)
+        del t
+    torch.cuda.empty_cache()
     progress("read ceiling and per-shape figures")
 
     mixed = make_tensors(torch, synth.MIXED)
@@ -795,6 +853,8 @@ def main():
         "read_at_size": size_reads,
         "cpu_baseline": cpu,
         "per_gemv": shapes,
+        "small_gemv": small_out,
+        "iq4_xs": iq4_out,
         "mixed_types": mixed_out,
         "planar_rows": planar_out,
         "verify": verify_out,

@@ -11,10 +11,12 @@ run from the repository root on the GPU:
 `run` launches, a few times each on distinct weight copies and directly (one
 dispatch per launch), the groups of plan(): the three Q4_K projection shapes
 (N = 10240, 12288, 17408; K = 5120) -- the benchmark's step --, the Q4_K
-17408 x 5120 verify form at 2, 4 and 8 columns, and the one-column Q6_K and
-Q5_K shapes; then a plain device-to-device copy of 512 MiB as the
-calibration: its counters are scaled to the known 512 MiB read and 512 MiB
-written, and the same factors are applied to the GEMV's counters.  `parse`
+17408 x 5120 verify form at 2, 4, 8, 16 and 17 columns, the one-column Q6_K
+and Q5_K shapes and IQ4_XS 17408 x 5120; then three known reads of 512 MiB
+as the calibration: a device-to-device copy (512 MiB read, 512 MiB
+written), and the plain read of libqkcalib.so with non-temporal and with
+ordinary loads.  The copy's factors scale the GEMV's counters; the two
+reads give independent FETCH_SIZE factors as a cross-check.  `parse`
 maps the dispatches back to plan() by their order and writes
 profiles/traffic.json (per-launch HBM bytes of each group against its
 algorithmic bytes, with the hash of the kernel sources it was measured on)
@@ -58,12 +60,17 @@ def plan():
     from quant_dequant_gemv_amd import synth
     v = synth.VERIFY
     groups = [(STEP, [(e["qtype"], e["N"], e["K"], e["seed"], 1) for e in synth.Q4K_PROJECTIONS])]
-    for nc in (2, 4, 8):
+    for nc in (2, 4, 8, 16, 17):
         groups.append((f"verify_kernel<Q4_K> {v['N']}x{v['K']} ncols {nc}", [(v["qtype"], v["N"], v["K"], v["seed"], nc)]))
     for e in synth.MIXED:
         groups.append((f"gemv1_kernel<{synth.TYPE_NAMES[e['qtype']]}> {e['N']}x{e['K']}",
                        [(e["qtype"], e["N"], e["K"], e["seed"], 1)]))
+    groups.append(("gemv1_kernel<IQ4_XS> 17408x5120", [(synth.IQ4_XS, 17408, 5120, 1003, 1)]))
     return groups
+
+
+READS = (("read_nt", "qk_stream_read", "stream_read_kernel<true>"),
+         ("read_plain", "qk_stream_read_plain", "stream_read_kernel<false>"))
 
 
 def run(reps: int = REPS) -> None:
@@ -89,6 +96,15 @@ def run(reps: int = REPS) -> None:
     for _ in range(reps):
         dst.copy_(src)
         torch.cuda.synchronize()
+    del dst
+    from quant_dequant_gemv_amd import calib
+    cl = calib.load()
+    out = torch.empty(1024 * 1024, dtype=torch.int32, device="cuda")
+    for _, fn, _ in READS:
+        for _ in range(reps):
+            if getattr(cl, fn)(src.data_ptr(), COPY_BYTES, out.data_ptr(), 1024, 1024, stream):
+                raise RuntimeError(fn)
+            torch.cuda.synchronize()
     print("traffic run done", flush=True)
 
 
@@ -121,13 +137,22 @@ def parse(fetch_db: str, write_db: str, reps: int = REPS, out_path: str = OUT) -
         if len(ours) != want or not copy:
             raise RuntimeError(f"{counter}: {len(ours)} GEMV dispatches (expected {want}), {len(copy)} copies")
         factor = COPY_BYTES / (max(copy) * 1024.0)  # the 512 MiB copy is the largest copy dispatch
+        refs = {}
+        if counter == "FETCH_SIZE":  # the plain reads: independent factors for the same counter
+            for key, _, kname in READS:
+                v = [x for _, n, x in d if kname in n]
+                if len(v) != reps:
+                    raise RuntimeError(f"{counter}: {len(v)} dispatches of {kname} (expected {reps})")
+                kib = sum(v) / len(v)
+                refs[key] = {"kib_mean": kib, "scale": COPY_BYTES / (kib * 1024.0)}
         per_group, i = {}, 0
         for name, launches in groups:
             n = reps * len(launches)
             kib = sum(ours[i:i + n]) / n  # mean over the group's launches
             per_group[name] = {"kib_mean": kib, "bytes": kib * 1024.0 * factor}
             i += n
-        res[label] = {"counter": counter, "copy_kib": max(copy), "scale": factor, "groups": per_group}
+        res[label] = {"counter": counter, "copy_kib": max(copy), "scale": factor, "groups": per_group,
+                      "read_refs": refs}
     per_launch, alg, ratio = {}, {}, {}
     for name, launches in groups:
         per_launch[name] = round(res["fetch"]["groups"][name]["bytes"] + res["write"]["groups"][name]["bytes"])
@@ -141,7 +166,7 @@ def parse(fetch_db: str, write_db: str, reps: int = REPS, out_path: str = OUT) -
            "ratios": ratio,
            "counters": res,
            "note": "means over each group's launches (the step: its three shapes); counters scaled by a "
-                   "512 MiB device copy"}
+                   "512 MiB device copy, cross-checked by 512 MiB plain reads (non-temporal and ordinary loads)"}
     with open(out_path, "w") as f:
         json.dump(out, f, indent=1)
     return out
@@ -153,11 +178,18 @@ def markdown(out: dict, reps: int = REPS) -> str:
     lines = ["# HBM traffic of the GEMV kernels at the workload shapes: rocprofv3 counters", "",
              "Commands (run from the repository root on one MI355X; one counter per pass):", "", COMMANDS, "",
              f"`traffic run` launches each group below {reps} times on distinct weight copies (one dispatch per "
-             "launch), then a 512 MiB device-to-device copy.", "",
+             "launch), then a 512 MiB device-to-device copy and two plain reads of 512 MiB.", "",
              "Calibration by the copy (known 512 MiB read, 512 MiB written):", "",
              "| counter | copy reads as | scale |", "|---|---|---|",
              f"| FETCH_SIZE | {f['copy_kib']:.1f} KiB | {f['scale']:.4f} |",
              f"| WRITE_SIZE | {w['copy_kib']:.1f} KiB | {w['scale']:.4f} |", "",
+             "Cross-check of the FETCH_SIZE scale by two reads of the same 512 MiB with libqkcalib.so's plain "
+             "read kernel (1024 x 1024 threads):", "",
+             "| reference | FETCH_SIZE reads as | scale |", "|---|---|---|"]
+    for key, _, kname in READS:
+        r = f["read_refs"][key]
+        lines.append(f"| `{kname}` | {r['kib_mean']:.1f} KiB | {r['scale']:.4f} |")
+    lines += ["",
              "Per launch (mean over the group's dispatches; the step: its three Q4_K shapes 10240 / 12288 / "
              "17408 x 5120):", "",
              "| group | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes | algorithmic bytes (W + x + y) | ratio |",
@@ -166,7 +198,9 @@ def markdown(out: dict, reps: int = REPS) -> str:
         lines.append(f"| `{name}` | {f['groups'][name]['kib_mean']:.1f} | {w['groups'][name]['kib_mean']:.1f} | "
                      f"{out['per_launch_bytes'][name]} | {out['algorithmic_bytes'][name]} | {out['ratios'][name]:.4f} |")
     lines += ["", "A ratio near 1 means every weight byte is fetched from HBM once per launch (the verify form "
-              "included: W is read once for all its columns).  Kernel source hash " + out["kernel_hash"] +
+              "up to 8 columns included: W is read once for all its columns; wider calls stream W once per "
+              "column group, and the ratio above 1 is what the caches did not absorb).  Kernel source hash " +
+              out["kernel_hash"] +
               " (bench.py reports `roofline.traffic` from profiles/traffic.json only while the sources hash the "
               "same).", ""]
     return "\n".join(lines)
