@@ -57,14 +57,16 @@ __device__ __forceinline__ float vdpp(float a) {
 template <int NCB>
 __host__ __device__ constexpr int v_max_threads() { return NCB == 1 ? 768 : 512; }
 constexpr int V_MAX_RL = 8;  // quads per straight-line round, at most
-// Plain Q4_K launches of two column blocks in rounds of at most V_SHORT_RL
-// quads fit 168 registers without spills, so they may take 12 waves: two
-// row phases at K = 5120 (measured 4-5% faster at 17408 x 5120, 6 and 8
-// columns).  The epilogue and group-loop variants would spill there.
-constexpr int V_SHORT_RL = 3;
+// Plain launches of two column blocks in short rounds fit 168 registers
+// without spills, so they may take 12 waves (two row phases at K = 5120):
+// Q4_K and IQ4_XS in rounds of up to 3 quads, Q5_K and Q6_K of one (measured
+// 4-5% faster for Q4_K at 17408 x 5120, 6 and 8 columns).  The epilogue and
+// group-loop variants would spill there.
+template <int T>
+__host__ __device__ constexpr int v_short_rl() { return T == Q4_K || T == IQ4_XS ? 3 : 1; }
 template <int T, int NCB, int RL, bool PAIR, bool EPI, bool WIDE>
 constexpr int v_bound() {
-    return NCB == 2 && T == Q4_K && RL <= V_SHORT_RL && !PAIR && !EPI && !WIDE ? 768 : v_max_threads<NCB>();
+    return NCB == 2 && RL <= v_short_rl<T>() && !PAIR && !EPI && !WIDE ? 768 : v_max_threads<NCB>();
 }
 constexpr int V_RAW_BUDGET = 96 * 1024;  // LDS for the x planes of one segment
 constexpr int V_LDS_MAX = 160 * 1024;
@@ -181,6 +183,13 @@ __device__ __forceinline__ void stage_planes_strided(const uint16_t *xg, int ldx
 template <int J>
 __device__ __forceinline__ float quad_bcast(float a) { return vdpp<J | (J << 2) | (J << 4) | (J << 6)>(a); }
 
+// v_mfma_f32_4x4x1_16b_f32: in each of the 16 blocks (lanes 4b..4b+3) lane
+// 4b+j supplies a = A[j][0] and b = B[0][j] and receives D[0..3][j] +=
+// A[i][0] * B[0][j], the same lane roles as mfma4.
+__device__ __forceinline__ float4_t mfma1f32(float a, float b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
+}
+
 // PAIR (the SwiGLU epilogue): the workgroup's rows of W and then of ep.W2
 // form one schedule of 2R rows; row r's outputs combine the sums of rows r
 // and R + r.  EPI: the store applies ep's residual / fp16 options (else it is
@@ -256,32 +265,35 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
         __syncthreads();
         // this lane's columns j, j+4 in registers; group sums of all columns of the unit
         uint32_t xr[NCB][32];
-        float xsum[NC][G];
-        {
-            float own[NCB][G];
+        // Q4_K/Q5_K: the sums of this lane's own columns (4cb + j) over the
+        // unit's two sub-blocks, pre-scaled for the 2^-48 units of the partials
+        float xs[NCB][2];
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                const int c = 4 * cb + j;
-                if (c < nc) {
-                    gather_x<T>(planes + c * ps, u - s0, xr[cb], own[cb]);
-                } else {
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int c = 4 * cb + j;
+            float own[G];
+            if (c < nc) {
+                gather_x<T>(planes + c * ps, u - s0, xr[cb], own);
+            } else {
 #pragma unroll
-                    for (int i = 0; i < 32; ++i) xr[cb][i] = 0u;
+                for (int i = 0; i < 32; ++i) xr[cb][i] = 0u;
 #pragma unroll
-                    for (int g = 0; g < G; ++g) own[cb][g] = 0.f;
-                }
+                for (int g = 0; g < G; ++g) own[g] = 0.f;
             }
+            xs[cb][0] = own[0] * 0x1p-24f;
+            xs[cb][1] = own[1] * 0x1p-24f;
+        }
+        // one column block: every lane keeps the four columns' sums (quad
+        // broadcasts), and the min terms are four fmas per column
+        float xq[NCB == 1 ? 4 : 1][2];
+        if constexpr (NCB == 1) {
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    // pre-scaled for the 2^-48 units of the Q4_K/Q5_K partials
-                    const float v = T == Q6_K ? own[cb][g] : own[cb][g] * 0x1p-24f;
-                    xsum[4 * cb + 0][g] = quad_bcast<0>(v);
-                    xsum[4 * cb + 1][g] = quad_bcast<1>(v);
-                    xsum[4 * cb + 2][g] = quad_bcast<2>(v);
-                    xsum[4 * cb + 3][g] = quad_bcast<3>(v);
-                }
+            for (int g = 0; g < 2; ++g) {
+                xq[0][g] = quad_bcast<0>(xs[0][g]);
+                xq[1][g] = quad_bcast<1>(xs[0][g]);
+                xq[2][g] = quad_bcast<2>(xs[0][g]);
+                xq[3][g] = quad_bcast<3>(xs[0][g]);
+            }
         }
         const UnitAddr<T, GGUF> ua(K >> 8, u);
 
@@ -395,13 +407,27 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
                             Dh[cb] = mfma4(xr[cb][16 + 2 * i], xr[cb][17 + 2 * i], pt[2], pt[3], Dh[cb]);
                         }
                     }
+                    // the min terms e_L * sum x_lo + e_H * sum x_hi of every (row j,
+                    // column i) of a block.  Two column blocks: a rank-2 outer
+                    // product of the rows' e and the columns' x sums on the matrix
+                    // cores in fp32 (the broadcast sums of eight columns would not
+                    // fit the registers of 12-wave launches: measured 10% faster
+                    // at 5-8 columns); one block: fmas on the broadcast sums (2%
+                    // faster there).
 #pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb)
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        float4_t E;
+                        if constexpr (NCB == 1) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float ex = __builtin_fmaf(kL.e, xsum[4 * cb + i][0], kH.e * xsum[4 * cb + i][1]);
-                            val[4 * cb + i] = __builtin_fmaf(kL.a, Dl[cb][i], __builtin_fmaf(fh, Dh[cb][i], ex));
+                            for (int i = 0; i < 4; ++i) E[i] = __builtin_fmaf(kL.e, xq[i][0], kH.e * xq[i][1]);
+                        } else {
+                            E = mfma1f32(xs[cb][0], kL.e, float4_t{0.f, 0.f, 0.f, 0.f});
+                            E = mfma1f32(xs[cb][1], kH.e, E);
                         }
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            val[4 * cb + i] = __builtin_fmaf(kL.a, Dl[cb][i], __builtin_fmaf(fh, Dh[cb][i], E[i]));
+                    }
                 }
                 if (p + DD < RL) load_quad(buf[p % DD], p + DD);
                 // fold the 4 blocks of each 16-lane row (same row j, consecutive units)
@@ -503,9 +529,9 @@ struct VGeo { int G, useg, P, RL, threads; size_t lds; };
 static int cus_v() { return device_cus(); }
 
 // mult = 2: each workgroup streams its rows of two tensors (SwiGLU).
-// short_threads: the largest workgroup for rounds of at most V_SHORT_RL
+// short_threads: the largest workgroup for rounds of at most short_rl
 // quads (at least the general limit).
-static bool vgeo(int64_t N, int64_t K, int nc, int ncb, int mult, int short_threads, VGeo &g) {
+static bool vgeo(int64_t N, int64_t K, int nc, int ncb, int mult, int short_threads, int short_rl, VGeo &g) {
     const int64_t U = K / 64;
     const int64_t xs = (int64_t)VXSTRIDE * nc;  // plane bytes per unit column
     const int long_threads = ncb == 1 ? v_max_threads<1>() : v_max_threads<2>();
@@ -533,7 +559,7 @@ static bool vgeo(int64_t N, int64_t K, int nc, int ncb, int mult, int short_thre
         int64_t best[4] = {INT64_MAX, INT64_MAX, INT64_MAX, INT64_MAX};
         for (int p = 1; p <= pmax; ++p) {
             // above the general limit only short rounds fit the registers
-            const int maxrl = p * wpp * 64 <= long_threads ? V_MAX_RL : V_SHORT_RL;
+            const int maxrl = p * wpp * 64 <= long_threads ? V_MAX_RL : short_rl;
             const int64_t ql = (Q + p - 1) / p;
             const int64_t rounds = (ql + maxrl - 1) / maxrl;
             const int rl = (int)((ql + rounds - 1) / rounds);
@@ -599,7 +625,8 @@ static hipError_t verify_dispatch(const void *W, const void *x, void *y, int64_t
     // plain launches of up to 8 columns may take the larger workgroups of short rounds
     const bool plain = !PAIR && !ep.res && !ep.f16 && nc <= 8;
     const int short_threads = plain ? v_bound<T, NCB, 1, false, false, false>() : v_max_threads<NCB>();
-    if (!vgeo(N, K, widest_group(nc), NCB, PAIR ? 2 : 1, short_threads, g)) return hipErrorInvalidValue;
+    if (!vgeo(N, K, widest_group(nc), NCB, PAIR ? 2 : 1, short_threads, v_short_rl<T>(), g))
+        return hipErrorInvalidValue;
     switch (g.RL) {
     case 1: return launch_v<T, NCB, 1, PAIR>(W, x, y, N, K, nc, g, ep, st);
     case 2: return launch_v<T, NCB, 2, PAIR>(W, x, y, N, K, nc, g, ep, st);
