@@ -301,11 +301,13 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     const int rows_lane = (RV + P - 1) / P;  // same schedule for every lane
     // Q4_K issues the first round's weights of a segment before staging its
     // x, except where the ring live across the staging would spill under the
-    // 128-register bound (six-row rounds; four-row rounds with an epilogue).
-    // Measured: PLANAR rows 2-3% faster, 1024 x 5120 3-12%; Q5_K (no gain)
-    // and Q6_K (x read per lane) keep the plain order.
+    // 128-register bound (rounds of four or six rows, and every epilogue or
+    // pair variant: 12 bytes per lane of scratch each; without the early
+    // ring the SwiGLU pair at 17408 x 5120 runs 25.2 -> 24.0 us).  Measured:
+    // PLANAR rows 2-3% faster, 1024 x 5120 3-12%; Q5_K (no gain), Q6_K (x read
+    // per lane) and IQ4_XS keep the plain order.
     constexpr bool CHAIN = !__is_same(Hook, NoHook);
-    constexpr bool PRE = CHAIN || (T == Q4_K && RL != 6 && !(RL == 4 && (EPI || PAIR)));
+    constexpr bool PRE = CHAIN || (T == Q4_K && RL != 6 && RL != 4 && !EPI && !PAIR);
     // Partial sums: the lane of phase ph (tail lanes ph >= P included) writes
     // its i-th row to slot row i*PT + ph, PT = phases incl. the tail, so every
     // lane owns a distinct slot and no write needs a guard.  Row r of the
