@@ -108,12 +108,11 @@ enum {
  *   y      device pointer to N*ncols fp32 values, 4-byte aligned (written)
  *   N      rows (output features), >= 1
  *   K      columns of W (input features), a multiple of 256
- *   ncols  columns of x and y, 1..32: 1 is the decode GEMV, 2..8 the
- *          few-column verify form with W read once per call; 9..32 take
- *          the columns in ceil(ncols / 8) groups of (nearly) equal width
- *          inside one launch, each group streaming W again (from the
- *          on-chip caches where W fits them) -- the B70 plan's checklist
- *          asks for verifier widths up to 17
+ *   ncols  columns of x and y, 1..32: 1 is the decode GEMV, 2..16 the
+ *          few-column verify form with W read once per call; 17..32 take
+ *          the columns in two groups of (nearly) equal width inside one
+ *          launch, each group streaming W (the B70 plan's checklist asks
+ *          for verifier widths up to 17)
  *   stream hipStream_t to enqueue on
  *
  * y must not overlap W or x (QK_EINVAL_PTR): other workgroups are still

@@ -226,10 +226,12 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
     // first column group
     if constexpr (!WIDE) ngrp = 1;
     const int nc0 = nct / ngrp;  // width of group 0
-    float res0[NC];
+    // (three or four column blocks: no prefetch, the registers are taken by x)
+    constexpr bool RES0 = EPI && NCB < 3;
+    float res0[RES0 ? NC : 1];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) res0[c] = 0.f;
-    if constexpr (EPI)
+    for (int c = 0; c < (RES0 ? NC : 1); ++c) res0[c] = 0.f;
+    if constexpr (RES0)
         if (ep.res && (tid & 15) == 0 && (tid >> 4) < R)
 #pragma unroll
             for (int c = 0; c < NC; ++c)
@@ -499,12 +501,12 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
         if (rok && s16 == 0) {
             const size_t o = (size_t)(r0 + rr) * nct + c0;
             if constexpr (EPI) {
-                const bool first = rr == (tid >> 4) && grp == 0;
+                const bool first = RES0 && rr == (tid >> 4) && grp == 0;
 #pragma unroll
                 for (int c = 0; c < NC; ++c)
                     if (c < nc) {
                         float v = a[c];
-                        if (ep.res) v += first ? res0[c] : ep.res[o + c];
+                        if (ep.res) v += first ? res0[RES0 ? c : 0] : ep.res[o + c];
                         store_y(y, ep.f16, o + c, v);
                     }
             } else {
@@ -531,7 +533,8 @@ static int cus_v() { return device_cus(); }
 // mult = 2: each workgroup streams its rows of two tensors (SwiGLU).
 // short_threads: the largest workgroup for rounds of at most short_rl
 // quads (at least the general limit).
-static bool vgeo(int64_t N, int64_t K, int nc, int ncb, int mult, int short_threads, int short_rl, VGeo &g) {
+static bool vgeo(int64_t N, int64_t K, int nc, int ncb, int mult, int short_threads, int short_rl, int max_rl,
+                 VGeo &g) {
     const int64_t U = K / 64;
     const int64_t xs = (int64_t)VXSTRIDE * nc;  // plane bytes per unit column
     const int long_threads = ncb == 1 ? v_max_threads<1>() : v_max_threads<2>();
@@ -559,7 +562,7 @@ static bool vgeo(int64_t N, int64_t K, int nc, int ncb, int mult, int short_thre
         int64_t best[4] = {INT64_MAX, INT64_MAX, INT64_MAX, INT64_MAX};
         for (int p = 1; p <= pmax; ++p) {
             // above the general limit only short rounds fit the registers
-            const int maxrl = p * wpp * 64 <= long_threads ? V_MAX_RL : short_rl;
+            const int maxrl = p * wpp * 64 <= long_threads ? max_rl : short_rl;
             const int64_t ql = (Q + p - 1) / p;
             const int64_t rounds = (ql + maxrl - 1) / maxrl;
             const int rl = (int)((ql + rounds - 1) / rounds);
@@ -591,31 +594,57 @@ static hipError_t launch_ve(const void *W, const void *x, void *y, int64_t N, in
     if (g.threads > v_bound<T, NCB, RL, PAIR, EPI, WIDE>()) return hipErrorInvalidValue;
     const hipError_t e = v_allow_lds<verify_kernel<T, NCB, RL, D, PAIR, EPI, WIDE>>();
     if (e != hipSuccess) return e;
-    const int ngrp = (nc + 7) / 8;
+    const int ngrp = (nc + 4 * NCB - 1) / (4 * NCB);
     hipLaunchKernelGGL((verify_kernel<T, NCB, RL, D, PAIR, EPI, WIDE>), dim3((unsigned)g.G), dim3(g.threads), g.lds,
                        st, (const uint8_t *)W, (const uint16_t *)x, y, (int)N, (int)K, nc, ngrp, g.useg, g.P, ep);
     return hipGetLastError();
 }
 
 // Plain launches run a body without the epilogue's store options.  More
-// than 8 columns run the group loop (always with two column blocks: the
-// groups are then 5 to 8 wide), with the general store.
+// than 8 columns run the group loop with three or four column blocks
+// (groups of 9 to 16 columns, vplan), with the general store.
 template <int T, int NCB, int RL, bool PAIR>
 static hipError_t launch_v(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, const VGeo &g,
                            const Epilogue &ep, hipStream_t st) {
-    if (nc > 8) {
-        if constexpr (NCB == 2) return launch_ve<T, NCB, RL, PAIR, true, true>(W, x, y, N, K, nc, g, ep, st);
+    if constexpr (NCB >= 3) {
+        if (nc > 8) return launch_ve<T, NCB, RL, PAIR, true, true>(W, x, y, N, K, nc, g, ep, st);
         return hipErrorInvalidValue;
+    } else {
+        if (nc > 8) return hipErrorInvalidValue;
+        if (!PAIR && !ep.res && !ep.f16)
+            return launch_ve<T, NCB, RL, false, false, false>(W, x, y, N, K, nc, g, ep, st);
+        return launch_ve<T, NCB, RL, PAIR, true, false>(W, x, y, N, K, nc, g, ep, st);
     }
-    if (!PAIR && !ep.res && !ep.f16) return launch_ve<T, NCB, RL, false, false, false>(W, x, y, N, K, nc, g, ep, st);
-    return launch_ve<T, NCB, RL, PAIR, true, false>(W, x, y, N, K, nc, g, ep, st);
 }
 
-// nc: all columns; the launch takes them in groups of at most 8, of widths
-// differing by at most one (the widest decides the planes' size and NCB)
-static int widest_group(int nc) {
-    const int ngrp = (nc + 7) / 8;
-    return (nc + ngrp - 1) / ngrp;
+// How a launch takes its nc columns: up to 8 in one group of one or two
+// column blocks; more in ngrp groups of widths differing by at most one
+// (c0 = grp * nc / ngrp), each group 9 to 16 wide with three or four blocks
+// (ngrp = ceil(nc / (4 * ncb))).  Each group streams W once, and a unit's
+// unpacking and matrix work grow with the blocks, so the plan takes the
+// fewest groups x blocks, then the fewest groups: 9-12 columns one group of
+// three blocks, 13-16 one of four, 17-24 two of three, 25-32 two of four
+// (measured at 17408 x 5120 Q4_K: 12 columns 59.8 us as two groups of two
+// blocks, 47.1 us as one of four).
+struct VPlan { int ngrp, ncb, width; };
+static VPlan vplan(int nc) {
+    if (nc <= 8) return {1, nc > 4 ? 2 : 1, nc};
+    VPlan best{0, 0, 0};
+    for (int ngrp = (nc + 15) / 16; ngrp <= (nc + 8) / 9; ++ngrp) {
+        const int width = (nc + ngrp - 1) / ngrp, ncb = (width + 3) / 4;
+        if (ncb < 3 || ncb > 4 || (nc + 4 * ncb - 1) / (4 * ncb) != ngrp) continue;
+        if (!best.ngrp || ngrp * ncb < best.ngrp * best.ncb) best = {ngrp, ncb, width};
+    }
+    return best;
+}
+
+// Rounds of up to 8 quads; three or four column blocks up to 4 (their
+// registers are mostly x, and fewer instances keep the build short), four
+// blocks of Q5_K up to 2 and of Q6_K 1 (longer rounds spill: the Q6_K
+// accumulators alone are 64 registers).
+template <int T, int NCB>
+constexpr int v_max_rl() {
+    return NCB < 3 ? V_MAX_RL : NCB == 3 ? 4 : T == Q6_K ? 1 : T == Q5_K ? 2 : 4;
 }
 
 template <int T, int NCB, bool PAIR>
@@ -625,29 +654,47 @@ static hipError_t verify_dispatch(const void *W, const void *x, void *y, int64_t
     // plain launches of up to 8 columns may take the larger workgroups of short rounds
     const bool plain = !PAIR && !ep.res && !ep.f16 && nc <= 8;
     const int short_threads = plain ? v_bound<T, NCB, 1, false, false, false>() : v_max_threads<NCB>();
-    if (!vgeo(N, K, widest_group(nc), NCB, PAIR ? 2 : 1, short_threads, v_short_rl<T>(), g))
+    if (!vgeo(N, K, vplan(nc).width, NCB, PAIR ? 2 : 1, short_threads, v_short_rl<T>(), v_max_rl<T, NCB>(), g))
         return hipErrorInvalidValue;
+    constexpr int MRL = v_max_rl<T, NCB>();
     switch (g.RL) {
     case 1: return launch_v<T, NCB, 1, PAIR>(W, x, y, N, K, nc, g, ep, st);
-    case 2: return launch_v<T, NCB, 2, PAIR>(W, x, y, N, K, nc, g, ep, st);
-    case 3: return launch_v<T, NCB, 3, PAIR>(W, x, y, N, K, nc, g, ep, st);
-    case 4: return launch_v<T, NCB, 4, PAIR>(W, x, y, N, K, nc, g, ep, st);
-    case 5: return launch_v<T, NCB, 5, PAIR>(W, x, y, N, K, nc, g, ep, st);
-    case 6: return launch_v<T, NCB, 6, PAIR>(W, x, y, N, K, nc, g, ep, st);
-    case 7: return launch_v<T, NCB, 7, PAIR>(W, x, y, N, K, nc, g, ep, st);
-    default: return launch_v<T, NCB, 8, PAIR>(W, x, y, N, K, nc, g, ep, st);
+    case 2: if constexpr (MRL >= 2) return launch_v<T, NCB, 2, PAIR>(W, x, y, N, K, nc, g, ep, st); break;
+    case 3: if constexpr (MRL >= 3) return launch_v<T, NCB, 3, PAIR>(W, x, y, N, K, nc, g, ep, st); break;
+    case 4: if constexpr (MRL >= 4) return launch_v<T, NCB, 4, PAIR>(W, x, y, N, K, nc, g, ep, st); break;
+    default: break;
     }
+    if constexpr (MRL > 4) {
+        switch (g.RL) {
+        case 5: return launch_v<T, NCB, 5, PAIR>(W, x, y, N, K, nc, g, ep, st);
+        case 6: return launch_v<T, NCB, 6, PAIR>(W, x, y, N, K, nc, g, ep, st);
+        case 7: return launch_v<T, NCB, 7, PAIR>(W, x, y, N, K, nc, g, ep, st);
+        default: return launch_v<T, NCB, 8, PAIR>(W, x, y, N, K, nc, g, ep, st);
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int T>
 static hipError_t verify_type(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
                               const Epilogue &ep, hipStream_t st) {
-    const bool two = widest_group(nc) > 4;
-    if (ep.W2)
-        return two ? verify_dispatch<T, 2, true>(W, x, y, N, K, nc, ep, st)
-                   : verify_dispatch<T, 1, true>(W, x, y, N, K, nc, ep, st);
-    return two ? verify_dispatch<T, 2, false>(W, x, y, N, K, nc, ep, st)
-               : verify_dispatch<T, 1, false>(W, x, y, N, K, nc, ep, st);
+    const VPlan pl = vplan(nc);
+    if (ep.W2) {
+        switch (pl.ncb) {
+        case 1: return verify_dispatch<T, 1, true>(W, x, y, N, K, nc, ep, st);
+        case 2: return verify_dispatch<T, 2, true>(W, x, y, N, K, nc, ep, st);
+        case 3: return verify_dispatch<T, 3, true>(W, x, y, N, K, nc, ep, st);
+        case 4: return verify_dispatch<T, 4, true>(W, x, y, N, K, nc, ep, st);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (pl.ncb) {
+    case 1: return verify_dispatch<T, 1, false>(W, x, y, N, K, nc, ep, st);
+    case 2: return verify_dispatch<T, 2, false>(W, x, y, N, K, nc, ep, st);
+    case 3: return verify_dispatch<T, 3, false>(W, x, y, N, K, nc, ep, st);
+    case 4: return verify_dispatch<T, 4, false>(W, x, y, N, K, nc, ep, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace qk
