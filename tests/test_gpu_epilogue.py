@@ -34,7 +34,9 @@ def _residual(N, ncols, seed):
     return (np.random.default_rng([seed, 7]).standard_normal((N, ncols)) * 4).astype(np.float32)
 
 
-@pytest.mark.parametrize("ncols", [1, 2, 5, 8, 12, 17])
+# 12 / 16 / 17 / 32 columns: one group of three and of four column blocks,
+# two groups of three and of four (the residual then read at the store)
+@pytest.mark.parametrize("ncols", [1, 2, 5, 8, 12, 16, 17, 32])
 @pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_residual_and_f16(qt, N, K, ncols):
@@ -71,7 +73,7 @@ def test_ex_without_epilogue_is_qk_gemv(qt, ncols):
     assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
 
 
-@pytest.mark.parametrize("ncols", [1, 2, 4, 5, 8, 9, 16])
+@pytest.mark.parametrize("ncols", [1, 2, 4, 5, 8, 9, 16, 24])
 @pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_swiglu(qt, N, K, ncols):

@@ -121,10 +121,12 @@ def test_verify_round_lengths_sampled(qt, N, K, ncols):
     assert np.isfinite(y).all()
 
 
-# Wider verification: the columns go in ceil(ncols / 8) groups of nearly equal
-# width (9 -> 4 + 5, 17 -> 5 + 6 + 6, 32 -> 4 x 8), each staged from the
-# strided rows of x and written to its columns of y.
-@pytest.mark.parametrize("ncols", [9, 12, 16, 17, 24, 32])
+# Wider verification: 9-16 columns in one group of three or four column
+# blocks (9, 12 / 13, 16), 17-32 in two groups of nearly equal width (17 ->
+# 8 + 9 and 24 -> 12 + 12 with three blocks, 25 -> 12 + 13 and 32 -> 16 + 16
+# with four), each staged from the strided rows of x and written to its
+# columns of y.
+@pytest.mark.parametrize("ncols", [9, 12, 13, 16, 17, 24, 25, 32])
 @pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
 @pytest.mark.parametrize("N,K", [(5, 512), (130, 5120), (37, 17408)])
 def test_verify_wide_row_bound(qt, N, K, ncols):
