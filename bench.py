@@ -765,6 +765,13 @@ def main():
     small = make_tensors(torch, [dict(synth.SMALL, name="small_q4k_1024x5120")])
     small_out = per_shape(torch, launcher, small)[0]
     del small
+    # one GPU's share of an 8-way row split (N / 8 rows, the whole K): the kernel at a shard's real
+    # shape (the split itself, x replicated and y gathered, is not part of this single-GPU build)
+    shards = make_tensors(torch, [dict(name=f"shard8_{e['name']}", qtype=e["qtype"], N=e["N"] // 8, K=e["K"],
+                                       seed=e["seed"] + 100)
+                                  for e in list(entries[:1]) + list(entries[2:]) + list(synth.MIXED)])
+    shard_out = per_shape(torch, launcher, shards)
+    del shards
     iq4_out = []
     for nc in (1, 8):
         t = make_tensors(torch, [dict(name=f"iq4xs_ffn_up_ncols{nc}", qtype=synth.IQ4_XS, N=17408, K=5120, seed=1003,
@@ -854,6 +861,7 @@ def main():
         "cpu_baseline": cpu,
         "per_gemv": shapes,
         "small_gemv": small_out,
+        "shard8": shard_out,
         "iq4_xs": iq4_out,
         "mixed_types": mixed_out,
         "planar_rows": planar_out,

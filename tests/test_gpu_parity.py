@@ -124,7 +124,14 @@ FULL_SHAPES = [dict(synth.SMALL, name="small")] + synth.Q4K_PROJECTIONS + synth.
     dict(name="iq4xs_ffn_down", qtype=IQ4, N=5120, K=17408, seed=1004)]
 
 
-@pytest.mark.parametrize("case", FULL_SHAPES, ids=lambda c: c["name"])
+# one GPU's share of an 8-way row split of the large projections (N / 8 rows)
+SHARD_SHAPES = [dict(name="shard8_attn_qkv", qtype=Q4, N=1280, K=5120, seed=1101),
+                dict(name="shard8_ffn_up", qtype=Q4, N=2176, K=5120, seed=1103),
+                dict(name="shard8_ffn_down", qtype=Q6, N=640, K=17408, seed=1104),
+                dict(name="shard8_ssm_out", qtype=Q5, N=640, K=6144, seed=1105)]
+
+
+@pytest.mark.parametrize("case", FULL_SHAPES + SHARD_SHAPES, ids=lambda c: c["name"])
 def test_gemv_full_shapes_all_rows(case):
     qt, N, K, seed = case["qtype"], case["N"], case["K"], case["seed"]
     W = synth.superblocks(qt, N, K, seed)
