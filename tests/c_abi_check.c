@@ -57,6 +57,34 @@ int main(void) {
     expect(qk_gemv_batch(items, QK_MAX_BATCH + 1, NULL) == QK_EINVAL_SHAPE, "batch: count too large");
     expect(qk_gemv_batch(items, 2, NULL) == QK_EINVAL_TYPE, "batch: bad entry type");
 
+    /* IQ4_XS: a type of its own, no PLANAR layout */
+    expect(qk_block_bytes(QK_IQ4_XS) == 136, "IQ4_XS block bytes");
+    expect(qk_row_bytes(QK_IQ4_XS, 5120) == 20 * 136, "IQ4_XS row bytes");
+    expect(qk_row_bytes(QK_IQ4_XS | QK_PLANAR, 5120) == -1, "IQ4_XS has no PLANAR rows");
+    expect(qk_gemv(QK_IQ4_XS | QK_PLANAR, W, x, y, 4, 256, 1, NULL) == QK_EINVAL_TYPE, "gemv: IQ4_XS | PLANAR");
+    expect(qk_repack(QK_IQ4_XS, W, y, 4, 256, NULL) == QK_EINVAL_TYPE, "repack: IQ4_XS");
+
+    /* chains: sizes and the checks made before anything reaches the GPU */
+    {
+        qk_chain_entry ce = {QK_IQ4_XS, 0, W, NULL, x, y, NULL, 4, 256};
+        int one = 1;
+        static unsigned char plan[4096];
+        expect(qk_chain_plan_bytes(0, 1) == -1 && qk_chain_plan_bytes(1, 0) == -1, "chain plan bytes: empty");
+        expect(qk_chain_plan_bytes(1, 1) > 0 && qk_chain_plan_bytes(1, 1) <= (int64_t)sizeof plan,
+               "chain plan bytes: one entry");
+        expect(qk_chain_workspace_bytes(0) == -1 && qk_chain_workspace_bytes(10) == 256, "chain workspace bytes");
+        expect(qk_chain_plan(&ce, 1, &one, 1, plan, (int64_t)sizeof plan) == QK_EINVAL_TYPE, "chain: IQ4_XS entry");
+        ce.type = QK_Q4_K;
+        one = QK_MAX_BATCH + 1;
+        expect(qk_chain_plan(&ce, 1, &one, 1, plan, (int64_t)sizeof plan) == QK_EINVAL_SHAPE, "chain: step size");
+        expect(qk_gemv_chain(NULL, W, W, 256, 0, NULL) == QK_EINVAL_PTR, "chain: NULL plan");
+        expect(qk_gemv_chain_noalloc(NULL, W, NULL, 0, NULL) == QK_EINVAL_PTR, "chain noalloc: NULL plan");
+        expect(qk_gemv_chain_noalloc(plan, buf + 8, NULL, 0, NULL) == QK_EINVAL_PTR,
+               "chain noalloc: misaligned plan_dev");
+        memset(plan, 0, sizeof plan);  /* not a plan */
+        expect(qk_gemv_chain_noalloc(plan, W, NULL, 0, NULL) == QK_EINVAL_SHAPE, "chain noalloc: not a plan");
+    }
+
     if (failures == 0) printf("c_abi_check: all checks held\n");
     return failures;
 }
