@@ -1301,7 +1301,9 @@ hipError_t chain_plan(const ChainEntryIn *in, int nentries, const int *step_size
             if (given + share > (int)h.G) return hipErrorInvalidValue;  // more entries than workgroups
             Geo g = chain_geo_of(e.type, e.N, e.K, share, mult);
             const int base = body_code(e.type, g.RL);
-            if (base < 0 || (e.W2 && (e.type & ~PLANAR_FLAG) != Q4_K)) return hipErrorInvalidValue;
+            // the chain compiles bodies for the k-quants only (SwiGLU pairs: Q4_K)
+            if (base < 0 || (e.type & ~PLANAR_FLAG) == IQ4_XS || (e.W2 && (e.type & ~PLANAR_FLAG) != Q4_K))
+                return hipErrorInvalidValue;
             const size_t l = part_lds(e.N, g, mult);
             if (l > (size_t)CHAIN_LDS_MAX) return hipErrorInvalidValue;
             lds = std::max(lds, l);
