@@ -10,7 +10,8 @@ workspace.
   array, starts clean and is whole;
 * the largest chain it takes (QK_CHAIN_NOALLOC_MAX_STEPS steps) runs and
   matches; one step more, a null plan_dev or a misaligned status word are
-  rejected before anything is launched.
+  rejected before anything is launched;
+* repeated calls leave the device's free memory unchanged.
 """
 import numpy as np
 import pytest
@@ -99,6 +100,23 @@ def test_noalloc_timeout_flag_then_clean_run():
     assert int(status.item()) & binding.CHAIN_TIMEOUT
     small, chs = _chain(14, 256, 512)
     _check_same_as_workspace_run(small, chs, status)
+
+
+def test_noalloc_calls_leave_device_memory_unchanged():
+    """After a first call (module loading and the per-device address of the
+    counter array), further calls take no device memory: the free memory the
+    driver reports (hipMemGetInfo) is the same before and after 20 calls."""
+    status = torch.empty(1, dtype=torch.int32, device="cuda")
+    t, ch = _chain(15, 512, 1024)
+    assert _noalloc(ch, status) == binding.QK_OK
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    for _ in range(20):
+        assert _noalloc(ch, status) == binding.QK_OK
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 == free0
+    assert int(status.item()) == 0
 
 
 def test_noalloc_step_limit_and_bad_pointers():
