@@ -111,6 +111,27 @@ template <> struct UnitAddr<Q6_K, PLANAR> {
         : a(16u * u), b(64u * S + 16u * u), c(128u * S + 16u * u), sc(192u * S + 4u * u), d(208u * S + 2u * (u >> 2)) {}
 };
 
+// floor(a / b) for 0 <= a < 2^21 and b >= 1 in three instructions: with
+// rcp's error of at most one ulp the product is within (a + 1/2) / b * 2^-22
+// < 1/(4b) of (a + 1/2) / b, whose distance to the integers is at least 1/(2b).
+// (The compiler's integer division is a long scalar sequence that every wave
+// runs before its first weight load.)
+__device__ __forceinline__ int small_div(int a, int b) {
+    return (int)(((float)a + 0.5f) * __builtin_amdgcn_rcpf((float)b));
+}
+
+// Rows [r0, r1) of workgroup blk of nblk: N rows split as evenly as possible,
+// the first N % nblk workgroups taking one row more.  A row's arithmetic does
+// not depend on its workgroup.
+struct RowSplit {
+    int r0, r1;
+    __device__ RowSplit(int N, int blk, int nblk) {
+        const int q = (int)((uint32_t)N / (uint32_t)nblk), r = N - q * nblk;
+        r0 = blk * q + min(blk, r);
+        r1 = r0 + q + (blk < r ? 1 : 0);
+    }
+};
+
 // fp32 += a.lo*b.lo + a.hi*b.hi with fp16 operands (v_dot2_f32_f16).
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);

@@ -246,8 +246,9 @@ __device__ __forceinline__ float unit_dot(const Unit<T> &U, int q, const KScaleS
 // ---------------------------------------------------------------------------
 // One column, x-stationary and row-balanced.
 //
-// Workgroup b owns the contiguous rows [b*N/G, (b+1)*N/G) (G = gridDim.x), so
-// every workgroup streams the same number of bytes to within one row.  K is
+// Workgroup b owns a contiguous run of floor(N/G) or ceil(N/G) rows (G =
+// gridDim.x; RowSplit), so every workgroup streams the same number of bytes
+// to within one row.  K is
 // walked in segments of at most `useg` units.  Inside a segment lane
 // t < P*useg owns unit column uc = t % useg and row phase ph = t / useg: it
 // holds x of that unit in registers and visits rows r0+ph, r0+ph+P, ... ; a
@@ -263,8 +264,8 @@ __device__ __forceinline__ float unit_dot(const Unit<T> &U, int q, const KScaleS
 // overlaps the arrival of the later ones.  At the end every row's partials
 // are added in a fixed order.
 // ---------------------------------------------------------------------------
-// Workgroup blk of nblk (nthr threads, a multiple of 64) takes rows
-// [blk*N/nblk, (blk+1)*N/nblk).  PAIR (the SwiGLU epilogue): the workgroup
+// Workgroup blk of nblk (nthr threads, a multiple of 64) takes the rows
+// RowSplit(N, blk, nblk) gives it.  PAIR (the SwiGLU epilogue): the workgroup
 // streams those rows of W and then of ep.W2 as 2R rows of one schedule, and
 // row r's output combines the sums of rows r and R + r.  EPI: the store
 // applies ep's residual / fp16 options (else it is the plain fp32 store).
@@ -289,16 +290,16 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     extern __shared__ __attribute__((aligned(16))) float part[];  // partial sums, slot rows of useg floats
     constexpr int DD = D < RL ? D : RL;  // units in flight
     const int tid = (int)threadIdx.x;
-    const int r0 = (int)((int64_t)blk * N / nblk);
-    const int r1 = (int)((int64_t)(blk + 1) * N / nblk);
+    const RowSplit split(N, blk, nblk);
+    const int r0 = split.r0, r1 = split.r1;
     const int R = r1 - r0;
     const int RV = PAIR ? 2 * R : R;  // rows of the schedule
     const int U = K >> 6;
     const size_t row_bytes = (size_t)layout_row_bytes(T, L, K);
-    const int ph = tid / useg, uc = tid - ph * useg;
+    const int ph = small_div(tid, useg), uc = tid - ph * useg;
     const bool lane_ok = ph < P;
     const int ph_c = lane_ok ? ph : 0;
-    const int rows_lane = (RV + P - 1) / P;  // same schedule for every lane
+    const int rows_lane = small_div(RV + P - 1, P);  // same schedule for every lane
     // Q4_K issues the first round's weights of a segment before staging its
     // x, except where the ring live across the staging would spill under the
     // 128-register bound (rounds of four or six rows, and every epilogue or
@@ -312,7 +313,7 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     // its i-th row to slot row i*PT + ph, PT = phases incl. the tail, so every
     // lane owns a distinct slot and no write needs a guard.  Row r of the
     // workgroup is slot row (r / P) * PT + r % P.
-    const int PT = (nthr + useg - 1) / useg;
+    const int PT = small_div(nthr + useg - 1, useg);
     const int slot0 = ph * useg + uc, slot_step = PT * useg;
     uint8_t *xl = reinterpret_cast<uint8_t *>(part + rows_lane * PT * useg);  // the segment's x
     // residuals for the store: the final reduction gives row group g = tid/16

@@ -207,12 +207,12 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
     const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int blk = lane >> 2, j = lane & 3;
     const int wpp = useg >> 4;  // waves per phase
-    const int ph = wave / wpp, wip = wave - ph * wpp;
+    const int ph = small_div(wave, wpp), wip = wave - ph * wpp;
     const int uc = 16 * wip + blk;  // unit column within the segment
-    const int r0 = (int)((int64_t)blockIdx.x * N / gridDim.x);
-    const int r1 = (int)((int64_t)(blockIdx.x + 1) * N / gridDim.x);
+    const RowSplit split(N, (int)blockIdx.x, (int)gridDim.x);
+    const int r0 = split.r0, r1 = split.r1;
     const int R = r1 - r0, RV = PAIR ? 2 * R : R, Q = (RV + 3) >> 2;
-    const int quads_lane = (Q + P - 1) / P;
+    const int quads_lane = small_div(Q + P - 1, P);
     const int U = K >> 6;
     const size_t row_bytes = (size_t)(K >> 8) * Fmt<T>::bytes;
     const int nslot = 4 * wpp;  // partial slots per (row, column): 4 per wave of a phase
