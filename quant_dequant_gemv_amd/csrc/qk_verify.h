@@ -94,8 +94,9 @@ __device__ __forceinline__ float vx_pairs16(const uint4 &v0, const uint4 &v1, ui
     for (int g = 0; g < 4; ++g) {
         o[2 * g] = (w[2 * g] & 0xffffu) | (w[2 * g + 1] << 16);
         o[2 * g + 1] = (w[2 * g] >> 16) | (w[2 * g + 1] & 0xffff0000u);
-        s += (f16_lo(w[2 * g]) + f16_hi(w[2 * g])) + (f16_lo(w[2 * g + 1]) + f16_hi(w[2 * g + 1]));
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s = dot2(w[i], 0x3c003c00u, s);  // (1, 1) pairs
     return s;
 }
 
