@@ -177,8 +177,10 @@ struct KShift {
 template <int QMAX, int S>
 __device__ __forceinline__ KShift k_shift(float d, float dmin, float sc_p, float m_p) {
     KShift k;
-    k.a = d * sc_p;                 // exact: 11 x 6 significant bits
-    const float b = dmin * m_p;     // exact
+    // exact products (11 x 6 significant bits), written as fmas with a zero
+    // addend so that both factors stay fp16 operands (v_fma_mix_f32)
+    k.a = __builtin_fmaf(d, sc_p, 0.f);
+    const float b = __builtin_fmaf(dmin, m_p, 0.f);
     // a = 0 gives b * inf (inf or NaN): fmaxf takes 0 for NaN, the clamp
     // handles inf; with a = 0 the quant sum is multiplied by 0 anyway
     const float c = fminf(fmaxf(rintf(b * __builtin_amdgcn_rcpf(k.a)), 0.f), (float)QMAX);
@@ -295,12 +297,15 @@ template <int T> struct Unit;
 //   p[2] = high-sub-block pair A (s = 16)   p[3] = high pair B (s = 16)
 template <> struct Unit<Q4_K> {
     uint4 h, a, b;
-    // base: uniform pointer; off: byte offset of the row from base (< 2^31)
+    // row: the row's first byte.  On GGUF rows the second half of the
+    // quants follows the first (b = a + 16): addressed as an immediate offset
+    // of the first half's pointer, one 64-bit address less per unit.
     template <bool NT, int L>
-    __device__ __forceinline__ void load(const uint8_t *base, uint32_t off, const UnitAddr<Q4_K, L> &o) {
-        h = ld16<NT>(base + (off + o.h));
-        a = ld16<NT>(base + (off + o.a));
-        b = ld16<NT>(base + (off + o.b));
+    __device__ __forceinline__ void load(const uint8_t *row, const UnitAddr<Q4_K, L> &o) {
+        const uint8_t *pa = row + o.a;
+        h = ld16<NT>(row + o.h);
+        a = ld16<NT>(pa);
+        b = ld16<NT>(L == GGUF ? pa + 16 : row + o.b);
         issue_together();
     }
     __device__ __forceinline__ uint4 header() const { return h; }
@@ -320,12 +325,15 @@ template <> struct Unit<Q4_K> {
 template <> struct Unit<Q5_K> {
     uint4 h, qh0, qh1, a, b;
     template <bool NT, int L>
-    __device__ __forceinline__ void load(const uint8_t *base, uint32_t off, const UnitAddr<Q5_K, L> &o) {
-        h = ld16<NT>(base + (off + o.h));
-        qh0 = ld16<NT>(base + (off + o.qh0));
-        qh1 = ld16<NT>(base + (off + o.qh1));
-        a = ld16<NT>(base + (off + o.a));
-        b = ld16<NT>(base + (off + o.b));
+    // (GGUF rows: qh0 / qh1 at 16 / 32 bytes past the header, b = a + 16,
+    // as immediate offsets)
+    __device__ __forceinline__ void load(const uint8_t *row, const UnitAddr<Q5_K, L> &o) {
+        const uint8_t *ph = row + o.h, *pa = row + o.a;
+        h = ld16<NT>(ph);
+        qh0 = ld16<NT>(L == GGUF ? ph + 16 : row + o.qh0);
+        qh1 = ld16<NT>(L == GGUF ? ph + 32 : row + o.qh1);
+        a = ld16<NT>(pa);
+        b = ld16<NT>(L == GGUF ? pa + 16 : row + o.b);
         issue_together();
     }
     __device__ __forceinline__ uint4 header() const { return h; }
@@ -352,13 +360,15 @@ template <> struct Unit<Q6_K> {
     uint2 sc;      // GGUF: scales[8n .. 8n+7];  PLANAR: .x = this unit's 4 scales, quarter order
     uint32_t d;    // fp16 d in the low half
     template <bool NT, int L>
-    __device__ __forceinline__ void load(const uint8_t *base, uint32_t off, const UnitAddr<Q6_K, L> &o) {
-        a = ld16<NT>(base + (off + o.a));
-        b = ld16<NT>(base + (off + o.b));
-        c = ld16<NT>(base + (off + o.c));
-        if constexpr (L == PLANAR) sc = make_uint2(ld4<NT>(base + (off + o.sc)), 0u);
-        else sc = ld8<NT>(base + (off + o.sc));
-        d = ld2<NT>(base + (off + o.d));
+    // (GGUF rows: b = a + 32 as an immediate offset)
+    __device__ __forceinline__ void load(const uint8_t *row, const UnitAddr<Q6_K, L> &o) {
+        const uint8_t *pa = row + o.a;
+        a = ld16<NT>(pa);
+        b = ld16<NT>(L == GGUF ? pa + 32 : row + o.b);
+        c = ld16<NT>(row + o.c);
+        if constexpr (L == PLANAR) sc = make_uint2(ld4<NT>(row + o.sc), 0u);
+        else sc = ld8<NT>(row + o.sc);
+        d = ld2<NT>(row + o.d);
         issue_together();
     }
     __device__ __forceinline__ void patterns(int i, int /*q*/, uint32_t p[8]) const {
@@ -426,10 +436,12 @@ template <> struct Unit<IQ4_XS> {
     uint2 h;  // .x = d | scales_h << 16, .y = scales_l[0..3]
     uint4 a, b;
     template <bool NT, int L>
-    __device__ __forceinline__ void load(const uint8_t *base, uint32_t off, const UnitAddr<IQ4_XS, L> &o) {
-        h = ld8<NT>(base + (off + o.h));
-        a = ld16<NT>(base + (off + o.a));
-        b = ld16<NT>(base + (off + o.b));
+    // (b = a + 16 as an immediate offset)
+    __device__ __forceinline__ void load(const uint8_t *row, const UnitAddr<IQ4_XS, L> &o) {
+        const uint8_t *pa = row + o.a;
+        h = ld8<NT>(row + o.h);
+        a = ld16<NT>(pa);
+        b = ld16<NT>(pa + 16);
         issue_together();
     }
     __device__ __forceinline__ uint32_t qword(int i) const { return i < 4 ? word(a, i) : word(b, i - 4); }

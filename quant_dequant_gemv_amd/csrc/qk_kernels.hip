@@ -348,10 +348,10 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
                 const uint8_t *base = v < R ? W + (size_t)(r0 + v) * row_bytes
                                             : reinterpret_cast<const uint8_t *>(ep.W2) +
                                                   (size_t)(r0 + v - R) * row_bytes;
-                dst.template load<NT, L>(base, 0u, ua);
+                dst.template load<NT, L>(base, ua);
             } else {
                 const int row = min(r0 + ph_c + P * i, r1 - 1);
-                dst.template load<NT, L>(W + (size_t)row * row_bytes, 0u, ua);
+                dst.template load<NT, L>(W + (size_t)row * row_bytes, ua);
             }
         };
         // the round of RL rows from row i0 of the lane: a straight line with
@@ -583,7 +583,7 @@ __global__ void __launch_bounds__(WG) dequant_kernel(const uint8_t *__restrict__
     const int s = u >> 2, q = u & 3;
     float *o = out + (size_t)row * (size_t)K + 256 * s;
     Unit<T> U;
-    U.template load<false, L>(W + (size_t)row * (size_t)layout_row_bytes(T, L, K), 0u, UnitAddr<T, L>(K >> 8, u));
+    U.template load<false, L>(W + (size_t)row * (size_t)layout_row_bytes(T, L, K), UnitAddr<T, L>(K >> 8, u));
     if constexpr (T == IQ4_XS) {
         // d*2^24*(ls - 32) exact (17 significant bits), times kv*2^-24 from
         // the pattern: at most 24 significant bits, exact

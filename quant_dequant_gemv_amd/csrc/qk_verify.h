@@ -308,10 +308,10 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
                     const uint8_t *base = v < R ? W + (size_t)(r0 + v) * row_bytes
                                                 : reinterpret_cast<const uint8_t *>(ep.W2) +
                                                       (size_t)(r0 + v - R) * row_bytes;
-                    dst.template load<false, GGUF>(base, 0u, ua);
+                    dst.template load<false, GGUF>(base, ua);
                 } else {
                     const int row = min(r0 + 4 * (ph + P * (i0 + i)) + j, r1 - 1);
-                    dst.template load<false, GGUF>(W + (size_t)row * row_bytes, 0u, ua);
+                    dst.template load<false, GGUF>(W + (size_t)row * row_bytes, ua);
                 }
             };
 #pragma unroll
