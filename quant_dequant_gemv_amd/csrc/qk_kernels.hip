@@ -93,15 +93,22 @@ __device__ __forceinline__ uint4 x_chunk(const uint8_t *xl, int c) {
 // of 4) has the residue of tid mod 4: they sit in one quad of lanes, whose
 // DPP sum (pairs, then the two pairs) every lane of the quad holds.
 // Indices past the segment are clamped for the reads (every lane takes part
-// in the DPP sums) and write nothing.
+// in the DPP sums) and write nothing.  between() runs once, after the first
+// chunks' loads are issued and before they are waited for (the caller's
+// weight loads then queue behind them).
+struct NoLoads {
+    __device__ void operator()() const {}
+};
+template <class Between = NoLoads>
 __device__ __forceinline__ void stage_x(uint8_t *xl, const uint16_t *__restrict__ x, int s0, int ns, int tid,
-                                        int nthr) {
+                                        int nthr, const Between &between = Between()) {
     const uint4 *xg = reinterpret_cast<const uint4 *>(x) + (size_t)s0 * 8;
     const int nch = ns * 8;
     for (int b = 0; b < nch; b += 4 * nthr) {
         uint4 v[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) v[k] = xg[min(b + tid + k * nthr, nch - 1)];
+        if (b == 0) between();  // after the first chunks' loads, before their wait
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int c = b + tid + k * nthr;
@@ -300,15 +307,13 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     const bool lane_ok = ph < P;
     const int ph_c = lane_ok ? ph : 0;
     const int rows_lane = small_div(RV + P - 1, P);  // same schedule for every lane
-    // Q4_K issues the first round's weights of a segment before staging its
-    // x, except where the ring live across the staging would spill under the
-    // 128-register bound (rounds of four or six rows, and every epilogue or
-    // pair variant: 12 bytes per lane of scratch each; without the early
-    // ring the SwiGLU pair at 17408 x 5120 runs 25.2 -> 24.0 us).  Measured:
-    // PLANAR rows 2-3% faster, 1024 x 5120 3-12%; Q5_K (no gain), Q6_K (x read
-    // per lane) and IQ4_XS keep the plain order.
+    // Q4_K issues weight loads of a segment's first round before staging its
+    // x (the early ring: see below), except where a unit live across the
+    // staging would spill under the 128-register bound: rounds of four rows,
+    // and the epilogue and pair variants on PLANAR rows.  Q5_K (no gain),
+    // Q6_K (x read per lane) and IQ4_XS keep the plain order.
     constexpr bool CHAIN = !__is_same(Hook, NoHook);
-    constexpr bool PRE = CHAIN || (T == Q4_K && RL != 6 && RL != 4 && !EPI && !PAIR);
+    constexpr bool PRE = CHAIN || (T == Q4_K && RL != 4 && (L == GGUF || (!EPI && !PAIR)));
     // Partial sums: the lane of phase ph (tail lanes ph >= P included) writes
     // its i-th row to slot row i*PT + ph, PT = phases incl. the tail, so every
     // lane owns a distinct slot and no write needs a guard.  Row r of the
@@ -377,16 +382,32 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
             // loads retire in order, and the ring is older)
             Unit<T> buf[DD];
             if (T != Q6_K && s0 > 0) __syncthreads();  // every lane holds the previous segment's x in registers
+            // Before the copy the chain issues its whole first ring (its wait
+            // for the previous step comes next); a single launch issues the
+            // first unit only -- the smaller opening burst of the whole grid
+            // brings every wave's first unit in sooner -- and the rest of the
+            // ring after the copy's loads (GGUF rows) or after its wait
+            // (PLANAR rows), as measured fastest.
+            constexpr int EARLY = CHAIN ? DD : 1;
 #pragma unroll
-            for (int p = 0; p < DD; ++p) load_row(buf[p], p);
+            for (int p = 0; p < EARLY; ++p) load_row(buf[p], p);
+            auto rest = [&]() {
+#pragma unroll
+                for (int p = EARLY; p < DD; ++p) load_row(buf[p], p);
+            };
             if (s0 == 0) {
                 hook();
                 read_res();
             }
             if constexpr (T == Q6_K) {
                 load_x_q6(X, x, u);
+            } else if constexpr (L == GGUF) {
+                stage_x(xl, x, s0, ns, tid, nthr, rest);
+                __syncthreads();
+                load_x<T>(X, xl, u - s0);
             } else {
                 stage_x(xl, x, s0, ns, tid, nthr);
+                rest();
                 __syncthreads();
                 load_x<T>(X, xl, u - s0);
             }
