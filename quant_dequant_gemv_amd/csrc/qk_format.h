@@ -123,11 +123,31 @@ __device__ __forceinline__ int small_div(int a, int b) {
 // Rows [r0, r1) of workgroup blk of nblk: N rows split as evenly as possible,
 // the first N % nblk workgroups taking one row more.  A row's arithmetic does
 // not depend on its workgroup.
+//
+// Front-loaded (fc > 0): the workgroups are dispatched in rounds of fc, one
+// per CU, and a CU's memory requests are served oldest workgroup first, so
+// the last round's weights arrive last.  The workgroups of every round but
+// the last take fcap rows each (a full straight-line round), the last round
+// the rest, split evenly: the launch's tail is shorter.  The launcher checks
+// nblk % fc == 0 and (nblk - fc) * fcap <= N.
 struct RowSplit {
     int r0, r1;
-    __device__ RowSplit(int N, int blk, int nblk) {
+    __device__ RowSplit(int N, int blk, int nblk, int fc = 0, int fcap = 0) {
+        int base = 0;
+        if (fc > 0) {
+            const int front = nblk - fc;
+            if (blk < front) {
+                r0 = blk * fcap;
+                r1 = r0 + fcap;
+                return;
+            }
+            base = front * fcap;
+            N -= base;
+            blk -= front;
+            nblk = fc;
+        }
         const int q = (int)((uint32_t)N / (uint32_t)nblk), r = N - q * nblk;
-        r0 = blk * q + min(blk, r);
+        r0 = base + blk * q + min(blk, r);
         r1 = r0 + q + (blk < r ? 1 : 0);
     }
 };

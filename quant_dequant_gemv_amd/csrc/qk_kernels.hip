@@ -293,11 +293,12 @@ __host__ __device__ constexpr int body_syncs(int T, int U, int useg) {
 template <int T, int L, int RL, int D, bool NT, bool PAIR, bool EPI, class Hook = NoHook>
 __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const uint16_t *__restrict__ x,
                                            void *y, int N, int K, int useg, int P, int blk, int nblk,
-                                           int nthr, const Epilogue &ep, const Hook &hook = Hook()) {
+                                           int nthr, const Epilogue &ep, const Hook &hook = Hook(), int fc = 0,
+                                           int fcap = 0) {
     extern __shared__ __attribute__((aligned(16))) float part[];  // partial sums, slot rows of useg floats
     constexpr int DD = D < RL ? D : RL;  // units in flight
     const int tid = (int)threadIdx.x;
-    const RowSplit split(N, blk, nblk);
+    const RowSplit split(N, blk, nblk, fc, fcap);
     const int r0 = split.r0, r1 = split.r1;
     const int R = r1 - r0;
     const int RV = PAIR ? 2 * R : R;  // rows of the schedule
@@ -500,9 +501,9 @@ constexpr int gemv1_bound() {
 template <int T, int L, int RL, int D, bool NT, bool PAIR, bool EPI>
 __global__ void __launch_bounds__((gemv1_bound<T, RL, D>())) gemv1_kernel(const uint8_t *__restrict__ W,
                                                       const uint16_t *__restrict__ x, void *y, int N, int K,
-                                                      int useg, int P, const Epilogue ep) {
+                                                      int useg, int P, int fc, int fcap, const Epilogue ep) {
     gemv1_body<T, L, RL, D, NT, PAIR, EPI>(W, x, y, N, K, useg, P, (int)blockIdx.x, (int)gridDim.x,
-                                           (int)blockDim.x, ep);
+                                           (int)blockDim.x, ep, NoHook(), fc, fcap);
 }
 
 // ---------------------------------------------------------------------------
@@ -733,7 +734,7 @@ constexpr int LDS_PART = 128 * 1024;  // LDS budget of one workgroup: partial su
 constexpr int LDS_MAX = 160 * 1024;   // gfx950: the most one workgroup may take
 
 // Launch geometry of the ncols = 1 kernel.
-struct Geo { int G, threads, useg, P, RL; };
+struct Geo { int G, threads, useg, P, RL, fc = 0, fcap = 0; };  // fc, fcap: RowSplit's front loading
 
 static int cu_count() { return device_cus(); }
 
@@ -759,7 +760,7 @@ static_assert(RowRounds<Q5_K>::max_threads <= gemv1_bound<Q5_K, 4, 2>(), "gemv1_
 // LDS of one workgroup: ceil(R / P) slot rows per phase, tail phase included
 // (mult = 2: the paired rows of the SwiGLU epilogue).
 static size_t part_lds(int64_t N, const Geo &g, int mult = 1) {
-    const int64_t R = mult * ((N + g.G - 1) / g.G), rows_lane = (R + g.P - 1) / g.P;
+    const int64_t R = mult * std::max<int64_t>((N + g.G - 1) / g.G, g.fcap), rows_lane = (R + g.P - 1) / g.P;
     const int64_t PT = (g.threads + g.useg - 1) / g.useg;
     return (size_t)(rows_lane * PT * g.useg) * 4 + (size_t)g.useg * XSTRIDE;  // partial sums + x copy (Q4_K/Q5_K)
 }
@@ -798,6 +799,13 @@ static bool small_workgroups(int64_t N, int cus, int mult, Geo &g) {
         for (int k = 0; k < RR::n; ++k)
             if (RR::rl[k] >= rows) { g.RL = RR::rl[k]; break; }
         g.threads = (p4 * g.useg + 63) / 64 * 64;
+        // several rounds of one workgroup per CU in one straight-line round:
+        // front-load them (RowSplit)
+        const int64_t rounds = G % cus == 0 ? G / cus : 0, fcap = (int64_t)p4 * g.RL / mult;
+        if (rounds >= 2 && (G - cus) * fcap <= N && rows <= g.RL) {
+            g.fc = cus;
+            g.fcap = (int)fcap;
+        }
         return part_lds(N, g, mult) <= (size_t)LDS_PART;
     }
 }
@@ -865,11 +873,13 @@ static hipError_t launch1(const void *W, const void *x, void *y, int64_t N, int6
     if (!PAIR && !ep.res && !ep.f16) {
         allow_lds<gemv1_kernel<T, L, RL, D, NT, false, false>>();
         hipLaunchKernelGGL((gemv1_kernel<T, L, RL, D, NT, false, false>), dim3(geo.G), dim3(geo.threads), lds, st,
-                           (const uint8_t *)W, (const uint16_t *)x, y, (int)N, (int)K, geo.useg, geo.P, ep);
+                           (const uint8_t *)W, (const uint16_t *)x, y, (int)N, (int)K, geo.useg, geo.P, geo.fc,
+                           geo.fcap, ep);
     } else {
         allow_lds<gemv1_kernel<T, L, RL, D, NT, PAIR, true>>();
         hipLaunchKernelGGL((gemv1_kernel<T, L, RL, D, NT, PAIR, true>), dim3(geo.G), dim3(geo.threads), lds, st,
-                           (const uint8_t *)W, (const uint16_t *)x, y, (int)N, (int)K, geo.useg, geo.P, ep);
+                           (const uint8_t *)W, (const uint16_t *)x, y, (int)N, (int)K, geo.useg, geo.P, geo.fc,
+                           geo.fcap, ep);
     }
     return hipGetLastError();
 }
@@ -919,14 +929,18 @@ hipError_t launch_gemv1(int type, const void *W, const void *x, void *y, int64_t
     }
 }
 
+// (the merged launch splits each entry's rows evenly: no front loading)
 static Geo geometry_of(int type, int64_t N, int64_t K, int cus) {
     const bool planar = (type & PLANAR_FLAG) != 0;
+    Geo g;
     switch (type & ~PLANAR_FLAG) {
-    case Q4_K: return planar ? geometry<Q4_K, PLANAR>(N, K, cus) : geometry<Q4_K, GGUF>(N, K, cus);
-    case Q5_K: return geometry<Q5_K>(N, K, cus);
-    case IQ4_XS: return geometry<IQ4_XS>(N, K, cus);
-    default: return planar ? geometry<Q6_K, PLANAR>(N, K, cus) : geometry<Q6_K, GGUF>(N, K, cus);
+    case Q4_K: g = planar ? geometry<Q4_K, PLANAR>(N, K, cus) : geometry<Q4_K, GGUF>(N, K, cus); break;
+    case Q5_K: g = geometry<Q5_K>(N, K, cus); break;
+    case IQ4_XS: g = geometry<IQ4_XS>(N, K, cus); break;
+    default: g = planar ? geometry<Q6_K, PLANAR>(N, K, cus) : geometry<Q6_K, GGUF>(N, K, cus); break;
     }
+    g.fc = g.fcap = 0;
+    return g;
 }
 
 static int body_code_gguf(int type, int rl);

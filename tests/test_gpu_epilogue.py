@@ -147,6 +147,34 @@ def test_residual_down_shape_all_rows():
     _assert_within(y, y_ref, oracle.residual_bound(y_ref, S), "ffn down + residual")
 
 
+@pytest.mark.parametrize("planar", [False, True], ids=["GGUF", "PLANAR"])
+def test_front_loaded_epilogues_all_rows(planar):
+    """Front-loaded row splits with empty workgroups in the last dispatch
+    round: the SwiGLU pair at 9220 x 5120 (252 of the last round's workgroups
+    have no rows) and the residual added in place at 18440 x 5120 (248).
+    Every row."""
+    K = 5120
+    Ng, Nr = 9220, 18440
+    Wg, Wu = synth.superblocks(Q4, Ng, K, 31), synth.superblocks(Q4, Ng, K, 32)
+    Wr = synth.superblocks(Q4, Nr, K, 33)
+    x = synth.activations(K, 1, 31)
+    r = _residual(Nr, 1, 33)
+    Wgd, Wud, Wrd, xd = dev(Wg.reshape(-1)), dev(Wu.reshape(-1)), dev(Wr.reshape(-1)), dev(x)
+    t = Q4
+    if planar:
+        Wgd, Wud = binding.repack(Q4, Wgd, Ng, K), binding.repack(Q4, Wud, Ng, K)
+        Wrd = binding.repack(Q4, Wrd, Nr, K)
+        t = Q4 | binding.PLANAR
+    ys = binding.gemv_swiglu(t, Wgd, Wud, xd, Ng, K)
+    yr = dev(r.copy())
+    binding.gemv_ex(t, Wrd, xd, Nr, K, residual=yr, out=yr)
+    torch.cuda.synchronize()
+    y_ref, g, Sg, u, Su = oracle.swiglu(Q4, Wg, Wu, x, K)
+    _assert_within(ys.cpu().numpy(), y_ref, oracle.swiglu_bound(y_ref, g, Sg, u, Su), f"swiglu {Ng}x{K}")
+    y_ref, S = oracle.gemv_residual(Q4, Wr, x, K, r)
+    _assert_within(yr.cpu().numpy().reshape(Nr, 1), y_ref, oracle.residual_bound(y_ref, S), f"residual {Nr}x{K}")
+
+
 @pytest.mark.parametrize("qt,N,K", [(Q4, 17408, 5120), (Q4, 200000, 256), (Q5, 120000, 512)],
                          ids=["rows68_per_wg", "rows782_per_wg", "Q5_rows469_per_wg"])
 def test_residual_many_rows_per_workgroup(qt, N, K):

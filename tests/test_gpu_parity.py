@@ -12,9 +12,9 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import assert_row_bound, gpu_dequant, gpu_gemv, needs_gpu, same_f32
+from gpu_util import assert_row_bound, dev, gpu_dequant, gpu_gemv, needs_gpu, same_f32, torch
 from kquant_pack import load_golden
-from quant_dequant_gemv_amd import synth
+from quant_dequant_gemv_amd import binding, synth
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -174,6 +174,29 @@ def test_gemv_row_rounds_all_rows(qt, N):
     y = gpu_gemv(qt, W, x, N, K)
     y_ref, S = oracle.gemv(qt, W, x, K)
     assert_row_bound(y, y_ref, S, f"{NAMES[qt]} {N}x{K}")
+
+
+# Front-loaded row splits: a launch of two to four small workgroups per CU
+# gives every dispatch round but the last a full straight-line round of rows
+# and the last round the rest.  At K = 5120: 9220 and 13830 rows (two and
+# three workgroups per CU), 18440 (four per CU; the last round has 8 rows, so
+# 248 of its workgroups have none), 24576 (four full rounds).  Every row is
+# checked, on GGUF and PLANAR rows.
+@pytest.mark.parametrize("planar", [False, True], ids=["GGUF", "PLANAR"])
+@pytest.mark.parametrize("qt,N", [(Q4, 9220), (Q4, 13830), (Q4, 18440), (Q4, 24576), (IQ4, 18440)],
+                         ids=lambda v: NAMES.get(v, str(v)))
+def test_gemv_front_loaded_rounds_all_rows(qt, N, planar):
+    if planar and qt == IQ4:
+        pytest.skip("IQ4_XS has no PLANAR layout")
+    K = 5120
+    W, x = _case(qt, N, K, 600 + N)
+    Wd, t = dev(W.reshape(-1)), qt
+    if planar:
+        Wd, t = binding.repack(qt, Wd, N, K), qt | binding.PLANAR
+    y = binding.gemv(t, Wd, dev(x), N, K)
+    torch.cuda.synchronize()
+    y_ref, S = oracle.gemv(qt, W, x, K)
+    assert_row_bound(y.cpu().numpy(), y_ref, S, f"{NAMES[qt]} {N}x{K} planar={planar}")
 
 
 # K > 16384 leaves room for one row phase of useg = K/64 lanes (Q4_K/Q5_K:
