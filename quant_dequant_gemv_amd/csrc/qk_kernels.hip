@@ -532,6 +532,7 @@ struct BatchItem {
     const uint16_t *x;
     float *y;
     int N, K, useg, P, threads, code;
+    int fc, fcap;  // RowSplit's front loading over the entry's workgroups (fc = 0: even)
 };
 struct BatchArgs {
     int count;
@@ -548,10 +549,10 @@ __global__ void __launch_bounds__(1024) gemv1_batch_kernel(const BatchArgs a) {
     const Epilogue plain{nullptr, nullptr, 0};
 #define QK_BODY(T, RL, D) \
     gemv1_body<T, GGUF, RL, D, false, false, false>(e.W, e.x, e.y, e.N, e.K, e.useg, e.P, blk, nblk, e.threads, \
-                                                    plain)
+                                                    plain, NoHook(), e.fc, e.fcap)
 #define QK_BODYP(T, RL, D) \
     gemv1_body<T, PLANAR, RL, D, true, false, false>(e.W, e.x, e.y, e.N, e.K, e.useg, e.P, blk, nblk, e.threads, \
-                                                      plain)
+                                                      plain, NoHook(), e.fc, e.fcap)
     switch (e.code) {
     case B_Q4_1: QK_BODY(Q4_K, 1, 1); break;
     case B_Q4_2: QK_BODY(Q4_K, 2, 2); break;
@@ -929,7 +930,18 @@ hipError_t launch_gemv1(int type, const void *W, const void *x, void *y, int64_t
     }
 }
 
-// (the merged launch splits each entry's rows evenly: no front loading)
+static Geo geometry_front(int type, int64_t N, int64_t K, int cus) {
+    const bool planar = (type & PLANAR_FLAG) != 0;
+    switch (type & ~PLANAR_FLAG) {
+    case Q4_K: return planar ? geometry<Q4_K, PLANAR>(N, K, cus) : geometry<Q4_K, GGUF>(N, K, cus);
+    case Q5_K: return geometry<Q5_K>(N, K, cus);
+    case IQ4_XS: return geometry<IQ4_XS>(N, K, cus);
+    default: return planar ? geometry<Q6_K, PLANAR>(N, K, cus) : geometry<Q6_K, GGUF>(N, K, cus);
+    }
+}
+
+// (the merged launch splits an entry's rows evenly unless it front-loads a
+// run itself)
 static Geo geometry_of(int type, int64_t N, int64_t K, int cus) {
     const bool planar = (type & PLANAR_FLAG) != 0;
     Geo g;
@@ -1000,10 +1012,32 @@ hipError_t launch_gemv_batch(const BatchEntry *in, int count, hipStream_t st) {
         int64_t t = total;
         size_t l = lds;
         int th = threads;
+        // Front loading (RowSplit) for a run that starts at a dispatch round
+        // and takes several rounds of small workgroups: the first entry's
+        // rows fill every round but the last at fcap rows per workgroup, and
+        // its remaining rows and the later entries share the last round.
+        const Geo gf = geometry_front(in[i0].type, rows, in[i0].K, cus);
+        const int64_t front = gf.fc ? (int64_t)gf.G - cus : 0;
+        const bool fl = joint && front > 0 && total % cus == 0 && gf.G == g.G && gf.RL == g.RL &&
+                        in[i0].N >= front * gf.fcap;
+        const int64_t last_rows = rows - front * gf.fcap;  // rows of the run's last round
         for (int i = i0; i < i1; ++i) {
             const BatchEntry &e = in[i];
             Geo gi = joint ? g : geometry_of(e.type, e.N, e.K, cus);
-            if (joint) {
+            if (fl) {
+                // entry i's last-round workgroups in proportion to its last-round rows
+                const int64_t lr = i == i0 ? e.N - front * gf.fcap : e.N;
+                done += lr;
+                const int64_t upto = last_rows > 0 ? (int64_t)cus * done / last_rows : 0;
+                int64_t nl = std::min<int64_t>(upto - given, lr);
+                if (lr > 0) nl = std::max<int64_t>(nl, 1);
+                given += nl;
+                if (nl * gf.fcap < lr) return false;  // (cannot happen: the last round fits)
+                gi.G = (int)((i == i0 ? front : 0) + nl);
+                gi.fc = (int)nl;
+                gi.fcap = gf.fcap;
+                if (gi.G < 1 || part_lds(e.N, gi) > (size_t)LDS_PART) return false;
+            } else if (joint) {
                 // workgroups in proportion to the rows (cumulative rounding:
                 // the run's total is the joint launch's), at least one each
                 done += e.N;
@@ -1015,7 +1049,7 @@ hipError_t launch_gemv_batch(const BatchEntry *in, int count, hipStream_t st) {
             const int code = body_code(e.type, gi.RL);
             if (code < 0) return false;
             a.it[i] = BatchItem{(const uint8_t *)e.W, (const uint16_t *)e.x, (float *)e.y, (int)e.N, (int)e.K,
-                                gi.useg, gi.P, gi.threads, code};
+                                gi.useg, gi.P, gi.threads, code, gi.fc, gi.fcap};
             t += gi.G;
             if (t > INT32_MAX) return false;
             a.first[i + 1] = (int)t;
@@ -1036,7 +1070,8 @@ hipError_t launch_gemv_batch(const BatchEntry *in, int count, hipStream_t st) {
             ++i1;
         }
         const Geo g = geometry_of(in[i0].type, rows, in[i0].K, cus);
-        if (!(i1 - i0 > 1 && place(i0, i1, true, g, rows)) && !place(i0, i1, false, g, rows))
+        // (a single entry placed jointly takes the run's geometry: its own)
+        if (!place(i0, i1, true, g, rows) && !place(i0, i1, false, g, rows))
             return hipErrorInvalidValue;
         i0 = i1;
     }
