@@ -450,6 +450,30 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
     const uint32_t inv_p2 = (0x80000000u + (uint32_t)P - 1u) / (uint32_t)P;
     constexpr float oscale = T == Q6_K || T == IQ4_XS ? 1.f : 0x1p48f;
     // the sum of schedule row v (valid or not, every lane of the 16 takes part)
+    // as two steps: `issue` reads the lane's float4 groups c = j, j + 16, ...
+    // (at most NRD of them; groups past c4 read as zero, which leaves every
+    // sum unchanged: it starts at +0), `fold` adds them in that order and sums
+    // over the 16-lane row with DPP (no LDS round trips): pairs, quads, the
+    // two quads of each half-row, the two half-rows
+    constexpr int NRD = T == Q6_K ? 5 : 2;
+    auto issue = [&](int v, bool ok, float4 (&w)[NRD]) {
+        const int vi = (int)__umulhi(2u * (uint32_t)v, inv_p2);
+        const int sr = ok ? vi * PT + (v - vi * P) : 0;
+        const float4 *pr = reinterpret_cast<const float4 *>(part + (size_t)sr * useg);
+#pragma unroll
+        for (int k = 0; k < NRD; ++k) w[k] = j + 16 * k < c4 ? pr[j + 16 * k] : make_float4(0.f, 0.f, 0.f, 0.f);
+    };
+    auto fold = [&](float a, const float4 (&w)[NRD], int n) {
+#pragma unroll
+        for (int k = 0; k < NRD; ++k)
+            if (k < n) a += (w[k].x + w[k].y) + (w[k].z + w[k].w);
+        a += dpp_f32<0xb1>(a);   // quad_perm [1,0,3,2]
+        a += dpp_f32<0x4e>(a);   // quad_perm [2,3,0,1]
+        a += dpp_f32<0x141>(a);  // row_half_mirror
+        a += dpp_f32<0x140>(a);  // row_mirror
+        return a * oscale;
+    };
+    // the general form: any number of groups per lane, read and added in turn
     auto row_sum = [&](int v, bool ok) {
         const int vi = (int)__umulhi(2u * (uint32_t)v, inv_p2);
         const int sr = ok ? vi * PT + (v - vi * P) : 0;
@@ -460,19 +484,12 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
             const float4 w = pr[c];
             a += (w.x + w.y) + (w.z + w.w);
         }
-        // sum over the 16-lane row with DPP (no LDS round trips): pairs, quads,
-        // the two quads of each half-row, the two half-rows
-        a += dpp_f32<0xb1>(a);   // quad_perm [1,0,3,2]
-        a += dpp_f32<0x4e>(a);   // quad_perm [2,3,0,1]
-        a += dpp_f32<0x141>(a);  // row_half_mirror
-        a += dpp_f32<0x140>(a);  // row_mirror
-        return a * oscale;
+        const float4 none[NRD] = {};
+        return fold(a, none, 0);
     };
-    int pass = 0;
-    for (int rr = tid >> 4; rr - (tid >> 4) < R; rr += nthr >> 4, ++pass) {
+    // the store of schedule row rr (pass: the lane's round of rows so far)
+    auto store = [&](int rr, int pass, float v) {
         const bool rok = rr < R;
-        float v = row_sum(rr, rok);
-        if constexpr (PAIR) v = silu(v) * row_sum(R + rr, rok);
         float rv = 0.f;
         if constexpr (EPI)  // (all 16 lanes take part in the cross-lane read)
             if (pass < 16) rv = __shfl(resp, (tid & 63 & ~15) + pass);
@@ -483,6 +500,38 @@ __device__ __forceinline__ void gemv1_body(const uint8_t *__restrict__ W, const 
             } else {
                 reinterpret_cast<float *>(y)[r0 + rr] = v;
             }
+        }
+    };
+    const int rpp = nthr >> 4;  // rows per round of the 16-lane groups
+    // at most two rounds: every LDS read of a lane's rows is issued before
+    // the first sum, one wait instead of one per group and round
+    auto rounds = [&](auto np) {
+        constexpr int NP = decltype(np)::value, NS = PAIR ? 2 : 1;
+        float4 w[NP][NS][NRD];
+#pragma unroll
+        for (int pass = 0; pass < NP; ++pass) {
+            const int g = (tid >> 4) + pass * rpp;
+            issue(g, g < R, w[pass][0]);
+            if constexpr (PAIR) issue(R + g, g < R, w[pass][NS - 1]);
+        }
+#pragma unroll
+        for (int pass = 0; pass < NP; ++pass) {
+            float v = fold(0.f, w[pass][0], NRD);
+            if constexpr (PAIR) v = silu(v) * fold(0.f, w[pass][NS - 1], NRD);
+            store((tid >> 4) + pass * rpp, pass, v);
+        }
+    };
+    if (c4 <= 16 * NRD && R <= rpp) {
+        rounds(std::integral_constant<int, 1>());
+    } else if (c4 <= 16 * NRD && R <= 2 * rpp) {
+        rounds(std::integral_constant<int, 2>());
+    } else {
+        int pass = 0;
+        for (int rr = tid >> 4; rr - (tid >> 4) < R; rr += rpp, ++pass) {
+            const bool rok = rr < R;
+            float v = row_sum(rr, rok);
+            if constexpr (PAIR) v = silu(v) * row_sum(R + rr, rok);
+            store(rr, pass, v);
         }
     }
 }

@@ -182,12 +182,12 @@ def test_gemv_row_rounds_all_rows(qt, N):
 # three workgroups per CU), 18440 (four per CU; the last round has 8 rows, so
 # 248 of its workgroups have none), 24576 (four full rounds).  Every row is
 # checked, on GGUF and PLANAR rows.
-@pytest.mark.parametrize("planar", [False, True], ids=["GGUF", "PLANAR"])
-@pytest.mark.parametrize("qt,N", [(Q4, 9220), (Q4, 13830), (Q4, 18440), (Q4, 24576), (IQ4, 18440)],
-                         ids=lambda v: NAMES.get(v, str(v)))
+# (IQ4_XS has no PLANAR layout: GGUF rows only)
+@pytest.mark.parametrize("qt,N,planar",
+                         [(q, n, p) for q, n in [(Q4, 9220), (Q4, 13830), (Q4, 18440), (Q4, 24576), (IQ4, 18440)]
+                          for p in ((False, True) if q != IQ4 else (False,))],
+                         ids=lambda v: {True: "PLANAR", False: "GGUF"}[v] if isinstance(v, bool) else NAMES.get(v, str(v)))
 def test_gemv_front_loaded_rounds_all_rows(qt, N, planar):
-    if planar and qt == IQ4:
-        pytest.skip("IQ4_XS has no PLANAR layout")
     K = 5120
     W, x = _case(qt, N, K, 600 + N)
     Wd, t = dev(W.reshape(-1)), qt
