@@ -266,6 +266,28 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
             }
         }
         __syncthreads();
+        // Launches of up to 8 columns issue the segment's first ring of
+        // weight loads here, before the x reads of the planes (2-7% faster
+        // at 2-8 columns); the column-group variant issues it after them
+        // (4 column blocks of x leave no room: 2.5% slower).
+        constexpr bool EARLY = !WIDE;
+        const UnitAddr<T, GGUF> ua(K >> 8, u);
+        auto load_quad = [&](Unit<T> &dst, int qi) {  // qi: the lane's quad index
+            if constexpr (PAIR) {
+                const int v = min(4 * (ph + P * qi) + j, RV - 1);  // row of the schedule
+                const uint8_t *base = v < R ? W + (size_t)(r0 + v) * row_bytes
+                                            : reinterpret_cast<const uint8_t *>(ep.W2) +
+                                                  (size_t)(r0 + v - R) * row_bytes;
+                dst.template load<false, GGUF>(base, ua);
+            } else {
+                const int row = min(r0 + 4 * (ph + P * qi) + j, r1 - 1);
+                dst.template load<false, GGUF>(W + (size_t)row * row_bytes, ua);
+            }
+        };
+        Unit<T> buf[DD];
+        if constexpr (EARLY)
+#pragma unroll
+            for (int p = 0; p < DD; ++p) load_quad(buf[p], p);
         // this lane's columns j, j+4 in registers; group sums of all columns of the unit
         uint32_t xr[NCB][32];
         // Q4_K/Q5_K: the sums of this lane's own columns (4cb + j) over the
@@ -298,24 +320,10 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
                 xq[3][g] = quad_bcast<3>(xs[0][g]);
             }
         }
-        const UnitAddr<T, GGUF> ua(K >> 8, u);
-
         for (int i0 = 0; i0 < quads_lane; i0 += RL) {
-            Unit<T> buf[DD];
-            auto load_quad = [&](Unit<T> &dst, int i) {
-                if constexpr (PAIR) {
-                    const int v = min(4 * (ph + P * (i0 + i)) + j, RV - 1);  // row of the schedule
-                    const uint8_t *base = v < R ? W + (size_t)(r0 + v) * row_bytes
-                                                : reinterpret_cast<const uint8_t *>(ep.W2) +
-                                                      (size_t)(r0 + v - R) * row_bytes;
-                    dst.template load<false, GGUF>(base, ua);
-                } else {
-                    const int row = min(r0 + 4 * (ph + P * (i0 + i)) + j, r1 - 1);
-                    dst.template load<false, GGUF>(W + (size_t)row * row_bytes, ua);
-                }
-            };
+            if (!EARLY || i0 > 0)
 #pragma unroll
-            for (int p = 0; p < DD; ++p) load_quad(buf[p], p);
+                for (int p = 0; p < DD; ++p) load_quad(buf[p], i0 + p);
 #pragma unroll
             for (int p = 0; p < RL; ++p) {
                 const Unit<T> &Un = buf[p % DD];
@@ -432,7 +440,7 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
                             val[4 * cb + i] = __builtin_fmaf(kL.a, Dl[cb][i], __builtin_fmaf(fh, Dh[cb][i], E[i]));
                     }
                 }
-                if (p + DD < RL) load_quad(buf[p % DD], p + DD);
+                if (p + DD < RL) load_quad(buf[p % DD], i0 + p + DD);
                 // fold the 4 blocks of each 16-lane row (same row j, consecutive units)
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
