@@ -821,6 +821,18 @@ def main():
         del vt
         torch.cuda.empty_cache()
 
+    # the verify form on the mixed-type shapes (Q6_K FFN down, Q5_K output
+    # projection) at 2, 4 and 8 columns
+    verify_mixed = []
+    for e in synth.MIXED:
+        for nc in (2, 4, 8):
+            vt = make_tensors(torch, [dict(e, name=f"{e['name']}_ncols{nc}", ncols=nc)])
+            r = per_shape(torch, launcher, vt)[0]
+            r["ncols"] = nc
+            verify_mixed.append(r)
+            del vt
+            torch.cuda.empty_cache()
+
     progress("verify")
     fused_out = fused_epilogues(torch)
     progress("fused epilogues")
@@ -866,6 +878,7 @@ def main():
         "mixed_types": mixed_out,
         "planar_rows": planar_out,
         "verify": verify_out,
+        "verify_mixed": verify_mixed,
         "fused_epilogues": fused_out,
         "decode_stream": stream_out,
         "event_span_ms_per_step": round(span / args.steps * 1e3, 5),
