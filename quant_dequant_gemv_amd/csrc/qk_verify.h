@@ -68,7 +68,13 @@ template <int T, int NCB, int RL, bool PAIR, bool EPI, bool WIDE>
 constexpr int v_bound() {
     return NCB == 2 && RL <= v_short_rl<T>() && !PAIR && !EPI && !WIDE ? 768 : v_max_threads<NCB>();
 }
-constexpr int V_RAW_BUDGET = 96 * 1024;  // LDS for the x planes of one segment
+// LDS for the x planes of one segment: 112 KB for launches of up to 8
+// columns, so that 5120 x 6144 takes one segment instead of two and
+// 5120 x 17408 three instead of four at 8 columns (Q5_K 17.0 -> 13.3 us,
+// Q6_K 44.5 -> 37.7 us); 96 KB for the column-group variant (9-32 columns),
+// where the larger budget picked segments of three waves instead of two:
+// 50.7 -> 67.7 us at 16 columns.
+constexpr int V_RAW_BUDGET = 112 * 1024, V_RAW_BUDGET_WIDE = 96 * 1024;
 constexpr int V_LDS_MAX = 160 * 1024;
 
 template <int T>
@@ -549,7 +555,7 @@ static bool vgeo(int64_t N, int64_t K, int nc, int ncb, int mult, int short_thre
     const int long_threads = ncb == 1 ? v_max_threads<1>() : v_max_threads<2>();
     short_threads = std::max(short_threads, long_threads);
     const int max_waves = long_threads / 64;
-    const int cap = (int)std::min<int64_t>(16 * max_waves, V_RAW_BUDGET / xs) / 16 * 16;
+    const int cap = (int)std::min<int64_t>(16 * max_waves, (nc > 8 ? V_RAW_BUDGET_WIDE : V_RAW_BUDGET) / xs) / 16 * 16;
     if (cap < 16) return false;
     const int64_t nseg = (U + cap - 1) / cap;
     g.useg = (int)(((U + nseg - 1) / nseg + 15) / 16 * 16);
