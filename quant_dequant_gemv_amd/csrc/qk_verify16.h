@@ -1,0 +1,244 @@
+// qk_verify16.h -- Q4_K at 9 to 16 columns in one pass on 16x16x16 matrix
+// tiles (the verify form of drafted tokens: B70 plan, "Phase 4: True Xe2
+// Batched Verification", and its checklist's verifier widths up to 17).
+//
+// v_mfma_f32_16x16x16_f16 (probed on the box: A[i][k] from lane i + 16(k/4),
+// element k % 4; B[k][j] from lane j + 16(k/4); D[i][j] to lane j + 16(i/4),
+// element i % 4).  Here A is x (i = column of x, up to 16) and B the weights
+// (j = row), so D[column][row]: lane l holds row l % 16 and columns
+// 4(l / 16) .. +3 -- its own row's outputs, so the per-row scales of the
+// shifted form apply in the lane that unpacked them.
+//
+// A workgroup owns whole tiles of 16 rows; a wave owns one tile and a share
+// of the superblocks of each K segment.  Per superblock lane l = r + 16g
+// loads the header of row r and, for each of the four units, bytes 8g ..
+// 8g+7 of the unit's 32 quant bytes (low nibbles: 8 weights of the low
+// sub-block, high nibbles: the same positions of the high one), forms the
+// exact fp16 patterns s(q - c)2^-24 of the one-column kernel and issues, per
+// unit, two matrix instructions per sub-block (16 of its 32 weights each) and
+// two more per sub-block on the same x operands against fp16 ones: the sums
+// of x per column that the min terms take (exact products, fp32 sums).  The
+// x operands come from LDS planes staged per segment in exactly that order
+// (2 KB per unit: 80 units, all of K = 5120, fit the 160 KB), so each lane
+// reads them as two 16-byte vectors.  Every (row, column) is accumulated by
+// one lane per share, in unit order; the shares of a tile are added in a
+// fixed order at the end.  Weights are read once; the first ring of each
+// segment is issued before its x is staged.
+#pragma once
+
+#include "qk_epilogue.h"
+#include "qk_format.h"
+#include "qk_launch.h"
+
+namespace qk {
+
+constexpr int V16_UB = 2048;        // LDS bytes per unit: the x operands of 16 columns
+constexpr int V16_SEG_MAX = 80;      // units per segment (160 KB of planes)
+constexpr int V16_D = 2;             // superblocks in flight per lane
+
+typedef _Float16 v16_half4 __attribute__((ext_vector_type(4)));
+typedef float v16_f4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t V16_ONES = 0x3c003c00u;  // the fp16 pair (1, 1)
+
+__device__ __forceinline__ v16_f4 mfma16(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, v16_f4 c) {
+    const uint2 a = make_uint2(a0, a1), b = make_uint2(b0, b1);
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v16_half4, a), __builtin_bit_cast(v16_half4, b),
+                                                  c, 0, 0, 0);
+}
+
+// A lane's share of one superblock of its row: the header and, for each of
+// the four units, its 8 quant bytes.
+struct V16Sb {
+    uint4 h;
+    uint2 q[4];
+};
+
+// Stage the x of units [s0, s0 + ns) (all nc columns; columns nc..15 zero)
+// into the planes.  Unit ul at ul * V16_UB: [sb * 1024 + l * 16, +16) holds
+// the x operands of lane l = c + 16g for sub-block sb -- halves 0..3 of the
+// first instruction (weights 8g + 0, 2, 1, 3 of the sub-block), halves 4..7
+// of the second (8g + 4, 6, 5, 7).
+template <int NCV>
+__device__ __forceinline__ void v16_copy(const uint16_t *__restrict__ x, int s0, int ns, uint8_t *planes, int tid,
+                                         int nthr) {
+    // task: (unit, sub-block, group): its 8 rows of x, contiguous (NCV
+    // 16-byte loads), transposed in registers into one 16-byte vector per
+    // column
+    const int ntask = ns * 8;
+    for (int t = tid; t < ntask; t += nthr) {
+        const int g = t & 3, sb = (t >> 2) & 1, ul = t >> 3;
+        const uint8_t *src = reinterpret_cast<const uint8_t *>(x) +
+                             (size_t)(64 * (s0 + ul) + 32 * sb + 8 * g) * NCV * 2;
+        uint32_t h[4 * NCV];
+#pragma unroll
+        for (int i = 0; i < NCV; ++i) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(src + 16 * i);
+            h[4 * i] = v.x; h[4 * i + 1] = v.y; h[4 * i + 2] = v.z; h[4 * i + 3] = v.w;
+        }
+        // half e of the task is x[8 rows][NCV]: row e / NCV, column e % NCV
+        auto half = [&](int e) -> uint32_t { return (h[e >> 1] >> (16 * (e & 1))) & 0xffffu; };
+        uint8_t *dst = planes + (size_t)ul * V16_UB + sb * 1024 + 16 * g * 16;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            uint4 o = make_uint4(0u, 0u, 0u, 0u);
+            if (c < NCV) {  // pattern order within each four: rows 0, 2, 1, 3
+                o.x = half(0 * NCV + c) | (half(2 * NCV + c) << 16);
+                o.y = half(1 * NCV + c) | (half(3 * NCV + c) << 16);
+                o.z = half(4 * NCV + c) | (half(6 * NCV + c) << 16);
+                o.w = half(5 * NCV + c) | (half(7 * NCV + c) << 16);
+            }
+            *reinterpret_cast<uint4 *>(dst + c * 16) = o;
+        }
+    }
+}
+
+__device__ __forceinline__ void v16_stage(const uint16_t *__restrict__ x, int nc, int s0, int ns, uint8_t *planes,
+                                          int tid, int nthr) {
+    switch (nc) {
+    case 9: v16_copy<9>(x, s0, ns, planes, tid, nthr); break;
+    case 10: v16_copy<10>(x, s0, ns, planes, tid, nthr); break;
+    case 11: v16_copy<11>(x, s0, ns, planes, tid, nthr); break;
+    case 12: v16_copy<12>(x, s0, ns, planes, tid, nthr); break;
+    case 13: v16_copy<13>(x, s0, ns, planes, tid, nthr); break;
+    case 14: v16_copy<14>(x, s0, ns, planes, tid, nthr); break;
+    case 15: v16_copy<15>(x, s0, ns, planes, tid, nthr); break;
+    default: v16_copy<16>(x, s0, ns, planes, tid, nthr); break;
+    }
+}
+
+// Launch: G workgroups of T * UG waves; workgroup b owns rows [r0, r1)
+// (RowSplit, at most 16 * T), wave w the tile w % T (16 rows) and unit share
+// w / T of every segment.  LDS: the planes of useg units, then one float4 per
+// lane for the final sum of the shares.
+template <int T_>
+__global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ x,
+                                                   float *__restrict__ y, int N, int K, int nc, int useg, int T,
+                                                   int UG) {
+    static_assert(T_ == Q4_K, "Q4_K only");
+    extern __shared__ __attribute__((aligned(16))) uint8_t v16sm[];
+    const int tid = (int)threadIdx.x, nthr = (int)blockDim.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int tile = wave % T, ug = wave / T;
+    const int r = lane & 15, g = lane >> 4;
+    // whole 16-row tiles per workgroup (the last tile of the tensor may be
+    // short): ceil(N / 16) tiles split as evenly as possible
+    const RowSplit split((N + 15) >> 4, (int)blockIdx.x, (int)gridDim.x);
+    const int r0 = 16 * split.r0, r1 = min(16 * split.r1, N);
+    const int row = r0 + 16 * tile + r;
+    const bool tile_ok = r0 + 16 * tile < r1;  // (wave-uniform)
+    const uint8_t *wrow = W + (size_t)min(row, r1 - 1) * (size_t)((K >> 8) * 144);
+    const int U = K >> 6;
+    uint8_t *planes = v16sm;
+    v16_f4 acc = {0.f, 0.f, 0.f, 0.f};
+
+    for (int s0 = 0; s0 < U; s0 += useg) {
+        const int ns = min(useg, U - s0);
+        // this wave's share of the segment's superblocks (segments start at
+        // superblock boundaries); its first ring is issued before the x of
+        // the segment is staged (the weights do not depend on it)
+        const int nsb = ns >> 2;
+        const int b0 = ug * nsb / UG, b1 = (ug + 1) * nsb / UG;
+        const bool busy = tile_ok && b0 < b1;  // (wave-uniform)
+        const uint8_t *wseg = wrow + 144 * (s0 >> 2);
+        auto load = [&](V16Sb &d, int sbl) {
+            const uint8_t *p = wseg + 144 * min(sbl, b1 - 1);
+            d.h = *reinterpret_cast<const uint4 *>(p);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) d.q[k] = *reinterpret_cast<const uint2 *>(p + 16 + 32 * k + 8 * g);
+        };
+        V16Sb buf[V16_D];
+        if (busy)
+#pragma unroll
+            for (int k = 0; k < V16_D; ++k) load(buf[k], b0 + k);
+        if (s0 > 0) __syncthreads();  // every wave is done with the previous segment's planes
+        v16_stage(x, nc, s0, ns, planes, tid, nthr);
+        __syncthreads();
+        if (!busy) continue;
+        for (int i0 = b0; i0 < b1; i0 += V16_D) {
+#pragma unroll
+            for (int kk = 0; kk < V16_D; ++kk) {
+                const int sbl = i0 + kk;
+                const V16Sb sb = buf[kk];
+                load(buf[kk], sbl + V16_D);
+                if (sbl < b1) {  // (wave-uniform)
+                    const float d = f16_lo(sb.h.x), dmin = f16_hi(sb.h.x);
+                    auto pat = [](uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)v); };
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint8_t *blk = planes + (size_t)(4 * sbl + k) * V16_UB;
+                        const uint4 xl = *reinterpret_cast<const uint4 *>(blk + lane * 16);
+                        const uint4 xh = *reinterpret_cast<const uint4 *>(blk + 1024 + lane * 16);
+                        // the shifted form of each sub-block (KShift), units of 2^-48
+                        const KScales sk = k_scales(sb.h, KScaleSel(k));
+                        const KShift kL = k_shift<15, 1>(d, dmin, pat(sk.sc_lo), pat(sk.m_lo));
+                        const KShift kH = k_shift<15, 16>(d, dmin, pat(sk.sc_hi), pat(sk.m_hi));
+                        const uint32_t w0 = sb.q[k].x, w1 = sb.q[k].y, t0 = w0 >> 8, t1 = w1 >> 8;
+                        // low sub-block: weights (8g, 8g+2), (8g+1, 8g+3) of w0, then of w1
+                        v16_f4 DL = {0.f, 0.f, 0.f, 0.f}, DH = {0.f, 0.f, 0.f, 0.f};
+                        DL = mfma16(xl.x, xl.y, padd(w0 & 0x000f000fu, kL.neg), padd(t0 & 0x000f000fu, kL.neg), DL);
+                        DH = mfma16(xh.x, xh.y, padd(w0 & 0x00f000f0u, kH.neg), padd(t0 & 0x00f000f0u, kH.neg), DH);
+                        DL = mfma16(xl.z, xl.w, padd(w1 & 0x000f000fu, kL.neg), padd(t1 & 0x000f000fu, kL.neg), DL);
+                        DH = mfma16(xh.z, xh.w, padd(w1 & 0x00f000f0u, kH.neg), padd(t1 & 0x00f000f0u, kH.neg), DH);
+                        // the sums of x per sub-block and column, for the min terms:
+                        // the same operands against fp16 ones (exact products)
+                        v16_f4 SL = {0.f, 0.f, 0.f, 0.f}, SH = {0.f, 0.f, 0.f, 0.f};
+                        SL = mfma16(xl.x, xl.y, V16_ONES, V16_ONES, SL);
+                        SH = mfma16(xh.x, xh.y, V16_ONES, V16_ONES, SH);
+                        SL = mfma16(xl.z, xl.w, V16_ONES, V16_ONES, SL);
+                        SH = mfma16(xh.z, xh.w, V16_ONES, V16_ONES, SH);
+                        const float fh = kH.a * 0x1p-4f, eL = kL.e * 0x1p-24f, eH = kH.e * 0x1p-24f;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float E = __builtin_fmaf(eL, SL[e], eH * SH[e]);
+                            acc[e] += __builtin_fmaf(kL.a, DL[e], __builtin_fmaf(fh, DH[e], E));
+                        }
+                    }
+                }
+            }
+        }
+    }
+    // the shares of each tile, added in share order
+    __syncthreads();
+    float4 *part = reinterpret_cast<float4 *>(v16sm);
+    part[tid] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    __syncthreads();
+    if (ug == 0 && tile_ok && row < r1) {
+        float o[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < UG; ++s) {
+            const float4 v = part[(s * T + tile) * 64 + lane];
+            o[0] += v.x;
+            o[1] += v.y;
+            o[2] += v.z;
+            o[3] += v.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (4 * g + e < nc) y[(size_t)row * nc + 4 * g + e] = o[e] * 0x1p48f;
+    }
+}
+
+// Whole 16-row tiles per workgroup, at most 8; one workgroup per CU unless
+// N has fewer tiles (or more than 8 per CU); 1, 2 or 4 shares per tile (at
+// most 12 waves: 168 registers); segments of at most V16_SEG_MAX units, as
+// even as possible, in whole superblocks.
+template <int T_>
+static hipError_t launch_v16(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, hipStream_t st) {
+    const int cus = device_cus();
+    const int64_t tiles = (N + 15) / 16;
+    const int64_t G = std::max<int64_t>(std::min<int64_t>(cus, tiles), (tiles + 7) / 8);
+    const int T = (int)((tiles + G - 1) / G);  // tiles of the largest workgroup
+    const int UG = T <= 3 ? 4 : T <= 6 ? 2 : 1;  // at most 12 waves (168 registers)
+    const int threads = 64 * T * UG;
+    const int64_t U = K / 64;
+    const int64_t nseg = (U + V16_SEG_MAX - 1) / V16_SEG_MAX;
+    const int useg = (int)(((U + nseg - 1) / nseg + 3) / 4 * 4);  // whole superblocks
+    const size_t lds = std::max<size_t>((size_t)useg * V16_UB, (size_t)threads * 16);  // (planes, then the shares)
+    if (T < 1 || T > 8 || threads > 768 || lds > 160 * 1024) return hipErrorInvalidValue;
+    const hipError_t e = lds_opt_in<v16_kernel<T_>>(160 * 1024);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(v16_kernel<T_>, dim3((unsigned)G), dim3(threads), lds, st, (const uint8_t *)W,
+                       (const uint16_t *)x, (float *)y, (int)N, (int)K, nc, useg, T, UG);
+    return hipGetLastError();
+}
+
+}  // namespace qk
