@@ -694,9 +694,9 @@ static hipError_t verify_dispatch(const void *W, const void *x, void *y, int64_t
 template <int T>
 static hipError_t verify_type(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
                               const Epilogue &ep, hipStream_t st) {
-    // Q4_K at 9-16 columns without an epilogue: one pass on 16x16x16 tiles
+    // Q4_K at 9-32 columns without an epilogue: one pass on 16x16x16 tiles
     if constexpr (T == Q4_K)
-        if (nc > 8 && nc <= 16 && !ep.W2 && !ep.res && !ep.f16) return launch_v16<T>(W, x, y, N, K, nc, st);
+        if (nc > 8 && nc <= 32 && !ep.W2 && !ep.res && !ep.f16) return launch_v16<T>(W, x, y, N, K, nc, st);
     const VPlan pl = vplan(nc);
     if (ep.W2) {
         switch (pl.ncb) {

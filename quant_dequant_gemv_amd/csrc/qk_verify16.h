@@ -32,8 +32,8 @@
 
 namespace qk {
 
-constexpr int V16_UB = 2048;        // LDS bytes per unit: the x operands of 16 columns
-constexpr int V16_SEG_MAX = 80;      // units per segment (160 KB of planes)
+constexpr int V16_UB = 2048;        // LDS bytes per unit and group of 16 columns: their x operands
+constexpr int V16_PLANES = 160 * 1024;  // LDS for the planes of a segment
 constexpr int V16_D = 2;             // superblocks in flight per lane
 
 typedef _Float16 v16_half4 __attribute__((ext_vector_type(4)));
@@ -61,56 +61,77 @@ struct V16Sb {
 template <int NCV>
 __device__ __forceinline__ void v16_copy(const uint16_t *__restrict__ x, int s0, int ns, uint8_t *planes, int tid,
                                          int nthr) {
-    // task: (unit, sub-block, group): its 8 rows of x, contiguous (NCV
-    // 16-byte loads), transposed in registers into one 16-byte vector per
-    // column
-    const int ntask = ns * 8;
+    constexpr int NG = NCV > 16 ? 2 : 1;  // groups of 16 columns
+    // task: (unit, sub-block, group[, half]): RPT consecutive rows of x,
+    // contiguous (NCV loads of 2 * RPT bytes), transposed in registers into
+    // RPT halves of each column's operand vector (rows 0, 2, 1, 3 within each
+    // four: the pattern order).  Eight rows (whole 16-byte vectors) up to 16
+    // columns; four (half vectors) beyond, for the registers.
+    constexpr int RPT = NG == 1 ? 8 : 4;
+    const int ntask = ns * 8 * (8 / RPT);
     for (int t = tid; t < ntask; t += nthr) {
-        const int g = t & 3, sb = (t >> 2) & 1, ul = t >> 3;
+        const int hf = RPT == 8 ? 0 : t & 1, tt = RPT == 8 ? t : t >> 1;
+        const int g = tt & 3, sb = (tt >> 2) & 1, ul = tt >> 3;
         const uint8_t *src = reinterpret_cast<const uint8_t *>(x) +
-                             (size_t)(64 * (s0 + ul) + 32 * sb + 8 * g) * NCV * 2;
-        uint32_t h[4 * NCV];
+                             (size_t)(64 * (s0 + ul) + 32 * sb + 8 * g + 4 * hf) * NCV * 2;
+        uint32_t h[RPT / 2 * NCV];
 #pragma unroll
         for (int i = 0; i < NCV; ++i) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(src + 16 * i);
-            h[4 * i] = v.x; h[4 * i + 1] = v.y; h[4 * i + 2] = v.z; h[4 * i + 3] = v.w;
-        }
-        // half e of the task is x[8 rows][NCV]: row e / NCV, column e % NCV
-        auto half = [&](int e) -> uint32_t { return (h[e >> 1] >> (16 * (e & 1))) & 0xffffu; };
-        uint8_t *dst = planes + (size_t)ul * V16_UB + sb * 1024 + 16 * g * 16;
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            uint4 o = make_uint4(0u, 0u, 0u, 0u);
-            if (c < NCV) {  // pattern order within each four: rows 0, 2, 1, 3
-                o.x = half(0 * NCV + c) | (half(2 * NCV + c) << 16);
-                o.y = half(1 * NCV + c) | (half(3 * NCV + c) << 16);
-                o.z = half(4 * NCV + c) | (half(6 * NCV + c) << 16);
-                o.w = half(5 * NCV + c) | (half(7 * NCV + c) << 16);
+            if constexpr (RPT == 8) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(src + 16 * i);
+                h[4 * i] = v.x; h[4 * i + 1] = v.y; h[4 * i + 2] = v.z; h[4 * i + 3] = v.w;
+            } else {
+                const uint2 v = *reinterpret_cast<const uint2 *>(src + 8 * i);
+                h[2 * i] = v.x; h[2 * i + 1] = v.y;
             }
-            *reinterpret_cast<uint4 *>(dst + c * 16) = o;
+        }
+        // half e of the task is x[RPT rows][NCV]: row e / NCV, column e % NCV
+        auto half = [&](int e) -> uint32_t { return (h[e >> 1] >> (16 * (e & 1))) & 0xffffu; };
+        uint8_t *dst = planes + (size_t)ul * NG * V16_UB + sb * 1024 + 16 * g * 16 + 8 * hf;
+#pragma unroll
+        for (int c = 0; c < 16 * NG; ++c) {
+            uint8_t *o = dst + (c >> 4) * V16_UB + (c & 15) * 16;
+            if constexpr (RPT == 8) {
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                if (c < NCV) {
+                    v.x = half(0 * NCV + c) | (half(2 * NCV + c) << 16);
+                    v.y = half(1 * NCV + c) | (half(3 * NCV + c) << 16);
+                    v.z = half(4 * NCV + c) | (half(6 * NCV + c) << 16);
+                    v.w = half(5 * NCV + c) | (half(7 * NCV + c) << 16);
+                }
+                *reinterpret_cast<uint4 *>(o) = v;
+            } else {
+                uint2 v = make_uint2(0u, 0u);
+                if (c < NCV) {
+                    v.x = half(0 * NCV + c) | (half(2 * NCV + c) << 16);
+                    v.y = half(1 * NCV + c) | (half(3 * NCV + c) << 16);
+                }
+                *reinterpret_cast<uint2 *>(o) = v;
+            }
         }
     }
 }
 
+template <int NG>
 __device__ __forceinline__ void v16_stage(const uint16_t *__restrict__ x, int nc, int s0, int ns, uint8_t *planes,
                                           int tid, int nthr) {
-    switch (nc) {
-    case 9: v16_copy<9>(x, s0, ns, planes, tid, nthr); break;
-    case 10: v16_copy<10>(x, s0, ns, planes, tid, nthr); break;
-    case 11: v16_copy<11>(x, s0, ns, planes, tid, nthr); break;
-    case 12: v16_copy<12>(x, s0, ns, planes, tid, nthr); break;
-    case 13: v16_copy<13>(x, s0, ns, planes, tid, nthr); break;
-    case 14: v16_copy<14>(x, s0, ns, planes, tid, nthr); break;
-    case 15: v16_copy<15>(x, s0, ns, planes, tid, nthr); break;
-    default: v16_copy<16>(x, s0, ns, planes, tid, nthr); break;
+#define V16_CASE(n) case n: v16_copy<n>(x, s0, ns, planes, tid, nthr); break;
+    if constexpr (NG == 1) {
+        switch (nc) {
+        V16_CASE(9) V16_CASE(10) V16_CASE(11) V16_CASE(12) V16_CASE(13) V16_CASE(14) V16_CASE(15)
+        default: v16_copy<16>(x, s0, ns, planes, tid, nthr); break;
+        }
+    } else {
+        switch (nc) {
+        V16_CASE(17) V16_CASE(18) V16_CASE(19) V16_CASE(20) V16_CASE(21) V16_CASE(22) V16_CASE(23) V16_CASE(24)
+        V16_CASE(25) V16_CASE(26) V16_CASE(27) V16_CASE(28) V16_CASE(29) V16_CASE(30) V16_CASE(31)
+        default: v16_copy<32>(x, s0, ns, planes, tid, nthr); break;
+        }
     }
+#undef V16_CASE
 }
 
-// Launch: G workgroups of T * UG waves; workgroup b owns rows [r0, r1)
-// (RowSplit, at most 16 * T), wave w the tile w % T (16 rows) and unit share
-// w / T of every segment.  LDS: the planes of useg units, then one float4 per
-// lane for the final sum of the shares.
-template <int T_>
+template <int T_, int NG>
 __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ x,
                                                    float *__restrict__ y, int N, int K, int nc, int useg, int T,
                                                    int UG) {
@@ -129,7 +150,9 @@ __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W,
     const uint8_t *wrow = W + (size_t)min(row, r1 - 1) * (size_t)((K >> 8) * 144);
     const int U = K >> 6;
     uint8_t *planes = v16sm;
-    v16_f4 acc = {0.f, 0.f, 0.f, 0.f};
+    v16_f4 acc[NG];
+#pragma unroll
+    for (int cg = 0; cg < NG; ++cg) acc[cg] = v16_f4{0.f, 0.f, 0.f, 0.f};
 
     for (int s0 = 0; s0 < U; s0 += useg) {
         const int ns = min(useg, U - s0);
@@ -151,7 +174,7 @@ __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W,
 #pragma unroll
             for (int k = 0; k < V16_D; ++k) load(buf[k], b0 + k);
         if (s0 > 0) __syncthreads();  // every wave is done with the previous segment's planes
-        v16_stage(x, nc, s0, ns, planes, tid, nthr);
+        v16_stage<NG>(x, nc, s0, ns, planes, tid, nthr);
         __syncthreads();
         if (!busy) continue;
         for (int i0 = b0; i0 < b1; i0 += V16_D) {
@@ -165,32 +188,38 @@ __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W,
                     auto pat = [](uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)v); };
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
-                        const uint8_t *blk = planes + (size_t)(4 * sbl + k) * V16_UB;
-                        const uint4 xl = *reinterpret_cast<const uint4 *>(blk + lane * 16);
-                        const uint4 xh = *reinterpret_cast<const uint4 *>(blk + 1024 + lane * 16);
                         // the shifted form of each sub-block (KShift), units of 2^-48
                         const KScales sk = k_scales(sb.h, KScaleSel(k));
                         const KShift kL = k_shift<15, 1>(d, dmin, pat(sk.sc_lo), pat(sk.m_lo));
                         const KShift kH = k_shift<15, 16>(d, dmin, pat(sk.sc_hi), pat(sk.m_hi));
                         const uint32_t w0 = sb.q[k].x, w1 = sb.q[k].y, t0 = w0 >> 8, t1 = w1 >> 8;
-                        // low sub-block: weights (8g, 8g+2), (8g+1, 8g+3) of w0, then of w1
-                        v16_f4 DL = {0.f, 0.f, 0.f, 0.f}, DH = {0.f, 0.f, 0.f, 0.f};
-                        DL = mfma16(xl.x, xl.y, padd(w0 & 0x000f000fu, kL.neg), padd(t0 & 0x000f000fu, kL.neg), DL);
-                        DH = mfma16(xh.x, xh.y, padd(w0 & 0x00f000f0u, kH.neg), padd(t0 & 0x00f000f0u, kH.neg), DH);
-                        DL = mfma16(xl.z, xl.w, padd(w1 & 0x000f000fu, kL.neg), padd(t1 & 0x000f000fu, kL.neg), DL);
-                        DH = mfma16(xh.z, xh.w, padd(w1 & 0x00f000f0u, kH.neg), padd(t1 & 0x00f000f0u, kH.neg), DH);
-                        // the sums of x per sub-block and column, for the min terms:
-                        // the same operands against fp16 ones (exact products)
-                        v16_f4 SL = {0.f, 0.f, 0.f, 0.f}, SH = {0.f, 0.f, 0.f, 0.f};
-                        SL = mfma16(xl.x, xl.y, V16_ONES, V16_ONES, SL);
-                        SH = mfma16(xh.x, xh.y, V16_ONES, V16_ONES, SH);
-                        SL = mfma16(xl.z, xl.w, V16_ONES, V16_ONES, SL);
-                        SH = mfma16(xh.z, xh.w, V16_ONES, V16_ONES, SH);
                         const float fh = kH.a * 0x1p-4f, eL = kL.e * 0x1p-24f, eH = kH.e * 0x1p-24f;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float E = __builtin_fmaf(eL, SL[e], eH * SH[e]);
-                            acc[e] += __builtin_fmaf(kL.a, DL[e], __builtin_fmaf(fh, DH[e], E));
+                        for (int cg = 0; cg < NG; ++cg) {  // each group of 16 columns
+                            const uint8_t *blk = planes + ((size_t)(4 * sbl + k) * NG + cg) * V16_UB;
+                            const uint4 xl = *reinterpret_cast<const uint4 *>(blk + lane * 16);
+                            const uint4 xh = *reinterpret_cast<const uint4 *>(blk + 1024 + lane * 16);
+                            // low sub-block: weights (8g, 8g+2), (8g+1, 8g+3) of w0, then
+                            // of w1 (the patterns formed again per group: fewer live
+                            // registers)
+                            v16_f4 DL = {0.f, 0.f, 0.f, 0.f}, DH = {0.f, 0.f, 0.f, 0.f};
+                            DL = mfma16(xl.x, xl.y, padd(w0 & 0x000f000fu, kL.neg), padd(t0 & 0x000f000fu, kL.neg), DL);
+                            DH = mfma16(xh.x, xh.y, padd(w0 & 0x00f000f0u, kH.neg), padd(t0 & 0x00f000f0u, kH.neg), DH);
+                            DL = mfma16(xl.z, xl.w, padd(w1 & 0x000f000fu, kL.neg), padd(t1 & 0x000f000fu, kL.neg), DL);
+                            DH = mfma16(xh.z, xh.w, padd(w1 & 0x00f000f0u, kH.neg), padd(t1 & 0x00f000f0u, kH.neg), DH);
+                            // the sums of x per sub-block and column, for the min
+                            // terms: the same operands against fp16 ones (exact
+                            // products)
+                            v16_f4 SL = {0.f, 0.f, 0.f, 0.f}, SH = {0.f, 0.f, 0.f, 0.f};
+                            SL = mfma16(xl.x, xl.y, V16_ONES, V16_ONES, SL);
+                            SH = mfma16(xh.x, xh.y, V16_ONES, V16_ONES, SH);
+                            SL = mfma16(xl.z, xl.w, V16_ONES, V16_ONES, SL);
+                            SH = mfma16(xh.z, xh.w, V16_ONES, V16_ONES, SH);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float E = __builtin_fmaf(eL, SL[e], eH * SH[e]);
+                                acc[cg][e] += __builtin_fmaf(kL.a, DL[e], __builtin_fmaf(fh, DH[e], E));
+                            }
                         }
                     }
                 }
@@ -200,29 +229,35 @@ __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W,
     // the shares of each tile, added in share order
     __syncthreads();
     float4 *part = reinterpret_cast<float4 *>(v16sm);
-    part[tid] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+    for (int cg = 0; cg < NG; ++cg) part[cg * nthr + tid] = make_float4(acc[cg][0], acc[cg][1], acc[cg][2], acc[cg][3]);
     __syncthreads();
     if (ug == 0 && tile_ok && row < r1) {
-        float o[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < UG; ++s) {
-            const float4 v = part[(s * T + tile) * 64 + lane];
-            o[0] += v.x;
-            o[1] += v.y;
-            o[2] += v.z;
-            o[3] += v.w;
-        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (4 * g + e < nc) y[(size_t)row * nc + 4 * g + e] = o[e] * 0x1p48f;
+        for (int cg = 0; cg < NG; ++cg) {
+            float o[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < UG; ++s) {
+                const float4 v = part[cg * nthr + (s * T + tile) * 64 + lane];
+                o[0] += v.x;
+                o[1] += v.y;
+                o[2] += v.z;
+                o[3] += v.w;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = 16 * cg + 4 * g + e;
+                if (c < nc) y[(size_t)row * nc + c] = o[e] * 0x1p48f;
+            }
+        }
     }
 }
 
 // Whole 16-row tiles per workgroup, at most 8; one workgroup per CU unless
 // N has fewer tiles (or more than 8 per CU); 1, 2 or 4 shares per tile (at
-// most 12 waves: 168 registers); segments of at most V16_SEG_MAX units, as
+// most 12 waves: 168 registers); segments of at most 160 KB of planes, as
 // even as possible, in whole superblocks.
-template <int T_>
-static hipError_t launch_v16(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, hipStream_t st) {
+template <int T_, int NG>
+static hipError_t launch_v16g(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, hipStream_t st) {
     const int cus = device_cus();
     const int64_t tiles = (N + 15) / 16;
     const int64_t G = std::max<int64_t>(std::min<int64_t>(cus, tiles), (tiles + 7) / 8);
@@ -230,15 +265,22 @@ static hipError_t launch_v16(const void *W, const void *x, void *y, int64_t N, i
     const int UG = T <= 3 ? 4 : T <= 6 ? 2 : 1;  // at most 12 waves (168 registers)
     const int threads = 64 * T * UG;
     const int64_t U = K / 64;
-    const int64_t nseg = (U + V16_SEG_MAX - 1) / V16_SEG_MAX;
+    const int64_t smax = V16_PLANES / (NG * V16_UB) / 4 * 4;  // units per segment at most
+    const int64_t nseg = (U + smax - 1) / smax;
     const int useg = (int)(((U + nseg - 1) / nseg + 3) / 4 * 4);  // whole superblocks
-    const size_t lds = std::max<size_t>((size_t)useg * V16_UB, (size_t)threads * 16);  // (planes, then the shares)
+    const size_t lds = std::max<size_t>((size_t)useg * NG * V16_UB, (size_t)threads * 16 * NG);  // (planes, then the shares)
     if (T < 1 || T > 8 || threads > 768 || lds > 160 * 1024) return hipErrorInvalidValue;
-    const hipError_t e = lds_opt_in<v16_kernel<T_>>(160 * 1024);
+    const hipError_t e = lds_opt_in<v16_kernel<T_, NG>>(160 * 1024);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(v16_kernel<T_>, dim3((unsigned)G), dim3(threads), lds, st, (const uint8_t *)W,
+    hipLaunchKernelGGL((v16_kernel<T_, NG>), dim3((unsigned)G), dim3(threads), lds, st, (const uint8_t *)W,
                        (const uint16_t *)x, (float *)y, (int)N, (int)K, nc, useg, T, UG);
     return hipGetLastError();
+}
+
+// 9-16 columns: one group; 17-32: two groups sharing each unit's patterns
+template <int T_>
+static hipError_t launch_v16(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, hipStream_t st) {
+    return nc > 16 ? launch_v16g<T_, 2>(W, x, y, N, K, nc, st) : launch_v16g<T_, 1>(W, x, y, N, K, nc, st);
 }
 
 }  // namespace qk
