@@ -694,8 +694,8 @@ static hipError_t verify_dispatch(const void *W, const void *x, void *y, int64_t
 template <int T>
 static hipError_t verify_type(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
                               const Epilogue &ep, hipStream_t st) {
-    // Q4_K at 9-32 columns without an epilogue: one pass on 16x16x16 tiles
-    if constexpr (T == Q4_K)
+    // Q4_K and Q5_K at 9-32 columns without an epilogue: one pass on 16x16x16 tiles
+    if constexpr (T == Q4_K || T == Q5_K)
         if (nc > 8 && nc <= 32 && !ep.W2 && !ep.res && !ep.f16) return launch_v16<T>(W, x, y, N, K, nc, st);
     const VPlan pl = vplan(nc);
     if (ep.W2) {

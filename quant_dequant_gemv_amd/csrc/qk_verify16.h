@@ -1,4 +1,4 @@
-// qk_verify16.h -- Q4_K at 9 to 16 columns in one pass on 16x16x16 matrix
+// qk_verify16.h -- Q4_K and Q5_K at 9 to 32 columns in one pass on 16x16x16 matrix
 // tiles (the verify form of drafted tokens: B70 plan, "Phase 4: True Xe2
 // Batched Verification", and its checklist's verifier widths up to 17).
 //
@@ -51,7 +51,13 @@ __device__ __forceinline__ v16_f4 mfma16(uint32_t a0, uint32_t a1, uint32_t b0, 
 struct V16Sb {
     uint4 h;
     uint2 q[4];
+    uint2 qh;  // Q5_K: bytes 8g .. 8g+7 of qh (bit 2u / 2u + 1: the fifth bit of unit u's sub-blocks)
 };
+
+// Superblock geometry of the k-quants with 32-weight sub-blocks and a min
+template <int T> struct V16Fmt;
+template <> struct V16Fmt<Q4_K> { static constexpr int bytes = 144, qs = 16, qmax = 15; };
+template <> struct V16Fmt<Q5_K> { static constexpr int bytes = 176, qs = 48, qmax = 31; };
 
 // Stage the x of units [s0, s0 + ns) (all nc columns; columns nc..15 zero)
 // into the planes.  Unit ul at ul * V16_UB: [sb * 1024 + l * 16, +16) holds
@@ -135,7 +141,9 @@ template <int T_, int NG>
 __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ x,
                                                    float *__restrict__ y, int N, int K, int nc, int useg, int T,
                                                    int UG) {
-    static_assert(T_ == Q4_K, "Q4_K only");
+    static_assert(T_ == Q4_K || T_ == Q5_K, "Q4_K and Q5_K");
+    constexpr int SBB = V16Fmt<T_>::bytes, QSO = V16Fmt<T_>::qs, QMAX = V16Fmt<T_>::qmax;
+    constexpr int DD = T_ == Q5_K ? 1 : V16_D;  // superblocks in flight (Q5_K: its qh bits take the registers)
     extern __shared__ __attribute__((aligned(16))) uint8_t v16sm[];
     const int tid = (int)threadIdx.x, nthr = (int)blockDim.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -147,7 +155,7 @@ __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W,
     const int r0 = 16 * split.r0, r1 = min(16 * split.r1, N);
     const int row = r0 + 16 * tile + r;
     const bool tile_ok = r0 + 16 * tile < r1;  // (wave-uniform)
-    const uint8_t *wrow = W + (size_t)min(row, r1 - 1) * (size_t)((K >> 8) * 144);
+    const uint8_t *wrow = W + (size_t)min(row, r1 - 1) * (size_t)((K >> 8) * SBB);
     const int U = K >> 6;
     uint8_t *planes = v16sm;
     v16_f4 acc[NG];
@@ -162,27 +170,28 @@ __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W,
         const int nsb = ns >> 2;
         const int b0 = ug * nsb / UG, b1 = (ug + 1) * nsb / UG;
         const bool busy = tile_ok && b0 < b1;  // (wave-uniform)
-        const uint8_t *wseg = wrow + 144 * (s0 >> 2);
+        const uint8_t *wseg = wrow + SBB * (s0 >> 2);
         auto load = [&](V16Sb &d, int sbl) {
-            const uint8_t *p = wseg + 144 * min(sbl, b1 - 1);
+            const uint8_t *p = wseg + SBB * min(sbl, b1 - 1);
             d.h = *reinterpret_cast<const uint4 *>(p);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) d.q[k] = *reinterpret_cast<const uint2 *>(p + 16 + 32 * k + 8 * g);
+            for (int k = 0; k < 4; ++k) d.q[k] = *reinterpret_cast<const uint2 *>(p + QSO + 32 * k + 8 * g);
+            if constexpr (T_ == Q5_K) d.qh = *reinterpret_cast<const uint2 *>(p + 16 + 8 * g);
         };
-        V16Sb buf[V16_D];
+        V16Sb buf[DD];
         if (busy)
 #pragma unroll
-            for (int k = 0; k < V16_D; ++k) load(buf[k], b0 + k);
+            for (int k = 0; k < DD; ++k) load(buf[k], b0 + k);
         if (s0 > 0) __syncthreads();  // every wave is done with the previous segment's planes
         v16_stage<NG>(x, nc, s0, ns, planes, tid, nthr);
         __syncthreads();
         if (!busy) continue;
-        for (int i0 = b0; i0 < b1; i0 += V16_D) {
+        for (int i0 = b0; i0 < b1; i0 += DD) {
 #pragma unroll
-            for (int kk = 0; kk < V16_D; ++kk) {
+            for (int kk = 0; kk < DD; ++kk) {
                 const int sbl = i0 + kk;
                 const V16Sb sb = buf[kk];
-                load(buf[kk], sbl + V16_D);
+                load(buf[kk], sbl + DD);
                 if (sbl < b1) {  // (wave-uniform)
                     const float d = f16_lo(sb.h.x), dmin = f16_hi(sb.h.x);
                     auto pat = [](uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)v); };
@@ -190,9 +199,12 @@ __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W,
                     for (int k = 0; k < 4; ++k) {
                         // the shifted form of each sub-block (KShift), units of 2^-48
                         const KScales sk = k_scales(sb.h, KScaleSel(k));
-                        const KShift kL = k_shift<15, 1>(d, dmin, pat(sk.sc_lo), pat(sk.m_lo));
-                        const KShift kH = k_shift<15, 16>(d, dmin, pat(sk.sc_hi), pat(sk.m_hi));
+                        const KShift kL = k_shift<QMAX, 1>(d, dmin, pat(sk.sc_lo), pat(sk.m_lo));
+                        const KShift kH = k_shift<QMAX, 16>(d, dmin, pat(sk.sc_hi), pat(sk.m_hi));
                         const uint32_t w0 = sb.q[k].x, w1 = sb.q[k].y, t0 = w0 >> 8, t1 = w1 >> 8;
+                        // Q5_K: the fifth bits (bit 0 / 1 of each qh byte after the
+                        // shift: low / high sub-block), as the one-column kernel sets them
+                        const uint32_t H0 = T_ == Q5_K ? sb.qh.x >> (2 * k) : 0u, H1 = T_ == Q5_K ? sb.qh.y >> (2 * k) : 0u;
                         const float fh = kH.a * 0x1p-4f, eL = kL.e * 0x1p-24f, eH = kH.e * 0x1p-24f;
 #pragma unroll
                         for (int cg = 0; cg < NG; ++cg) {  // each group of 16 columns
@@ -203,10 +215,14 @@ __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W,
                             // of w1 (the patterns formed again per group: fewer live
                             // registers)
                             v16_f4 DL = {0.f, 0.f, 0.f, 0.f}, DH = {0.f, 0.f, 0.f, 0.f};
-                            DL = mfma16(xl.x, xl.y, padd(w0 & 0x000f000fu, kL.neg), padd(t0 & 0x000f000fu, kL.neg), DL);
-                            DH = mfma16(xh.x, xh.y, padd(w0 & 0x00f000f0u, kH.neg), padd(t0 & 0x00f000f0u, kH.neg), DH);
-                            DL = mfma16(xl.z, xl.w, padd(w1 & 0x000f000fu, kL.neg), padd(t1 & 0x000f000fu, kL.neg), DL);
-                            DH = mfma16(xh.z, xh.w, padd(w1 & 0x00f000f0u, kH.neg), padd(t1 & 0x00f000f0u, kH.neg), DH);
+                            DL = mfma16(xl.x, xl.y, padd((w0 & 0x000f000fu) | ((H0 << 4) & 0x00100010u), kL.neg),
+                                        padd((t0 & 0x000f000fu) | ((H0 >> 4) & 0x00100010u), kL.neg), DL);
+                            DH = mfma16(xh.x, xh.y, padd((w0 & 0x00f000f0u) | ((H0 << 7) & 0x01000100u), kH.neg),
+                                        padd((t0 & 0x00f000f0u) | ((H0 >> 1) & 0x01000100u), kH.neg), DH);
+                            DL = mfma16(xl.z, xl.w, padd((w1 & 0x000f000fu) | ((H1 << 4) & 0x00100010u), kL.neg),
+                                        padd((t1 & 0x000f000fu) | ((H1 >> 4) & 0x00100010u), kL.neg), DL);
+                            DH = mfma16(xh.z, xh.w, padd((w1 & 0x00f000f0u) | ((H1 << 7) & 0x01000100u), kH.neg),
+                                        padd((t1 & 0x00f000f0u) | ((H1 >> 1) & 0x01000100u), kH.neg), DH);
                             // the sums of x per sub-block and column, for the min
                             // terms: the same operands against fp16 ones (exact
                             // products)
