@@ -773,7 +773,7 @@ def main():
     shard_out = per_shape(torch, launcher, shards)
     del shards
     iq4_out = []
-    for nc in (1, 8):
+    for nc in (1, 2, 4, 8, 16, 17):
         t = make_tensors(torch, [dict(name=f"iq4xs_ffn_up_ncols{nc}", qtype=synth.IQ4_XS, N=17408, K=5120, seed=1003,
                                       ncols=nc)])
         r = per_shape(torch, launcher, t)[0]
@@ -822,10 +822,10 @@ def main():
         torch.cuda.empty_cache()
 
     # the verify form on the mixed-type shapes (Q6_K FFN down, Q5_K output
-    # projection) at 2, 4 and 8 columns
+    # projection) at 2, 4, 8, 16 and 17 columns
     verify_mixed = []
     for e in synth.MIXED:
-        for nc in (2, 4, 8):
+        for nc in (2, 4, 8, 16, 17):
             vt = make_tensors(torch, [dict(e, name=f"{e['name']}_ncols{nc}", ncols=nc)])
             r = per_shape(torch, launcher, vt)[0]
             r["ncols"] = nc
