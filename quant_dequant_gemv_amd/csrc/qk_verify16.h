@@ -299,4 +299,246 @@ static hipError_t launch_v16(const void *W, const void *x, void *y, int64_t N, i
     return nc > 16 ? launch_v16g<T_, 2>(W, x, y, N, K, nc, st) : launch_v16g<T_, 1>(W, x, y, N, K, nc, st);
 }
 
+// ---------------------------------------------------------------------------
+// Q6_K on the same tiles.  w = d * sc * (q - 32) with an int8 scale per 16
+// weights, so each matrix instruction covers one scale group: group (n, t, h)
+// of a superblock is its weights 128n + 32t + 16h + 0..15 (half n, quarter t,
+// half-quarter h); they sit in the 16 ql bytes 64n + 32(t % 2) + 16h + 0..15
+// (nibble t / 2) and the 16 qh bytes 32n + 16h + 0..15 (bits 2t, 2t + 1).
+// Lane l = r + 16g of a tile supplies weights 4g..4g+3 of a group: dword g of
+// its ql and qh chunks.  The four lanes of a row (g = 0..3) each read whole
+// 16-byte chunks (ql chunks g and 4 + g, qh chunk g) and a 4 x 4 transpose
+// across them (two rounds of lane-row swaps) hands every lane dword g of
+// every chunk.  The patterns hold s(q - 32)2^-24 (s = 1 for the low nibbles,
+// 16 for the high ones, as in the one-column kernel); no min term.  x planes:
+// 8 KB per superblock and group of 16 columns, [n][t][lane][h][4 halves].
+// ---------------------------------------------------------------------------
+constexpr int V16Q6_SB = 8192;  // LDS bytes per superblock and group of 16 columns
+constexpr int V16Q6_MIN = 9;  // fewest columns a Q6_K call takes on the tiles (at 5-8 the 4x4x4 form is faster)
+
+struct V16Q6Sb {
+    uint4 ql0, ql1, qh;  // ql chunks g and 4 + g, qh chunk g (lane row g)
+    uint4 sc;            // the 16 int8 scales
+    uint32_t d;          // fp16 d in the low half
+};
+
+// Lane row g (lanes 16g..16g+15) holds dwords R0..R3 of a 16-byte chunk of
+// its own; afterwards dword m of lane row g is dword g of row m's chunk.
+// v_permlane32_swap exchanges rows 2-3 of its first operand with rows 0-1 of
+// its second, v_permlane16_swap rows 1, 3 of the first with rows 0, 2 of the
+// second.
+__device__ __forceinline__ uint4 v16_xpose(uint4 v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto e = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    return make_uint4(c[0], c[1], e[0], e[1]);
+}
+
+template <int NCV>
+__device__ __forceinline__ void v16q6_copy(const uint16_t *__restrict__ x, int sb0, int nsb, uint8_t *planes, int tid,
+                                           int nthr) {
+    constexpr int NG = NCV > 16 ? 2 : 1;
+    // task: (superblock, n, t, h, g): rows 128n + 32t + 16h + 4g + 0..3,
+    // contiguous (NCV loads of 8 bytes), into half a 16-byte vector per column
+    const int ntask = nsb * 64;
+    for (int t = tid; t < ntask; t += nthr) {
+        const int g = t & 3, h = (t >> 2) & 1, qt = (t >> 3) & 3, n = (t >> 5) & 1, sbl = t >> 6;
+        const uint8_t *src = reinterpret_cast<const uint8_t *>(x) +
+                             (size_t)(256 * (sb0 + sbl) + 128 * n + 32 * qt + 16 * h + 4 * g) * NCV * 2;
+        uint32_t hv[2 * NCV];
+#pragma unroll
+        for (int i = 0; i < NCV; ++i) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(src + 8 * i);
+            hv[2 * i] = v.x;
+            hv[2 * i + 1] = v.y;
+        }
+        auto half = [&](int e) -> uint32_t { return (hv[e >> 1] >> (16 * (e & 1))) & 0xffffu; };
+        uint8_t *dst = planes + (size_t)sbl * NG * V16Q6_SB + ((n * 4 + qt) * 64 + 16 * g) * 16 + 8 * h;
+#pragma unroll
+        for (int c = 0; c < 16 * NG; ++c) {
+            uint2 v = make_uint2(0u, 0u);
+            if (c < NCV) {  // rows 0, 2, 1, 3: the pattern order
+                v.x = half(0 * NCV + c) | (half(2 * NCV + c) << 16);
+                v.y = half(1 * NCV + c) | (half(3 * NCV + c) << 16);
+            }
+            *reinterpret_cast<uint2 *>(dst + (c >> 4) * V16Q6_SB + (c & 15) * 16) = v;
+        }
+    }
+}
+
+template <int NG>
+__device__ __forceinline__ void v16q6_stage(const uint16_t *__restrict__ x, int nc, int sb0, int nsb, uint8_t *planes,
+                                            int tid, int nthr) {
+#define V16_CASE(n) \
+    case n: v16q6_copy<n>(x, sb0, nsb, planes, tid, nthr); break;
+    if constexpr (NG == 1) {
+        switch (nc) {
+        V16_CASE(5) V16_CASE(6) V16_CASE(7) V16_CASE(8) V16_CASE(9) V16_CASE(10) V16_CASE(11) V16_CASE(12)
+        V16_CASE(13) V16_CASE(14) V16_CASE(15)
+        default: v16q6_copy<16>(x, sb0, nsb, planes, tid, nthr); break;
+        }
+    } else {
+        switch (nc) {
+        V16_CASE(17) V16_CASE(18) V16_CASE(19) V16_CASE(20) V16_CASE(21) V16_CASE(22) V16_CASE(23) V16_CASE(24)
+        V16_CASE(25) V16_CASE(26) V16_CASE(27) V16_CASE(28) V16_CASE(29) V16_CASE(30) V16_CASE(31)
+        default: v16q6_copy<32>(x, sb0, nsb, planes, tid, nthr); break;
+        }
+    }
+#undef V16_CASE
+}
+
+// Workgroups, tiles and shares as in v16_kernel; segments of whole
+// superblocks (segsb of them, at most 160 KB of planes).
+template <int NG>
+__global__ void __launch_bounds__(768) v16q6_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ x,
+                                                    float *__restrict__ y, int N, int K, int nc, int segsb, int T,
+                                                    int UG) {
+    constexpr int DD = NG == 2 ? 1 : V16_D;  // superblocks in flight (two groups: the accumulators take the registers)
+    extern __shared__ __attribute__((aligned(16))) uint8_t v16sm[];
+    const int tid = (int)threadIdx.x, nthr = (int)blockDim.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int tile = wave % T, ug = wave / T;
+    const int r = lane & 15, g = lane >> 4;
+    const RowSplit split((N + 15) >> 4, (int)blockIdx.x, (int)gridDim.x);
+    const int r0 = 16 * split.r0, r1 = min(16 * split.r1, N);
+    const int row = r0 + 16 * tile + r;
+    const bool tile_ok = r0 + 16 * tile < r1;  // (wave-uniform)
+    const int S = K >> 8;
+    const uint8_t *wrow = W + (size_t)min(row, r1 - 1) * (size_t)(S * 210);
+    uint8_t *planes = v16sm;
+    v16_f4 acc[NG];
+#pragma unroll
+    for (int cg = 0; cg < NG; ++cg) acc[cg] = v16_f4{0.f, 0.f, 0.f, 0.f};
+
+    for (int sb0 = 0; sb0 < S; sb0 += segsb) {
+        const int nsb = min(segsb, S - sb0);
+        const int b0 = ug * nsb / UG, b1 = (ug + 1) * nsb / UG;
+        const bool busy = tile_ok && b0 < b1;  // (wave-uniform)
+        const uint8_t *wseg = wrow + 210 * sb0;
+        // superblocks are 2-byte aligned: unaligned 16-byte loads
+        auto load = [&](V16Q6Sb &d, int sbl) {
+            const uint8_t *p = wseg + 210 * min(sbl, b1 - 1);
+            d.ql0 = *reinterpret_cast<const uint4 *>(p + 16 * g);
+            d.ql1 = *reinterpret_cast<const uint4 *>(p + 64 + 16 * g);
+            d.qh = *reinterpret_cast<const uint4 *>(p + 128 + 16 * g);
+            d.sc = *reinterpret_cast<const uint4 *>(p + 192);
+            d.d = *reinterpret_cast<const uint16_t *>(p + 208);
+        };
+        V16Q6Sb buf[DD];
+        if (busy)
+#pragma unroll
+            for (int k = 0; k < DD; ++k) load(buf[k], b0 + k);
+        if (sb0 > 0) __syncthreads();  // every wave is done with the previous segment's planes
+        v16q6_stage<NG>(x, nc, sb0, nsb, planes, tid, nthr);
+        __syncthreads();
+        if (!busy) continue;
+        for (int i0 = b0; i0 < b1; i0 += DD) {
+#pragma unroll
+            for (int kk = 0; kk < DD; ++kk) {
+                const int sbl = i0 + kk;
+                const V16Q6Sb sb = buf[kk];
+                load(buf[kk], sbl + DD);
+                if (sbl < b1) {  // (wave-uniform)
+                    // dword g of ql chunk 4n + 2(t % 2) + h and of qh chunk 2n + h
+                    const uint4 L0 = v16_xpose(sb.ql0), L1 = v16_xpose(sb.ql1), HQ = v16_xpose(sb.qh);
+                    const uint32_t ql[8] = {L0.x, L0.y, L0.z, L0.w, L1.x, L1.y, L1.z, L1.w};
+                    const uint32_t qh[4] = {HQ.x, HQ.y, HQ.z, HQ.w};
+                    const float d = f16_lo(sb.d);
+                    const uint32_t scw[4] = {sb.sc.x, sb.sc.y, sb.sc.z, sb.sc.w};
+#pragma unroll
+                    for (int n = 0; n < 2; ++n)
+#pragma unroll
+                        for (int qt = 0; qt < 4; ++qt) {
+                            uint4 xv[NG];
+#pragma unroll
+                            for (int cg = 0; cg < NG; ++cg)
+                                xv[cg] = *reinterpret_cast<const uint4 *>(
+                                    planes + ((size_t)sbl * NG + cg) * V16Q6_SB + ((n * 4 + qt) * 64 + lane) * 16);
+#pragma unroll
+                            for (int h = 0; h < 2; ++h) {
+                                const uint32_t QL = ql[4 * n + 2 * (qt & 1) + h], QH = qh[2 * n + h];
+                                uint32_t p0, p1;
+                                if (qt < 2) {  // low nibbles, s = 1
+                                    p0 = (QL & 0x000f000fu) | (((QH >> (2 * qt)) << 4) & 0x00300030u);
+                                    p1 = ((QL >> 8) & 0x000f000fu) | (((QH >> (2 * qt + 8)) << 4) & 0x00300030u);
+                                    p0 = padd(p0, Q6_OFF_LO);
+                                    p1 = padd(p1, Q6_OFF_LO);
+                                } else {  // high nibbles in place, s = 16
+                                    p0 = (QL & 0x00f000f0u) | (((QH >> (2 * qt)) << 8) & 0x03000300u);
+                                    p1 = ((QL >> 8) & 0x00f000f0u) | (((QH >> (2 * qt + 8)) << 8) & 0x03000300u);
+                                    p0 = padd(p0, Q6_OFF_HI);
+                                    p1 = padd(p1, Q6_OFF_HI);
+                                }
+                                const int si = 8 * n + 2 * qt + h;  // scale of the group
+                                const int scv = (int)(int8_t)(uint8_t)(scw[si >> 2] >> (8 * (si & 3)));
+                                const float f = d * (float)scv * (qt < 2 ? 0x1p24f : 0x1p20f);
+#pragma unroll
+                                for (int cg = 0; cg < NG; ++cg) {
+                                    const v16_f4 D = mfma16(h ? xv[cg].z : xv[cg].x, h ? xv[cg].w : xv[cg].y, p0, p1,
+                                                            v16_f4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                                    for (int e = 0; e < 4; ++e) acc[cg][e] = __builtin_fmaf(f, D[e], acc[cg][e]);
+                                }
+                            }
+                        }
+                }
+            }
+        }
+    }
+    // the shares of each tile, added in share order
+    __syncthreads();
+    float4 *part = reinterpret_cast<float4 *>(v16sm);
+#pragma unroll
+    for (int cg = 0; cg < NG; ++cg) part[cg * nthr + tid] = make_float4(acc[cg][0], acc[cg][1], acc[cg][2], acc[cg][3]);
+    __syncthreads();
+    if (ug == 0 && tile_ok && row < r1) {
+#pragma unroll
+        for (int cg = 0; cg < NG; ++cg) {
+            float o[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < UG; ++s) {
+                const float4 v = part[cg * nthr + (s * T + tile) * 64 + lane];
+                o[0] += v.x;
+                o[1] += v.y;
+                o[2] += v.z;
+                o[3] += v.w;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = 16 * cg + 4 * g + e;
+                if (c < nc) y[(size_t)row * nc + c] = o[e];
+            }
+        }
+    }
+}
+
+template <int NG>
+static hipError_t launch_v16q6g(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, hipStream_t st) {
+    const int cus = device_cus();
+    const int64_t tiles = (N + 15) / 16;
+    const int64_t G = std::max<int64_t>(std::min<int64_t>(cus, tiles), (tiles + 7) / 8);
+    const int T = (int)((tiles + G - 1) / G);
+    // shares per tile: one group of columns runs faster with two shares at
+    // 2-3 tiles (more superblocks per wave between the segment barriers)
+    const int UG = T <= 1 ? 4 : T <= 3 ? (NG == 1 ? 2 : 4) : T <= 6 ? 2 : 1;
+    const int threads = 64 * T * UG;
+    const int64_t S = K / 256;
+    const int64_t smax = V16_PLANES / (NG * V16Q6_SB);  // superblocks per segment at most
+    const int64_t nseg = (S + smax - 1) / smax;
+    const int segsb = (int)((S + nseg - 1) / nseg);
+    const size_t lds = std::max<size_t>((size_t)segsb * NG * V16Q6_SB, (size_t)threads * 16 * NG);
+    if (T < 1 || T > 8 || threads > 768 || lds > 160 * 1024) return hipErrorInvalidValue;
+    const hipError_t e = lds_opt_in<v16q6_kernel<NG>>(160 * 1024);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((v16q6_kernel<NG>), dim3((unsigned)G), dim3(threads), lds, st, (const uint8_t *)W,
+                       (const uint16_t *)x, (float *)y, (int)N, (int)K, nc, segsb, T, UG);
+    return hipGetLastError();
+}
+
+// 5-16 columns: one group; 17-32: two
+static inline hipError_t launch_v16q6(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
+                                      hipStream_t st) {
+    return nc > 16 ? launch_v16q6g<2>(W, x, y, N, K, nc, st) : launch_v16q6g<1>(W, x, y, N, K, nc, st);
+}
+
 }  // namespace qk

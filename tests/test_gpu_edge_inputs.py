@@ -100,7 +100,7 @@ def test_scale_sweep_dequant_bit_exact(sweep):
     assert same_f32(gpu_dequant(qt, W, N, K), oracle.dequant(qt, W, K))
 
 
-@pytest.mark.parametrize("ncols", [1, 4, 8])
+@pytest.mark.parametrize("ncols", [1, 4, 8, 12, 17])
 def test_scale_sweep_gemv_rows(sweep, ncols):
     qt, W, N, K = sweep
     x = synth.activations(K, ncols, 4100 + ncols)

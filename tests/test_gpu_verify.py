@@ -150,8 +150,11 @@ def test_verify_wide_one_hot_columns_exact(qt):
 
 
 @pytest.mark.parametrize("ncols", [16, 17])
-def test_verify_wide_full_shape_all_rows(ncols):
-    c = synth.VERIFY
+@pytest.mark.parametrize("case", [synth.VERIFY] + list(synth.MIXED), ids=lambda c: c.get("name", "q4k_17408x5120"))
+def test_verify_wide_full_shape_all_rows(case, ncols):
+    """Every row at the verify shape and the mixed-type shapes (Q6_K FFN
+    down: four segments of x planes on the tiles; Q5_K output projection)."""
+    c = case
     N, K = c["N"], c["K"]
     W = synth.superblocks(c["qtype"], N, K, c["seed"])
     x = synth.activations(K, ncols, c["seed"])
