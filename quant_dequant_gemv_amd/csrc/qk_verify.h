@@ -697,8 +697,8 @@ static hipError_t verify_type(const void *W, const void *x, void *y, int64_t N, 
     // Q4_K and Q5_K at 9-32 columns without an epilogue: one pass on 16x16x16 tiles
     if constexpr (T == Q4_K || T == Q5_K)
         if (nc > 8 && nc <= 32 && !ep.W2 && !ep.res && !ep.f16) return launch_v16<T>(W, x, y, N, K, nc, st);
-    if constexpr (T == Q6_K)
-        if (nc >= V16Q6_MIN && nc <= 32 && !ep.W2 && !ep.res && !ep.f16) return launch_v16q6(W, x, y, N, K, nc, st);
+    if constexpr (T == Q6_K || T == IQ4_XS)
+        if (nc >= V16Q6_MIN && nc <= 32 && !ep.W2 && !ep.res && !ep.f16) return launch_v16q6<T>(W, x, y, N, K, nc, st);
     const VPlan pl = vplan(nc);
     if (ep.W2) {
         switch (pl.ncb) {

@@ -1,5 +1,5 @@
-// qk_verify16.h -- Q4_K and Q5_K at 9 to 32 columns in one pass on 16x16x16 matrix
-// tiles (the verify form of drafted tokens: B70 plan, "Phase 4: True Xe2
+// qk_verify16.h -- 9 to 32 columns in one pass on 16x16x16 matrix tiles, every
+// type (Q4_K / Q5_K: v16_kernel; Q6_K / IQ4_XS: v16q6_kernel, further down) (the verify form of drafted tokens: B70 plan, "Phase 4: True Xe2
 // Batched Verification", and its checklist's verifier widths up to 17).
 //
 // v_mfma_f32_16x16x16_f16 (probed on the box: A[i][k] from lane i + 16(k/4),
@@ -23,7 +23,8 @@
 // reads them as two 16-byte vectors.  Every (row, column) is accumulated by
 // one lane per share, in unit order; the shares of a tile are added in a
 // fixed order at the end.  Weights are read once; the first ring of each
-// segment is issued before its x is staged.
+// segment is issued before its x is staged.  (This paragraph describes the
+// Q4_K / Q5_K kernel; the Q6_K / IQ4_XS one is described above it.)
 #pragma once
 
 #include "qk_epilogue.h"
@@ -390,7 +391,14 @@ __device__ __forceinline__ void v16q6_stage(const uint16_t *__restrict__ x, int 
 
 // Workgroups, tiles and shares as in v16_kernel; segments of whole
 // superblocks (segsb of them, at most 160 KB of planes).
-template <int NG>
+//
+// IQ4_XS on the same kernel: sub-block ib (weights 32ib + 0..31, one 6-bit
+// scale) is qs chunk ib (16 bytes: weight j in the low nibble of byte j,
+// weight 16 + j in the high one), so plane group (n, t, h) is sub-block
+// 4n + t, nibble h, and lane row g loads chunks g and 4 + g; the codebook
+// lookup gives the patterns kv 2^-24 (signed, exact) and the scale is
+// d 2^24 (ls - 32).
+template <int T_, int NG>
 __global__ void __launch_bounds__(768) v16q6_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ x,
                                                     float *__restrict__ y, int N, int K, int nc, int segsb, int T,
                                                     int UG) {
@@ -405,7 +413,9 @@ __global__ void __launch_bounds__(768) v16q6_kernel(const uint8_t *__restrict__ 
     const int row = r0 + 16 * tile + r;
     const bool tile_ok = r0 + 16 * tile < r1;  // (wave-uniform)
     const int S = K >> 8;
-    const uint8_t *wrow = W + (size_t)min(row, r1 - 1) * (size_t)(S * 210);
+    static_assert(T_ == Q6_K || T_ == IQ4_XS, "Q6_K and IQ4_XS");
+    constexpr int SBB = T_ == Q6_K ? 210 : 136;
+    const uint8_t *wrow = W + (size_t)min(row, r1 - 1) * (size_t)(S * SBB);
     uint8_t *planes = v16sm;
     v16_f4 acc[NG];
 #pragma unroll
@@ -415,15 +425,23 @@ __global__ void __launch_bounds__(768) v16q6_kernel(const uint8_t *__restrict__ 
         const int nsb = min(segsb, S - sb0);
         const int b0 = ug * nsb / UG, b1 = (ug + 1) * nsb / UG;
         const bool busy = tile_ok && b0 < b1;  // (wave-uniform)
-        const uint8_t *wseg = wrow + 210 * sb0;
-        // superblocks are 2-byte aligned: unaligned 16-byte loads
+        const uint8_t *wseg = wrow + SBB * sb0;
+        // superblocks are 2-byte (Q6_K) or 8-byte (IQ4_XS) aligned: unaligned 16-byte loads
         auto load = [&](V16Q6Sb &d, int sbl) {
-            const uint8_t *p = wseg + 210 * min(sbl, b1 - 1);
-            d.ql0 = *reinterpret_cast<const uint4 *>(p + 16 * g);
-            d.ql1 = *reinterpret_cast<const uint4 *>(p + 64 + 16 * g);
-            d.qh = *reinterpret_cast<const uint4 *>(p + 128 + 16 * g);
-            d.sc = *reinterpret_cast<const uint4 *>(p + 192);
-            d.d = *reinterpret_cast<const uint16_t *>(p + 208);
+            const uint8_t *p = wseg + SBB * min(sbl, b1 - 1);
+            if constexpr (T_ == Q6_K) {
+                d.ql0 = *reinterpret_cast<const uint4 *>(p + 16 * g);
+                d.ql1 = *reinterpret_cast<const uint4 *>(p + 64 + 16 * g);
+                d.qh = *reinterpret_cast<const uint4 *>(p + 128 + 16 * g);
+                d.sc = *reinterpret_cast<const uint4 *>(p + 192);
+                d.d = *reinterpret_cast<const uint16_t *>(p + 208);
+            } else {  // d | scales_h << 16, scales_l, qs
+                const uint2 h = *reinterpret_cast<const uint2 *>(p);
+                d.d = h.x;
+                d.sc.x = h.y;
+                d.ql0 = *reinterpret_cast<const uint4 *>(p + 8 + 16 * g);
+                d.ql1 = *reinterpret_cast<const uint4 *>(p + 72 + 16 * g);
+            }
         };
         V16Q6Sb buf[DD];
         if (busy)
@@ -441,7 +459,9 @@ __global__ void __launch_bounds__(768) v16q6_kernel(const uint8_t *__restrict__ 
                 load(buf[kk], sbl + DD);
                 if (sbl < b1) {  // (wave-uniform)
                     // dword g of ql chunk 4n + 2(t % 2) + h and of qh chunk 2n + h
-                    const uint4 L0 = v16_xpose(sb.ql0), L1 = v16_xpose(sb.ql1), HQ = v16_xpose(sb.qh);
+                    // (IQ4_XS: dword g of qs chunk 4n + t)
+                    const uint4 L0 = v16_xpose(sb.ql0), L1 = v16_xpose(sb.ql1);
+                    const uint4 HQ = T_ == Q6_K ? v16_xpose(sb.qh) : make_uint4(0u, 0u, 0u, 0u);
                     const uint32_t ql[8] = {L0.x, L0.y, L0.z, L0.w, L1.x, L1.y, L1.z, L1.w};
                     const uint32_t qh[4] = {HQ.x, HQ.y, HQ.z, HQ.w};
                     const float d = f16_lo(sb.d);
@@ -457,8 +477,16 @@ __global__ void __launch_bounds__(768) v16q6_kernel(const uint8_t *__restrict__ 
                                     planes + ((size_t)sbl * NG + cg) * V16Q6_SB + ((n * 4 + qt) * 64 + lane) * 16);
 #pragma unroll
                             for (int h = 0; h < 2; ++h) {
-                                const uint32_t QL = ql[4 * n + 2 * (qt & 1) + h], QH = qh[2 * n + h];
                                 uint32_t p0, p1;
+                                float f;
+                                if constexpr (T_ == IQ4_XS) {
+                                    const int ib = 4 * n + qt;
+                                    iq4_pairs(h ? ql[ib] >> 4 : ql[ib], p0, p1);
+                                    const uint32_t lo4 = __builtin_amdgcn_ubfe(sb.sc.x, 4u * ib, 4u);
+                                    const uint32_t hi2 = __builtin_amdgcn_ubfe(sb.d, 16u + 2u * ib, 2u);
+                                    f = d * 0x1p24f * (float)((int)(lo4 | hi2 << 4) - 32);
+                                } else {
+                                const uint32_t QL = ql[4 * n + 2 * (qt & 1) + h], QH = qh[2 * n + h];
                                 if (qt < 2) {  // low nibbles, s = 1
                                     p0 = (QL & 0x000f000fu) | (((QH >> (2 * qt)) << 4) & 0x00300030u);
                                     p1 = ((QL >> 8) & 0x000f000fu) | (((QH >> (2 * qt + 8)) << 4) & 0x00300030u);
@@ -472,7 +500,8 @@ __global__ void __launch_bounds__(768) v16q6_kernel(const uint8_t *__restrict__ 
                                 }
                                 const int si = 8 * n + 2 * qt + h;  // scale of the group
                                 const int scv = (int)(int8_t)(uint8_t)(scw[si >> 2] >> (8 * (si & 3)));
-                                const float f = d * (float)scv * (qt < 2 ? 0x1p24f : 0x1p20f);
+                                f = d * (float)scv * (qt < 2 ? 0x1p24f : 0x1p20f);
+                                }
 #pragma unroll
                                 for (int cg = 0; cg < NG; ++cg) {
                                     const v16_f4 D = mfma16(h ? xv[cg].z : xv[cg].x, h ? xv[cg].w : xv[cg].y, p0, p1,
@@ -512,7 +541,7 @@ __global__ void __launch_bounds__(768) v16q6_kernel(const uint8_t *__restrict__ 
     }
 }
 
-template <int NG>
+template <int T_, int NG>
 static hipError_t launch_v16q6g(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, hipStream_t st) {
     const int cus = device_cus();
     const int64_t tiles = (N + 15) / 16;
@@ -528,17 +557,18 @@ static hipError_t launch_v16q6g(const void *W, const void *x, void *y, int64_t N
     const int segsb = (int)((S + nseg - 1) / nseg);
     const size_t lds = std::max<size_t>((size_t)segsb * NG * V16Q6_SB, (size_t)threads * 16 * NG);
     if (T < 1 || T > 8 || threads > 768 || lds > 160 * 1024) return hipErrorInvalidValue;
-    const hipError_t e = lds_opt_in<v16q6_kernel<NG>>(160 * 1024);
+    const hipError_t e = lds_opt_in<v16q6_kernel<T_, NG>>(160 * 1024);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((v16q6_kernel<NG>), dim3((unsigned)G), dim3(threads), lds, st, (const uint8_t *)W,
+    hipLaunchKernelGGL((v16q6_kernel<T_, NG>), dim3((unsigned)G), dim3(threads), lds, st, (const uint8_t *)W,
                        (const uint16_t *)x, (float *)y, (int)N, (int)K, nc, segsb, T, UG);
     return hipGetLastError();
 }
 
 // 5-16 columns: one group; 17-32: two
+template <int T_>
 static inline hipError_t launch_v16q6(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
                                       hipStream_t st) {
-    return nc > 16 ? launch_v16q6g<2>(W, x, y, N, K, nc, st) : launch_v16q6g<1>(W, x, y, N, K, nc, st);
+    return nc > 16 ? launch_v16q6g<T_, 2>(W, x, y, N, K, nc, st) : launch_v16q6g<T_, 1>(W, x, y, N, K, nc, st);
 }
 
 }  // namespace qk
