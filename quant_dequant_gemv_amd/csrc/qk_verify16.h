@@ -140,8 +140,8 @@ __device__ __forceinline__ void v16_stage(const uint16_t *__restrict__ x, int nc
 
 template <int T_, int NG>
 __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ x,
-                                                   float *__restrict__ y, int N, int K, int nc, int useg, int T,
-                                                   int UG) {
+                                                   void *__restrict__ y, int N, int K, int nc, int useg, int T,
+                                                   int UG, Epilogue ep) {
     static_assert(T_ == Q4_K || T_ == Q5_K, "Q4_K and Q5_K");
     constexpr int SBB = V16Fmt<T_>::bytes, QSO = V16Fmt<T_>::qs, QMAX = V16Fmt<T_>::qmax;
     constexpr int DD = T_ == Q5_K ? 1 : V16_D;  // superblocks in flight (Q5_K: its qh bits take the registers)
@@ -243,6 +243,16 @@ __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W,
             }
         }
     }
+    // the residual of the lane's outputs, read before the shares are added
+    // (res may be y itself: each element is read and written by one lane)
+    float rv[NG][4];
+#pragma unroll
+    for (int cg = 0; cg < NG; ++cg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = 16 * cg + 4 * g + e;
+            rv[cg][e] = ep.res && ug == 0 && tile_ok && row < r1 && c < nc ? ep.res[(size_t)row * nc + c] : 0.f;
+        }
     // the shares of each tile, added in share order
     __syncthreads();
     float4 *part = reinterpret_cast<float4 *>(v16sm);
@@ -263,7 +273,7 @@ __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W,
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int c = 16 * cg + 4 * g + e;
-                if (c < nc) y[(size_t)row * nc + c] = o[e] * 0x1p48f;
+                if (c < nc) store_y(y, ep.f16, (size_t)row * nc + c, ep.res ? o[e] * 0x1p48f + rv[cg][e] : o[e] * 0x1p48f);
             }
         }
     }
@@ -274,7 +284,8 @@ __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W,
 // most 12 waves: 168 registers); segments of at most 160 KB of planes, as
 // even as possible, in whole superblocks.
 template <int T_, int NG>
-static hipError_t launch_v16g(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, hipStream_t st) {
+static hipError_t launch_v16g(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
+                              const Epilogue &ep, hipStream_t st) {
     const int cus = device_cus();
     const int64_t tiles = (N + 15) / 16;
     const int64_t G = std::max<int64_t>(std::min<int64_t>(cus, tiles), (tiles + 7) / 8);
@@ -290,14 +301,15 @@ static hipError_t launch_v16g(const void *W, const void *x, void *y, int64_t N, 
     const hipError_t e = lds_opt_in<v16_kernel<T_, NG>>(160 * 1024);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((v16_kernel<T_, NG>), dim3((unsigned)G), dim3(threads), lds, st, (const uint8_t *)W,
-                       (const uint16_t *)x, (float *)y, (int)N, (int)K, nc, useg, T, UG);
+                       (const uint16_t *)x, y, (int)N, (int)K, nc, useg, T, UG, ep);
     return hipGetLastError();
 }
 
 // 9-16 columns: one group; 17-32: two groups sharing each unit's patterns
 template <int T_>
-static hipError_t launch_v16(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, hipStream_t st) {
-    return nc > 16 ? launch_v16g<T_, 2>(W, x, y, N, K, nc, st) : launch_v16g<T_, 1>(W, x, y, N, K, nc, st);
+static hipError_t launch_v16(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, const Epilogue &ep,
+                             hipStream_t st) {
+    return nc > 16 ? launch_v16g<T_, 2>(W, x, y, N, K, nc, ep, st) : launch_v16g<T_, 1>(W, x, y, N, K, nc, ep, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -400,8 +412,8 @@ __device__ __forceinline__ void v16q6_stage(const uint16_t *__restrict__ x, int 
 // d 2^24 (ls - 32).
 template <int T_, int NG>
 __global__ void __launch_bounds__(768) v16q6_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ x,
-                                                    float *__restrict__ y, int N, int K, int nc, int segsb, int T,
-                                                    int UG) {
+                                                    void *__restrict__ y, int N, int K, int nc, int segsb, int T,
+                                                    int UG, Epilogue ep) {
     constexpr int DD = NG == 2 ? 1 : V16_D;  // superblocks in flight (two groups: the accumulators take the registers)
     extern __shared__ __attribute__((aligned(16))) uint8_t v16sm[];
     const int tid = (int)threadIdx.x, nthr = (int)blockDim.x;
@@ -515,6 +527,16 @@ __global__ void __launch_bounds__(768) v16q6_kernel(const uint8_t *__restrict__ 
             }
         }
     }
+    // the residual of the lane's outputs, read before the shares are added
+    // (res may be y itself: each element is read and written by one lane)
+    float rv[NG][4];
+#pragma unroll
+    for (int cg = 0; cg < NG; ++cg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = 16 * cg + 4 * g + e;
+            rv[cg][e] = ep.res && ug == 0 && tile_ok && row < r1 && c < nc ? ep.res[(size_t)row * nc + c] : 0.f;
+        }
     // the shares of each tile, added in share order
     __syncthreads();
     float4 *part = reinterpret_cast<float4 *>(v16sm);
@@ -535,14 +557,15 @@ __global__ void __launch_bounds__(768) v16q6_kernel(const uint8_t *__restrict__ 
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int c = 16 * cg + 4 * g + e;
-                if (c < nc) y[(size_t)row * nc + c] = o[e];
+                if (c < nc) store_y(y, ep.f16, (size_t)row * nc + c, ep.res ? o[e] + rv[cg][e] : o[e]);
             }
         }
     }
 }
 
 template <int T_, int NG>
-static hipError_t launch_v16q6g(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, hipStream_t st) {
+static hipError_t launch_v16q6g(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
+                              const Epilogue &ep, hipStream_t st) {
     const int cus = device_cus();
     const int64_t tiles = (N + 15) / 16;
     const int64_t G = std::max<int64_t>(std::min<int64_t>(cus, tiles), (tiles + 7) / 8);
@@ -560,15 +583,15 @@ static hipError_t launch_v16q6g(const void *W, const void *x, void *y, int64_t N
     const hipError_t e = lds_opt_in<v16q6_kernel<T_, NG>>(160 * 1024);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((v16q6_kernel<T_, NG>), dim3((unsigned)G), dim3(threads), lds, st, (const uint8_t *)W,
-                       (const uint16_t *)x, (float *)y, (int)N, (int)K, nc, segsb, T, UG);
+                       (const uint16_t *)x, y, (int)N, (int)K, nc, segsb, T, UG, ep);
     return hipGetLastError();
 }
 
 // 5-16 columns: one group; 17-32: two
 template <int T_>
 static inline hipError_t launch_v16q6(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
-                                      hipStream_t st) {
-    return nc > 16 ? launch_v16q6g<T_, 2>(W, x, y, N, K, nc, st) : launch_v16q6g<T_, 1>(W, x, y, N, K, nc, st);
+                                      const Epilogue &ep, hipStream_t st) {
+    return nc > 16 ? launch_v16q6g<T_, 2>(W, x, y, N, K, nc, ep, st) : launch_v16q6g<T_, 1>(W, x, y, N, K, nc, ep, st);
 }
 
 }  // namespace qk
