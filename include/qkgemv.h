@@ -112,9 +112,9 @@ enum {
  *          few-column verify form with W read once per call; 17..32 take
  *          the columns in two groups of (nearly) equal width inside one
  *          launch, each group streaming W (the B70 plan's checklist asks
- *          for verifier widths up to 17) -- except calls without the
- *          SwiGLU pair (qk_gemv, qk_gemv_ex), which take 9..32 columns in
- *          one pass over W
+ *          for verifier widths up to 17) -- the calls of this library
+ *          take 9..32 columns in one pass over W (each of W and W2 read
+ *          once by qk_gemv_swiglu)
  *   stream hipStream_t to enqueue on
  *
  * y must not overlap W or x (QK_EINVAL_PTR): other workgroups are still

@@ -694,11 +694,11 @@ static hipError_t verify_dispatch(const void *W, const void *x, void *y, int64_t
 template <int T>
 static hipError_t verify_type(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
                               const Epilogue &ep, hipStream_t st) {
-    // 9-32 columns (residual and fp16 y included; not the SwiGLU pair): one pass on 16x16x16 tiles
+    // 9-32 columns, every epilogue: one pass on 16x16x16 tiles
     if constexpr (T == Q4_K || T == Q5_K)
-        if (nc > 8 && nc <= 32 && !ep.W2) return launch_v16<T>(W, x, y, N, K, nc, ep, st);
+        if (nc > 8 && nc <= 32) return launch_v16<T>(W, x, y, N, K, nc, ep, st);
     if constexpr (T == Q6_K || T == IQ4_XS)
-        if (nc >= V16Q6_MIN && nc <= 32 && !ep.W2) return launch_v16q6<T>(W, x, y, N, K, nc, ep, st);
+        if (nc >= V16Q6_MIN && nc <= 32) return launch_v16q6<T>(W, x, y, N, K, nc, ep, st);
     const VPlan pl = vplan(nc);
     if (ep.W2) {
         switch (pl.ncb) {

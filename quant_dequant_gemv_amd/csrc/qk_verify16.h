@@ -147,16 +147,21 @@ __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W,
     constexpr int DD = T_ == Q5_K ? 1 : V16_D;  // superblocks in flight (Q5_K: its qh bits take the registers)
     extern __shared__ __attribute__((aligned(16))) uint8_t v16sm[];
     const int tid = (int)threadIdx.x, nthr = (int)blockDim.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // (wave-uniform)
     const int tile = wave % T, ug = wave / T;
+    // SwiGLU pair: waves of tiles TH..T-1 stream the same rows of ep.W2
+    const int TH = ep.W2 ? T >> 1 : T;
+    const bool second = tile >= TH;  // (wave-uniform)
+    const int trow = second ? tile - TH : tile;
+    const uint8_t *Wt = second ? reinterpret_cast<const uint8_t *>(ep.W2) : W;
     const int r = lane & 15, g = lane >> 4;
     // whole 16-row tiles per workgroup (the last tile of the tensor may be
     // short): ceil(N / 16) tiles split as evenly as possible
     const RowSplit split((N + 15) >> 4, (int)blockIdx.x, (int)gridDim.x);
     const int r0 = 16 * split.r0, r1 = min(16 * split.r1, N);
-    const int row = r0 + 16 * tile + r;
-    const bool tile_ok = r0 + 16 * tile < r1;  // (wave-uniform)
-    const uint8_t *wrow = W + (size_t)min(row, r1 - 1) * (size_t)((K >> 8) * SBB);
+    const int row = r0 + 16 * trow + r;
+    const bool tile_ok = r0 + 16 * trow < r1;  // (wave-uniform)
+    const uint8_t *wrow = Wt + (size_t)min(row, r1 - 1) * (size_t)((K >> 8) * SBB);
     const int U = K >> 6;
     uint8_t *planes = v16sm;
     v16_f4 acc[NG];
@@ -251,7 +256,7 @@ __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int c = 16 * cg + 4 * g + e;
-            rv[cg][e] = ep.res && ug == 0 && tile_ok && row < r1 && c < nc ? ep.res[(size_t)row * nc + c] : 0.f;
+            rv[cg][e] = ep.res && ug == 0 && !second && tile_ok && row < r1 && c < nc ? ep.res[(size_t)row * nc + c] : 0.f;
         }
     // the shares of each tile, added in share order
     __syncthreads();
@@ -259,21 +264,31 @@ __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W,
 #pragma unroll
     for (int cg = 0; cg < NG; ++cg) part[cg * nthr + tid] = make_float4(acc[cg][0], acc[cg][1], acc[cg][2], acc[cg][3]);
     __syncthreads();
-    if (ug == 0 && tile_ok && row < r1) {
+    if (ug == 0 && !second && tile_ok && row < r1) {
 #pragma unroll
         for (int cg = 0; cg < NG; ++cg) {
-            float o[4] = {0.f, 0.f, 0.f, 0.f};
+            float o[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
             for (int s = 0; s < UG; ++s) {
                 const float4 v = part[cg * nthr + (s * T + tile) * 64 + lane];
                 o[0] += v.x;
                 o[1] += v.y;
                 o[2] += v.z;
                 o[3] += v.w;
+                if (ep.W2) {  // the same rows of W2: tile + TH
+                    const float4 w = part[cg * nthr + (s * T + tile + TH) * 64 + lane];
+                    u[0] += w.x;
+                    u[1] += w.y;
+                    u[2] += w.z;
+                    u[3] += w.w;
+                }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int c = 16 * cg + 4 * g + e;
-                if (c < nc) store_y(y, ep.f16, (size_t)row * nc + c, ep.res ? o[e] * 0x1p48f + rv[cg][e] : o[e] * 0x1p48f);
+                float v = o[e] * 0x1p48f;
+                if (ep.W2) v = silu(v) * (u[e] * 0x1p48f);
+                if (ep.res) v += rv[cg][e];
+                if (c < nc) store_y(y, ep.f16, (size_t)row * nc + c, v);
             }
         }
     }
@@ -288,8 +303,9 @@ static hipError_t launch_v16g(const void *W, const void *x, void *y, int64_t N, 
                               const Epilogue &ep, hipStream_t st) {
     const int cus = device_cus();
     const int64_t tiles = (N + 15) / 16;
-    const int64_t G = std::max<int64_t>(std::min<int64_t>(cus, tiles), (tiles + 7) / 8);
-    const int T = (int)((tiles + G - 1) / G);  // tiles of the largest workgroup
+    const int tmax = ep.W2 ? 6 : 8;  // (the pair streams each tile twice)
+    const int64_t G = std::max<int64_t>(std::min<int64_t>(cus, tiles), (tiles + tmax - 1) / tmax);
+    const int T = (int)((tiles + G - 1) / G) * (ep.W2 ? 2 : 1);  // tiles of the largest workgroup
     const int UG = T <= 3 ? 4 : T <= 6 ? 2 : 1;  // at most 12 waves (168 registers)
     const int threads = 64 * T * UG;
     const int64_t U = K / 64;
@@ -297,7 +313,7 @@ static hipError_t launch_v16g(const void *W, const void *x, void *y, int64_t N, 
     const int64_t nseg = (U + smax - 1) / smax;
     const int useg = (int)(((U + nseg - 1) / nseg + 3) / 4 * 4);  // whole superblocks
     const size_t lds = std::max<size_t>((size_t)useg * NG * V16_UB, (size_t)threads * 16 * NG);  // (planes, then the shares)
-    if (T < 1 || T > 8 || threads > 768 || lds > 160 * 1024) return hipErrorInvalidValue;
+    if (T < 1 || T > 12 || threads > 768 || lds > 160 * 1024) return hipErrorInvalidValue;
     const hipError_t e = lds_opt_in<v16_kernel<T_, NG>>(160 * 1024);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((v16_kernel<T_, NG>), dim3((unsigned)G), dim3(threads), lds, st, (const uint8_t *)W,
@@ -417,17 +433,22 @@ __global__ void __launch_bounds__(768) v16q6_kernel(const uint8_t *__restrict__ 
     constexpr int DD = NG == 2 ? 1 : V16_D;  // superblocks in flight (two groups: the accumulators take the registers)
     extern __shared__ __attribute__((aligned(16))) uint8_t v16sm[];
     const int tid = (int)threadIdx.x, nthr = (int)blockDim.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // (wave-uniform)
     const int tile = wave % T, ug = wave / T;
+    // SwiGLU pair: waves of tiles TH..T-1 stream the same rows of ep.W2
+    const int TH = ep.W2 ? T >> 1 : T;
+    const bool second = tile >= TH;  // (wave-uniform)
+    const int trow = second ? tile - TH : tile;
+    const uint8_t *Wt = second ? reinterpret_cast<const uint8_t *>(ep.W2) : W;
     const int r = lane & 15, g = lane >> 4;
     const RowSplit split((N + 15) >> 4, (int)blockIdx.x, (int)gridDim.x);
     const int r0 = 16 * split.r0, r1 = min(16 * split.r1, N);
-    const int row = r0 + 16 * tile + r;
-    const bool tile_ok = r0 + 16 * tile < r1;  // (wave-uniform)
+    const int row = r0 + 16 * trow + r;
+    const bool tile_ok = r0 + 16 * trow < r1;  // (wave-uniform)
     const int S = K >> 8;
     static_assert(T_ == Q6_K || T_ == IQ4_XS, "Q6_K and IQ4_XS");
     constexpr int SBB = T_ == Q6_K ? 210 : 136;
-    const uint8_t *wrow = W + (size_t)min(row, r1 - 1) * (size_t)(S * SBB);
+    const uint8_t *wrow = Wt + (size_t)min(row, r1 - 1) * (size_t)(S * SBB);
     uint8_t *planes = v16sm;
     v16_f4 acc[NG];
 #pragma unroll
@@ -535,7 +556,7 @@ __global__ void __launch_bounds__(768) v16q6_kernel(const uint8_t *__restrict__ 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int c = 16 * cg + 4 * g + e;
-            rv[cg][e] = ep.res && ug == 0 && tile_ok && row < r1 && c < nc ? ep.res[(size_t)row * nc + c] : 0.f;
+            rv[cg][e] = ep.res && ug == 0 && !second && tile_ok && row < r1 && c < nc ? ep.res[(size_t)row * nc + c] : 0.f;
         }
     // the shares of each tile, added in share order
     __syncthreads();
@@ -543,21 +564,31 @@ __global__ void __launch_bounds__(768) v16q6_kernel(const uint8_t *__restrict__ 
 #pragma unroll
     for (int cg = 0; cg < NG; ++cg) part[cg * nthr + tid] = make_float4(acc[cg][0], acc[cg][1], acc[cg][2], acc[cg][3]);
     __syncthreads();
-    if (ug == 0 && tile_ok && row < r1) {
+    if (ug == 0 && !second && tile_ok && row < r1) {
 #pragma unroll
         for (int cg = 0; cg < NG; ++cg) {
-            float o[4] = {0.f, 0.f, 0.f, 0.f};
+            float o[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
             for (int s = 0; s < UG; ++s) {
                 const float4 v = part[cg * nthr + (s * T + tile) * 64 + lane];
                 o[0] += v.x;
                 o[1] += v.y;
                 o[2] += v.z;
                 o[3] += v.w;
+                if (ep.W2) {  // the same rows of W2: tile + TH
+                    const float4 w = part[cg * nthr + (s * T + tile + TH) * 64 + lane];
+                    u[0] += w.x;
+                    u[1] += w.y;
+                    u[2] += w.z;
+                    u[3] += w.w;
+                }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int c = 16 * cg + 4 * g + e;
-                if (c < nc) store_y(y, ep.f16, (size_t)row * nc + c, ep.res ? o[e] + rv[cg][e] : o[e]);
+                float v = o[e];
+                if (ep.W2) v = silu(v) * (u[e]);
+                if (ep.res) v += rv[cg][e];
+                if (c < nc) store_y(y, ep.f16, (size_t)row * nc + c, v);
             }
         }
     }
@@ -568,8 +599,9 @@ static hipError_t launch_v16q6g(const void *W, const void *x, void *y, int64_t N
                               const Epilogue &ep, hipStream_t st) {
     const int cus = device_cus();
     const int64_t tiles = (N + 15) / 16;
-    const int64_t G = std::max<int64_t>(std::min<int64_t>(cus, tiles), (tiles + 7) / 8);
-    const int T = (int)((tiles + G - 1) / G);
+    const int tmax = ep.W2 ? 6 : 8;  // (the pair streams each tile twice)
+    const int64_t G = std::max<int64_t>(std::min<int64_t>(cus, tiles), (tiles + tmax - 1) / tmax);
+    const int T = (int)((tiles + G - 1) / G) * (ep.W2 ? 2 : 1);
     // shares per tile: one group of columns runs faster with two shares at
     // 2-3 tiles (more superblocks per wave between the segment barriers)
     const int UG = T <= 1 ? 4 : T <= 3 ? (NG == 1 ? 2 : 4) : T <= 6 ? 2 : 1;
@@ -579,7 +611,7 @@ static hipError_t launch_v16q6g(const void *W, const void *x, void *y, int64_t N
     const int64_t nseg = (S + smax - 1) / smax;
     const int segsb = (int)((S + nseg - 1) / nseg);
     const size_t lds = std::max<size_t>((size_t)segsb * NG * V16Q6_SB, (size_t)threads * 16 * NG);
-    if (T < 1 || T > 8 || threads > 768 || lds > 160 * 1024) return hipErrorInvalidValue;
+    if (T < 1 || T > 12 || threads > 768 || lds > 160 * 1024) return hipErrorInvalidValue;
     const hipError_t e = lds_opt_in<v16q6_kernel<T_, NG>>(160 * 1024);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((v16q6_kernel<T_, NG>), dim3((unsigned)G), dim3(threads), lds, st, (const uint8_t *)W,
