@@ -61,21 +61,19 @@ constexpr int V_MAX_RL = 8;  // quads per straight-line round, at most
 // Plain launches of two column blocks in short rounds fit 168 registers
 // without spills, so they may take 12 waves (two row phases at K = 5120):
 // Q4_K and IQ4_XS in rounds of up to 3 quads, Q5_K and Q6_K of one (measured
-// 4-5% faster for Q4_K at 17408 x 5120, 6 and 8 columns).  The epilogue and
-// group-loop variants would spill there.
+// 4-5% faster for Q4_K at 17408 x 5120, 6 and 8 columns).  The epilogue
+// variants would spill there.
 template <int T>
 __host__ __device__ constexpr int v_short_rl() { return T == Q4_K || T == IQ4_XS ? 3 : 1; }
-template <int T, int NCB, int RL, bool PAIR, bool EPI, bool WIDE>
+template <int T, int NCB, int RL, bool PAIR, bool EPI>
 constexpr int v_bound() {
-    return NCB == 2 && RL <= v_short_rl<T>() && !PAIR && !EPI && !WIDE ? 768 : v_max_threads<NCB>();
+    return NCB == 2 && RL <= v_short_rl<T>() && !PAIR && !EPI ? 768 : v_max_threads<NCB>();
 }
 // LDS for the x planes of one segment: 112 KB for launches of up to 8
 // columns, so that 5120 x 6144 takes one segment instead of two and
 // 5120 x 17408 three instead of four at 8 columns (Q5_K 17.0 -> 13.3 us,
-// Q6_K 44.5 -> 37.7 us); 96 KB for the column-group variant (9-32 columns),
-// where the larger budget picked segments of three waves instead of two:
-// 50.7 -> 67.7 us at 16 columns.
-constexpr int V_RAW_BUDGET = 112 * 1024, V_RAW_BUDGET_WIDE = 96 * 1024;
+// Q6_K 44.5 -> 37.7 us).
+constexpr int V_RAW_BUDGET = 112 * 1024;
 constexpr int V_LDS_MAX = 160 * 1024;
 
 template <int T>
@@ -163,30 +161,6 @@ __device__ __forceinline__ void stage_planes(const uint8_t *xg, uint8_t *planes,
     }
 }
 
-// The same planes for a column window of a wider x (row stride ldx halves,
-// the window's first column at xg): one task per 8 rows and column, eight
-// 16-bit loads, one 16-byte write.
-template <int T>
-__device__ __forceinline__ void stage_planes_strided(const uint16_t *xg, int ldx, int nc, uint8_t *planes, int ps,
-                                                     int ns, int tid) {
-    const int ntask = ns * 8 * nc;
-    for (int t = tid; t < ntask; t += (int)blockDim.x) {
-        const int c = t % nc, b = t / nc;  // column, block of 8 rows
-        const uint16_t *src = xg + (size_t)b * 8 * ldx + c;
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = (uint32_t)src[(2 * i) * ldx] | ((uint32_t)src[(2 * i + 1) * ldx] << 16);
-        int off;
-        if constexpr (T == Q6_K) {
-            const int g = (b >> 1) & 15;
-            off = (4 * (b >> 5) + 2 * (g >> 3) + (g & 1)) * VXSTRIDE + 32 * ((g >> 1) & 3) + 16 * (b & 1);
-        } else {
-            off = (b >> 3) * VXSTRIDE + 16 * (b & 7);
-        }
-        *reinterpret_cast<uint4 *>(planes + c * ps + off) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-}
-
 // DPP quad_perm broadcast of lane J of each quad (J = 0..3)
 template <int J>
 __device__ __forceinline__ float quad_bcast(float a) { return vdpp<J | (J << 2) | (J << 4) | (J << 6)>(a); }
@@ -201,13 +175,12 @@ __device__ __forceinline__ float4_t mfma1f32(float a, float b, float4_t c) {
 // PAIR (the SwiGLU epilogue): the workgroup's rows of W and then of ep.W2
 // form one schedule of 2R rows; row r's outputs combine the sums of rows r
 // and R + r.  EPI: the store applies ep's residual / fp16 options (else it is
-// the plain fp32 store).  x is [K][nct], y (and the residual) [N][nct]; the
-// nct columns are taken in ngrp groups of at most 4 * NCB (WIDE; otherwise
-// ngrp is 1 and the group loop compiles away).
-template <int T, int NCB, int RL, int D, bool PAIR, bool EPI, bool WIDE>
-__global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) verify_kernel(const uint8_t *__restrict__ W,
+// the plain fp32 store).  x is [K][nc], y (and the residual) [N][nc], nc at
+// most 4 * NCB.
+template <int T, int NCB, int RL, int D, bool PAIR, bool EPI>
+__global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI>())) verify_kernel(const uint8_t *__restrict__ W,
                                                                const uint16_t *__restrict__ x, void *y,
-                                                               int N, int K, int nct, int ngrp, int useg, int P,
+                                                               int N, int K, int nc, int useg, int P,
                                                                const Epilogue ep) {
     extern __shared__ __attribute__((aligned(16))) float vsm[];
     constexpr int G = vgroups<T>(), NC = 4 * NCB;
@@ -230,12 +203,8 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
     uint8_t *planes = reinterpret_cast<uint8_t *>(vsm + (size_t)quads_lane * P * 4 * nslot * NC);
     const int ps = useg * VXSTRIDE;  // bytes per column plane
     const int slot = 4 * wip + (blk >> 2);  // this lane's slot if it writes (blk % 4 == 0)
-    // the residuals of the first row this lane stores (lane 0 of each 16),
-    // first column group
-    if constexpr (!WIDE) ngrp = 1;
-    const int nc0 = nct / ngrp;  // width of group 0
-    // (three or four column blocks: no prefetch, the registers are taken by x)
-    constexpr bool RES0 = EPI && NCB < 3;
+    // the residuals of the first row this lane stores (lane 0 of each 16)
+    constexpr bool RES0 = EPI;
     float res0[RES0 ? NC : 1];
 #pragma unroll
     for (int c = 0; c < (RES0 ? NC : 1); ++c) res0[c] = 0.f;
@@ -243,12 +212,8 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
         if (ep.res && (tid & 15) == 0 && (tid >> 4) < R)
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-                if (c < nc0) res0[c] = ep.res[(size_t)(r0 + (tid >> 4)) * nct + c];
+                if (c < nc) res0[c] = ep.res[(size_t)(r0 + (tid >> 4)) * nc + c];
 
-  for (int grp = 0; grp < ngrp; ++grp) {
-    // columns [c0, c0 + nc) of x, y and the residual
-    const int c0 = grp * nct / ngrp, nc = (grp + 1) * nct / ngrp - c0;
-    if (grp > 0) __syncthreads();  // the previous group's partial sums are read everywhere
     for (int s0 = 0; s0 < U; s0 += useg) {
         const int ns = min(useg, U - s0);
         const bool col_ok = uc < ns;
@@ -258,26 +223,19 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
 
         // x of the segment into the column planes
         if (s0 > 0) __syncthreads();  // the previous segment's x is in registers everywhere
-        if constexpr (WIDE) {
-            stage_planes_strided<T>(x + (size_t)s0 * 64 * nct + c0, nct, nc, planes, ps, ns, tid);
-        } else {
-            const uint8_t *xg = reinterpret_cast<const uint8_t *>(x + (size_t)s0 * 64 * nc);
-            switch (nc) {
-            case 2: stage_planes<T, 2>(xg, planes, ps, ns, tid); break;
-            case 3: if constexpr (NC >= 4) stage_planes<T, 3>(xg, planes, ps, ns, tid); break;
-            case 4: if constexpr (NC >= 4) stage_planes<T, 4>(xg, planes, ps, ns, tid); break;
-            case 5: if constexpr (NC >= 8) stage_planes<T, 5>(xg, planes, ps, ns, tid); break;
-            case 6: if constexpr (NC >= 8) stage_planes<T, 6>(xg, planes, ps, ns, tid); break;
-            case 7: if constexpr (NC >= 8) stage_planes<T, 7>(xg, planes, ps, ns, tid); break;
-            default: if constexpr (NC >= 8) stage_planes<T, 8>(xg, planes, ps, ns, tid); break;
-            }
+        const uint8_t *xg = reinterpret_cast<const uint8_t *>(x + (size_t)s0 * 64 * nc);
+        switch (nc) {
+        case 2: stage_planes<T, 2>(xg, planes, ps, ns, tid); break;
+        case 3: if constexpr (NC >= 4) stage_planes<T, 3>(xg, planes, ps, ns, tid); break;
+        case 4: if constexpr (NC >= 4) stage_planes<T, 4>(xg, planes, ps, ns, tid); break;
+        case 5: if constexpr (NC >= 8) stage_planes<T, 5>(xg, planes, ps, ns, tid); break;
+        case 6: if constexpr (NC >= 8) stage_planes<T, 6>(xg, planes, ps, ns, tid); break;
+        case 7: if constexpr (NC >= 8) stage_planes<T, 7>(xg, planes, ps, ns, tid); break;
+        default: if constexpr (NC >= 8) stage_planes<T, 8>(xg, planes, ps, ns, tid); break;
         }
         __syncthreads();
-        // Launches of up to 8 columns issue the segment's first ring of
-        // weight loads here, before the x reads of the planes (2-7% faster
-        // at 2-8 columns); the column-group variant issues it after them
-        // (4 column blocks of x leave no room: 2.5% slower).
-        constexpr bool EARLY = !WIDE;
+        // The segment's first ring of weight loads is issued here, before
+        // the x reads of the planes (2-7% faster at 2-8 columns).
         const UnitAddr<T, GGUF> ua(K >> 8, u);
         auto load_quad = [&](Unit<T> &dst, int qi) {  // qi: the lane's quad index
             if constexpr (PAIR) {
@@ -292,9 +250,8 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
             }
         };
         Unit<T> buf[DD];
-        if constexpr (EARLY)
 #pragma unroll
-            for (int p = 0; p < DD; ++p) load_quad(buf[p], p);
+        for (int p = 0; p < DD; ++p) load_quad(buf[p], p);
         // this lane's columns j, j+4 in registers; group sums of all columns of the unit
         uint32_t xr[NCB][32];
         // Q4_K/Q5_K: the sums of this lane's own columns (4cb + j) over the
@@ -328,7 +285,7 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
             }
         }
         for (int i0 = 0; i0 < quads_lane; i0 += RL) {
-            if (!EARLY || i0 > 0)
+            if (i0 > 0)
 #pragma unroll
                 for (int p = 0; p < DD; ++p) load_quad(buf[p], i0 + p);
 #pragma unroll
@@ -515,9 +472,9 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
             for (int c = 0; c < NC; ++c) a[c] = silu(a[c]) * b[c];
         }
         if (rok && s16 == 0) {
-            const size_t o = (size_t)(r0 + rr) * nct + c0;
+            const size_t o = (size_t)(r0 + rr) * nc;
             if constexpr (EPI) {
-                const bool first = RES0 && rr == (tid >> 4) && grp == 0;
+                const bool first = RES0 && rr == (tid >> 4);
 #pragma unroll
                 for (int c = 0; c < NC; ++c)
                     if (c < nc) {
@@ -532,7 +489,6 @@ __global__ void __launch_bounds__((v_bound<T, NCB, RL, PAIR, EPI, WIDE>())) veri
             }
         }
     }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -556,7 +512,7 @@ static bool vgeo(int64_t N, int64_t K, int nc, int ncb, int mult, int short_thre
     const int long_threads = ncb == 1 ? v_max_threads<1>() : v_max_threads<2>();
     short_threads = std::max(short_threads, long_threads);
     const int max_waves = long_threads / 64;
-    const int cap = (int)std::min<int64_t>(16 * max_waves, (nc > 8 ? V_RAW_BUDGET_WIDE : V_RAW_BUDGET) / xs) / 16 * 16;
+    const int cap = (int)std::min<int64_t>(16 * max_waves, V_RAW_BUDGET / xs) / 16 * 16;
     if (cap < 16) return false;
     const int64_t nseg = (U + cap - 1) / cap;
     g.useg = (int)(((U + nseg - 1) / nseg + 15) / 16 * 16);
@@ -603,64 +559,35 @@ static hipError_t v_allow_lds() {
     return lds_opt_in<Kernel>(V_LDS_MAX);
 }
 
-template <int T, int NCB, int RL, bool PAIR, bool EPI, bool WIDE>
+template <int T, int NCB, int RL, bool PAIR, bool EPI>
 static hipError_t launch_ve(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, const VGeo &g,
                             const Epilogue &ep, hipStream_t st) {
     constexpr int D = 2;
-    if (g.threads > v_bound<T, NCB, RL, PAIR, EPI, WIDE>()) return hipErrorInvalidValue;
-    const hipError_t e = v_allow_lds<verify_kernel<T, NCB, RL, D, PAIR, EPI, WIDE>>();
+    if (g.threads > v_bound<T, NCB, RL, PAIR, EPI>()) return hipErrorInvalidValue;
+    const hipError_t e = v_allow_lds<verify_kernel<T, NCB, RL, D, PAIR, EPI>>();
     if (e != hipSuccess) return e;
-    const int ngrp = (nc + 4 * NCB - 1) / (4 * NCB);
-    hipLaunchKernelGGL((verify_kernel<T, NCB, RL, D, PAIR, EPI, WIDE>), dim3((unsigned)g.G), dim3(g.threads), g.lds,
-                       st, (const uint8_t *)W, (const uint16_t *)x, y, (int)N, (int)K, nc, ngrp, g.useg, g.P, ep);
+    hipLaunchKernelGGL((verify_kernel<T, NCB, RL, D, PAIR, EPI>), dim3((unsigned)g.G), dim3(g.threads), g.lds,
+                       st, (const uint8_t *)W, (const uint16_t *)x, y, (int)N, (int)K, nc, g.useg, g.P, ep);
     return hipGetLastError();
 }
 
-// Plain launches run a body without the epilogue's store options.  More
-// than 8 columns run the group loop with three or four column blocks
-// (groups of 9 to 16 columns, vplan), with the general store.
+// Plain launches run a body without the epilogue's store options.
 template <int T, int NCB, int RL, bool PAIR>
 static hipError_t launch_v(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, const VGeo &g,
                            const Epilogue &ep, hipStream_t st) {
-    if constexpr (NCB >= 3) {
-        if (nc > 8) return launch_ve<T, NCB, RL, PAIR, true, true>(W, x, y, N, K, nc, g, ep, st);
-        return hipErrorInvalidValue;
-    } else {
-        if (nc > 8) return hipErrorInvalidValue;
-        if (!PAIR && !ep.res && !ep.f16)
-            return launch_ve<T, NCB, RL, false, false, false>(W, x, y, N, K, nc, g, ep, st);
-        return launch_ve<T, NCB, RL, PAIR, true, false>(W, x, y, N, K, nc, g, ep, st);
-    }
+    static_assert(NCB == 1 || NCB == 2, "one or two column blocks");
+    if (nc > 8) return hipErrorInvalidValue;
+    if (!PAIR && !ep.res && !ep.f16) return launch_ve<T, NCB, RL, false, false>(W, x, y, N, K, nc, g, ep, st);
+    return launch_ve<T, NCB, RL, PAIR, true>(W, x, y, N, K, nc, g, ep, st);
 }
 
-// How a launch takes its nc columns: up to 8 in one group of one or two
-// column blocks; more in ngrp groups of widths differing by at most one
-// (c0 = grp * nc / ngrp), each group 9 to 16 wide with three or four blocks
-// (ngrp = ceil(nc / (4 * ncb))).  Each group streams W once, and a unit's
-// unpacking and matrix work grow with the blocks, so the plan takes the
-// fewest groups x blocks, then the fewest groups: 9-12 columns one group of
-// three blocks, 13-16 one of four, 17-24 two of three, 25-32 two of four
-// (measured at 17408 x 5120 Q4_K: 12 columns 59.8 us as two groups of two
-// blocks, 47.1 us as one of four).
-struct VPlan { int ngrp, ncb, width; };
-static VPlan vplan(int nc) {
-    if (nc <= 8) return {1, nc > 4 ? 2 : 1, nc};
-    VPlan best{0, 0, 0};
-    for (int ngrp = (nc + 15) / 16; ngrp <= (nc + 8) / 9; ++ngrp) {
-        const int width = (nc + ngrp - 1) / ngrp, ncb = (width + 3) / 4;
-        if (ncb < 3 || ncb > 4 || (nc + 4 * ncb - 1) / (4 * ncb) != ngrp) continue;
-        if (!best.ngrp || ngrp * ncb < best.ngrp * best.ncb) best = {ngrp, ncb, width};
-    }
-    return best;
-}
+// Up to 8 columns: one or two column blocks of 4 (wider calls run on the
+// 16x16x16 tiles of qk_verify16.h).
 
-// Rounds of up to 8 quads; three or four column blocks up to 4 (their
-// registers are mostly x, and fewer instances keep the build short), four
-// blocks of Q5_K up to 2 and of Q6_K 1 (longer rounds spill: the Q6_K
-// accumulators alone are 64 registers).
+// Rounds of up to 8 quads.
 template <int T, int NCB>
 constexpr int v_max_rl() {
-    return NCB < 3 ? V_MAX_RL : NCB == 3 ? 4 : T == Q6_K ? 1 : T == Q5_K ? 2 : 4;
+    return V_MAX_RL;
 }
 
 template <int T, int NCB, bool PAIR>
@@ -669,8 +596,8 @@ static hipError_t verify_dispatch(const void *W, const void *x, void *y, int64_t
     VGeo g;
     // plain launches of up to 8 columns may take the larger workgroups of short rounds
     const bool plain = !PAIR && !ep.res && !ep.f16 && nc <= 8;
-    const int short_threads = plain ? v_bound<T, NCB, 1, false, false, false>() : v_max_threads<NCB>();
-    if (!vgeo(N, K, vplan(nc).width, NCB, PAIR ? 2 : 1, short_threads, v_short_rl<T>(), v_max_rl<T, NCB>(), g))
+    const int short_threads = plain ? v_bound<T, NCB, 1, false, false>() : v_max_threads<NCB>();
+    if (!vgeo(N, K, nc, NCB, PAIR ? 2 : 1, short_threads, v_short_rl<T>(), v_max_rl<T, NCB>(), g))
         return hipErrorInvalidValue;
     constexpr int MRL = v_max_rl<T, NCB>();
     switch (g.RL) {
@@ -699,23 +626,13 @@ static hipError_t verify_type(const void *W, const void *x, void *y, int64_t N, 
         if (nc > 8 && nc <= 32) return launch_v16<T>(W, x, y, N, K, nc, ep, st);
     if constexpr (T == Q6_K || T == IQ4_XS)
         if (nc >= V16Q6_MIN && nc <= 32) return launch_v16q6<T>(W, x, y, N, K, nc, ep, st);
-    const VPlan pl = vplan(nc);
-    if (ep.W2) {
-        switch (pl.ncb) {
-        case 1: return verify_dispatch<T, 1, true>(W, x, y, N, K, nc, ep, st);
-        case 2: return verify_dispatch<T, 2, true>(W, x, y, N, K, nc, ep, st);
-        case 3: return verify_dispatch<T, 3, true>(W, x, y, N, K, nc, ep, st);
-        case 4: return verify_dispatch<T, 4, true>(W, x, y, N, K, nc, ep, st);
-        default: return hipErrorInvalidValue;
-        }
-    }
-    switch (pl.ncb) {
-    case 1: return verify_dispatch<T, 1, false>(W, x, y, N, K, nc, ep, st);
-    case 2: return verify_dispatch<T, 2, false>(W, x, y, N, K, nc, ep, st);
-    case 3: return verify_dispatch<T, 3, false>(W, x, y, N, K, nc, ep, st);
-    case 4: return verify_dispatch<T, 4, false>(W, x, y, N, K, nc, ep, st);
-    default: return hipErrorInvalidValue;
-    }
+    if (nc < 2 || nc > 8) return hipErrorInvalidValue;
+    const int ncb = nc > 4 ? 2 : 1;
+    if (ep.W2)
+        return ncb == 1 ? verify_dispatch<T, 1, true>(W, x, y, N, K, nc, ep, st)
+                        : verify_dispatch<T, 2, true>(W, x, y, N, K, nc, ep, st);
+    return ncb == 1 ? verify_dispatch<T, 1, false>(W, x, y, N, K, nc, ep, st)
+                    : verify_dispatch<T, 2, false>(W, x, y, N, K, nc, ep, st);
 }
 
 }  // namespace qk

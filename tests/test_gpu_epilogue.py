@@ -34,8 +34,8 @@ def _residual(N, ncols, seed):
     return (np.random.default_rng([seed, 7]).standard_normal((N, ncols)) * 4).astype(np.float32)
 
 
-# 12 / 16 / 17 / 32 columns: one group of three and of four column blocks,
-# two groups of three and of four (the residual then read at the store)
+# 12 / 16 / 17 / 32 columns: the tile kernels, one and two groups of 16
+# columns (the residual read before the shares are added)
 @pytest.mark.parametrize("ncols", [1, 2, 5, 8, 12, 16, 17, 32])
 @pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
 @pytest.mark.parametrize("N,K", SHAPES)

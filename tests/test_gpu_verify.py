@@ -116,11 +116,10 @@ def test_verify_round_lengths_all_rows(qt, N, K, ncols):
     assert np.isfinite(y).all()
 
 
-# Wider verification: 9-16 columns in one group of three or four column
-# blocks (9, 12 / 13, 16), 17-32 in two groups of nearly equal width (17 ->
-# 8 + 9 and 24 -> 12 + 12 with three blocks, 25 -> 12 + 13 and 32 -> 16 + 16
-# with four), each staged from the strided rows of x and written to its
-# columns of y.
+# Wider verification on the 16x16x16 tiles: 9-16 columns in one group of 16
+# (the unused columns of the tile zero), 17-32 in two groups; K = 17408 takes
+# several segments of x planes (Q6_K / IQ4_XS: four), N = 5 and 37 leave
+# short tiles and idle waves.
 @pytest.mark.parametrize("ncols", [9, 12, 13, 16, 17, 24, 25, 32])
 @pytest.mark.parametrize("qt", TYPES, ids=lambda t: NAMES[t])
 @pytest.mark.parametrize("N,K", [(5, 512), (130, 5120), (37, 17408)])
