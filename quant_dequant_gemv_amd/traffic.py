@@ -60,12 +60,17 @@ def plan():
     from quant_dequant_gemv_amd import synth
     v = synth.VERIFY
     groups = [(STEP, [(e["qtype"], e["N"], e["K"], e["seed"], 1) for e in synth.Q4K_PROJECTIONS])]
-    for nc in (2, 4, 8, 16, 17):
-        groups.append((f"verify_kernel<Q4_K> {v['N']}x{v['K']} ncols {nc}", [(v["qtype"], v["N"], v["K"], v["seed"], nc)]))
+    for nc in (2, 4, 8, 16, 17):  # (9-32 columns: the 16x16x16 tile kernel)
+        kern = "verify_kernel" if nc <= 8 else "v16_kernel"
+        groups.append((f"{kern}<Q4_K> {v['N']}x{v['K']} ncols {nc}", [(v["qtype"], v["N"], v["K"], v["seed"], nc)]))
     for e in synth.MIXED:
         groups.append((f"gemv1_kernel<{synth.TYPE_NAMES[e['qtype']]}> {e['N']}x{e['K']}",
                        [(e["qtype"], e["N"], e["K"], e["seed"], 1)]))
     groups.append(("gemv1_kernel<IQ4_XS> 17408x5120", [(synth.IQ4_XS, 17408, 5120, 1003, 1)]))
+    q6 = synth.MIXED[0]  # Q6_K FFN down: four segments of x planes on the tiles
+    for nc in (16, 17):
+        groups.append((f"v16q6_kernel<Q6_K> {q6['N']}x{q6['K']} ncols {nc}", [(q6["qtype"], q6["N"], q6["K"], q6["seed"], nc)]))
+    groups.append(("v16q6_kernel<IQ4_XS> 17408x5120 ncols 17", [(synth.IQ4_XS, 17408, 5120, 1003, 17)]))
     return groups
 
 
