@@ -39,7 +39,7 @@ COMMANDS = """    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/traffic_fetch -o run 
     rocprofv3 --pmc WRITE_SIZE -d gpurun_out/traffic_write -o run -- python3 -m quant_dequant_gemv_amd.traffic run
     python3 -m quant_dequant_gemv_amd.traffic parse gpurun_out/traffic_fetch/run_results.db gpurun_out/traffic_write/run_results.db"""
 KERNEL_SOURCES = ["quant_dequant_gemv_amd/csrc/qk_kernels.hip", "quant_dequant_gemv_amd/csrc/qk_verify.h",
-                  "quant_dequant_gemv_amd/csrc/qk_format.h",
+                  "quant_dequant_gemv_amd/csrc/qk_verify16.h", "quant_dequant_gemv_amd/csrc/qk_format.h",
                   "quant_dequant_gemv_amd/csrc/qk_epilogue.h"]
 
 
