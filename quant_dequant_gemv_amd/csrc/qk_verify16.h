@@ -383,15 +383,23 @@ __device__ __forceinline__ void v16q6_copy(const uint16_t *__restrict__ x, int s
             hv[2 * i + 1] = v.y;
         }
         auto half = [&](int e) -> uint32_t { return (hv[e >> 1] >> (16 * (e & 1))) & 0xffffu; };
-        uint8_t *dst = planes + (size_t)sbl * NG * V16Q6_SB + ((n * 4 + qt) * 64 + 16 * g) * 16 + 8 * h;
+        if constexpr (NG == 1 && NCV < 16) {  // compact: NCV vectors per (n, t, g), 512 NCV bytes per superblock
+            uint8_t *dst = planes + (size_t)sbl * 512 * NCV + ((n * 4 + qt) * 4 + g) * NCV * 16 + 8 * h;
 #pragma unroll
-        for (int c = 0; c < 16 * NG; ++c) {
-            uint2 v = make_uint2(0u, 0u);
-            if (c < NCV) {  // rows 0, 2, 1, 3: the pattern order
-                v.x = half(0 * NCV + c) | (half(2 * NCV + c) << 16);
-                v.y = half(1 * NCV + c) | (half(3 * NCV + c) << 16);
+            for (int c = 0; c < NCV; ++c)  // rows 0, 2, 1, 3: the pattern order
+                *reinterpret_cast<uint2 *>(dst + c * 16) =
+                    make_uint2(half(0 * NCV + c) | (half(2 * NCV + c) << 16), half(1 * NCV + c) | (half(3 * NCV + c) << 16));
+        } else {
+            uint8_t *dst = planes + (size_t)sbl * NG * V16Q6_SB + ((n * 4 + qt) * 64 + 16 * g) * 16 + 8 * h;
+#pragma unroll
+            for (int c = 0; c < 16 * NG; ++c) {
+                uint2 v = make_uint2(0u, 0u);
+                if (c < NCV) {  // rows 0, 2, 1, 3: the pattern order
+                    v.x = half(0 * NCV + c) | (half(2 * NCV + c) << 16);
+                    v.y = half(1 * NCV + c) | (half(3 * NCV + c) << 16);
+                }
+                *reinterpret_cast<uint2 *>(dst + (c >> 4) * V16Q6_SB + (c & 15) * 16) = v;
             }
-            *reinterpret_cast<uint2 *>(dst + (c >> 4) * V16Q6_SB + (c & 15) * 16) = v;
         }
     }
 }
@@ -426,7 +434,7 @@ __device__ __forceinline__ void v16q6_stage(const uint16_t *__restrict__ x, int 
 // 4n + t, nibble h, and lane row g loads chunks g and 4 + g; the codebook
 // lookup gives the patterns kv 2^-24 (signed, exact) and the scale is
 // d 2^24 (ls - 32).
-template <int T_, int NG>
+template <int T_, int NG, bool CP>
 __global__ void __launch_bounds__(768) v16q6_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ x,
                                                     void *__restrict__ y, int N, int K, int nc, int segsb, int T,
                                                     int UG, Epilogue ep) {
@@ -450,6 +458,12 @@ __global__ void __launch_bounds__(768) v16q6_kernel(const uint8_t *__restrict__ 
     constexpr int SBB = T_ == Q6_K ? 210 : 136;
     const uint8_t *wrow = Wt + (size_t)min(row, r1 - 1) * (size_t)(S * SBB);
     uint8_t *planes = v16sm;
+    // CP (one group, fewer than 16 columns): compact planes of nc columns;
+    // the lanes of columns nc..15 read a zero vector after them (written
+    // here, ordered by the first segment's barrier).  At 16 columns the
+    // plane offsets are compile-time constants (immediate LDS offsets).
+    uint8_t *zero16 = planes + (size_t)segsb * 512 * nc;
+    if (CP && tid == 0) *reinterpret_cast<uint4 *>(zero16) = make_uint4(0u, 0u, 0u, 0u);
     v16_f4 acc[NG];
 #pragma unroll
     for (int cg = 0; cg < NG; ++cg) acc[cg] = v16_f4{0.f, 0.f, 0.f, 0.f};
@@ -507,7 +521,9 @@ __global__ void __launch_bounds__(768) v16q6_kernel(const uint8_t *__restrict__ 
 #pragma unroll
                             for (int cg = 0; cg < NG; ++cg)
                                 xv[cg] = *reinterpret_cast<const uint4 *>(
-                                    planes + ((size_t)sbl * NG + cg) * V16Q6_SB + ((n * 4 + qt) * 64 + lane) * 16);
+                                    CP ? (r < nc ? planes + (size_t)sbl * 512 * nc + (((n * 4 + qt) * 4 + g) * nc + r) * 16
+                                                 : zero16)
+                                       : planes + ((size_t)sbl * NG + cg) * V16Q6_SB + ((n * 4 + qt) * 64 + lane) * 16);
 #pragma unroll
                             for (int h = 0; h < 2; ++h) {
                                 uint32_t p0, p1;
@@ -594,7 +610,7 @@ __global__ void __launch_bounds__(768) v16q6_kernel(const uint8_t *__restrict__ 
     }
 }
 
-template <int T_, int NG>
+template <int T_, int NG, bool CP>
 static hipError_t launch_v16q6g(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
                               const Epilogue &ep, hipStream_t st) {
     const int cus = device_cus();
@@ -607,14 +623,17 @@ static hipError_t launch_v16q6g(const void *W, const void *x, void *y, int64_t N
     const int UG = T <= 1 ? 4 : T <= 3 ? (NG == 1 ? 2 : 4) : T <= 6 ? 2 : 1;
     const int threads = 64 * T * UG;
     const int64_t S = K / 256;
-    const int64_t smax = V16_PLANES / (NG * V16Q6_SB);  // superblocks per segment at most
+    // bytes per superblock: compact 512 per column (then a zero vector),
+    // else 8 KB per group of 16 columns
+    const int64_t sbb = CP ? 512 * nc : NG * V16Q6_SB, extra = CP ? 16 : 0;
+    const int64_t smax = (V16_PLANES - extra) / sbb;  // superblocks per segment at most
     const int64_t nseg = (S + smax - 1) / smax;
     const int segsb = (int)((S + nseg - 1) / nseg);
-    const size_t lds = std::max<size_t>((size_t)segsb * NG * V16Q6_SB, (size_t)threads * 16 * NG);
+    const size_t lds = std::max<size_t>((size_t)(segsb * sbb + extra), (size_t)threads * 16 * NG);
     if (T < 1 || T > 12 || threads > 768 || lds > 160 * 1024) return hipErrorInvalidValue;
-    const hipError_t e = lds_opt_in<v16q6_kernel<T_, NG>>(160 * 1024);
+    const hipError_t e = lds_opt_in<v16q6_kernel<T_, NG, CP>>(160 * 1024);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((v16q6_kernel<T_, NG>), dim3((unsigned)G), dim3(threads), lds, st, (const uint8_t *)W,
+    hipLaunchKernelGGL((v16q6_kernel<T_, NG, CP>), dim3((unsigned)G), dim3(threads), lds, st, (const uint8_t *)W,
                        (const uint16_t *)x, y, (int)N, (int)K, nc, segsb, T, UG, ep);
     return hipGetLastError();
 }
@@ -623,7 +642,9 @@ static hipError_t launch_v16q6g(const void *W, const void *x, void *y, int64_t N
 template <int T_>
 static inline hipError_t launch_v16q6(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
                                       const Epilogue &ep, hipStream_t st) {
-    return nc > 16 ? launch_v16q6g<T_, 2>(W, x, y, N, K, nc, ep, st) : launch_v16q6g<T_, 1>(W, x, y, N, K, nc, ep, st);
+    if (nc > 16) return launch_v16q6g<T_, 2, false>(W, x, y, N, K, nc, ep, st);
+    return nc < 16 ? launch_v16q6g<T_, 1, true>(W, x, y, N, K, nc, ep, st)
+                   : launch_v16q6g<T_, 1, false>(W, x, y, N, K, nc, ep, st);
 }
 
 }  // namespace qk
