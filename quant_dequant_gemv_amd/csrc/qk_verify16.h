@@ -65,7 +65,7 @@ template <> struct V16Fmt<Q5_K> { static constexpr int bytes = 176, qs = 48, qma
 // the x operands of lane l = c + 16g for sub-block sb -- halves 0..3 of the
 // first instruction (weights 8g + 0, 2, 1, 3 of the sub-block), halves 4..7
 // of the second (8g + 4, 6, 5, 7).
-template <int NCV>
+template <int NCV, bool CP = false>
 __device__ __forceinline__ void v16_copy(const uint16_t *__restrict__ x, int s0, int ns, uint8_t *planes, int tid,
                                          int nthr) {
     constexpr int NG = NCV > 16 ? 2 : 1;  // groups of 16 columns
@@ -94,6 +94,15 @@ __device__ __forceinline__ void v16_copy(const uint16_t *__restrict__ x, int s0,
         }
         // half e of the task is x[RPT rows][NCV]: row e / NCV, column e % NCV
         auto half = [&](int e) -> uint32_t { return (h[e >> 1] >> (16 * (e & 1))) & 0xffffu; };
+        if constexpr (CP) {  // compact: NCV vectors per (sub-block, g), 128 NCV bytes per unit
+            uint8_t *dst = planes + (size_t)ul * 128 * NCV + (sb * 4 + g) * NCV * 16;
+#pragma unroll
+            for (int c = 0; c < NCV; ++c)
+                *reinterpret_cast<uint4 *>(dst + c * 16) =
+                    make_uint4(half(0 * NCV + c) | (half(2 * NCV + c) << 16), half(1 * NCV + c) | (half(3 * NCV + c) << 16),
+                               half(4 * NCV + c) | (half(6 * NCV + c) << 16), half(5 * NCV + c) | (half(7 * NCV + c) << 16));
+            continue;
+        }
         uint8_t *dst = planes + (size_t)ul * NG * V16_UB + sb * 1024 + 16 * g * 16 + 8 * hf;
 #pragma unroll
         for (int c = 0; c < 16 * NG; ++c) {
@@ -119,14 +128,14 @@ __device__ __forceinline__ void v16_copy(const uint16_t *__restrict__ x, int s0,
     }
 }
 
-template <int NG>
+template <int NG, bool CP>
 __device__ __forceinline__ void v16_stage(const uint16_t *__restrict__ x, int nc, int s0, int ns, uint8_t *planes,
                                           int tid, int nthr) {
-#define V16_CASE(n) case n: v16_copy<n>(x, s0, ns, planes, tid, nthr); break;
+#define V16_CASE(n) case n: v16_copy<n, CP>(x, s0, ns, planes, tid, nthr); break;
     if constexpr (NG == 1) {
         switch (nc) {
         V16_CASE(9) V16_CASE(10) V16_CASE(11) V16_CASE(12) V16_CASE(13) V16_CASE(14) V16_CASE(15)
-        default: v16_copy<16>(x, s0, ns, planes, tid, nthr); break;
+        default: v16_copy<16>(x, s0, ns, planes, tid, nthr); break;  // (16 columns: never compact)
         }
     } else {
         switch (nc) {
@@ -138,7 +147,7 @@ __device__ __forceinline__ void v16_stage(const uint16_t *__restrict__ x, int nc
 #undef V16_CASE
 }
 
-template <int T_, int NG>
+template <int T_, int NG, bool CP>
 __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ x,
                                                    void *__restrict__ y, int N, int K, int nc, int useg, int T,
                                                    int UG, Epilogue ep) {
@@ -164,6 +173,11 @@ __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W,
     const uint8_t *wrow = Wt + (size_t)min(row, r1 - 1) * (size_t)((K >> 8) * SBB);
     const int U = K >> 6;
     uint8_t *planes = v16sm;
+    // CP (one group, fewer than 16 columns): compact planes of nc columns;
+    // the lanes of columns nc..15 read a zero vector after them (written
+    // here, ordered by the first segment's barrier)
+    uint8_t *zero16 = planes + (size_t)useg * 128 * nc;
+    if (CP && tid == 0) *reinterpret_cast<uint4 *>(zero16) = make_uint4(0u, 0u, 0u, 0u);
     v16_f4 acc[NG];
 #pragma unroll
     for (int cg = 0; cg < NG; ++cg) acc[cg] = v16_f4{0.f, 0.f, 0.f, 0.f};
@@ -189,7 +203,7 @@ __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W,
 #pragma unroll
             for (int k = 0; k < DD; ++k) load(buf[k], b0 + k);
         if (s0 > 0) __syncthreads();  // every wave is done with the previous segment's planes
-        v16_stage<NG>(x, nc, s0, ns, planes, tid, nthr);
+        v16_stage<NG, CP>(x, nc, s0, ns, planes, tid, nthr);
         __syncthreads();
         if (!busy) continue;
         for (int i0 = b0; i0 < b1; i0 += DD) {
@@ -214,9 +228,16 @@ __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W,
                         const float fh = kH.a * 0x1p-4f, eL = kL.e * 0x1p-24f, eH = kH.e * 0x1p-24f;
 #pragma unroll
                         for (int cg = 0; cg < NG; ++cg) {  // each group of 16 columns
-                            const uint8_t *blk = planes + ((size_t)(4 * sbl + k) * NG + cg) * V16_UB;
-                            const uint4 xl = *reinterpret_cast<const uint4 *>(blk + lane * 16);
-                            const uint4 xh = *reinterpret_cast<const uint4 *>(blk + 1024 + lane * 16);
+                            uint4 xl, xh;
+                            if constexpr (CP) {
+                                const uint8_t *ub = planes + (size_t)(4 * sbl + k) * 128 * nc + (g * nc + r) * 16;
+                                xl = *reinterpret_cast<const uint4 *>(r < nc ? ub : zero16);
+                                xh = *reinterpret_cast<const uint4 *>(r < nc ? ub + 64 * nc : zero16);
+                            } else {
+                                const uint8_t *blk = planes + ((size_t)(4 * sbl + k) * NG + cg) * V16_UB;
+                                xl = *reinterpret_cast<const uint4 *>(blk + lane * 16);
+                                xh = *reinterpret_cast<const uint4 *>(blk + 1024 + lane * 16);
+                            }
                             // low sub-block: weights (8g, 8g+2), (8g+1, 8g+3) of w0, then
                             // of w1 (the patterns formed again per group: fewer live
                             // registers)
@@ -298,7 +319,7 @@ __global__ void __launch_bounds__(768) v16_kernel(const uint8_t *__restrict__ W,
 // N has fewer tiles (or more than 8 per CU); 1, 2 or 4 shares per tile (at
 // most 12 waves: 168 registers); segments of at most 160 KB of planes, as
 // even as possible, in whole superblocks.
-template <int T_, int NG>
+template <int T_, int NG, bool CP>
 static hipError_t launch_v16g(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc,
                               const Epilogue &ep, hipStream_t st) {
     const int cus = device_cus();
@@ -309,14 +330,16 @@ static hipError_t launch_v16g(const void *W, const void *x, void *y, int64_t N, 
     const int UG = T <= 3 ? 4 : T <= 6 ? 2 : 1;  // at most 12 waves (168 registers)
     const int threads = 64 * T * UG;
     const int64_t U = K / 64;
-    const int64_t smax = V16_PLANES / (NG * V16_UB) / 4 * 4;  // units per segment at most
+    // bytes per unit: compact 128 per column (then a zero vector), else 2 KB per group of 16 columns
+    const int64_t ubb = CP ? 128 * nc : NG * V16_UB, extra = CP ? 16 : 0;
+    const int64_t smax = (V16_PLANES - extra) / ubb / 4 * 4;  // units per segment at most
     const int64_t nseg = (U + smax - 1) / smax;
     const int useg = (int)(((U + nseg - 1) / nseg + 3) / 4 * 4);  // whole superblocks
-    const size_t lds = std::max<size_t>((size_t)useg * NG * V16_UB, (size_t)threads * 16 * NG);  // (planes, then the shares)
+    const size_t lds = std::max<size_t>((size_t)(useg * ubb + extra), (size_t)threads * 16 * NG);  // (planes, then the shares)
     if (T < 1 || T > 12 || threads > 768 || lds > 160 * 1024) return hipErrorInvalidValue;
-    const hipError_t e = lds_opt_in<v16_kernel<T_, NG>>(160 * 1024);
+    const hipError_t e = lds_opt_in<v16_kernel<T_, NG, CP>>(160 * 1024);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((v16_kernel<T_, NG>), dim3((unsigned)G), dim3(threads), lds, st, (const uint8_t *)W,
+    hipLaunchKernelGGL((v16_kernel<T_, NG, CP>), dim3((unsigned)G), dim3(threads), lds, st, (const uint8_t *)W,
                        (const uint16_t *)x, y, (int)N, (int)K, nc, useg, T, UG, ep);
     return hipGetLastError();
 }
@@ -325,7 +348,16 @@ static hipError_t launch_v16g(const void *W, const void *x, void *y, int64_t N, 
 template <int T_>
 static hipError_t launch_v16(const void *W, const void *x, void *y, int64_t N, int64_t K, int nc, const Epilogue &ep,
                              hipStream_t st) {
-    return nc > 16 ? launch_v16g<T_, 2>(W, x, y, N, K, nc, ep, st) : launch_v16g<T_, 1>(W, x, y, N, K, nc, ep, st);
+    if (nc > 16) return launch_v16g<T_, 2, false>(W, x, y, N, K, nc, ep, st);
+    // compact planes only where they save K segments (their addressing costs
+    // 1-4% where the segment count is the same)
+    const int64_t U = K / 64;
+    auto nseg = [&](int64_t ubb, int64_t extra) {
+        const int64_t smax = (V16_PLANES - extra) / ubb / 4 * 4;
+        return (U + smax - 1) / smax;
+    };
+    if (nc < 16 && nseg(128 * nc, 16) < nseg(V16_UB, 0)) return launch_v16g<T_, 1, true>(W, x, y, N, K, nc, ep, st);
+    return launch_v16g<T_, 1, false>(W, x, y, N, K, nc, ep, st);
 }
 
 // ---------------------------------------------------------------------------
