@@ -108,13 +108,9 @@ enum {
  *   y      device pointer to N*ncols fp32 values, 4-byte aligned (written)
  *   N      rows (output features), >= 1
  *   K      columns of W (input features), a multiple of 256
- *   ncols  columns of x and y, 1..32: 1 is the decode GEMV, 2..16 the
- *          few-column verify form with W read once per call; 17..32 take
- *          the columns in two groups of (nearly) equal width inside one
- *          launch, each group streaming W (the B70 plan's checklist asks
- *          for verifier widths up to 17) -- the calls of this library
- *          take 9..32 columns in one pass over W (each of W and W2 read
- *          once by qk_gemv_swiglu)
+ *   ncols  columns of x and y, 1..32: 1 is the decode GEMV, 2..32 the
+ *          few-column verify form with W read once per call (the B70
+ *          plan's checklist asks for verifier widths up to 17)
  *   stream hipStream_t to enqueue on
  *
  * y must not overlap W or x (QK_EINVAL_PTR): other workgroups are still

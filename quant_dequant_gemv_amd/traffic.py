@@ -203,8 +203,8 @@ def markdown(out: dict, reps: int = REPS) -> str:
         lines.append(f"| `{name}` | {f['groups'][name]['kib_mean']:.1f} | {w['groups'][name]['kib_mean']:.1f} | "
                      f"{out['per_launch_bytes'][name]} | {out['algorithmic_bytes'][name]} | {out['ratios'][name]:.4f} |")
     lines += ["", "A ratio near 1 means every weight byte is fetched from HBM once per launch (the verify form "
-              "up to 8 columns included: W is read once for all its columns; wider calls stream W once per "
-              "column group, and the ratio above 1 is what the caches did not absorb).  Kernel source hash " +
+              "included, at every width: W is read once for all its columns; the ratio above 1 is what the "
+              "caches did not absorb).  Kernel source hash " +
               out["kernel_hash"] +
               " (bench.py reports `roofline.traffic` from profiles/traffic.json only while the sources hash the "
               "same).", ""]
