@@ -68,7 +68,9 @@ def plan():
             ("gemv1_kernel<Q5_K> 5120x6144", Q5, 5120, 6144, 5, 1),
             ("gemv1_kernel<IQ4_XS> 17408x5120", IQ4, 17408, 5120, 1003, 1),
             ("verify_kernel<Q4_K> 17408x5120 ncols 8", Q4, 17408, 5120, 6, 8),
-            ("verify_kernel<Q6_K> 5120x17408 ncols 8", Q6, 5120, 17408, 4, 8)]
+            ("verify_kernel<Q6_K> 5120x17408 ncols 8", Q6, 5120, 17408, 4, 8),
+            ("v16_kernel<Q4_K> 17408x5120 ncols 16", Q4, 17408, 5120, 6, 16),
+            ("v16q6_kernel<Q6_K> 5120x17408 ncols 16", Q6, 5120, 17408, 4, 16)]
 
 
 def run(reps: int = REPS) -> None:
